@@ -1,0 +1,358 @@
+"""Pins for the fp64 oracle against facts fixed by the pages and by mathematics.
+
+Each test checks the oracle against something other than itself: numbers the
+pages print, closed forms, a library routine (torch's fp64 CPU attention) for
+the special cases that reduce to it, an exact brute-force enumeration, and
+invariants of the definition. Citations name the PaperTrace page "2.1.3 MoBA"
+(yayajjiang.github.io) unless stated otherwise.
+"""
+import itertools
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _load(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _sdpa_rows(q, k, v, mask, scale):
+    """torch fp64 CPU attention with an explicit boolean mask [Hq, N, N]."""
+    N, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    qt = torch.from_numpy(np.asarray(q, np.float64)).permute(1, 0, 2)
+    kt = torch.from_numpy(np.asarray(k, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    vt = torch.from_numpy(np.asarray(v, np.float64)).permute(1, 0, 2).repeat_interleave(G, 0)
+    o = torch.nn.functional.scaled_dot_product_attention(
+        qt.contiguous(), kt.contiguous(), vt.contiguous(), attn_mask=torch.from_numpy(mask),
+        scale=scale)
+    return o.permute(1, 0, 2).numpy()
+
+
+def _f32(x):
+    return np.asarray(x, np.float32)
+
+
+# ---------------------------------------------------------------- P1, P2 ---
+def _worked_inputs(x=7.0, y=-3.0, a=-5.0, b=8.0):
+    g = _load("worked_example.json")
+    keys = [x if t is None else t for t in g["keys"]]
+    vals = list(g["values"])
+    vals[0], vals[1], vals[5] = a, b, y
+    N = g["N"]
+    q = _f32(np.full((N, 1, 1), g["q_row"]))
+    return g, q, _f32(keys).reshape(N, 1, 1), _f32(vals).reshape(N, 1, 1)
+
+
+def test_p1_worked_example_matches_printed_numbers():
+    """Section 2 worked example: selection, weights and output as printed."""
+    g, q, k, v = _worked_inputs()
+    pr = g["printed"]
+    sel, o, _ = oracle.rows(q, k, v, g["B"], g["k"], [g["row"]], [0], scale=g["scale"])
+    assert list(sel[0]) == pr["selected_blocks"]
+    tol = 0.5 * 10 ** -pr["printed_decimals"]
+    assert abs(o[0, 0] - pr["output"]) <= tol
+    # block scores as printed (means 1 and 3)
+    kb = oracle.block_means(k, g["B"])
+    assert list(kb[0, :2, 0]) == pr["block_scores"]
+    # the printed weights: recover them from the oracle by one-hot values
+    w = []
+    for r in pr["candidate_rows"]:
+        onehot = np.zeros_like(v)
+        onehot[r] = 1.0
+        w.append(oracle.rows(q, k, onehot, g["B"], g["k"], [g["row"]], [0], scale=1.0)[1][0, 0])
+    assert np.allclose(w, pr["weights"], atol=tol, rtol=0)
+    assert abs(sum(w) - 1.0) < 1e-15
+    # closed form: common denominator 1 + e^-2 + e^-3 after subtracting the max logit 4
+    den = 1 + math.exp(-2) + math.exp(-3)
+    assert abs(o[0, 0] - (10 + 20 * math.exp(-2) + 30 * math.exp(-3)) / den) < 1e-12
+
+
+@pytest.mark.parametrize("x,y,a,b", [(100.0, 5.0, 0.0, 0.0), (-50.0, 1e3, 77.0, -9.0)])
+def test_p1_invariant_to_unseen_entries(x, y, a, b):
+    """The future key/value of the own block and the unselected block never matter."""
+    g, q, k, v = _worked_inputs(x, y, a, b)
+    _, o, _ = oracle.rows(q, k, v, g["B"], g["k"], [g["row"]], [0], scale=1.0)
+    assert abs(o[0, 0] - 11.982153) < 1e-6
+
+
+def test_p2_naive_sum_differs():
+    """Section 2: adding separately normalised branches is wrong (41.19 vs 11.98)."""
+    g, q, k, v = _worked_inputs()
+    _, o_naive, _ = oracle.rows(q, k, v, 2, 2, [4], [0], scale=1.0, mode=oracle.MODE_NAIVE)
+    hist = (10 + 20 * math.exp(-2)) / (1 + math.exp(-2))
+    assert abs(o_naive[0, 0] - (hist + 30.0)) < 1e-12
+    assert abs(o_naive[0, 0] - 41.192029) < 1e-6
+    _, o, _ = oracle.rows(q, k, v, 2, 2, [4], [0], scale=1.0)
+    assert abs(o_naive[0, 0] - o[0, 0]) > 29
+
+
+def test_p2_naive_differs_on_random_rows_with_history():
+    q, k, v = synth.random_qkv(64, 2, 1, 8, seed=11)
+    r, h = oracle.all_rows(64, 2)
+    sel, o, _ = oracle.rows(q, k, v, 8, 3, r, h)
+    _, on, _ = oracle.rows(q, k, v, 8, 3, r, h, mode=oracle.MODE_NAIVE)
+    has_hist = r >= 8
+    diff = np.abs(on - o).max(axis=1)
+    assert np.all(diff[has_hist] > 1e-3)
+    assert np.all(diff[~has_hist] < 1e-14)
+
+
+# ---------------------------------------------------------------- P3, P5 ---
+def _causal_mask(N, Hq):
+    m = np.tril(np.ones((N, N), bool))
+    return np.broadcast_to(m, (Hq, N, N)).copy()
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,d,B,k", [(40, 2, 1, 8, 8, 5), (33, 4, 2, 16, 4, 9),
+                                              (24, 1, 1, 4, 32, 1), (50, 3, 3, 8, 7, 8)])
+def test_p3_full_attention_when_k_covers_all_blocks(N, Hq, Hkv, d, B, k):
+    """Section 4: when k covers every legal block, MoBA is causal full attention."""
+    assert k * B >= N
+    q, kk, v = synth.random_qkv(N, Hq, Hkv, d, seed=N * 7 + k)
+    scale = 0.37
+    sel, o = oracle.prefill(q, kk, v, B, k, scale=scale)
+    ref = _sdpa_rows(q, kk, v, _causal_mask(N, Hq), scale)
+    assert np.max(np.abs(o - ref)) < 1e-12
+    r, h = oracle.all_rows(N, Hq)
+    o2 = oracle.causal_full(q, kk, v, r, h, scale=scale).reshape(N, Hq, d)
+    assert np.max(np.abs(o2 - ref)) < 1e-12
+
+
+def test_p5_block_size_one_is_token_topk():
+    """B = 1: each query keeps its own token and the k-1 best earlier tokens by q.k."""
+    N, d, k = 14, 4, 4
+    q, kk, v = synth.random_qkv(N, 1, 1, d, seed=5)
+    sel, o = oracle.prefill(q, kk, v, 1, k, scale=1.0)
+    for p in range(N):
+        s = [float(np.dot(q[p, 0].astype(np.float64), kk[j, 0].astype(np.float64))) for j in range(p)]
+        order = sorted(range(p), key=lambda j: (-s[j], j))[: k - 1]
+        keep = sorted(order) + [p]
+        assert list(sel[p, 0, : len(keep)]) == keep
+        z = np.array([np.dot(q[p, 0].astype(np.float64), kk[j, 0].astype(np.float64)) for j in keep])
+        w = np.exp(z - z.max())
+        w /= w.sum()
+        ref = (w[:, None] * v[keep, 0].astype(np.float64)).sum(0)
+        assert np.max(np.abs(o[p, 0] - ref)) < 1e-13
+
+
+def test_p5_k_one_is_block_diagonal_causal():
+    """k = 1: only the own block, causally — block-diagonal causal attention."""
+    N, Hq, Hkv, d, B = 45, 2, 1, 8, 6
+    q, kk, v = synth.random_qkv(N, Hq, Hkv, d, seed=3)
+    sel, o = oracle.prefill(q, kk, v, B, 1, scale=0.5)
+    blk = np.arange(N) // B
+    m = np.tril(np.ones((N, N), bool)) & (blk[:, None] == blk[None, :])
+    ref = _sdpa_rows(q, kk, v, np.broadcast_to(m, (Hq, N, N)).copy(), 0.5)
+    assert np.max(np.abs(o - ref)) < 1e-12
+    assert np.all(sel[:, :, 0] == blk[:, None])
+
+
+def test_p5_block_covers_sequence_is_causal_full():
+    N, d = 30, 8
+    q, kk, v = synth.random_qkv(N, 2, 2, d, seed=4)
+    _, o = oracle.prefill(q, kk, v, 64, 3, scale=0.3)
+    ref = _sdpa_rows(q, kk, v, _causal_mask(N, 2), 0.3)
+    assert np.max(np.abs(o - ref)) < 1e-12
+
+
+# ---------------------------------------------------------------------- P4 ---
+def _brute(q, k, v, B, topk, scale):
+    """Exact enumeration: every candidate set, Fractions for the gate, loops for attention."""
+    N, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    sel_all, o_all = [], []
+    for p in range(N):
+        for h in range(Hq):
+            g = h // G
+            c = p // B
+            qf = [Fraction(float(x)) for x in q[p, h]]
+            scores = []
+            for i in range(c):
+                mean = [sum(Fraction(float(k[j, g, t])) for j in range(i * B, (i + 1) * B)) / B
+                        for t in range(d)]
+                scores.append(sum(a * b for a, b in zip(qf, mean)))
+            m = min(topk - 1, c)
+            best, best_sum = None, None
+            for combo in itertools.combinations(range(c), m):
+                ssum = sum((scores[i] for i in combo), Fraction(0))
+                if best is None or ssum > best_sum or (ssum == best_sum and combo < best):
+                    best, best_sum = combo, ssum
+            keys = [j for i in best for j in range(i * B, (i + 1) * B)]
+            keys += list(range(c * B, p + 1))
+            z = []
+            for j in keys:
+                z.append(scale * sum(float(q[p, h, t]) * float(k[j, g, t]) for t in range(d)))
+            mx = max(z)
+            w = [math.exp(x - mx) for x in z]
+            den = sum(w)
+            o = [sum(w[i] * float(v[j, g, t]) for i, j in enumerate(keys)) / den for t in range(d)]
+            sel_all.append(list(best) + [c] + [-1] * (topk - m - 1))
+            o_all.append(o)
+    return np.array(sel_all), np.array(o_all)
+
+
+@pytest.mark.parametrize("case", range(10))
+def test_p4_brute_force(case):
+    rng = np.random.default_rng(100 + case)
+    B = int(rng.integers(1, 5))
+    N = int(rng.integers(2, 17 if B == 1 else 33))
+    topk = int(rng.integers(1, 6))
+    d = int(rng.integers(1, 5))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 3))
+    integer = case % 2 == 0  # integer keys force exact gate ties
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=case, integer=integer)
+    scale = float(rng.uniform(0.2, 1.5))
+    sel, o = oracle.prefill(q, k, v, B, topk, scale=scale)
+    bsel, bo = _brute(q, k, v, B, topk, scale)
+    assert np.array_equal(sel.reshape(-1, topk), bsel)
+    assert np.max(np.abs(o.reshape(-1, d) - bo)) < 1e-12
+
+
+# ---------------------------------------------------------------------- P6 ---
+def test_p6_zero_keys_tie_to_lowest_blocks():
+    """K == 0: every score and logit ties; the lowest blocks win and O is a plain mean."""
+    N, Hq, d, B, topk = 40, 2, 8, 4, 4
+    q, _, v = synth.random_qkv(N, Hq, 1, d, seed=9)
+    k = np.zeros((N, 1, d), np.float32)
+    sel, o = oracle.prefill(q, k, v, B, topk)
+    for p in range(N):
+        c = p // B
+        m = min(topk - 1, c)
+        want = list(range(m)) + [c] + [-1] * (topk - m - 1)
+        keys = list(range(m * B)) + list(range(c * B, p + 1))
+        mean = v[keys, 0].astype(np.float64).mean(0)
+        for h in range(Hq):
+            assert list(sel[p, h]) == want
+            assert np.max(np.abs(o[p, h] - mean)) < 1e-14
+
+
+def test_p6_negative_zero_equals_positive_zero():
+    N, d, B = 24, 4, 4
+    q, _, v = synth.random_qkv(N, 1, 1, d, seed=2)
+    k = np.zeros((N, 1, d), np.float32)
+    k[: 2 * B] = -0.0  # blocks 0 and 1 hold -0.0, the rest +0.0
+    sel, _ = oracle.prefill(q, k, v, B, 3)
+    assert list(sel[N - 1, 0]) == [0, 1, 5]
+
+
+# ---------------------------------------------------------------------- P7 ---
+def test_p7_recency_gate_is_block_sliding_window():
+    """Section 3: a gate that always prefers recent blocks yields a blocked window."""
+    N, Hq, d, B, topk = 64, 2, 8, 8, 3
+    rng = np.random.default_rng(7)
+    u = rng.standard_normal(d)
+    u /= np.linalg.norm(u)
+    k = rng.standard_normal((N, 1, d)) * 0.05
+    k += (np.arange(N) // B)[:, None, None] * 2.0 * u[None, None, :]
+    q = np.abs(rng.standard_normal((N, Hq, 1))) * u[None, None, :] + 0.0
+    q, k = _f32(q), _f32(k)
+    v = _f32(rng.standard_normal((N, 1, d)))
+    sel, o = oracle.prefill(q, k, v, B, topk, scale=0.25)
+    blk = np.arange(N) // B
+    win = (blk[None, :] >= blk[:, None] - (topk - 1)) & (blk[None, :] <= blk[:, None])
+    m = np.tril(np.ones((N, N), bool)) & win
+    ref = _sdpa_rows(q, k, v, np.broadcast_to(m, (Hq, N, N)).copy(), 0.25)
+    assert np.max(np.abs(o - ref)) < 1e-12
+    for p in range(N):
+        c = p // B
+        hist = list(range(max(0, c - topk + 1), c))
+        assert list(sel[p, 0, : len(hist) + 1]) == hist + [c]
+
+
+# ---------------------------------------------------------------------- P8 ---
+def test_p8_mean_dilution_routes_to_diffuse_block():
+    """Section 5.2: one key scoring 8 in 256 averages to 0.03125 < 0.05."""
+    g = _load("dilution.json")
+    B = g["B"]
+    N = 3 * B
+    k = np.zeros((N, 1, 1), np.float32)
+    k[0, 0, 0] = g["block_a"]["spike"]
+    k[B: 2 * B, 0, 0] = g["block_b"]["all"]
+    q = np.ones((N, 1, 1), np.float32)
+    v = np.ones((N, 1, 1), np.float32)
+    kb = oracle.block_means(k, B)
+    assert kb[0, 0, 0] == g["printed"]["score_a"]
+    assert abs(kb[0, 1, 0] - g["printed"]["score_b"]) < 1e-8
+    sel, _, gap = oracle.rows(q, k, v, B, 2, [N - 1], [0])
+    assert list(sel[0]) == [1, 2]
+    assert gap[0, 0] > 0
+
+
+# ---------------------------------------------------------------------- P9 ---
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_p9_merge_identity(seed):
+    """Eqs. (7)-(8) on the two branches equal the union softmax of eq. (4)."""
+    q, k, v = synth.random_qkv(96, 4, 2, 16, seed=seed)
+    r, h = oracle.all_rows(96, 4)
+    _, o, _ = oracle.rows(q, k, v, 8, 4, r, h, scale=0.25)
+    _, o2, _ = oracle.rows(q, k, v, 8, 4, r, h, scale=0.25, mode=oracle.MODE_TWO_BRANCH)
+    assert np.max(np.abs(o - o2) / (np.abs(o) + 1e-300)) < 1e-11 or np.max(np.abs(o - o2)) < 1e-13
+
+
+# --------------------------------------------------------------------- P10 ---
+def test_p10_invariants():
+    N, Hq, Hkv, d, B, topk = 80, 2, 1, 8, 8, 3
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=21)
+    r, h = oracle.all_rows(N, Hq)
+    sel, o, _ = oracle.rows(q, k, v, B, topk, r, h)
+    # weights sum to one: V == 1 gives O == 1
+    _, o1, _ = oracle.rows(q, k, np.ones_like(v), B, topk, r, h)
+    assert np.max(np.abs(o1 - 1.0)) < 1e-14
+    # O lies in the per-coordinate hull of V over the candidate set
+    for i in range(len(r)):
+        p, c = r[i], r[i] // B
+        keys = [j for b in sel[i] if 0 <= b < c for j in range(b * B, (b + 1) * B)]
+        keys += list(range(c * B, p + 1))
+        vv = v[keys, 0].astype(np.float64)
+        assert np.all(o[i] >= vv.min(0) - 1e-12) and np.all(o[i] <= vv.max(0) + 1e-12)
+    # permuting tokens inside a history block changes nothing
+    perm = np.arange(N)
+    perm[8:16] = perm[8:16][::-1]
+    _, op, _ = oracle.rows(q, k[perm], v[perm], B, topk, r, h)
+    mask = r >= 16
+    assert np.max(np.abs(op[mask] - o[mask])) < 1e-12
+    # causality: rewriting every key/value after row p leaves row p alone
+    p0 = 43
+    k2, v2 = k.copy(), v.copy()
+    k2[p0 + 1:] = 9.0
+    v2[p0 + 1:] = -9.0
+    _, o3, _ = oracle.rows(q, k2, v2, B, topk, r, h)
+    early = r <= p0
+    assert np.array_equal(o3[early], o[early])
+
+
+def test_oracle_bf16_widening_is_exact():
+    """bf16 inputs are widened exactly: same result as the float32 copy of the values."""
+    q, k, v = synth.random_qkv(48, 2, 2, 8, seed=5, dtype="bf16")
+    qf, kf, vf = (synth.bf16_to_f32(x) for x in (q, k, v))
+    s1, o1 = oracle.prefill(q, k, v, 8, 3)
+    s2, o2 = oracle.prefill(qf, kf, vf, 8, 3)
+    assert np.array_equal(s1, s2) and np.array_equal(o1, o2)
+
+
+def test_gap_reports_selection_margin():
+    q, k, v = synth.random_qkv(64, 1, 1, 4, seed=8)
+    r, h = oracle.all_rows(64, 1)
+    sel, _, gap = oracle.rows(q, k, v, 4, 3, r, h, want_o=False)
+    kb = oracle.block_means(k, 4)
+    for i in range(64):
+        c = r[i] // 4
+        if c <= 2:
+            assert np.isnan(gap[i, 0])
+            continue
+        s = kb[0, :c] @ q[r[i], 0].astype(np.float64)
+        srt = np.sort(s)[::-1]
+        assert abs(gap[i, 0] - (srt[1] - srt[2])) < 1e-12
