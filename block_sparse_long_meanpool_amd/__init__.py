@@ -1,0 +1,258 @@
+"""MoBA prefill forward on MI355X (gfx950) — Python binding of ``libmoba.so``.
+
+This module only marshals arguments: it checks tensor shapes, allocates the
+output and workspace through torch, and calls the C ABI declared in
+``include/moba.h`` on torch's current HIP stream. Every stage of the
+computation runs in the library's HIP kernels; if the library is missing the
+calls raise, there is no other implementation behind them.
+
+The operation (PaperTrace "2.1.3 MoBA", eqs. (2)-(8)): block means of K are
+the routing keys, each query scores the blocks before its own with an unscaled
+dot product, keeps its own block plus the best ``topk - 1`` earlier blocks
+(ties to the lower index), and attends with one softmax over those tokens,
+causally inside its own block.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoba.so")
+
+MOBA_OK = 0
+MOBA_ERR_INVALID_ARGUMENT = 1
+MOBA_ERR_UNSUPPORTED = 2
+MOBA_ERR_WORKSPACE_TOO_SMALL = 3
+MOBA_ERR_HIP = 4
+MOBA_DTYPE_BF16 = 0
+MOBA_DTYPE_F32 = 1
+MOBA_STAGE_EVENTS = 6
+STAGES = ("meanpool", "gate_topk", "bucket", "attn_hist", "attn_self_merge")
+
+# Every symbol include/moba.h declares.
+EXPORTS = (
+    "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_prefill_ex",
+    "moba_select", "moba_dense_causal", "moba_status_string", "moba_last_error",
+    "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
+)
+
+
+class MobaProblem(ctypes.Structure):
+    _fields_ = [
+        ("seqlen", ctypes.c_int64),
+        ("num_q_heads", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("block_size", ctypes.c_int32),
+        ("topk", ctypes.c_int32),
+        ("scale", ctypes.c_float),
+        ("dtype", ctypes.c_int32),
+    ]
+
+
+class MobaError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        lib = _LIB
+        text = lib.moba_status_string(status).decode() if lib else str(status)
+        detail = lib.moba_last_error().decode() if lib else ""
+        super().__init__(f"{where}: {text} ({detail})")
+        self.status = status
+
+
+_LIB = None
+
+
+def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libmoba.so and declare its signatures (raises if it is not built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    if not os.path.exists(path):
+        raise ImportError(f"{path} is missing: build it with `python __graft_entry__.py` "
+                          "(or block_sparse_long_meanpool_amd/build.py)")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(MobaProblem)
+    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    sig = {
+        "moba_workspace_size": (sz, [P]),
+        "moba_select_workspace_size": (sz, [P]),
+        "moba_prefill": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_prefill_ex": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp, vp]),
+        "moba_select": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "moba_last_error": (ctypes.c_char_p, []),
+        "moba_debug_meanpool": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
+        "moba_debug_bucket_capacity": (sz, [P]),
+        "moba_debug_bucket": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "moba_debug_copy": (ctypes.c_int, [vp, vp, sz, vp]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    _LIB = lib
+    return lib
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MOBA_DTYPE_BF16
+    if t.dtype == torch.float32:
+        return MOBA_DTYPE_F32
+    raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
+
+
+def make_problem(N, Hq, Hkv, d, block_size, topk, scale=None, dtype=MOBA_DTYPE_BF16) -> MobaProblem:
+    if scale is None:
+        scale = 1.0 / (d ** 0.5)
+    return MobaProblem(int(N), int(Hq), int(Hkv), int(d), int(block_size), int(topk),
+                       float(scale), int(dtype))
+
+
+def _problem_from(q, k, block_size, topk, scale):
+    if q.dim() != 3 or k.dim() != 3:
+        raise ValueError("q must be [N, Hq, d] and k, v [N, Hkv, d]")
+    N, Hq, d = q.shape
+    if k.shape[0] != N or k.shape[2] != d:
+        raise ValueError(f"shape mismatch: q {tuple(q.shape)} vs k {tuple(k.shape)}")
+    if k.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    return make_problem(N, Hq, k.shape[1], d, block_size, topk, scale, _dtype_code(q))
+
+
+def _check_dev(*ts):
+    for t in ts:
+        if not t.is_cuda:
+            raise ValueError("tensors must live on the GPU")
+        if not t.is_contiguous():
+            raise ValueError("tensors must be contiguous")
+
+
+def _stream(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def _ok(status, where):
+    if status != MOBA_OK:
+        raise MobaError(status, where)
+
+
+def workspace_size(prob: MobaProblem) -> int:
+    return load_library().moba_workspace_size(ctypes.byref(prob))
+
+
+def select_workspace_size(prob: MobaProblem) -> int:
+    return load_library().moba_select_workspace_size(ctypes.byref(prob))
+
+
+def alloc_workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, events=None):
+    """MoBA prefill: O [N, Hq, d] from q [N, Hq, d], k, v [N, Hkv, d] (bf16 or fp32).
+
+    ``scale`` defaults to 1/sqrt(d). ``events`` may be a list of
+    ``MOBA_STAGE_EVENTS`` torch.cuda.Event (created with timing) recorded at the
+    stage boundaries on the current stream.
+    """
+    lib = load_library()
+    _check_dev(q, k, v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    prob = _problem_from(q, k, block_size, topk, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev(out)
+    need = lib.moba_workspace_size(ctypes.byref(prob))
+    if need == 0:
+        _ok(lib.moba_prefill(ctypes.byref(prob), None, None, None, None, None, 0, None),
+            "moba_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    ev_arr = None
+    if events is not None:
+        if len(events) != MOBA_STAGE_EVENTS:
+            raise ValueError(f"need {MOBA_STAGE_EVENTS} events")
+        ev_arr = (ctypes.c_void_p * MOBA_STAGE_EVENTS)(*[e.cuda_event for e in events])
+    st = lib.moba_prefill_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                             out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                             _stream(q.device), ev_arr)
+    _ok(st, "moba_prefill")
+    return out
+
+
+def select(q, k, block_size, topk, out=None, workspace=None):
+    """Selected blocks per (row, head): int32 [N, Hq, topk], ascending, -1 padded."""
+    lib = load_library()
+    _check_dev(q, k)
+    prob = _problem_from(q, k, block_size, topk, None)
+    N, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((N, Hq, topk), dtype=torch.int32, device=q.device)
+    need = lib.moba_select_workspace_size(ctypes.byref(prob))
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib.moba_select(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), out.data_ptr(),
+                         workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _ok(st, "moba_select")
+    return out
+
+
+def dense_causal(q, k, v, scale=None, out=None):
+    """Dense causal softmax attention (the full-attention baseline)."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    prob = _problem_from(q, k, 1, 1, scale)
+    if out is None:
+        out = torch.empty_like(q)
+    st = lib.moba_dense_causal(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                               out.data_ptr(), _stream(q.device))
+    _ok(st, "moba_dense_causal")
+    return out
+
+
+def debug_meanpool(k, block_size):
+    """Block means of k for the blocks that can be history: fp64 [Hkv, n-1, d]."""
+    lib = load_library()
+    _check_dev(k)
+    N, Hkv, d = k.shape
+    prob = make_problem(N, Hkv, Hkv, d, block_size, 1, None, _dtype_code(k))
+    n = -(-N // block_size)
+    kbar = torch.empty((Hkv, max(n - 1, 0), d), dtype=torch.float64, device=k.device)
+    ws = alloc_workspace(lib.moba_select_workspace_size(ctypes.byref(prob)), k.device)
+    ptr = kbar.data_ptr() if kbar.numel() else ws.data_ptr()
+    st = lib.moba_debug_meanpool(ctypes.byref(prob), k.data_ptr(), ptr, ws.data_ptr(), ws.numel(),
+                                 _stream(k.device))
+    _ok(st, "moba_debug_meanpool")
+    return kbar
+
+
+def debug_bucket(sel, num_kv_heads, block_size, head_dim=128, dtype=MOBA_DTYPE_BF16):
+    """Per-(KV head, block) lists from a selection: (offsets int32, entries int32)."""
+    lib = load_library()
+    _check_dev(sel)
+    N, Hq, topk = sel.shape
+    prob = make_problem(N, Hq, num_kv_heads, head_dim, block_size, topk, None, dtype)
+    n = -(-N // block_size)
+    cap = lib.moba_debug_bucket_capacity(ctypes.byref(prob))
+    offsets = torch.empty(num_kv_heads * max(n - 1, 0) + 1, dtype=torch.int32, device=sel.device)
+    entries = torch.empty(max(cap, 4), dtype=torch.int32, device=sel.device)
+    ws = alloc_workspace(lib.moba_workspace_size(ctypes.byref(prob)), sel.device)
+    st = lib.moba_debug_bucket(ctypes.byref(prob), sel.data_ptr(), offsets.data_ptr(),
+                               entries.data_ptr(), ws.data_ptr(), ws.numel(), _stream(sel.device))
+    _ok(st, "moba_debug_bucket")
+    return offsets, entries[:cap]
+
+
+def debug_copy(src, dst):
+    lib = load_library()
+    _check_dev(src, dst)
+    nbytes = src.numel() * src.element_size()
+    st = lib.moba_debug_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src.device))
+    _ok(st, "moba_debug_copy")
+    return dst

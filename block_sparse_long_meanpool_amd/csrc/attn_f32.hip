@@ -1,0 +1,219 @@
+// moba_attn (fp32) — the fp32 build of the history and own-block attention
+// stages (PaperTrace "2.1.3 MoBA", eqs. (5)-(8)), used when Q, K, V and O are
+// fp32. gfx950 has no fp32 path through the bf16 matrix cores that keeps fp32
+// accuracy, so these are vector-ALU kernels: four lanes share one query (32
+// head-dim elements each), keys stream through LDS in tiles of 32, and the
+// online softmax keeps fp32 statistics. Same inputs, outputs and partial
+// layout as the bf16 kernels, with fp32 partials.
+#include "moba_internal.hpp"
+
+namespace moba {
+
+hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
+                                 const void* V, const BucketBufs& b, void* part_o, float* part_lse,
+                                 hipStream_t s);
+hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* V,
+                                 const void* part_o, const float* part_lse, void* O, bool dense,
+                                 hipStream_t s);
+
+namespace {
+
+constexpr int kQ = 128;                 // queries per workgroup
+constexpr int kSub = 4;                 // lanes per query
+constexpr int kDim = kHeadDim / kSub;   // 32 elements per lane
+constexpr int kThreads = kQ * kSub;     // 512
+constexpr int KT = 32;                  // keys per LDS tile
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct QState {
+  float q[kDim];
+  float o[kDim];
+  float m, l;
+};
+
+__device__ inline void load_tile(float* ks, float* vs, const float* __restrict__ K,
+                                 const float* __restrict__ V, int64_t key0, int nvalid, int Hkv,
+                                 int g) {
+  // 32 keys x 128 floats each for K and V; 512 threads, 8 float4 per thread
+  for (int i = threadIdx.x; i < KT * (kHeadDim / 4); i += kThreads) {
+    const int key = i / (kHeadDim / 4), c4 = i % (kHeadDim / 4);
+    float4 kv = make_float4(0.f, 0.f, 0.f, 0.f), vv = kv;
+    if (key < nvalid) {
+      const size_t off = ((size_t)(key0 + key) * Hkv + g) * kHeadDim + 4 * c4;
+      kv = *reinterpret_cast<const float4*>(K + off);
+      vv = *reinterpret_cast<const float4*>(V + off);
+    }
+    reinterpret_cast<float4*>(ks)[i] = kv;
+    reinterpret_cast<float4*>(vs)[i] = vv;
+  }
+}
+
+// Process one staged tile of keys for this lane's query. valid(key) decides the mask.
+template <typename MaskFn>
+__device__ inline void tile_step(QState& S, const float* ks, const float* vs, int sub, float sl2e,
+                                 MaskFn valid) {
+  float z[KT];
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const float* kr = ks + t * kHeadDim + sub * kDim;
+    float a = 0.f;
+#pragma unroll
+    for (int c = 0; c < kDim; ++c) a = fmaf(S.q[c], kr[c], a);
+    a += __shfl_xor(a, 1);
+    a += __shfl_xor(a, 2);
+    z[t] = valid(t) ? a * sl2e : -INFINITY;
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) mx = fmaxf(mx, z[t]);
+  const float mnew = fmaxf(S.m, mx);
+  const float muse = (mnew == -INFINITY) ? 0.f : mnew;
+  const float alpha = __builtin_amdgcn_exp2f(S.m - muse);
+  S.m = mnew;
+  S.l *= alpha;
+#pragma unroll
+  for (int c = 0; c < kDim; ++c) S.o[c] *= alpha;
+#pragma unroll
+  for (int t = 0; t < KT; ++t) {
+    const float p = __builtin_amdgcn_exp2f(z[t] - muse);
+    S.l += p;
+    const float* vr = vs + t * kHeadDim + sub * kDim;
+#pragma unroll
+    for (int c = 0; c < kDim; ++c) S.o[c] = fmaf(p, vr[c], S.o[c]);
+  }
+}
+
+__device__ inline void init_state(QState& S, const float* qrow, bool valid, int sub) {
+#pragma unroll
+  for (int c = 0; c < kDim; ++c) {
+    S.q[c] = valid ? qrow[sub * kDim + c] : 0.f;
+    S.o[c] = 0.f;
+  }
+  S.m = -INFINITY;
+  S.l = 0.f;
+}
+
+__global__ __launch_bounds__(kThreads) void attn_hist_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
+    const uint32_t* __restrict__ entries, float* __restrict__ part_o, float* __restrict__ part_lse,
+    int Hkv, int B, int KH, int64_t nh, float sl2e) {
+  __shared__ float ks[KT * kHeadDim];
+  __shared__ float vs[KT * kHeadDim];
+  const int64_t w = blockIdx.x;
+  if (w >= scalars[1]) return;
+  const int bin = tile_map[w];
+  const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
+  const int64_t e_end = bin_off[bin + 1];
+  const int g = (int)(bin / nh);
+  const int64_t j = bin % nh;
+  const int qi = threadIdx.x / kSub, sub = threadIdx.x % kSub;
+  const int64_t my_e = e_begin + qi;
+  const bool valid = my_e < e_end;
+  const uint32_t ev = valid ? entries[my_e] : 0u;
+  QState S;
+  init_state(S, Q + (int64_t)(ev / (uint32_t)KH) * kHeadDim, valid, sub);
+  for (int k0 = 0; k0 < B; k0 += KT) {
+    const int nv = (B - k0) < KT ? B - k0 : KT;
+    __syncthreads();
+    load_tile(ks, vs, K, V, (int64_t)j * B + k0, nv, Hkv, g);
+    __syncthreads();
+    tile_step(S, ks, vs, sub, sl2e, [&](int t) { return t < nv; });
+  }
+  if (!valid) return;
+  const float inv = 1.f / S.l;
+  float* dst = part_o + (size_t)ev * kHeadDim + sub * kDim;
+#pragma unroll
+  for (int c = 0; c < kDim; ++c) dst[c] = S.o[c] * inv;
+  if (sub == 0) part_lse[ev] = S.m + __builtin_log2f(S.l);
+}
+
+__global__ __launch_bounds__(kThreads) void attn_self_f32(
+    const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
+    const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ O,
+    int64_t N, int Hq, int Hkv, int G, int64_t B, int KH, int64_t n, int tiles_per_block,
+    float sl2e) {
+  __shared__ float ks[KT * kHeadDim];
+  __shared__ float vs[KT * kHeadDim];
+  const int g = blockIdx.y;
+  const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
+  const int tile = tiles_per_block - 1 - (int)(blockIdx.x % tiles_per_block);
+  const int64_t row0 = c * B;
+  int64_t rows_c = N - row0;
+  if (rows_c > B) rows_c = B;
+  const int64_t npairs = rows_c * G;
+  const int64_t p0 = (int64_t)tile * kQ;
+  if (p0 >= npairs) return;
+  const int64_t plast = (p0 + kQ - 1 < npairs) ? p0 + kQ - 1 : npairs - 1;
+  const int64_t last_row = row0 + plast / G;
+  const int qi = threadIdx.x / kSub, sub = threadIdx.x % kSub;
+  const int64_t my_pi = p0 + qi;
+  const bool valid = my_pi < npairs;
+  const int64_t my_row = valid ? row0 + my_pi / G : -1;
+  const int my_h = valid ? g * G + (int)(my_pi % G) : 0;
+  const int64_t ph = valid ? my_row * Hq + my_h : 0;
+  QState S;
+  init_state(S, Q + ph * kHeadDim, valid, sub);
+  for (int64_t k0 = row0; k0 <= last_row; k0 += KT) {
+    const int64_t rem = last_row + 1 - k0;
+    const int nv = rem < KT ? (int)rem : KT;
+    __syncthreads();
+    load_tile(ks, vs, K, V, k0, nv, Hkv, g);
+    __syncthreads();
+    tile_step(S, ks, vs, sub, sl2e, [&](int t) { return t < nv && k0 + t <= my_row; });
+  }
+  if (!valid) return;
+  float l = S.l;
+  if (part_o != nullptr && KH > 0) {
+    const int64_t nhist = c < KH ? c : KH;
+    const int64_t ebase = ph * KH;
+    float M = S.m;
+    for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
+    const float ws = __builtin_amdgcn_exp2f(S.m - M);
+    l *= ws;
+#pragma unroll
+    for (int cc = 0; cc < kDim; ++cc) S.o[cc] *= ws;
+    for (int64_t s = 0; s < nhist; ++s) {
+      const float wgt = __builtin_amdgcn_exp2f(part_lse[ebase + s] - M);
+      l += wgt;
+      const float* src = part_o + (size_t)(ebase + s) * kHeadDim + sub * kDim;
+#pragma unroll
+      for (int cc = 0; cc < kDim; ++cc) S.o[cc] = fmaf(wgt, src[cc], S.o[cc]);
+    }
+  }
+  const float inv = 1.f / l;
+  float* dst = O + ph * kHeadDim + sub * kDim;
+#pragma unroll
+  for (int cc = 0; cc < kDim; ++cc) dst[cc] = S.o[cc] * inv;
+}
+
+}  // namespace
+
+hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
+                            const void* V, const BucketBufs& b, void* part_o, float* part_lse,
+                            hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_hist_bf16(P, bp, Q, K, V, b, part_o, part_lse, s);
+  if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
+  attn_hist_f32<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
+      (const float*)Q, (const float*)K, (const float*)V, b.tile_map, b.tile_off, b.bin_off,
+      b.scalars, b.entries, (float*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh, P.scale * kLog2e);
+  return hipGetLastError();
+}
+
+hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
+                            const int32_t* /*sel*/, const void* part_o, const float* part_lse,
+                            void* O, bool dense, hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_self_bf16(P, Q, K, V, part_o, part_lse, O, dense, s);
+  const int64_t B = dense ? P.N : P.B;
+  const int64_t n = dense ? 1 : P.n;
+  const int tiles_per_block = (int)ceil_div(B * P.G, kQ);
+  dim3 grid((unsigned)(n * tiles_per_block), (unsigned)P.Hkv);
+  attn_self_f32<<<grid, kThreads, 0, s>>>(
+      (const float*)Q, (const float*)K, (const float*)V, dense ? nullptr : (const float*)part_o,
+      dense ? nullptr : part_lse, (float*)O, P.N, P.Hq, P.Hkv, P.G, B, dense ? 0 : P.KH, n,
+      tiles_per_block, P.scale * kLog2e);
+  return hipGetLastError();
+}
+
+}  // namespace moba

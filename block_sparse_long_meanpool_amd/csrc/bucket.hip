@@ -1,0 +1,242 @@
+// moba_bucket — invert (query, block) selections into per-KV-block query lists
+// (PaperTrace "2.1.3 MoBA", section 3.1 step 3: queries are regrouped by the
+// KV block they read so that one contiguous K/V block serves a batch of
+// queries; section 5.4 on the sort / prefix-sum / reorder this costs).
+//
+// Bins are (KV head g, history block b). An entry is the flat selection index
+// e = (row * Hq + head) * (k - 1) + slot, which is also where history
+// attention writes that query's partial result. The lists come out ordered by
+// (row, head) within each bin, independently of scheduling:
+//   1. count:   per chunk of rows (one KV-head group) an LDS histogram;
+//   2. scan:    exclusive scan of the counts down the chunks of every bin,
+//               then over bins -> bin offsets and history-tile offsets;
+//   3. scatter: per chunk, an LDS bitmap per bin over the chunk's pairs gives
+//               each entry its rank by popcount; entries land at
+//               bin offset + chunk base + rank;
+//   4. tile map: tile index -> bin, for the history-attention grid.
+#include "moba_internal.hpp"
+
+namespace moba {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kScanRowGroups = 16;
+
+// Valid history entry of a selection row: block b in [0, c) at slot s < k-1.
+__device__ inline bool hist_entry(int32_t b, int64_t c) { return b >= 0 && b < c; }
+
+__global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restrict__ sel,
+                                                         int32_t* __restrict__ chunk_base,
+                                                         int64_t N, int Hq, int G, int B, int k,
+                                                         int64_t nh, int rows_per_chunk,
+                                                         int64_t nchunk) {
+  extern __shared__ int32_t hist[];
+  const int g = blockIdx.y;
+  const int64_t chunk = blockIdx.x;
+  for (int64_t b = threadIdx.x; b < nh; b += kThreads) hist[b] = 0;
+  __syncthreads();
+  const int KH = k - 1;
+  const int npairs = rows_per_chunk * G;
+  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+    const int64_t r = chunk * rows_per_chunk + pi / G;
+    if (r >= N) break;
+    const int h = g * G + pi % G;
+    const int64_t c = r / B;
+    const int32_t* row = sel + ((size_t)r * Hq + h) * k;
+    for (int s = 0; s < KH; ++s) {
+      const int32_t b = row[s];
+      if (hist_entry(b, c)) atomicAdd(&hist[b], 1);
+    }
+  }
+  __syncthreads();
+  int32_t* out = chunk_base + ((size_t)g * nchunk + chunk) * nh;
+  for (int64_t b = threadIdx.x; b < nh; b += kThreads) out[b] = hist[b];
+}
+
+// Column-wise exclusive scan of chunk_base over chunks; 16 columns per
+// workgroup, each column split into 16 contiguous chunk ranges.
+__global__ __launch_bounds__(kThreads) void bucket_scan_cols(int32_t* __restrict__ chunk_base,
+                                                             int32_t* __restrict__ bin_total,
+                                                             int64_t nbins, int64_t nh,
+                                                             int64_t nchunk) {
+  __shared__ int32_t part[kScanRowGroups][16];
+  const int cl = threadIdx.x % 16;
+  const int rg = threadIdx.x / 16;
+  const int64_t col = blockIdx.x * 16LL + cl;
+  const bool ok = col < nbins;
+  const int64_t g = ok ? col / nh : 0, b = ok ? col % nh : 0;
+  const int64_t cs = (nchunk + kScanRowGroups - 1) / kScanRowGroups;
+  const int64_t c0 = rg * cs;
+  const int64_t c1 = (c0 + cs < nchunk) ? c0 + cs : nchunk;
+  int32_t* base = chunk_base + (size_t)g * nchunk * nh + b;
+  int32_t sum = 0;
+  if (ok)
+    for (int64_t ch = c0; ch < c1; ++ch) sum += base[(size_t)ch * nh];
+  part[rg][cl] = sum;
+  __syncthreads();
+  int32_t run = 0;
+  for (int q = 0; q < rg; ++q) run += part[q][cl];
+  if (ok && rg == kScanRowGroups - 1) bin_total[col] = run + sum;
+  if (ok)
+    for (int64_t ch = c0; ch < c1; ++ch) {
+      const int32_t v = base[(size_t)ch * nh];
+      base[(size_t)ch * nh] = run;
+      run += v;
+    }
+}
+
+// Exclusive scans over bins: entry offsets and history-tile offsets.
+__global__ __launch_bounds__(1024) void bucket_scan_bins(const int32_t* __restrict__ bin_total,
+                                                         int32_t* __restrict__ bin_off,
+                                                         int32_t* __restrict__ tile_off,
+                                                         int32_t* __restrict__ scalars,
+                                                         int64_t nbins, int tile_q) {
+  __shared__ int32_t se[1024];
+  __shared__ int32_t st[1024];
+  __shared__ int32_t carry[2];
+  const int t = threadIdx.x;
+  if (t == 0) carry[0] = carry[1] = 0;
+  __syncthreads();
+  for (int64_t base = 0; base < nbins; base += 1024) {
+    const int64_t i = base + t;
+    const int32_t v = i < nbins ? bin_total[i] : 0;
+    const int32_t tv = (v + tile_q - 1) / tile_q;
+    se[t] = v;
+    st[t] = tv;
+    __syncthreads();
+    // Hillis-Steele inclusive scan
+    for (int off = 1; off < 1024; off <<= 1) {
+      const int32_t a = t >= off ? se[t - off] : 0;
+      const int32_t b = t >= off ? st[t - off] : 0;
+      __syncthreads();
+      se[t] += a;
+      st[t] += b;
+      __syncthreads();
+    }
+    if (i < nbins) {
+      bin_off[i] = carry[0] + se[t] - v;
+      tile_off[i] = carry[1] + st[t] - tv;
+    }
+    __syncthreads();
+    if (t == 1023) {
+      carry[0] += se[1023];
+      carry[1] += st[1023];
+    }
+    __syncthreads();
+  }
+  if (t == 0) {
+    bin_off[nbins] = carry[0];
+    tile_off[nbins] = carry[1];
+    scalars[0] = carry[0];
+    scalars[1] = carry[1];
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bucket_scatter(
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ chunk_base,
+    const int32_t* __restrict__ bin_off, uint32_t* __restrict__ entries, int64_t N, int Hq, int G,
+    int B, int k, int64_t nh, int rows_per_chunk, int64_t nchunk, int words) {
+  extern __shared__ uint32_t bm[];  // [nh][words]
+  const int g = blockIdx.y;
+  const int64_t chunk = blockIdx.x;
+  const int64_t nw = nh * words;
+  for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
+  __syncthreads();
+  const int KH = k - 1;
+  const int npairs = rows_per_chunk * G;
+  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+    const int64_t r = chunk * rows_per_chunk + pi / G;
+    if (r >= N) break;
+    const int h = g * G + pi % G;
+    const int64_t c = r / B;
+    const int32_t* row = sel + ((size_t)r * Hq + h) * k;
+    for (int s = 0; s < KH; ++s) {
+      const int32_t b = row[s];
+      if (hist_entry(b, c)) atomicOr(&bm[(size_t)b * words + (pi >> 5)], 1u << (pi & 31));
+    }
+  }
+  __syncthreads();
+  const int32_t* cb = chunk_base + ((size_t)g * nchunk + chunk) * nh;
+  const int32_t* bo = bin_off + (size_t)g * nh;
+  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+    const int64_t r = chunk * rows_per_chunk + pi / G;
+    if (r >= N) break;
+    const int h = g * G + pi % G;
+    const int64_t c = r / B;
+    const int64_t ph = (int64_t)r * Hq + h;
+    const int32_t* row = sel + ph * k;
+    for (int s = 0; s < KH; ++s) {
+      const int32_t b = row[s];
+      if (!hist_entry(b, c)) continue;
+      const uint32_t* w = bm + (size_t)b * words;
+      int rank = __popc(w[pi >> 5] & ((1u << (pi & 31)) - 1u));
+      for (int q = 0; q < (pi >> 5); ++q) rank += __popc(w[q]);
+      entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(ph * KH + s);
+    }
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void bucket_tile_map(const int32_t* __restrict__ tile_off,
+                                                            int32_t* __restrict__ tile_map) {
+  const int64_t b = blockIdx.x;
+  const int32_t t0 = tile_off[b], t1 = tile_off[b + 1];
+  for (int32_t t = t0 + threadIdx.x; t < t1; t += kThreads) tile_map[t] = (int32_t)b;
+}
+
+}  // namespace
+
+BucketPlan plan_bucket(const Prob& P) {
+  BucketPlan bp{};
+  const int64_t nh = P.nh > 0 ? P.nh : 1;
+  int64_t wmax = 8192 / nh;
+  if (wmax > 32) wmax = 32;
+  if (wmax < 1) wmax = 1;
+  int64_t rpc = (32 * wmax) / P.G;
+  if (rpc < 1) rpc = 1;
+  bp.rows_per_chunk = (int)rpc;
+  bp.words = (int)ceil_div(rpc * P.G, 32);
+  bp.nchunk = ceil_div(P.N, rpc);
+  bp.nbins = (int64_t)P.Hkv * P.nh;
+  int64_t e = 0;
+  for (int64_t c = 0; c < P.n; ++c) {
+    int64_t rows = P.N - c * P.B;
+    if (rows > P.B) rows = P.B;
+    e += rows * (c < P.KH ? c : P.KH);
+  }
+  bp.max_entries = e * P.Hq;
+  bp.max_tiles = ceil_div(bp.max_entries, kTileQ) + bp.nbins;
+  return bp;
+}
+
+hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
+                         const BucketBufs& b, hipStream_t s) {
+  if (P.nh <= 0 || P.KH <= 0) {
+    // No history anywhere: empty lists.
+    hipError_t e = launch_fill_i32(b.bin_off, 0, bp.nbins + 1, s);
+    if (e == hipSuccess) e = launch_fill_i32(b.tile_off, 0, bp.nbins + 1, s);
+    if (e == hipSuccess) e = launch_fill_i32(b.scalars, 0, 4, s);
+    return e;
+  }
+  dim3 grid((unsigned)bp.nchunk, (unsigned)P.Hkv);
+  bucket_count<<<grid, kThreads, sizeof(int32_t) * P.nh, s>>>(
+      sel, b.chunk_base, P.N, P.Hq, P.G, P.B, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  bucket_scan_cols<<<(unsigned)ceil_div(bp.nbins, 16), kThreads, 0, s>>>(b.chunk_base, b.bin_total,
+                                                                         bp.nbins, P.nh, bp.nchunk);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bucket_scan_bins<<<1, 1024, 0, s>>>(b.bin_total, b.bin_off, b.tile_off, b.scalars, bp.nbins,
+                                      kTileQ);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  bucket_scatter<<<grid, kThreads, sizeof(uint32_t) * P.nh * bp.words, s>>>(
+      sel, b.chunk_base, b.bin_off, b.entries, P.N, P.Hq, P.G, P.B, P.k, P.nh, bp.rows_per_chunk,
+      bp.nchunk, bp.words);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (b.tile_map) {
+    bucket_tile_map<<<(unsigned)bp.nbins, kThreads, 0, s>>>(b.tile_off, b.tile_map);
+    e = hipGetLastError();
+  }
+  return e;
+}
+
+}  // namespace moba

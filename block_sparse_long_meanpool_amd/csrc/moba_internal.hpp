@@ -1,0 +1,86 @@
+// Internal declarations shared by the kernels and the host runtime of libmoba.so.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "moba.h"
+
+namespace moba {
+
+constexpr int kHeadDim = 128;       // head_dim compiled in
+constexpr int kMaxTopk = 32;        // topk limit (selection lists live in LDS)
+constexpr int64_t kMaxHist = 8192;  // history-capable blocks (bucket bitmaps live in LDS)
+constexpr int kTileQ = 128;         // routed queries per history-attention tile
+constexpr int kMaxGroup = 64;       // Hq / Hkv limit
+
+// Problem with derived sizes; built and validated on the host.
+struct Prob {
+  int64_t N;
+  int Hq, Hkv, G, d, B, k;
+  int KH;      // history slots per (row, head) = k - 1
+  int64_t n;   // blocks = ceil(N / B)
+  int64_t nh;  // blocks that can be history = n - 1
+  float scale;
+  int dtype;   // MOBA_DTYPE_*
+};
+
+// Bucketing (per KV head, history block) of the selected (row, head, slot) entries.
+struct BucketPlan {
+  int rows_per_chunk;  // rows of one KV head group per counting chunk
+  int64_t nchunk;      // chunks per KV head = ceil(N / rows_per_chunk)
+  int words;           // 32-bit bitmap words per bin in a chunk
+  int64_t nbins;       // Hkv * nh
+  int64_t max_entries; // Hq * sum_p min(k-1, c(p))
+  int64_t max_tiles;   // bound on sum_b ceil(count_b / kTileQ)
+};
+
+struct BucketBufs {
+  int32_t* chunk_base;  // [Hkv][nchunk][nh] counts, then exclusive bases
+  int32_t* bin_total;   // [nbins]
+  int32_t* bin_off;     // [nbins + 1]
+  int32_t* tile_off;    // [nbins + 1]
+  int32_t* tile_map;    // [max_tiles]
+  int32_t* scalars;     // [4]: total entries, total tiles
+  uint32_t* entries;    // [max_entries]
+};
+
+BucketPlan plan_bucket(const Prob& P);
+
+// Stage launchers (each enqueues on `s`; return hipSuccess or the launch error).
+hipError_t launch_meanpool(const Prob& P, const void* K, double* kbar, double* part, int splits,
+                           hipStream_t s);
+int meanpool_splits(const Prob& P);
+
+hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, int32_t* sel,
+                            hipStream_t s);
+
+hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
+                         const BucketBufs& b, hipStream_t s);
+
+// History-block attention over the bucketed entries; writes normalised partials
+// part_o [entry][d] and log2-sum-exp part_lse [entry].
+hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
+                            const void* V, const BucketBufs& b, void* part_o, float* part_lse,
+                            hipStream_t s);
+
+// Own-block causal attention fused with the merge of the history partials.
+// With dense=true: one block covering the whole sequence and no partials
+// (causal full attention).
+hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
+                            const int32_t* sel, const void* part_o, const float* part_lse,
+                            void* O, bool dense, hipStream_t s);
+
+hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);
+
+// Element type of the partial outputs of history attention.
+inline size_t part_elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_F32 ? 4 : 2; }
+
+inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+}  // namespace moba

@@ -1,0 +1,160 @@
+/*
+ * moba.h — C ABI of the MI355X (gfx950) MoBA prefill library, libmoba.so.
+ *
+ * MoBA (Mixture of Block Attention) prefill forward for one attention layer.
+ * The operation is the one on the PaperTrace page "2.1.3 MoBA"
+ * (yayajjiang.github.io/PaperTrace, sparse-attention 2.1.3):
+ *   - keys are cut into contiguous blocks of block_size tokens (section 1,
+ *     eq. (2)); each block is summarised by the mean of its keys (eq. (3));
+ *   - a query scores each earlier block with the unscaled dot product
+ *     q . kbar_i (eq. (3)); blocks after its own block are excluded; its own
+ *     block is always taken and never ranked (section 2); top-k counts that
+ *     own block, so at most topk-1 earlier blocks are taken (section 2.1);
+ *     ties go to the lower block index;
+ *   - the output is one softmax over the union of the taken tokens — the own
+ *     block causally (keys j <= p), earlier blocks whole (eqs. (4)-(6)) — with
+ *     the two branches merged through (m, l, u) statistics (eqs. (7)-(8)).
+ * The MoonshotAI/MoBA README names the public interface of the original:
+ * Q, K, V, block size and top-k, as a drop-in for full attention.
+ *
+ * Conventions for every entry point below:
+ *   - Layout is token-major and contiguous: Q and O are [N][Hq][d], K and V
+ *     are [N][Hkv][d]; query head h reads KV head h / (Hq / Hkv).
+ *   - Positions and blocks are 0-based: block i holds rows [i*B, (i+1)*B); a
+ *     last partial block (B not dividing N) is only ever a query's own block.
+ *   - All tensor and workspace pointers are DEVICE pointers on the current HIP
+ *     device; problem structs are HOST pointers. The caller owns every buffer;
+ *     the library never allocates, frees or synchronises.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued
+ *     asynchronously; results are valid once the stream has been synchronised.
+ *   - Inputs are read-only; outputs must not alias inputs or the workspace.
+ *   - Calls return a status code and never throw. All argument checks run on
+ *     the host before anything is enqueued, so an error leaves outputs and
+ *     the workspace untouched and costs no HIP call.
+ *   - Calls that overlap on one stream are ordered; calls that share one
+ *     workspace on different streams race.
+ */
+#ifndef MOBA_H
+#define MOBA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* Exported symbols (the library is built with hidden default visibility). */
+#if defined(__GNUC__) || defined(__clang__)
+#define MOBA_API __attribute__((visibility("default")))
+#else
+#define MOBA_API
+#endif
+
+/* Status codes. */
+#define MOBA_OK 0
+#define MOBA_ERR_INVALID_ARGUMENT 1 /* null pointer, sizes < 1, Hq % Hkv != 0, bad scale/dtype */
+#define MOBA_ERR_UNSUPPORTED 2      /* valid but not compiled in (head_dim != 128, size limits) */
+#define MOBA_ERR_WORKSPACE_TOO_SMALL 3
+#define MOBA_ERR_HIP 4 /* a HIP launch/runtime error; text from moba_last_error() */
+
+/* Element type of Q, K, V and O. */
+typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_F32 = 1 } moba_dtype_t;
+
+typedef struct {
+  int64_t seqlen;       /* N >= 1 */
+  int32_t num_q_heads;  /* Hq >= 1 */
+  int32_t num_kv_heads; /* Hkv >= 1, Hq % Hkv == 0 */
+  int32_t head_dim;     /* d; 128 is compiled in */
+  int32_t block_size;   /* B >= 1 */
+  int32_t topk;         /* k >= 1, counting the own block; k >= ceil(N/B) = causal full attention */
+  float scale;          /* finite and > 0; multiplies attention logits only (the gate is unscaled) */
+  int32_t dtype;        /* moba_dtype_t of Q, K, V and O */
+} moba_problem_t;
+
+/*
+ * Size limits of this build (MOBA_ERR_UNSUPPORTED beyond them):
+ *   head_dim == 128; topk <= 32; ceil(N/B) - 1 <= 8192 history-capable blocks;
+ *   N * Hq * topk < 2^31; Hq / Hkv <= 64.
+ */
+
+/* Bytes of device workspace moba_prefill needs for *p; 0 if *p is invalid or unsupported. */
+MOBA_API size_t moba_workspace_size(const moba_problem_t *p);
+
+/* Bytes of device workspace moba_select needs for *p; 0 if *p is invalid or unsupported. */
+MOBA_API size_t moba_select_workspace_size(const moba_problem_t *p);
+
+/*
+ * MoBA prefill forward: O = MoBA-attention(Q, K, V) as defined above.
+ *   q  [N][Hq][d], k [N][Hkv][d], v [N][Hkv][d] (device, dtype of p)
+ *   o  [N][Hq][d] (device, dtype of p), written in full
+ *   workspace / ws_bytes: device scratch of at least moba_workspace_size(p)
+ *     bytes, 256-byte aligned; contents on entry are ignored.
+ * Numerics: bf16 inputs use bf16 matrix-core products with fp32 accumulation
+ * and fp32 softmax statistics; block means and gate scores are fp64, so the
+ * selection equals the exact one except where scores tie to fp64 rounding.
+ * fp32 inputs use fp32 arithmetic throughout the attention.
+ */
+MOBA_API int moba_prefill(const moba_problem_t *p, const void *q, const void *k, const void *v, void *o,
+                 void *workspace, size_t ws_bytes, void *stream);
+
+/* Stage boundaries that moba_prefill_ex can time. */
+#define MOBA_STAGE_EVENTS 6 /* start, after meanpool, gate_topk, bucket, history attn, self+merge */
+
+/*
+ * moba_prefill with optional per-stage timing: if `events` is not NULL it
+ * points to MOBA_STAGE_EVENTS caller-created hipEvent_t handles, recorded on
+ * `stream` before the first stage and after each of the five stages
+ * (meanpool, gate_topk, bucket, history attention, own-block attention with
+ * merge). Otherwise identical to moba_prefill.
+ */
+MOBA_API int moba_prefill_ex(const moba_problem_t *p, const void *q, const void *k, const void *v, void *o,
+                    void *workspace, size_t ws_bytes, void *stream, void *const *events);
+
+/*
+ * Block selection only (debug call): sel [N][Hq][topk] int32 (device), per
+ * (row, head) the selected blocks in ascending order — the chosen earlier
+ * blocks, then the own block — padded with -1.
+ */
+MOBA_API int moba_select(const moba_problem_t *p, const void *q, const void *k, int32_t *sel,
+                void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Dense causal softmax attention on the same tensors (PaperTrace section 1,
+ * eq. (1) with a causal mask): the full-attention baseline MoBA is measured
+ * against. block_size and topk of *p are ignored. No workspace.
+ */
+MOBA_API int moba_dense_causal(const moba_problem_t *p, const void *q, const void *k, const void *v,
+                      void *o, void *stream);
+
+/* Static text for a status code. */
+MOBA_API const char *moba_status_string(int status);
+
+/* Thread-local text of the last MOBA_ERR_HIP (or other error) on this thread. */
+MOBA_API const char *moba_last_error(void);
+
+/*
+ * Stage-level debug exports (used by the tests to check one stage at a time).
+ *   moba_debug_meanpool: kbar [Hkv][max(n-1,0)][d] fp64 (device) = block means
+ *     of K (eq. (3)) for the blocks that can be history. workspace as for
+ *     moba_select.
+ *   moba_debug_bucket: from a selection sel [N][Hq][topk] (device), build the
+ *     per-(KV head, block) lists: offsets [Hkv*(n-1)+1] int32 and entries
+ *     uint32 (capacity moba_debug_bucket_capacity(p)); entry value
+ *     ((row*Hq + head)*(topk-1) + slot), slot = position in the sel row.
+ *     Lists are ordered by (row, head). workspace as for moba_prefill.
+ *   moba_debug_copy: plain device copy of `bytes` bytes (a traffic calibration
+ *     kernel for hardware counters).
+ */
+MOBA_API int moba_debug_meanpool(const moba_problem_t *p, const void *k, double *kbar, void *workspace,
+                        size_t ws_bytes, void *stream);
+MOBA_API size_t moba_debug_bucket_capacity(const moba_problem_t *p);
+MOBA_API int moba_debug_bucket(const moba_problem_t *p, const int32_t *sel, int32_t *offsets,
+                      uint32_t *entries, void *workspace, size_t ws_bytes, void *stream);
+MOBA_API int moba_debug_copy(const void *src, void *dst, size_t bytes, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOBA_H */

@@ -1,0 +1,122 @@
+"""CPU-only checks of the C ABI: the library loads, exports what include/moba.h
+declares, and rejects bad arguments on the host before any HIP call."""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import block_sparse_long_meanpool_amd as moba
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_symbols():
+    with open(os.path.join(ROOT, "include", "moba.h")) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"MOBA_API[^;(]*?\b(moba_\w+)\s*\(", text)))
+
+
+def test_header_and_binding_agree():
+    assert _declared_symbols() == sorted(moba.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = moba.load_library()
+    for name in _declared_symbols():
+        assert hasattr(lib, name), name
+
+
+def test_status_strings():
+    lib = moba.load_library()
+    assert lib.moba_status_string(0) == b"MOBA_OK"
+    assert lib.moba_status_string(3) == b"MOBA_ERR_WORKSPACE_TOO_SMALL"
+    assert lib.moba_status_string(99) == b"MOBA_ERR_UNKNOWN"
+
+
+def _prob(**kw):
+    base = dict(N=4096, Hq=8, Hkv=2, d=128, block_size=256, topk=3, scale=0.088, dtype=0)
+    base.update(kw)
+    return moba.make_problem(base["N"], base["Hq"], base["Hkv"], base["d"], base["block_size"],
+                             base["topk"], base["scale"], base["dtype"])
+
+
+BAD = [
+    (dict(N=0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(Hq=6, Hkv=4), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(block_size=0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(topk=0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(scale=0.0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(scale=-1.0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.inf), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(scale=math.nan), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(dtype=7), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(d=0), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(d=64), moba.MOBA_ERR_UNSUPPORTED),
+    (dict(topk=33), moba.MOBA_ERR_UNSUPPORTED),
+    (dict(N=1 << 20, block_size=64), moba.MOBA_ERR_UNSUPPORTED),
+    (dict(N=1 << 24, Hq=64, Hkv=64, block_size=4096, topk=3), moba.MOBA_ERR_UNSUPPORTED),
+    (dict(Hq=128, Hkv=1), moba.MOBA_ERR_UNSUPPORTED),
+]
+
+FAKE = 1 << 20  # a non-NULL, aligned address that is never dereferenced: every case fails first
+
+
+@pytest.mark.parametrize("kw,code", BAD)
+def test_invalid_problems_rejected_before_any_hip_call(kw, code):
+    lib = moba.load_library()
+    p = _prob(**kw)
+    assert lib.moba_workspace_size(ctypes.byref(p)) == 0
+    assert lib.moba_select_workspace_size(ctypes.byref(p)) == 0
+    st = lib.moba_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None)
+    assert st == code
+    assert lib.moba_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == code
+    assert lib.moba_dense_causal(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.moba_last_error()
+
+
+def test_null_problem():
+    lib = moba.load_library()
+    assert lib.moba_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.moba_workspace_size(None) == 0
+
+
+@pytest.mark.parametrize("which", range(4))
+def test_null_and_misaligned_tensors(which):
+    lib = moba.load_library()
+    p = _prob()
+    ws = lib.moba_workspace_size(ctypes.byref(p))
+    for bad in (None, FAKE + 2):
+        ptrs = [FAKE] * 4
+        ptrs[which] = bad
+        assert lib.moba_prefill(ctypes.byref(p), *ptrs, FAKE, ws, None) == 1
+
+
+def test_workspace_checks():
+    lib = moba.load_library()
+    p = _prob()
+    ws = lib.moba_workspace_size(ctypes.byref(p))
+    assert ws > 0 and ws % 256 == 0
+    assert lib.moba_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, ws - 1, None) == 3
+    assert lib.moba_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None, ws, None) == 1
+    assert lib.moba_prefill(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE + 16, ws, None) == 1
+    sws = lib.moba_select_workspace_size(ctypes.byref(p))
+    assert 0 < sws < ws
+    assert lib.moba_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, sws - 1, None) == 3
+
+
+def test_workspace_scales_with_history_slots():
+    """The partial buffers dominate: (k-1) slots of d fp16 values (+ one fp32) per (row, head)."""
+    lib = moba.load_library()
+    a = lib.moba_workspace_size(ctypes.byref(_prob(topk=3)))
+    b = lib.moba_workspace_size(ctypes.byref(_prob(topk=5)))
+    per_slot = 4096 * 8 * (128 * 2 + 4)
+    assert per_slot * 2 <= b - a <= per_slot * 2 + 4096 * 8 * 2 * 4 * 2 + 4096 * 64
+
+
+def test_copy_rejects_bad_arguments():
+    lib = moba.load_library()
+    assert lib.moba_debug_copy(None, FAKE, 16, None) == 1
+    assert lib.moba_debug_copy(FAKE, FAKE, 15, None) == 1

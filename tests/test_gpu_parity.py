@@ -1,0 +1,240 @@
+"""GPU parity: every stage and the whole MoBA prefill, through the C ABI, against
+the fp64 oracle on the same seeded inputs.
+
+Bars: block selections bit-exact except rows whose gate margin is below 1e-5
+relative (those are re-checked with the GPU's selection forced into the
+oracle); O max-abs <= 1e-2 and mean-abs <= 1e-3 for bf16 (fp32 accumulation),
+max-abs <= 1e-5 for fp32. Block means (fp64 sums of the inputs) must match
+exactly.
+"""
+import numpy as np
+import pytest
+import torch
+
+import block_sparse_long_meanpool_amd as moba
+import oracle
+import synth
+from tests._gpu import DEV, check_output, check_selection, compare_rows, to_dev, to_np
+
+pytestmark = pytest.mark.gpu
+
+_CACHE = {}
+
+
+def inputs(name, dtype=None):
+    """Seeded workload inputs, host (numpy) and device, cached per (config, dtype)."""
+    w = synth.CONFIGS[name]
+    dtype = dtype or w.dtype
+    key = (name, dtype)
+    if key not in _CACHE:
+        q, k, v = synth.make_qkv(w, dtype)
+        _CACHE[key] = (w, q, k, v, to_dev(q), to_dev(k), to_dev(v))
+    return _CACHE[key]
+
+
+def small(N, Hq, Hkv, B, topk, seed, dtype="bf16", integer=False, zero_k=False):
+    q, k, v = synth.random_qkv(N, Hq, Hkv, 128, seed, dtype=dtype, integer=integer)
+    if zero_k:
+        k = np.zeros_like(k)
+    return q, k, v, to_dev(q), to_dev(k), to_dev(v)
+
+
+def all_rows(N, Hq):
+    return oracle.all_rows(N, Hq)
+
+
+# ------------------------------------------------------------------ stages ---
+@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None)])
+def test_meanpool_exact(name, dtype):
+    w, q, k, v, tq, tk, tv = inputs(name, dtype)
+    got = moba.debug_meanpool(tk, w.B).cpu().numpy()
+    ref = oracle.block_means(k, w.B)
+    if k.dtype == np.uint16:
+        assert np.array_equal(got, ref)
+    else:
+        assert np.allclose(got, ref, rtol=1e-15, atol=0)
+
+
+@pytest.mark.parametrize("N,Hkv,B", [(1000, 3, 96), (300, 2, 1), (777, 1, 250), (64, 4, 128)])
+def test_meanpool_irregular(N, Hkv, B):
+    q, k, v, tq, tk, tv = small(N, Hkv, Hkv, B, 2, seed=N + B)
+    got = moba.debug_meanpool(tk, B).cpu().numpy()
+    assert np.array_equal(got, oracle.block_means(k, B))
+
+
+@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None),
+                                        ("c3", None)])
+def test_select_all_rows(name, dtype):
+    w, q, k, v, tq, tk, tv = inputs(name, dtype)
+    sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
+    rows, heads = all_rows(w.N, w.Hq)
+    ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, rows, heads, want_o=False)
+    check_selection(sel.reshape(-1, w.k), ref_sel, gap, name)
+
+
+def _bucket_reference(sel, Hkv, B):
+    N, Hq, k = sel.shape
+    G = Hq // Hkv
+    n = -(-N // B)
+    lists = [[[] for _ in range(n - 1)] for _ in range(Hkv)]
+    for r in range(N):
+        c = r // B
+        for h in range(Hq):
+            for s in range(k - 1):
+                b = sel[r, h, s]
+                if 0 <= b < c:
+                    lists[h // G][b].append((r * Hq + h) * (k - 1) + s)
+    offs, ents = [0], []
+    for g in range(Hkv):
+        for b in range(n - 1):
+            ents += lists[g][b]
+            offs.append(len(ents))
+    return np.array(offs), np.array(ents)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk", [(2048, 4, 2, 128, 4), (999, 6, 3, 64, 3),
+                                             (512, 8, 1, 32, 5)])
+def test_bucket_lists(N, Hq, Hkv, B, topk):
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=7)
+    sel = moba.select(tq, tk, B, topk)
+    offs, ents = moba.debug_bucket(sel, Hkv, B)
+    ro, re_ = _bucket_reference(sel.cpu().numpy(), Hkv, B)
+    assert np.array_equal(offs.cpu().numpy(), ro)
+    assert np.array_equal(ents.cpu().numpy()[: len(re_)], re_)
+
+
+# ---------------------------------------------------------------- prefill ---
+@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None)])
+def test_prefill_all_rows(name, dtype):
+    w, q, k, v, tq, tk, tv = inputs(name, dtype)
+    o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
+    sel = moba.select(tq, tk, w.B, w.k)
+    rows, heads = all_rows(w.N, w.Hq)
+    (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads,
+                                    sel.cpu().numpy().reshape(-1, w.k),
+                                    to_np(o).reshape(-1, w.d), dtype or w.dtype, name)
+    print(f"{name} {dtype or w.dtype}: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
+
+
+def test_prefill_c3_sampled_and_needles():
+    w, q, k, v, tq, tk, tv = inputs("c3")
+    o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
+    sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
+    rows, heads = synth.sample_rows(w, 4096)
+    (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads, sel[rows, heads],
+                                    to_np(o)[rows, heads], "bf16", "c3")
+    # needle rows pick needle blocks: long-range selection is exercised
+    hits = 0
+    for h in range(2):
+        nb = set(synth.needle_blocks(w, h).tolist())
+        for r in synth.needle_rows(w, h):
+            c = r // w.B
+            legal = {b for b in nb if b < c}
+            if len(legal) >= w.k - 1:
+                hits += set(sel[r, h, : w.k - 1].tolist()) <= legal
+    assert hits > 0
+    print(f"c3: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied} needle rows routed {hits}")
+
+
+@pytest.mark.timeout(1200)
+def test_prefill_c5_sampled():
+    w, q, k, v, tq, tk, tv = inputs("c5")
+    o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
+    sel = moba.select(tq, tk, w.B, w.k)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    o_np = o.cpu()
+    rows, heads = synth.sample_rows(w, 4096)
+    kbar = oracle.block_means(k, w.B)
+    got_o = o_np[torch.from_numpy(rows), torch.from_numpy(heads.astype(np.int64))].float().numpy()
+    (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads, sel_np[rows, heads],
+                                    got_o.astype(np.float64), "bf16", "c5")
+    # selections on a larger seeded sample (gate only)
+    r2, h2 = synth.sample_rows(w.with_(seed=w.seed ^ 0xABCDEF), 1 << 20)
+    ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, r2, h2, want_o=False, kbar=kbar)
+    check_selection(sel_np[r2, h2], ref_sel, gap, "c5 sel")
+    print(f"c5: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
+
+
+# ------------------------------------------------------------- edge cases ---
+EDGE = [
+    # N, Hq, Hkv, B, topk, dtype
+    (1000, 2, 1, 96, 3, "bf16"),     # B does not divide N, partial key tiles
+    (700, 4, 2, 48, 4, "bf16"),      # B < 64: masked key tiles
+    (200, 2, 2, 256, 3, "bf16"),     # N < B: one partial block
+    (1, 2, 1, 64, 3, "bf16"),        # a single row
+    (300, 2, 1, 1, 4, "bf16"),       # B = 1: token-level routing
+    (2048, 8, 2, 128, 1, "bf16"),    # k = 1: own block only
+    (2048, 8, 8, 128, 16, "bf16"),   # k >= n: causal full attention
+    (1536, 8, 1, 128, 5, "bf16"),    # G = 8
+    (1536, 12, 3, 128, 4, "bf16"),   # odd KV head count
+    (1000, 2, 1, 96, 3, "f32"),
+    (2048, 4, 2, 128, 16, "f32"),
+    (300, 2, 1, 1, 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk,dtype", EDGE)
+def test_prefill_edge(N, Hq, Hkv, B, topk, dtype):
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N * 31 + topk, dtype=dtype)
+    scale = 0.09
+    o = moba.prefill(tq, tk, tv, B, topk, scale)
+    sel = moba.select(tq, tk, B, topk)
+    rows, heads = all_rows(N, Hq)
+    compare_rows(q, k, v, B, topk, scale, rows, heads, sel.cpu().numpy().reshape(-1, topk),
+                 to_np(o).reshape(-1, 128), dtype, f"edge {N},{Hq},{Hkv},{B},{topk}")
+
+
+def test_zero_keys_ties_are_exact():
+    """K == 0: every gate score ties; the lowest blocks must be chosen (no tie excuse)."""
+    N, Hq, Hkv, B, topk = 1024, 4, 2, 64, 4
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=3, zero_k=True)
+    sel = moba.select(tq, tk, B, topk).cpu().numpy().reshape(-1, topk)
+    rows, heads = all_rows(N, Hq)
+    ref_sel, ref_o, _ = oracle.rows(q, k, v, B, topk, rows, heads)
+    assert np.array_equal(sel, ref_sel)
+    o = moba.prefill(tq, tk, tv, B, topk)
+    check_output(to_np(o).reshape(-1, 128), ref_o, "bf16", "zero K")
+
+
+def test_integer_ties_are_exact():
+    N, Hq, Hkv, B, topk = 640, 2, 1, 16, 5
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=5, integer=True)
+    sel = moba.select(tq, tk, B, topk).cpu().numpy().reshape(-1, topk)
+    rows, heads = all_rows(N, Hq)
+    ref_sel, _, _ = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False)
+    assert np.array_equal(sel, ref_sel)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_dense_baseline_and_full_coverage(dtype):
+    """k covering every block equals causal full attention, and so does the dense kernel."""
+    N, Hq, Hkv, B = 2304, 4, 2, 256
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, 9, seed=11, dtype=dtype)
+    scale = 0.1
+    od = moba.dense_causal(tq, tk, tv, scale)
+    om = moba.prefill(tq, tk, tv, B, 9, scale)
+    rows, heads = all_rows(N, Hq)
+    ref = oracle.causal_full(q, k, v, rows, heads, scale=scale)
+    check_output(to_np(od).reshape(-1, 128), ref, dtype, "dense")
+    check_output(to_np(om).reshape(-1, 128), ref, dtype, "moba k>=n")
+
+
+def test_deterministic():
+    w, q, k, v, tq, tk, tv = inputs("c2")
+    a = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
+    b = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+
+
+def test_stage_events_and_copy():
+    w, q, k, v, tq, tk, tv = inputs("c2")
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_STAGE_EVENTS)]
+    moba.prefill(tq, tk, tv, w.B, w.k, w.scale, events=ev)
+    torch.cuda.synchronize()
+    times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
+    assert all(t >= 0 for t in times)
+    src = torch.arange(1 << 20, dtype=torch.int32, device=DEV)
+    dst = torch.empty_like(src)
+    moba.debug_copy(src, dst)
+    assert torch.equal(src, dst)
