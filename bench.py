@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""MoBA prefill benchmark on one MI355X.
+
+One step = one ``moba_prefill`` call (all five stages: meanpool, gate + top-k,
+bucketing, history attention, own-block attention + merge) over one layer of
+synthetic input already resident in HBM. Default workload: the 1M-token
+Llama-3.1-8B-shaped layer (N=1,048,576, 32 query heads over 8 KV heads,
+d=128, B=4096, k=12, bf16).
+
+Prints one JSON line with tokens/s, attended TFLOP/s against the bf16 MFMA
+peak, per-stage times (hipEvents recorded on the library's stream), the
+dominant kernel's roofline, the dense causal baseline on the same GPU and the
+fp64 CPU oracle timed on a bounded row sample.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import block_sparse_long_meanpool_amd as moba  # noqa: E402
+import synth  # noqa: E402
+
+METRIC = "MoBA prefill tokens/s per layer + attended TFLOP/s (% of bf16 MFMA peak)"
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA, 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+STAGES = moba.STAGES
+
+
+def pair_counts(w):
+    """Exact attended (query, key) pairs per head: own block causal + full history blocks."""
+    KH = w.k - 1
+    own = hist = 0
+    for c in range(w.n):
+        rows = min(w.B, w.N - c * w.B)
+        own += rows * (rows + 1) // 2
+        hist += rows * min(KH, c) * w.B
+    return own, hist
+
+
+def algorithmic_bytes(w):
+    """Bytes a stage must move at minimum (per launch)."""
+    nh = w.n - 1
+    meanpool = w.N * w.Hkv * w.d * 2 + nh * w.Hkv * w.d * 8
+    KH = w.k - 1
+    entries = 0
+    for c in range(w.n):
+        rows = min(w.B, w.N - c * w.B)
+        entries += rows * min(KH, c) * w.Hq
+    bucket = 2 * w.N * w.Hq * w.k * 4 + 4 * entries + 4 * (w.Hkv * nh + 1)
+    return meanpool, bucket, entries
+
+
+def to_dev(a):
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(a).cuda()
+
+
+def read_traffic(kernel_tag):
+    """HBM bytes per launch from the committed counter summary, if it is current."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and line.startswith("- "):
+                key, val = line[2:].split(":", 1)
+                fields[key.strip()] = val.strip().strip("`")
+    src = fields.get("kernel_source_sha256")
+    if src is None or "hbm_bytes_per_launch" not in fields:
+        return None
+    import hashlib
+    cur = hashlib.sha256(open(os.path.join(ROOT, fields["kernel_source"]), "rb").read()).hexdigest()
+    return float(fields["hbm_bytes_per_launch"]) if cur == src else None
+
+
+def cpu_baseline(w, q, k, v, rows_wanted):
+    import oracle  # the fp64 oracle: this leg only
+    rows, heads = synth.sample_rows(w, 4096)
+    sel = np.linspace(0, len(rows) - 1, rows_wanted).astype(np.int64)
+    rows, heads = rows[sel], heads[sel]
+    threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    kbar = oracle.block_means(k, w.B)
+    t1 = time.perf_counter()
+    oracle.rows(q, k, v, w.B, w.k, rows, heads, scale=w.scale, kbar=kbar, nthreads=threads)
+    t2 = time.perf_counter()
+    tok_s = (len(rows) / w.Hq) / (t2 - t1)
+    return {
+        "value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "sample": (f"{len(rows)} seeded (row, head) pairs of the same layer spread over all blocks; "
+                   f"value = pairs/{w.Hq} per second of the fp64 dense-masked row evaluation; the "
+                   f"one-time fp64 block means took {t1 - t0:.2f} s and are not in the rate"),
+    }
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--config", default="c5", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the MoBA prefill path here runs on a single "
+              "MI355X (a multi-GPU split by KV-head group is described in DESIGN.md, not built).",
+              file=sys.stderr)
+        sys.exit(2)
+
+    w = synth.CONFIGS[args.config]
+    dtype = "bf16" if w.dtype == "bf16" else "f32"
+    t0 = time.perf_counter()
+    q, k, v = synth.make_qkv(w, dtype)
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    gen_s = time.perf_counter() - t0
+    out = torch.empty_like(tq)
+    prob = moba.make_problem(w.N, w.Hq, w.Hkv, w.d, w.B, w.k, w.scale,
+                             moba.MOBA_DTYPE_BF16 if dtype == "bf16" else moba.MOBA_DTYPE_F32)
+    ws = moba.alloc_workspace(moba.workspace_size(prob), tq.device)
+    print(f"[bench] {w.name}: inputs ready in {gen_s:.1f} s, workspace {ws.numel() / 2**30:.1f} GiB",
+          file=sys.stderr, flush=True)
+
+    def step(ev=None):
+        moba.prefill(tq, tk, tv, w.B, w.k, w.scale, out=out, workspace=ws, events=ev)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_STAGE_EVENTS)]
+           for _ in range(args.steps)]
+    for ev in evs:
+        for e in ev:
+            e.record()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(evs[i])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    ms_per_step = elapsed * 1e3 / args.steps
+    stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs]))
+                for i, s in enumerate(STAGES)}
+    event_ms = float(np.mean([ev[0].elapsed_time(ev[-1]) for ev in evs]))
+    print(f"[bench] {args.steps} steps: {ms_per_step:.2f} ms/step, stages {stage_ms}",
+          file=sys.stderr, flush=True)
+
+    own, hist = pair_counts(w)
+    flop_total = 4.0 * w.d * w.Hq * (own + hist)
+    flop_hist = 4.0 * w.d * w.Hq * hist
+    tokens_s = w.N / (ms_per_step / 1e3)
+    tflops = flop_total / (ms_per_step / 1e3) / 1e12
+    hist_tflops = flop_hist / (stage_ms["attn_hist"] / 1e3) / 1e12
+    mp_bytes, bk_bytes, entries = algorithmic_bytes(w)
+
+    dense = None
+    if not args.no_dense:
+        od = torch.empty_like(tq)
+        moba.dense_causal(tq, tk, tv, w.scale, out=od)  # warm-up
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moba.dense_causal(tq, tk, tv, w.scale, out=od)
+        e1.record()
+        torch.cuda.synchronize()
+        dms = e0.elapsed_time(e1)
+        dense_flop = 4.0 * w.d * w.Hq * (w.N * (w.N + 1) // 2)
+        dense = {"ms": dms, "tflops": dense_flop / (dms / 1e3) / 1e12,
+                 "speedup_moba_vs_dense": dms / ms_per_step}
+        del od
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
+
+    rec = {
+        "metric": METRIC,
+        "value": tokens_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": dtype,
+        "data": "synthetic (seeded N(0,1) Q/K/V, per-block key offsets std 0.5)",
+        "config": {"workload": f"{w.name}: MoBA prefill layer N={w.N} Hq={w.Hq} Hkv={w.Hkv} "
+                               f"d={w.d} B={w.B} topk={w.k}",
+                   "seq_len": w.N, "num_q_heads": w.Hq, "num_kv_heads": w.Hkv, "head_dim": w.d,
+                   "block_size": w.B, "topk": w.k, "parallelism": "none (1 GPU)"},
+        "attended_tflops": tflops,
+        "attended_frac_of_bf16_peak": tflops / PEAK_BF16_TFLOPS,
+        "stage_ms": stage_ms,
+        "events_total_ms": event_ms,
+        "meanpool_gbps": mp_bytes / (stage_ms["meanpool"] / 1e3) / 1e9,
+        "meanpool_frac_of_hbm_peak": mp_bytes / (stage_ms["meanpool"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "bucket_gbps": bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9,
+        "bucket_frac_of_hbm_peak": bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "routed_entries": entries,
+        "roofline": {"bound": "mfma", "kernel": "attn_hist_bf16",
+                     "achieved": hist_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": hist_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": read_traffic("attn_hist_c5")},
+        "dense_causal": dense,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

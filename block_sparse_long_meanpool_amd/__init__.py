@@ -178,6 +178,9 @@ def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, eve
     if events is not None:
         if len(events) != MOBA_STAGE_EVENTS:
             raise ValueError(f"need {MOBA_STAGE_EVENTS} events")
+        for e in events:
+            if not e.cuda_event:  # torch creates the HIP event on first record
+                e.record()
         ev_arr = (ctypes.c_void_p * MOBA_STAGE_EVENTS)(*[e.cuda_event for e in events])
     st = lib.moba_prefill_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              out.data_ptr(), workspace.data_ptr(), workspace.numel(),

@@ -200,9 +200,9 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
     float* __restrict__ part_lse, int Hkv, int B, int KH, int64_t nh, float sl2e) {
   __shared__ Smem sm;
   // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous
-  // range of tiles so the tiles of one K/V block share that XCD's L2.
-  const int64_t U = gridDim.x;
-  const int64_t per = (U + 7) / 8;
+  // range of tiles so the tiles of one K/V block share that XCD's L2. The grid
+  // is a multiple of 8, so this is a bijection on [0, gridDim.x).
+  const int64_t per = gridDim.x / 8;
   const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (w >= scalars[1]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -366,7 +366,8 @@ hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void
                                  hipStream_t s) {
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   const float sl2e = P.scale * kLog2e;
-  attn_hist_bf16<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
+  const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
+  attn_hist_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, b.tile_map, b.tile_off, b.bin_off,
       b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh, sl2e);
   return hipGetLastError();

@@ -132,10 +132,11 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
         acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], b0, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], b1, acc1, 0, 0, 0);
       }
-      // D layout: lane holds rows (pairs) 4*(lane/16)+r, column (block) lane%16
+      // D layout of v_mfma_f64_16x16x4: register r of lane l holds row (pair)
+      // l/16 + 4r, column (block) l%16
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int p = wave * 16 + 4 * grp + r;
+        const int p = wave * 16 + grp + 4 * r;
         sc[p * kScPad + bl] = acc0[r];
         sc[p * kScPad + 16 + bl] = acc1[r];
       }

@@ -1,6 +1,7 @@
 // Host runtime and C ABI of libmoba.so: argument checks, workspace plan and
 // the launch sequence of the five stages on the caller's stream. The
 // operation and every entry point are specified in include/moba.h.
+#include <climits>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -225,8 +226,13 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
 
 int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, const void* v,
                       void* o, void* stream) {
+  if (!p) return fail(MOBA_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
+  // block_size and topk do not apply: one block spanning the sequence, no history
+  moba_problem_t d = *p;
+  d.block_size = p->seqlen > 0 && p->seqlen < INT32_MAX ? (int32_t)p->seqlen : 1;
+  d.topk = 1;
   Prob P;
-  int rc = make_prob(p, &P);
+  int rc = make_prob(&d, &P);
   if (rc) return rc;
   const void* ptrs[4] = {q, k, v, o};
   if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
