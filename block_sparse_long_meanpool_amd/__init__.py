@@ -29,13 +29,14 @@ MOBA_ERR_WORKSPACE_TOO_SMALL = 3
 MOBA_ERR_HIP = 4
 MOBA_DTYPE_BF16 = 0
 MOBA_DTYPE_F32 = 1
-MOBA_STAGE_EVENTS = 6
-STAGES = ("meanpool", "gate_topk", "bucket", "attn_hist", "attn_self_merge")
+MOBA_STAGE_EVENTS = 7
+STAGES = ("meanpool", "gate_topk", "bucket", "vpack", "attn_hist", "attn_self_merge")
 
 # Every symbol include/moba.h declares.
 EXPORTS = (
     "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_prefill_ex",
-    "moba_select", "moba_dense_causal", "moba_status_string", "moba_last_error",
+    "moba_select", "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
+    "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
 )
 
@@ -82,7 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_prefill": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_prefill_ex": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp, vp]),
         "moba_select": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
-        "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
+        "moba_dense_workspace_size": (sz, [P]),
+        "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "moba_last_error": (ctypes.c_char_p, []),
         "moba_debug_meanpool": (ctypes.c_int, [P, vp, vp, vp, sz, vp]),
@@ -206,15 +208,18 @@ def select(q, k, block_size, topk, out=None, workspace=None):
     return out
 
 
-def dense_causal(q, k, v, scale=None, out=None):
+def dense_causal(q, k, v, scale=None, out=None, workspace=None):
     """Dense causal softmax attention (the full-attention baseline)."""
     lib = load_library()
     _check_dev(q, k, v)
-    prob = _problem_from(q, k, 1, 1, scale)
+    prob = _problem_from(q, k, q.shape[0], 1, scale)
     if out is None:
         out = torch.empty_like(q)
+    if workspace is None:
+        workspace = alloc_workspace(lib.moba_dense_workspace_size(ctypes.byref(prob)), q.device)
     st = lib.moba_dense_causal(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
-                               out.data_ptr(), _stream(q.device))
+                               out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                               _stream(q.device))
     _ok(st, "moba_dense_causal")
     return out
 

@@ -3,21 +3,32 @@
 // causal own-block branch eq. (5), merged by eqs. (7)-(8); section 3.1 steps
 // 4-5; section 5.4 on tiling queries per KV block).
 //
-// Tile engine shared by both kernels. A wavefront owns 32 queries; a
-// workgroup of 4 waves streams one K/V block in 64-key tiles through LDS
-// (double buffered, one barrier per tile) so every tile read from HBM/L2
-// serves 128 queries. Per tile and wave:
-//   S^T = K Q^T   8 x v_mfma_f32_32x32x16_bf16 per 32 keys (keys on rows,
-//                 queries on columns, so each lane holds 16 keys of one query
-//                 and a softmax row needs one cross-half exchange);
-//   online softmax in the exp2 domain, fp32 statistics (m, l);
-//   O^T += V^T P^T  the P accumulator registers are reused directly as the B
-//                 operand; V is stored transposed in LDS with its keys
-//                 permuted to match, so each A operand is one 16-byte read.
-// History kernel: one workgroup per 128 routed queries of one (KV head,
-// block) list, full (non-causal) block; writes the normalised partial output
+// Tile engine shared by both kernels. A wavefront owns 64 queries (two
+// 32-column blocks); a workgroup of 4 waves streams one K/V block in 64-key
+// tiles through LDS (double buffered, one barrier per tile), so each K/V
+// byte read from L2 serves 256 queries and each LDS operand read feeds two
+// matrix-core ops. Tiles move global -> LDS with global_load_lds_dwordx4 (no
+// register staging); rows are stored with their 16-byte chunks XOR-swizzled
+// by the row index so the operand reads below are bank-conflict free.
+// Per 32-key subtile and wave:
+//   S^T = K Q^T     v_mfma_f32_32x32x16_bf16, keys on rows and queries on
+//                   columns: a lane holds 16 keys of one query, so a softmax
+//                   row needs a single cross-half exchange;
+//   softmax         exp2 domain, fp32 statistics. The reference max of a
+//                   query is fixed by its first unmasked subtile and never
+//                   moves, so the output accumulators stay in matrix-core
+//                   registers untouched by vector code for the whole loop.
+//                   Later scores may exceed it; if any exceeds it by more
+//                   than 2^64 (an overflow risk) the workgroup re-runs the
+//                   block starting from the true maximum (never for ordinary
+//                   data; the result is identical either way up to rounding);
+//   O^T += V^T P^T  P stays in the accumulator registers' layout and is the B
+//                   operand directly; V comes pre-transposed and key-permuted
+//                   (vt_pack) so each A operand is one 16-byte LDS read.
+// History kernel: one workgroup per 256 routed queries of one (KV head,
+// block) list, whole block (non-causal); writes the normalised partial output
 // (fp16) and its log2-sum-exp. Own-block kernel: causal inside the block,
-// then merges the history partials of its queries (eqs. (7)-(8)) and writes O.
+// then merges its queries' history partials (eqs. (7)-(8)) and writes O.
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -27,245 +38,293 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int KT = 64;                      // keys per tile
-constexpr int KS_STRIDE = kHeadDim + 8;     // bf16 per K row in LDS
-constexpr int VT_STRIDE = KT + 8;           // bf16 per V^T row in LDS
-constexpr int KS_ELEMS = KT * KS_STRIDE;
-constexpr int VT_ELEMS = kHeadDim * VT_STRIDE;
+constexpr int QB = 2;                       // 32-query blocks per wave
+constexpr int kWaveQ = 32 * QB;             // queries per wave
+constexpr int kGroupQ = 4 * kWaveQ;         // queries per workgroup
+static_assert(kGroupQ == kTileQ, "history tiles are one workgroup");
+constexpr int KT = 64;                      // keys per LDS tile
+constexpr int KS_ROW = kHeadDim;            // bf16 per K row in LDS (256 B, swizzled)
+constexpr int VT_ROW = KT;                  // bf16 per V^T row in LDS (128 B, swizzled)
+constexpr int KS_ELEMS = KT * KS_ROW;
+constexpr int VT_ELEMS = kHeadDim * VT_ROW;
 constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kRedoSlack = 64.f;          // scores this far above the reference max force a re-run
 
-struct __align__(16) Smem {
-  uint16_t k[2][KS_ELEMS];
-  uint16_t v[2][VT_ELEMS];
-};
-
-struct Prefetch {
-  uint4 k[4];
-  uint4 v[4];
+// One LDS tile buffer. The kernels declare two distinct buffers and unroll the
+// key loop by two, so the compiler can see that the copies into one buffer
+// never alias the operand reads from the other (and need not wait for them).
+struct __align__(16) Tile {
+  uint16_t k[KS_ELEMS];
+  uint16_t v[VT_ELEMS];
 };
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// Global -> registers for keys [key0, key0 + 64) of KV head g; keys >= nvalid are zero.
-__device__ inline void fetch_tile(Prefetch& pf, const uint16_t* __restrict__ K,
-                                  const uint16_t* __restrict__ V, int64_t key0, int nvalid,
-                                  int Hkv, int g, int tid) {
-  const int kk = tid >> 2, dc = (tid & 3) * 32;
-  if (kk < nvalid) {
-    const uint4* src = reinterpret_cast<const uint4*>(K + ((key0 + kk) * Hkv + g) * kHeadDim + dc);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pf.k[i] = src[i];
-  } else {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) pf.k[i] = make_uint4(0, 0, 0, 0);
-  }
-  const int kq = tid >> 4, dof = (tid & 15) * 8;
+// K row r keeps 16-byte chunk c at position c ^ (r & 15); V^T row d keeps chunk
+// c at c ^ (d & 7).
+__device__ inline const uint16_t* k_chunk(const uint16_t* ks, int row, int c) {
+  return ks + row * KS_ROW + ((c ^ (row & 15)) << 3);
+}
+__device__ inline const uint16_t* vt_chunk(const uint16_t* vt, int d, int c) {
+  return vt + d * VT_ROW + ((c ^ (d & 7)) << 3);
+}
+
+// Issue the global -> LDS copies of one tile: keys [key0, key0+64) of K (rows
+// >= nvalid re-read row 0: those keys are masked) and the 64 matching packed
+// V^T columns (block pads are zero). Each wave copies 4 KB of K and 4 KB of V^T,
+// 1 KB (64 lanes x 16 B) per instruction; the caller waits and barriers.
+__device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K,
+                                 int64_t key0, int nvalid, int Hkv, int g,
+                                 const uint16_t* __restrict__ vt_col, int64_t ldv, int wave,
+                                 int lane) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int key = 4 * kq + i;
-    if (key < nvalid)
-      pf.v[i] = *reinterpret_cast<const uint4*>(V + ((key0 + key) * Hkv + g) * kHeadDim + dof);
-    else
-      pf.v[i] = make_uint4(0, 0, 0, 0);
+    const int r = 16 * wave + 4 * i + (lane >> 4);
+    const int c = (lane & 15) ^ (r & 15);
+    const int rr = r < nvalid ? r : 0;
+    const uint16_t* src = K + ((key0 + rr) * Hkv + g) * kHeadDim + 8 * c;
+    __builtin_amdgcn_global_load_lds(src, t.k + (16 * wave + 4 * i) * KS_ROW, 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int d = 32 * wave + 8 * i + (lane >> 3);
+    const int c = (lane & 7) ^ (d & 7);
+    const uint16_t* src = vt_col + (int64_t)d * ldv + 8 * c;
+    __builtin_amdgcn_global_load_lds(src, t.v + (32 * wave + 8 * i) * VT_ROW, 16, 0, 0);
   }
 }
 
-__device__ inline uint32_t u4_word(const uint4& u, int w) {
-  return w == 0 ? u.x : (w == 1 ? u.y : (w == 2 ? u.z : u.w));
+// Wait for this wave's outstanding loads (all counters), then a workgroup barrier.
+__device__ inline void wait_tile() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
 }
 
-// Registers -> LDS: K row-major; V transposed to [d][key] with keys permuted
-// so that key 16u + 8a + 4h + b of each 32-key half lands at 16u + 8h + 4a + b.
-__device__ inline void store_tile(const Prefetch& pf, uint16_t* ks, uint16_t* vt, int tid) {
-  const int kk = tid >> 2, dc = (tid & 3) * 32;
-  uint4* dst = reinterpret_cast<uint4*>(ks + kk * KS_STRIDE + dc);
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[i] = pf.k[i];
-  const int kq = tid >> 4, dof = (tid & 15) * 8;
-  const int pbase = 16 * (kq >> 2) + 8 * (kq & 1) + 4 * ((kq >> 1) & 1);
-#pragma unroll
-  for (int dd = 0; dd < 8; ++dd) {
-    const int w = dd >> 1, sh = (dd & 1) * 16;
-    const uint32_t e0 = (u4_word(pf.v[0], w) >> sh) & 0xFFFFu;
-    const uint32_t e1 = (u4_word(pf.v[1], w) >> sh) & 0xFFFFu;
-    const uint32_t e2 = (u4_word(pf.v[2], w) >> sh) & 0xFFFFu;
-    const uint32_t e3 = (u4_word(pf.v[3], w) >> sh) & 0xFFFFu;
-    uint2 pk = make_uint2(e0 | (e1 << 16), e2 | (e3 << 16));
-    *reinterpret_cast<uint2*>(vt + (dof + dd) * VT_STRIDE + pbase) = pk;
-  }
-}
-
-// Per-wave attention state for 32 queries.
+// Per-wave attention state for 64 queries; lane l holds query 32*qb + l%32.
 struct Wave {
-  bf16x8 q[8];    // B operand of S^T = K Q^T: Q[query][16ks + 8h .. +8]
-  f32x16 o[4];    // O^T accumulators, d-blocks of 32
-  float m;        // running max (log2 domain)
-  float l;        // this lane's partial row sum
+  bf16x8 q[QB][8];   // B operand of S^T = K Q^T: Q[query][16kk + 8h .. +8]
+  f32x16 o[QB][4];   // O^T accumulators, d-blocks of 32
+  float m[QB];       // reference max (log2 domain), fixed once set
+  float mseen[QB];   // largest scaled score seen
+  float l[QB];       // this lane's partial row sum
 };
 
-__device__ inline void wave_init(Wave& W, const uint16_t* qrow, bool valid, int h) {
+__device__ inline void wave_load_q(Wave& W, const uint16_t* const (&qrow)[QB],
+                                   const bool (&valid)[QB], int h) {
 #pragma unroll
-  for (int ks = 0; ks < 8; ++ks) {
-    uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * ks + 8 * h) : make_uint4(0, 0, 0, 0);
-    W.q[ks] = as_bf16x8(u);
+  for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      uint4 u = valid[qb] ? *reinterpret_cast<const uint4*>(qrow[qb] + 16 * kk + 8 * h)
+                          : make_uint4(0, 0, 0, 0);
+      W.q[qb][kk] = as_bf16x8(u);
+    }
+}
+
+__device__ inline void wave_reset(Wave& W, const float (&mstart)[QB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) W.o[qb][db][r] = 0.f;
+    W.m[qb] = mstart[qb];
+    W.mseen[qb] = -INFINITY;
+    W.l[qb] = 0.f;
   }
+}
+
+// True when some valid query of this lane saw a score too far above its
+// reference max (the pass must be redone from the true maximum).
+__device__ inline bool wave_needs_redo(const Wave& W, const bool (&valid)[QB]) {
+  bool r = false;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) W.o[db][r] = 0.f;
-  W.m = -INFINITY;
-  W.l = 0.f;
+  for (int qb = 0; qb < QB; ++qb) r |= valid[qb] && (W.mseen[qb] > W.m[qb] + kRedoSlack);
+  return r;
 }
 
 // Key row (0..31) of accumulator element r in the 32x32 MFMA output layout.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// One 64-key tile for one wave. Mask: key (tile-relative) valid iff < nvalid
-// and, when causal, key0 + key <= qrow_abs.
+// One 32-key subtile `sub` of the LDS tile (ks, vt). Keys >= nvalid (counted
+// from the subtile start) are masked; when CAUSAL, also keys with
+// key0 + key > qrow.
 template <bool CAUSAL>
-__device__ inline void wave_tile(Wave& W, const uint16_t* ks, const uint16_t* vt, int lane,
-                                 int nvalid, int64_t key0, int64_t qrow_abs, float sl2e,
-                                 bool need_mask) {
+__device__ inline void wave_subtile(Wave& W, const uint16_t* ks_tile, const uint16_t* vt, int sub,
+                                    int lane, int nvalid, int64_t key0, const int64_t (&qrow)[QB],
+                                    float sl2e, bool need_mask) {
   const int h = lane >> 5, lr = lane & 31;
-  f32x16 s[2];
+  const uint16_t* ks = ks_tile + sub * 32 * KS_ROW;  // row swizzle uses (row & 15): same for row+32
+  const int csub = 4 * sub;
+  f32x16 s[QB];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) s[sub][r] = 0.f;
-    const uint16_t* krow = ks + (sub * 32 + lr) * KS_STRIDE + 8 * h;
+    for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(krow + 16 * kk));
-      s[sub] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, W.q[kk], s[sub], 0, 0, 0);
-    }
+  for (int kk = 0; kk < 8; ++kk) {
+    const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(k_chunk(ks, lr, 2 * kk + h)));
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+      s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, W.q[qb][kk], s[qb], 0, 0, 0);
   }
   if (need_mask) {
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub)
+    for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int key = sub * 32 + acc_row(r, h);
+        const int key = acc_row(r, h);
         bool ok = key < nvalid;
-        if (CAUSAL) ok = ok && (key0 + key <= qrow_abs);
-        if (!ok) s[sub][r] = -INFINITY;
+        if (CAUSAL) ok = ok && (key0 + key <= qrow[qb]);
+        if (!ok) s[qb][r] = -INFINITY;
       }
   }
-  float mx = -INFINITY;
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
+  for (int qb = 0; qb < QB; ++qb) {
+    float v = s[qb][0];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sub][r]);
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mnew = fmaxf(W.m, mx * sl2e);
-  const float muse = (mnew == -INFINITY) ? 0.f : mnew;
-  const float alpha = __builtin_amdgcn_exp2f(W.m - muse);
-  W.m = mnew;
-  W.l *= alpha;
+    for (int r = 1; r < 16; ++r) v = fmaxf(v, s[qb][r]);
+    v = fmaxf(v, __shfl_xor(v, 32)) * sl2e;
+    W.mseen[qb] = fmaxf(W.mseen[qb], v);
+    if (W.m[qb] == -INFINITY) W.m[qb] = v;  // first unmasked keys fix the reference
+  }
+  bf16x8 p[QB][2];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) W.o[db][r] *= alpha;
-  bf16x8 p[2][2];
-#pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
+  for (int qb = 0; qb < QB; ++qb) {
+    const float muse = (W.m[qb] == -INFINITY) ? 0.f : W.m[qb];
+    float lsum = 0.f;
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int t = 0; t < 8; ++t) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[sub][8 * u + t], sl2e, -muse));
-        W.l += e;
-        p[sub][u][t] = (__bf16)e;
+        const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + t], sl2e, -muse));
+        lsum += e;
+        p[qb][u][t] = (__bf16)e;
       }
+    W.l[qb] += lsum;
+  }
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub)
+  for (int u = 0; u < 2; ++u)
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const uint16_t* vcol = vt + lr * VT_STRIDE + 32 * sub + 16 * u + 8 * h;
+    for (int db = 0; db < 4; ++db) {
+      const bf16x8 a =
+          as_bf16x8(*reinterpret_cast<const uint4*>(vt_chunk(vt, 32 * db + lr, csub + 2 * u + h)));
 #pragma unroll
-      for (int db = 0; db < 4; ++db) {
-        bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(vcol + 32 * db * VT_STRIDE));
-        W.o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[sub][u], W.o[db], 0, 0, 0);
-      }
+      for (int qb = 0; qb < QB; ++qb)
+        W.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[qb][u], W.o[qb][db], 0, 0, 0);
     }
 }
 
+typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+
 // ----------------------------------------------------------------------------
-// History attention: one workgroup = up to 128 routed entries of one bin.
+// History attention: one workgroup = up to 256 routed entries of one bin.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
     const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
     const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
-    float* __restrict__ part_lse, int Hkv, int B, int KH, int64_t nh, float sl2e) {
-  __shared__ Smem sm;
-  // XCD-aware order: workgroup i runs on XCD i % 8; give each XCD a contiguous
-  // range of tiles so the tiles of one K/V block share that XCD's L2. The grid
-  // is a multiple of 8, so this is a bijection on [0, gridDim.x).
+    float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad, int64_t ldv, int KH, int64_t nh,
+    float sl2e) {
+  __shared__ Tile tA, tB;
+  // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
+  // contiguous range of tiles so the tiles of one K/V block share its L2.
+  // The grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
   const int64_t per = gridDim.x / 8;
   const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (w >= scalars[1]) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int bin = tile_map[w];
   const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
   const int64_t e_end = bin_off[bin + 1];
   const int g = (int)(bin / nh);
   const int64_t j = bin % nh;
 
-  const int64_t my_e = e_begin + wave * 32 + (lane & 31);
-  const bool valid = my_e < e_end;
-  const uint32_t ev = valid ? entries[my_e] : 0u;
-  const int64_t ph = ev / (uint32_t)KH;
+  uint32_t ev[QB];
+  bool valid[QB];
+  const uint16_t* qrow[QB];
+  int64_t dummy_row[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t e = e_begin + wave * kWaveQ + qb * 32 + (lane & 31);
+    valid[qb] = e < e_end;
+    ev[qb] = valid[qb] ? entries[e] : 0u;
+    qrow[qb] = Q + (int64_t)(ev[qb] / (uint32_t)KH) * kHeadDim;
+    dummy_row[qb] = 0;
+  }
   Wave W;
-  wave_init(W, Q + ph * kHeadDim, valid, lane >> 5);
+  wave_load_q(W, qrow, valid, h);
 
   const int64_t kbase = j * B;
+  const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + j * Bpad;
   const int ntiles = (B + KT - 1) / KT;
-  Prefetch pf;
-  fetch_tile(pf, K, V, kbase, B < KT ? B : KT, Hkv, g, tid);
-  store_tile(pf, sm.k[0], sm.v[0], tid);
-  __syncthreads();
-  const bool wave_live = (e_begin + wave * 32) < e_end;
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int nv_next = (kt + 1 < ntiles) ? ((B - (kt + 1) * KT) < KT ? B - (kt + 1) * KT : KT) : 0;
-    if (kt + 1 < ntiles) fetch_tile(pf, K, V, kbase + (int64_t)(kt + 1) * KT, nv_next, Hkv, g, tid);
-    const int nv = (B - kt * KT) < KT ? B - kt * KT : KT;
-    if (wave_live)
-      wave_tile<false>(W, sm.k[kt & 1], sm.v[kt & 1], lane, nv, 0, 0, sl2e, nv < KT);
-    if (kt + 1 < ntiles) store_tile(pf, sm.k[(kt + 1) & 1], sm.v[(kt + 1) & 1], tid);
-    __syncthreads();
-  }
-  if (!valid) return;
-  const float l = W.l + __shfl_xor(W.l, 32);
-  const float inv = 1.f / l;
-  const int h = lane >> 5;
-  _Float16* dst = part_o + (size_t)ev * kHeadDim;
+  const bool wave_live = (e_begin + wave * kWaveQ) < e_end;
+  float mstart[QB];
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      const int d0 = 32 * db + 8 * r4 + 4 * h;
-      typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-      h4 v;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = (_Float16)(W.o[db][4 * r4 + t] * inv);
-      *reinterpret_cast<h4*>(dst + d0) = v;
+  for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
+  for (int attempt = 0;; ++attempt) {
+    wave_reset(W, mstart);
+    auto step = [&](int kt, Tile& cur, Tile& nxt) {
+      if (kt + 1 < ntiles) {
+        const int rem = B - (kt + 1) * KT;
+        load_tile(nxt, K, kbase + (int64_t)(kt + 1) * KT, rem < KT ? rem : KT, Hkv, g,
+                  vt_col + (kt + 1) * KT, ldv, wave, lane);
+      }
+      const int nv = (B - kt * KT) < KT ? B - kt * KT : KT;
+      if (wave_live) {
+#pragma unroll 1
+        for (int sub = 0; sub < 2; ++sub) {
+          const int nvs = nv - 32 * sub;
+          if (nvs > 0)
+            wave_subtile<false>(W, cur.k, cur.v, sub, lane, nvs, 0, dummy_row, sl2e, nvs < 32);
+        }
+      }
+      wait_tile();
+    };
+    load_tile(tA, K, kbase, B < KT ? B : KT, Hkv, g, vt_col, ldv, wave, lane);
+    wait_tile();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(kt, tA, tB);
+      if (kt + 1 < ntiles) step(kt + 1, tB, tA);
     }
-  if (h == 0) part_lse[ev] = W.m + __builtin_log2f(l);
+    // workgroup-uniform decision: re-run only if some score overran the reference max
+    if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mstart[qb] = W.mseen[qb];
+  }
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
+    if (!valid[qb]) continue;
+    const float inv = 1.f / l;
+    _Float16* dst = part_o + (size_t)ev[qb] * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        h4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (_Float16)(W.o[qb][db][4 * r4 + t] * inv);
+        *reinterpret_cast<h4*>(dst + 32 * db + 8 * r4 + 4 * h) = v;
+      }
+    if (h == 0) part_lse[ev[qb]] = W.m[qb] + __builtin_log2f(l);
+  }
 }
 
 // ----------------------------------------------------------------------------
-// Own-block causal attention + merge. One workgroup = 128 (row, head) pairs of
-// one KV-head group inside one block; pairs ordered pi = (row - cB) * G + hh.
+// Own-block causal attention + merge. One workgroup = 256 (row, head) pairs
+// of one KV-head group inside one block; pairs ordered pi = (row - cB)*G + hh.
 // dense: the "block" is the whole sequence and there are no partials.
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_self_bf16(
-    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ V,
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
     const _Float16* __restrict__ part_o, const float* __restrict__ part_lse,
-    uint16_t* __restrict__ O, int64_t N, int Hq, int Hkv, int G, int64_t B, int KH,
-    int64_t n, int tiles_per_block, float sl2e) {
-  __shared__ Smem sm;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    uint16_t* __restrict__ O, int64_t N, int Hq, int Hkv, int G, int64_t B, int64_t Bpad,
+    int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
+  __shared__ Tile tA, tB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int g = blockIdx.y;
   // heavier (later) row tiles first
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
@@ -274,117 +333,148 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   int64_t rows_c = N - row0;
   if (rows_c > B) rows_c = B;
   const int64_t npairs = rows_c * G;
-  const int64_t p0 = (int64_t)tile * 128;
+  const int64_t p0 = (int64_t)tile * kGroupQ;
   if (p0 >= npairs) return;
-  const int64_t plast = (p0 + 127 < npairs) ? p0 + 127 : npairs - 1;
+  const int64_t plast = (p0 + kGroupQ - 1 < npairs) ? p0 + kGroupQ - 1 : npairs - 1;
   const int64_t last_row = row0 + plast / G;
 
-  const int64_t my_pi = p0 + wave * 32 + (lane & 31);
-  const bool valid = my_pi < npairs;
-  const int64_t my_row = valid ? row0 + my_pi / G : -1;
-  const int my_h = valid ? g * G + (int)(my_pi % G) : 0;
-  const int64_t ph = valid ? my_row * Hq + my_h : 0;
+  bool valid[QB];
+  int64_t my_row[QB], ph[QB];
+  const uint16_t* qrow[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const int64_t pi = p0 + wave * kWaveQ + qb * 32 + (lane & 31);
+    valid[qb] = pi < npairs;
+    my_row[qb] = valid[qb] ? row0 + pi / G : -1;
+    ph[qb] = valid[qb] ? my_row[qb] * Hq + g * G + (int)(pi % G) : 0;
+    qrow[qb] = Q + ph[qb] * kHeadDim;
+  }
   Wave W;
-  wave_init(W, Q + ph * kHeadDim, valid, lane >> 5);
+  wave_load_q(W, qrow, valid, h);
 
-  // row range of this wave (for skipping fully masked tiles / unmasked tiles)
-  const int64_t wp0 = p0 + wave * 32;
+  const int64_t wp0 = p0 + wave * kWaveQ;
   const bool wave_live = wp0 < npairs;
-  const int64_t wp1 = (wp0 + 31 < npairs) ? wp0 + 31 : npairs - 1;
+  const int64_t wp1 = (wp0 + kWaveQ - 1 < npairs) ? wp0 + kWaveQ - 1 : npairs - 1;
   const int64_t wrow_min = row0 + wp0 / G;
   const int64_t wrow_max = row0 + wp1 / G;
 
   const int64_t nkeys = last_row - row0 + 1;
   const int ntiles = (int)((nkeys + KT - 1) / KT);
-  Prefetch pf;
-  fetch_tile(pf, K, V, row0, nkeys < KT ? (int)nkeys : KT, Hkv, g, tid);
-  store_tile(pf, sm.k[0], sm.v[0], tid);
-  __syncthreads();
-  for (int kt = 0; kt < ntiles; ++kt) {
-    const int64_t key0 = row0 + (int64_t)kt * KT;
-    if (kt + 1 < ntiles) {
-      const int64_t rem = nkeys - (int64_t)(kt + 1) * KT;
-      fetch_tile(pf, K, V, key0 + KT, rem < KT ? (int)rem : KT, Hkv, g, tid);
+  const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + c * Bpad;
+  float mstart[QB];
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
+  for (int attempt = 0;; ++attempt) {
+    wave_reset(W, mstart);
+    auto step = [&](int kt, Tile& cur, Tile& nxt) {
+      const int64_t key0 = row0 + (int64_t)kt * KT;
+      if (kt + 1 < ntiles) {
+        const int64_t rem = nkeys - (int64_t)(kt + 1) * KT;
+        load_tile(nxt, K, key0 + KT, rem < KT ? (int)rem : KT, Hkv, g, vt_col + (kt + 1) * KT, ldv,
+                  wave, lane);
+      }
+      const int64_t remk = nkeys - (int64_t)kt * KT;
+      const int nv = remk < KT ? (int)remk : KT;
+      if (wave_live) {
+#pragma unroll 1
+        for (int sub = 0; sub < 2; ++sub) {
+          const int nvs = nv - 32 * sub;
+          const int64_t k0 = key0 + 32 * sub;
+          if (nvs > 0 && k0 <= wrow_max) {
+            const bool need_mask = (k0 + 31 > wrow_min) || nvs < 32;
+            wave_subtile<true>(W, cur.k, cur.v, sub, lane, nvs, k0, my_row, sl2e, need_mask);
+          }
+        }
+      }
+      wait_tile();
+    };
+    load_tile(tA, K, row0, nkeys < KT ? (int)nkeys : KT, Hkv, g, vt_col, ldv, wave, lane);
+    wait_tile();
+    for (int kt = 0; kt < ntiles; kt += 2) {
+      step(kt, tA, tB);
+      if (kt + 1 < ntiles) step(kt + 1, tB, tA);
     }
-    const int64_t remk = nkeys - (int64_t)kt * KT;
-    const int nv = remk < KT ? (int)remk : KT;
-    if (wave_live && key0 <= wrow_max) {
-      const bool need_mask = (key0 + KT - 1 > wrow_min) || nv < KT;
-      wave_tile<true>(W, sm.k[kt & 1], sm.v[kt & 1], lane, nv, key0, my_row, sl2e, need_mask);
-    }
-    if (kt + 1 < ntiles) store_tile(pf, sm.k[(kt + 1) & 1], sm.v[(kt + 1) & 1], tid);
-    __syncthreads();
+    if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb) mstart[qb] = W.mseen[qb];
   }
-  if (!valid) return;
-  const int h = lane >> 5;
-  float l = W.l + __shfl_xor(W.l, 32);
-  if (part_o != nullptr && KH > 0) {
-    // merge with the history partials of this (row, head): eqs. (7)-(8)
-    const int64_t nhist = c < KH ? c : KH;
-    const int64_t ebase = ph * KH;
-    float M = W.m;
-    for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
-    const float ws = __builtin_amdgcn_exp2f(W.m - M);
-    l *= ws;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) W.o[db][r] *= ws;
-    for (int64_t s = 0; s < nhist; ++s) {
-      const float wgt = __builtin_amdgcn_exp2f(part_lse[ebase + s] - M);
-      l += wgt;
-      const _Float16* src = part_o + (size_t)(ebase + s) * kHeadDim;
+  for (int qb = 0; qb < QB; ++qb) {
+    float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
+    if (!valid[qb]) continue;
+    if (part_o != nullptr && KH > 0) {
+      // merge with this (row, head)'s history partials: eqs. (7)-(8)
+      const int64_t nhist = c < KH ? c : KH;
+      const int64_t ebase = ph[qb] * KH;
+      float M = W.m[qb];
+      for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
+      const float ws = __builtin_amdgcn_exp2f(W.m[qb] - M);
+      l *= ws;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-          typedef _Float16 h4 __attribute__((ext_vector_type(4)));
-          const h4 v = *reinterpret_cast<const h4*>(src + 32 * db + 8 * r4 + 4 * h);
+        for (int r = 0; r < 16; ++r) W.o[qb][db][r] *= ws;
+      for (int64_t s = 0; s < nhist; ++s) {
+        const float wgt = __builtin_amdgcn_exp2f(part_lse[ebase + s] - M);
+        l += wgt;
+        const _Float16* src = part_o + (size_t)(ebase + s) * kHeadDim;
 #pragma unroll
-          for (int t = 0; t < 4; ++t) W.o[db][4 * r4 + t] += wgt * (float)v[t];
-        }
+        for (int db = 0; db < 4; ++db)
+#pragma unroll
+          for (int r4 = 0; r4 < 4; ++r4) {
+            const h4 v = *reinterpret_cast<const h4*>(src + 32 * db + 8 * r4 + 4 * h);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) W.o[qb][db][4 * r4 + t] += wgt * (float)v[t];
+          }
+      }
     }
+    const float inv = 1.f / l;
+    uint16_t* dst = O + ph[qb] * kHeadDim;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r4 = 0; r4 < 4; ++r4) {
+        b4 v;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) v[t] = (__bf16)(W.o[qb][db][4 * r4 + t] * inv);
+        *reinterpret_cast<b4*>(dst + 32 * db + 8 * r4 + 4 * h) = v;
+      }
   }
-  const float inv = 1.f / l;
-  uint16_t* dst = O + ph * kHeadDim;
-#pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int r4 = 0; r4 < 4; ++r4) {
-      typedef __bf16 b4 __attribute__((ext_vector_type(4)));
-      b4 v;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) v[t] = (__bf16)(W.o[db][4 * r4 + t] * inv);
-      *reinterpret_cast<b4*>(dst + 32 * db + 8 * r4 + 4 * h) = v;
-    }
 }
 
 }  // namespace
 
+int64_t vt_padded_block(int64_t B) { return ceil_div(B, KT) * KT; }
+
 hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                                 const void* V, const BucketBufs& b, void* part_o, float* part_lse,
-                                 hipStream_t s) {
+                                 const void* Vt, const BucketBufs& b, void* part_o,
+                                 float* part_lse, hipStream_t s) {
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   const float sl2e = P.scale * kLog2e;
+  const int64_t Bpad = vt_padded_block(P.B);
+  const int64_t ldv = P.n * Bpad;
   const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
   attn_hist_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V, b.tile_map, b.tile_off, b.bin_off,
-      b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh, sl2e);
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, b.tile_map, b.tile_off,
+      b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, Bpad, ldv, P.KH,
+      P.nh, sl2e);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* V,
+hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* Vt,
                                  const void* part_o, const float* part_lse, void* O, bool dense,
                                  hipStream_t s) {
   const float sl2e = P.scale * kLog2e;
   const int64_t B = dense ? P.N : P.B;
   const int64_t n = dense ? 1 : P.n;
-  const int tiles_per_block = (int)ceil_div(B * P.G, 128);
+  const int64_t Bpad = vt_padded_block(B);
+  const int64_t ldv = n * Bpad;
+  const int tiles_per_block = (int)ceil_div(B * P.G, kGroupQ);
   dim3 grid((unsigned)(n * tiles_per_block), (unsigned)P.Hkv);
   attn_self_bf16<<<grid, kThreads, 0, s>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)V,
-      dense ? nullptr : (const _Float16*)part_o, dense ? nullptr : part_lse, (uint16_t*)O, P.N, P.Hq,
-      P.Hkv, P.G, B, dense ? 0 : P.KH, n, tiles_per_block, sl2e);
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt,
+      dense ? nullptr : (const _Float16*)part_o, dense ? nullptr : part_lse, (uint16_t*)O, P.N,
+      P.Hq, P.Hkv, P.G, B, Bpad, ldv, dense ? 0 : P.KH, n, tiles_per_block, sl2e);
   return hipGetLastError();
 }
 

@@ -10,9 +10,9 @@
 namespace moba {
 
 hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                                 const void* V, const BucketBufs& b, void* part_o, float* part_lse,
-                                 hipStream_t s);
-hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* V,
+                                 const void* Vt, const BucketBufs& b, void* part_o,
+                                 float* part_lse, hipStream_t s);
+hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* Vt,
                                  const void* part_o, const float* part_lse, void* O, bool dense,
                                  hipStream_t s);
 
@@ -109,24 +109,27 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
   const int g = (int)(bin / nh);
   const int64_t j = bin % nh;
   const int qi = threadIdx.x / kSub, sub = threadIdx.x % kSub;
-  const int64_t my_e = e_begin + qi;
-  const bool valid = my_e < e_end;
-  const uint32_t ev = valid ? entries[my_e] : 0u;
-  QState S;
-  init_state(S, Q + (int64_t)(ev / (uint32_t)KH) * kHeadDim, valid, sub);
-  for (int k0 = 0; k0 < B; k0 += KT) {
-    const int nv = (B - k0) < KT ? B - k0 : KT;
-    __syncthreads();
-    load_tile(ks, vs, K, V, (int64_t)j * B + k0, nv, Hkv, g);
-    __syncthreads();
-    tile_step(S, ks, vs, sub, sl2e, [&](int t) { return t < nv; });
-  }
-  if (!valid) return;
-  const float inv = 1.f / S.l;
-  float* dst = part_o + (size_t)ev * kHeadDim + sub * kDim;
+  for (int64_t base = e_begin; base < e_begin + kTileQ && base < e_end; base += kQ) {
+    const int64_t my_e = base + qi;
+    const bool valid = my_e < e_end;
+    const uint32_t ev = valid ? entries[my_e] : 0u;
+    QState S;
+    init_state(S, Q + (int64_t)(ev / (uint32_t)KH) * kHeadDim, valid, sub);
+    for (int k0 = 0; k0 < B; k0 += KT) {
+      const int nv = (B - k0) < KT ? B - k0 : KT;
+      __syncthreads();
+      load_tile(ks, vs, K, V, (int64_t)j * B + k0, nv, Hkv, g);
+      __syncthreads();
+      tile_step(S, ks, vs, sub, sl2e, [&](int t) { return t < nv; });
+    }
+    if (valid) {
+      const float inv = 1.f / S.l;
+      float* dst = part_o + (size_t)ev * kHeadDim + sub * kDim;
 #pragma unroll
-  for (int c = 0; c < kDim; ++c) dst[c] = S.o[c] * inv;
-  if (sub == 0) part_lse[ev] = S.m + __builtin_log2f(S.l);
+      for (int c = 0; c < kDim; ++c) dst[c] = S.o[c] * inv;
+      if (sub == 0) part_lse[ev] = S.m + __builtin_log2f(S.l);
+    }
+  }
 }
 
 __global__ __launch_bounds__(kThreads) void attn_self_f32(
@@ -191,9 +194,9 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
 }  // namespace
 
 hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                            const void* V, const BucketBufs& b, void* part_o, float* part_lse,
-                            hipStream_t s) {
-  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_hist_bf16(P, bp, Q, K, V, b, part_o, part_lse, s);
+                            const void* V, const void* Vt, const BucketBufs& b, void* part_o,
+                            float* part_lse, hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_hist_bf16(P, bp, Q, K, Vt, b, part_o, part_lse, s);
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   attn_hist_f32<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
       (const float*)Q, (const float*)K, (const float*)V, b.tile_map, b.tile_off, b.bin_off,
@@ -202,9 +205,10 @@ hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, 
 }
 
 hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
-                            const int32_t* /*sel*/, const void* part_o, const float* part_lse,
-                            void* O, bool dense, hipStream_t s) {
-  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_self_bf16(P, Q, K, V, part_o, part_lse, O, dense, s);
+                            const void* Vt, const void* part_o, const float* part_lse, void* O,
+                            bool dense, hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16)
+    return launch_attn_self_bf16(P, Q, K, Vt, part_o, part_lse, O, dense, s);
   const int64_t B = dense ? P.N : P.B;
   const int64_t n = dense ? 1 : P.n;
   const int tiles_per_block = (int)ceil_div(B * P.G, kQ);

@@ -69,8 +69,15 @@ size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 
 struct Layout {
   size_t kbar, mp_part, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
-      part_lse, part_o, total;
+      part_lse, part_o, vt, total;
 };
+
+// Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
+size_t vt_bytes(const Prob& P, int64_t B) {
+  if (P.dtype != MOBA_DTYPE_BF16) return 0;
+  const int64_t n = ceil_div(P.N, B);
+  return sizeof(uint16_t) * (size_t)P.Hkv * P.d * (size_t)(n * vt_padded_block(B));
+}
 
 // Workspace layout; `full` = prefill (all stages), else select only.
 Layout plan_ws(const Prob& P, bool full) {
@@ -97,6 +104,7 @@ Layout plan_ws(const Prob& P, bool full) {
     const size_t slots = (size_t)(P.N * P.Hq) * (size_t)P.KH;
     L.part_lse = take(sizeof(float) * slots);
     L.part_o = take(part_elem_bytes(P) * slots * P.d);
+    L.vt = take(vt_bytes(P, P.B));
   }
   L.total = off;
   return L;
@@ -199,12 +207,18 @@ int moba_prefill_ex(const moba_problem_t* p, const void* q, const void* k, const
   if ((rc = record(events, 3, s))) return rc;
   void* part_o = at<void>(workspace, L.part_o);
   float* part_lse = at<float>(workspace, L.part_lse);
-  e = launch_attn_hist(P, bp, q, k, v, bb, part_o, part_lse, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
+  void* vt = at<void>(workspace, L.vt);
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    e = launch_vt_pack(v, vt, P.N, P.Hkv, P.B, s);
+    if (e != hipSuccess) return hip_fail(e, "V pack");
+  }
   if ((rc = record(events, 4, s))) return rc;
-  e = launch_attn_self(P, q, k, v, sel, part_o, part_lse, o, false, s);
+  e = launch_attn_hist(P, bp, q, k, v, vt, bb, part_o, part_lse, s);
+  if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
+  if ((rc = record(events, 5, s))) return rc;
+  e = launch_attn_self(P, q, k, v, vt, part_o, part_lse, o, false, s);
   if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
-  return record(events, 5, s);
+  return record(events, 6, s);
 }
 
 int moba_prefill(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
@@ -224,19 +238,36 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
   return run_select(P, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
 }
 
-int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, const void* v,
-                      void* o, void* stream) {
+static int dense_prob(const moba_problem_t* p, Prob* P) {
   if (!p) return fail(MOBA_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
   // block_size and topk do not apply: one block spanning the sequence, no history
   moba_problem_t d = *p;
   d.block_size = p->seqlen > 0 && p->seqlen < INT32_MAX ? (int32_t)p->seqlen : 1;
   d.topk = 1;
+  return make_prob(&d, P);
+}
+
+size_t moba_dense_workspace_size(const moba_problem_t* p) {
   Prob P;
-  int rc = make_prob(&d, &P);
+  if (dense_prob(p, &P) != MOBA_OK) return 0;
+  const size_t t = align_up(vt_bytes(P, P.N));
+  return t > 0 ? t : kAlign;
+}
+
+int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                      void* o, void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = dense_prob(p, &P);
   if (rc) return rc;
   const void* ptrs[4] = {q, k, v, o};
   if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
-  hipError_t e = launch_attn_self(P, q, k, v, nullptr, nullptr, nullptr, o, true, (hipStream_t)stream);
+  if ((rc = check_ws(workspace, ws_bytes, align_up(vt_bytes(P, P.N))))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    hipError_t e = launch_vt_pack(v, workspace, P.N, P.Hkv, P.N, s);
+    if (e != hipSuccess) return hip_fail(e, "V pack");
+  }
+  hipError_t e = launch_attn_self(P, q, k, v, workspace, nullptr, nullptr, o, true, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "dense causal attention");
 }
 

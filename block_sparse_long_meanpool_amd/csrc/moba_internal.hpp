@@ -15,7 +15,7 @@ namespace moba {
 constexpr int kHeadDim = 128;       // head_dim compiled in
 constexpr int kMaxTopk = 32;        // topk limit (selection lists live in LDS)
 constexpr int64_t kMaxHist = 8192;  // history-capable blocks (bucket bitmaps live in LDS)
-constexpr int kTileQ = 128;         // routed queries per history-attention tile
+constexpr int kTileQ = 256;         // routed queries per history-attention tile
 constexpr int kMaxGroup = 64;       // Hq / Hkv limit
 
 // Problem with derived sizes; built and validated on the host.
@@ -62,18 +62,23 @@ hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, in
 hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
                          const BucketBufs& b, hipStream_t s);
 
+// bf16 kernels read V through a transposed, block-padded, key-permuted copy
+// Vt [Hkv][d][n * Bpad] (see vpack.hip); fp32 kernels read V directly.
+int64_t vt_padded_block(int64_t B);
+hipError_t launch_vt_pack(const void* V, void* Vt, int64_t N, int Hkv, int64_t B, hipStream_t s);
+
 // History-block attention over the bucketed entries; writes normalised partials
 // part_o [entry][d] and log2-sum-exp part_lse [entry].
 hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                            const void* V, const BucketBufs& b, void* part_o, float* part_lse,
-                            hipStream_t s);
+                            const void* V, const void* Vt, const BucketBufs& b, void* part_o,
+                            float* part_lse, hipStream_t s);
 
 // Own-block causal attention fused with the merge of the history partials.
 // With dense=true: one block covering the whole sequence and no partials
-// (causal full attention).
+// (causal full attention); Vt must then be packed with B = N.
 hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
-                            const int32_t* sel, const void* part_o, const float* part_lse,
-                            void* O, bool dense, hipStream_t s);
+                            const void* Vt, const void* part_o, const float* part_lse, void* O,
+                            bool dense, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);

@@ -99,14 +99,14 @@ MOBA_API int moba_prefill(const moba_problem_t *p, const void *q, const void *k,
                  void *workspace, size_t ws_bytes, void *stream);
 
 /* Stage boundaries that moba_prefill_ex can time. */
-#define MOBA_STAGE_EVENTS 6 /* start, after meanpool, gate_topk, bucket, history attn, self+merge */
+#define MOBA_STAGE_EVENTS 7
 
 /*
  * moba_prefill with optional per-stage timing: if `events` is not NULL it
  * points to MOBA_STAGE_EVENTS caller-created hipEvent_t handles, recorded on
- * `stream` before the first stage and after each of the five stages
- * (meanpool, gate_topk, bucket, history attention, own-block attention with
- * merge). Otherwise identical to moba_prefill.
+ * `stream` before the first stage and after each of: meanpool, gate_topk,
+ * bucket, the V layout pack (bf16 only; empty for fp32), history attention,
+ * own-block attention with merge. Otherwise identical to moba_prefill.
  */
 MOBA_API int moba_prefill_ex(const moba_problem_t *p, const void *q, const void *k, const void *v, void *o,
                     void *workspace, size_t ws_bytes, void *stream, void *const *events);
@@ -122,10 +122,12 @@ MOBA_API int moba_select(const moba_problem_t *p, const void *q, const void *k, 
 /*
  * Dense causal softmax attention on the same tensors (PaperTrace section 1,
  * eq. (1) with a causal mask): the full-attention baseline MoBA is measured
- * against. block_size and topk of *p are ignored. No workspace.
+ * against. block_size and topk of *p are ignored. The workspace (device,
+ * 256-byte aligned) holds a transposed copy of V for bf16 inputs.
  */
+MOBA_API size_t moba_dense_workspace_size(const moba_problem_t *p);
 MOBA_API int moba_dense_causal(const moba_problem_t *p, const void *q, const void *k, const void *v,
-                      void *o, void *stream);
+                               void *o, void *workspace, size_t ws_bytes, void *stream);
 
 /* Static text for a status code. */
 MOBA_API const char *moba_status_string(int status);

@@ -75,7 +75,7 @@ def test_invalid_problems_rejected_before_any_hip_call(kw, code):
     assert lib.moba_select(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == code
     if not ({"block_size", "topk"} & set(kw)) and "N" not in kw or kw.get("N") == 0:
         # the dense baseline ignores block_size and topk
-        assert lib.moba_dense_causal(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, None) == code
+        assert lib.moba_dense_causal(ctypes.byref(p), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == code
     assert lib.moba_last_error()
 
 
