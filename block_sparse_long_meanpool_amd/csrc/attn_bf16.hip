@@ -35,12 +35,21 @@ namespace moba {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
-constexpr int kThreads = 256;
-constexpr int QB = 2;                       // 32-query blocks per wave
+#ifndef MOBA_ATTN_QB
+#define MOBA_ATTN_QB 1
+#endif
+#ifndef MOBA_ATTN_WAVES
+#define MOBA_ATTN_WAVES 8
+#endif
+constexpr int QB = MOBA_ATTN_QB;            // 32-query blocks per wave
+constexpr int NW = MOBA_ATTN_WAVES;         // waves per workgroup
+constexpr int kThreads = 64 * NW;
 constexpr int kWaveQ = 32 * QB;             // queries per wave
-constexpr int kGroupQ = 4 * kWaveQ;         // queries per workgroup
+constexpr int kGroupQ = NW * kWaveQ;        // queries per workgroup
+constexpr int kLoadsPerWave = 16 / NW;      // 1 KB tile copies per wave (K and V each)
 static_assert(kGroupQ == kTileQ, "history tiles are one workgroup");
 constexpr int KT = 64;                      // keys per LDS tile
 constexpr int KS_ROW = kHeadDim;            // bf16 per K row in LDS (256 B, swizzled)
@@ -50,47 +59,68 @@ constexpr int VT_ELEMS = kHeadDim * VT_ROW;
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kRedoSlack = 64.f;          // scores this far above the reference max force a re-run
 
-// One LDS tile buffer. The kernels declare two distinct buffers and unroll the
-// key loop by two, so the compiler can see that the copies into one buffer
-// never alias the operand reads from the other (and need not wait for them).
-struct __align__(16) Tile {
-  uint16_t k[KS_ELEMS];
-  uint16_t v[VT_ELEMS];
+// One LDS tile buffer: a K part and a V^T part. The kernels declare each part
+// of each of the three buffers as its own __shared__ array and unroll the key
+// loop by three, so the compiler can see that the copies into one buffer never
+// alias the operand reads from another (and need not wait for them).
+struct Tile {
+  uint16_t* k;  // [KT][KS_ROW]
+  uint16_t* v;  // [kHeadDim][VT_ROW]
 };
+#define MOBA_DECLARE_TILES                                                  \
+  __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS],    \
+      lds_k2[KS_ELEMS];                                                     \
+  __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS],    \
+      lds_v2[VT_ELEMS];                                                     \
+  Tile tA{lds_k0, lds_v0}, tB{lds_k1, lds_v1}, tC{lds_k2, lds_v2};
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
 
-// K row r keeps 16-byte chunk c at position c ^ (r & 15); V^T row d keeps chunk
-// c at c ^ (d & 7).
+// K row r keeps 16-byte chunk c at position c ^ (r & 15); V^T row d (two rows
+// per 64 banks) keeps chunk c at c ^ (d & 7) ^ ((d >> 3) & 1). With these, the
+// 16 lanes served together by one ds_read_b128 cycle hit 16 distinct bank quads.
+__device__ inline int k_swz(int row, int c) { return c ^ (row & 15); }
+__device__ inline int vt_swz(int d, int c) { return c ^ (d & 7) ^ ((d >> 3) & 1); }
 __device__ inline const uint16_t* k_chunk(const uint16_t* ks, int row, int c) {
-  return ks + row * KS_ROW + ((c ^ (row & 15)) << 3);
+  return ks + row * KS_ROW + (k_swz(row, c) << 3);
 }
 __device__ inline const uint16_t* vt_chunk(const uint16_t* vt, int d, int c) {
-  return vt + d * VT_ROW + ((c ^ (d & 7)) << 3);
+  return vt + d * VT_ROW + (vt_swz(d, c) << 3);
 }
 
-// Issue the global -> LDS copies of one tile: keys [key0, key0+64) of K (rows
-// >= nvalid re-read row 0: those keys are masked) and the 64 matching packed
-// V^T columns (block pads are zero). Each wave copies 4 KB of K and 4 KB of V^T,
-// 1 KB (64 lanes x 16 B) per instruction; the caller waits and barriers.
-__device__ inline void load_tile(Tile& t, const uint16_t* __restrict__ K,
-                                 int64_t key0, int nvalid, int Hkv, int g,
-                                 const uint16_t* __restrict__ vt_col, int64_t ldv, int wave,
-                                 int lane) {
+// Buffer-resource word 3 for plain (untyped, raw) buffer accesses.
+constexpr int kRawBufferFlags = 0x00020000;
+
+// Issue the global -> LDS copies of one tile: keys [key0, key0+64) of K and
+// the 64 matching packed V^T columns (block pads are zero). Each wave copies
+// 16/NW KB of K and of V^T, 1 KB (64 lanes x 16 B) per buffer_load ... lds;
+// the buffer resources are rebased per tile on the scalar side, so the
+// per-lane offsets are loop invariant, and K rows past nvalid fall outside
+// the resource's range and read as zero. The caller waits and barriers.
+__device__ inline void load_tile(Tile t, const uint16_t* __restrict__ K, int64_t key0,
+                                 int nvalid, int Hkv, int g, const uint16_t* __restrict__ vt_col,
+                                 int64_t ldv, int wave, int lane) {
+  const int64_t krow = (int64_t)Hkv * kHeadDim;  // elements between consecutive keys
+  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(K + (key0 * Hkv + g) * kHeadDim), 0,
+      (int)(((int64_t)(nvalid - 1) * krow + kHeadDim) * 2), kRawBufferFlags);
+  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)vt_col, 0, (int)(((int64_t)(kHeadDim - 1) * ldv + KT) * 2), kRawBufferFlags);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = 16 * wave + 4 * i + (lane >> 4);
-    const int c = (lane & 15) ^ (r & 15);
-    const int rr = r < nvalid ? r : 0;
-    const uint16_t* src = K + ((key0 + rr) * Hkv + g) * kHeadDim + 8 * c;
-    __builtin_amdgcn_global_load_lds(src, t.k + (16 * wave + 4 * i) * KS_ROW, 16, 0, 0);
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int ii = wave * kLoadsPerWave + i;  // 4 K rows per copy
+    const int r = 4 * ii + (lane >> 4);
+    const int c = k_swz(r, lane & 15);  // the swizzle is an involution in c
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, t.k + 4 * ii * KS_ROW, 16,
+                                             (unsigned)((r * krow + 8 * c) * 2), 0, 0, 0);
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int d = 32 * wave + 8 * i + (lane >> 3);
-    const int c = (lane & 7) ^ (d & 7);
-    const uint16_t* src = vt_col + (int64_t)d * ldv + 8 * c;
-    __builtin_amdgcn_global_load_lds(src, t.v + (32 * wave + 8 * i) * VT_ROW, 16, 0, 0);
+  for (int i = 0; i < kLoadsPerWave; ++i) {
+    const int ii = wave * kLoadsPerWave + i;  // 8 V^T rows per copy
+    const int d = 8 * ii + (lane >> 3);
+    const int c = vt_swz(d, lane & 7);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, t.v + 8 * ii * VT_ROW, 16,
+                                             (unsigned)((d * ldv + 8 * c) * 2), 0, 0, 0);
   }
 }
 
@@ -146,17 +176,10 @@ __device__ inline bool wave_needs_redo(const Wave& W, const bool (&valid)[QB]) {
 // Key row (0..31) of accumulator element r in the 32x32 MFMA output layout.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
 
-// One 32-key subtile `sub` of the LDS tile (ks, vt). Keys >= nvalid (counted
-// from the subtile start) are masked; when CAUSAL, also keys with
-// key0 + key > qrow.
-template <bool CAUSAL>
-__device__ inline void wave_subtile(Wave& W, const uint16_t* ks_tile, const uint16_t* vt, int sub,
-                                    int lane, int nvalid, int64_t key0, const int64_t (&qrow)[QB],
-                                    float sl2e, bool need_mask) {
+// S^T for 32-key subtile `sub` of an LDS tile: 8 matrix-core ops per query block.
+__device__ inline void wave_qk(const Wave& W, Tile t, int sub, int lane, f32x16 (&s)[QB]) {
   const int h = lane >> 5, lr = lane & 31;
-  const uint16_t* ks = ks_tile + sub * 32 * KS_ROW;  // row swizzle uses (row & 15): same for row+32
-  const int csub = 4 * sub;
-  f32x16 s[QB];
+  const uint16_t* ks = t.k + sub * 32 * KS_ROW;  // the row swizzle uses (row & 15): same for row+32
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
@@ -168,6 +191,15 @@ __device__ inline void wave_subtile(Wave& W, const uint16_t* ks_tile, const uint
     for (int qb = 0; qb < QB; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, W.q[qb][kk], s[qb], 0, 0, 0);
   }
+}
+
+// Softmax of one subtile's scores and its P.V product. Keys >= nvalid (from the
+// subtile start) are masked; when CAUSAL, also keys with key0 + key > qrow.
+template <bool CAUSAL>
+__device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int lane,
+                                 int nvalid, int64_t key0, const int64_t (&qrow)[QB], float sl2e,
+                                 bool need_mask) {
+  const int h = lane >> 5, lr = lane & 31;
   if (need_mask) {
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb)
@@ -189,30 +221,101 @@ __device__ inline void wave_subtile(Wave& W, const uint16_t* ks_tile, const uint
     if (W.m[qb] == -INFINITY) W.m[qb] = v;  // first unmasked keys fix the reference
   }
   bf16x8 p[QB][2];
+  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float muse = (W.m[qb] == -INFINITY) ? 0.f : W.m[qb];
-    float lsum = 0.f;
+    float lsum = W.l[qb];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        const float e = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + t], sl2e, -muse));
-        lsum += e;
-        p[qb][u][t] = (__bf16)e;
+      for (int e = 0; e < 8; e += 2) {
+        bf16x2 e2;
+        e2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e], sl2e, -muse));
+        e2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e + 1], sl2e, -muse));
+        p[qb][u][e] = e2[0];
+        p[qb][u][e + 1] = e2[1];
+        // the row sum adds the same rounded weights that multiply V
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, lsum, false);
       }
-    W.l[qb] += lsum;
+    W.l[qb] = lsum;
   }
+  const int csub = 4 * sub;
 #pragma unroll
   for (int u = 0; u < 2; ++u)
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
-      const bf16x8 a =
-          as_bf16x8(*reinterpret_cast<const uint4*>(vt_chunk(vt, 32 * db + lr, csub + 2 * u + h)));
+      const bf16x8 a = as_bf16x8(
+          *reinterpret_cast<const uint4*>(vt_chunk(t.v, 32 * db + lr, csub + 2 * u + h)));
 #pragma unroll
       for (int qb = 0; qb < QB; ++qb)
         W.o[qb][db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, p[qb][u], W.o[qb][db], 0, 0, 0);
     }
+}
+
+// Stream keys [key0, key0 + nkeys) of one block (K rows from K, V^T columns
+// from vt_col) through three LDS tile buffers and run the wave pipeline:
+// the scores of the next subtile are issued to the matrix cores before the
+// softmax of the current one, so exponentials overlap matrix work inside
+// each wave. One barrier per 64-key tile; the copy of tile t+2 starts right
+// after the barrier that publishes tile t+1 and lands in the buffer tile t-1
+// used (every wave is past it by then). Waves whose rows start after a
+// subtile (CAUSAL) or that hold no queries skip its compute, never a barrier.
+template <bool CAUSAL, bool FULL>
+__device__ inline void run_block(Wave& W, Tile b0, Tile b1, Tile b2,
+                                 const uint16_t* __restrict__ K, int64_t key0, int64_t nkeys,
+                                 int Hkv, int g, const uint16_t* __restrict__ vt_col, int64_t ldv,
+                                 int wave, int lane, const int64_t (&qrow)[QB], int64_t wrow_min,
+                                 int64_t wrow_max, bool wave_live, float sl2e) {
+  const int nt = (int)((nkeys + KT - 1) / KT);
+  // FULL: every subtile has 32 keys and every wave computes (the caller checked)
+  auto nvs_of = [&](int t, int sub) -> int {
+    if (FULL) return 32;
+    const int64_t rem = nkeys - (int64_t)t * KT - 32 * sub;
+    return rem <= 0 ? 0 : (rem < 32 ? (int)rem : 32);
+  };
+  auto active = [&](int t, int sub) -> bool {
+    if (FULL) return true;
+    if (!wave_live || nvs_of(t, sub) == 0) return false;
+    return !CAUSAL || key0 + (int64_t)t * KT + 32 * sub <= wrow_max;
+  };
+  auto issue = [&](int t, Tile dst) {
+    const int64_t rem = nkeys - (int64_t)t * KT;
+    load_tile(dst, K, key0 + (int64_t)t * KT, rem < KT ? (int)rem : KT, Hkv, g, vt_col + t * KT,
+              ldv, wave, lane);
+  };
+  auto smpv = [&](f32x16 (&s)[QB], Tile cur, int t, int sub) {
+    const int nv = nvs_of(t, sub);
+    const int64_t k0 = key0 + (int64_t)t * KT + 32 * sub;
+    const bool need_mask = nv < 32 || (CAUSAL && k0 + 31 > wrow_min);
+    wave_smpv<CAUSAL>(W, s, cur, sub, lane, nv, k0, qrow, sl2e, need_mask);
+  };
+  f32x16 sa[QB], sb[QB];
+  auto step = [&](int t, Tile cur, Tile nxt, Tile spare) {
+    // entering: sa holds the scores of (t, 0) when that subtile is active.
+    // Scheduling barriers keep each phase's matrix ops next to the vector
+    // work they are meant to overlap instead of letting later phases hoist.
+    if (active(t, 1)) wave_qk(W, cur, 1, lane, sb);
+    if (active(t, 0)) smpv(sa, cur, t, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (t + 1 < nt) {
+      wait_tile();
+      if (t + 2 < nt) issue(t + 2, spare);
+      if (active(t + 1, 0)) wave_qk(W, nxt, 0, lane, sa);
+    }
+    if (active(t, 1)) smpv(sb, cur, t, 1);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  issue(0, b0);
+  wait_tile();
+  if (nt > 1) issue(1, b1);
+  if (active(0, 0)) wave_qk(W, b0, 0, lane, sa);
+  for (int t = 0; t < nt; t += 3) {
+    step(t, b0, b1, b2);
+    if (t + 1 < nt) step(t + 1, b1, b2, b0);
+    if (t + 2 < nt) step(t + 2, b2, b0, b1);
+  }
+  __syncthreads();  // all waves are done with the buffers before they are reused
 }
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
@@ -228,7 +331,7 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
     const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
     float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad, int64_t ldv, int KH, int64_t nh,
     float sl2e) {
-  __shared__ Tile tA, tB;
+  MOBA_DECLARE_TILES
   // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
   // contiguous range of tiles so the tiles of one K/V block share its L2.
   // The grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
@@ -266,29 +369,12 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
   for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
   for (int attempt = 0;; ++attempt) {
     wave_reset(W, mstart);
-    auto step = [&](int kt, Tile& cur, Tile& nxt) {
-      if (kt + 1 < ntiles) {
-        const int rem = B - (kt + 1) * KT;
-        load_tile(nxt, K, kbase + (int64_t)(kt + 1) * KT, rem < KT ? rem : KT, Hkv, g,
-                  vt_col + (kt + 1) * KT, ldv, wave, lane);
-      }
-      const int nv = (B - kt * KT) < KT ? B - kt * KT : KT;
-      if (wave_live) {
-#pragma unroll 1
-        for (int sub = 0; sub < 2; ++sub) {
-          const int nvs = nv - 32 * sub;
-          if (nvs > 0)
-            wave_subtile<false>(W, cur.k, cur.v, sub, lane, nvs, 0, dummy_row, sl2e, nvs < 32);
-        }
-      }
-      wait_tile();
-    };
-    load_tile(tA, K, kbase, B < KT ? B : KT, Hkv, g, vt_col, ldv, wave, lane);
-    wait_tile();
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      step(kt, tA, tB);
-      if (kt + 1 < ntiles) step(kt + 1, tB, tA);
-    }
+    if (B % KT == 0 && e_begin + kGroupQ <= e_end)
+      run_block<false, true>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                             dummy_row, 0, 0, wave_live, sl2e);
+    else
+      run_block<false, false>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                              dummy_row, 0, 0, wave_live, sl2e);
     // workgroup-uniform decision: re-run only if some score overran the reference max
     if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
 #pragma unroll
@@ -323,7 +409,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const _Float16* __restrict__ part_o, const float* __restrict__ part_lse,
     uint16_t* __restrict__ O, int64_t N, int Hq, int Hkv, int G, int64_t B, int64_t Bpad,
     int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
-  __shared__ Tile tA, tB;
+  MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int g = blockIdx.y;
   // heavier (later) row tiles first
@@ -366,34 +452,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
   for (int attempt = 0;; ++attempt) {
     wave_reset(W, mstart);
-    auto step = [&](int kt, Tile& cur, Tile& nxt) {
-      const int64_t key0 = row0 + (int64_t)kt * KT;
-      if (kt + 1 < ntiles) {
-        const int64_t rem = nkeys - (int64_t)(kt + 1) * KT;
-        load_tile(nxt, K, key0 + KT, rem < KT ? (int)rem : KT, Hkv, g, vt_col + (kt + 1) * KT, ldv,
-                  wave, lane);
-      }
-      const int64_t remk = nkeys - (int64_t)kt * KT;
-      const int nv = remk < KT ? (int)remk : KT;
-      if (wave_live) {
-#pragma unroll 1
-        for (int sub = 0; sub < 2; ++sub) {
-          const int nvs = nv - 32 * sub;
-          const int64_t k0 = key0 + 32 * sub;
-          if (nvs > 0 && k0 <= wrow_max) {
-            const bool need_mask = (k0 + 31 > wrow_min) || nvs < 32;
-            wave_subtile<true>(W, cur.k, cur.v, sub, lane, nvs, k0, my_row, sl2e, need_mask);
-          }
-        }
-      }
-      wait_tile();
-    };
-    load_tile(tA, K, row0, nkeys < KT ? (int)nkeys : KT, Hkv, g, vt_col, ldv, wave, lane);
-    wait_tile();
-    for (int kt = 0; kt < ntiles; kt += 2) {
-      step(kt, tA, tB);
-      if (kt + 1 < ntiles) step(kt + 1, tB, tA);
-    }
+    run_block<true, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane, my_row,
+                    wrow_min, wrow_max, wave_live, sl2e);
     if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
 #pragma unroll
     for (int qb = 0; qb < QB; ++qb) mstart[qb] = W.mseen[qb];
