@@ -3,69 +3,337 @@
 // blocks excluded and own block forced, section 2; k counts the own block,
 // section 2.1; section 3.1 step 2).
 //
-// Scores are computed in fp64 on the fp64 matrix cores (v_mfma_f64_16x16x4):
-// Q (bf16 or fp32) widens exactly, block keys are fp64, so a selection differs
-// from the exact one only where two scores agree to fp64 rounding. Workgroup =
-// 64 (row, head) pairs of one KV-head group inside one block c, i.e. pairs
-// pi = (row - cB) * G + hh; wave w owns pairs 16w..16w+15 and holds their Q as
-// the A operand in registers for the whole kernel. History blocks 0..c-1 are
-// streamed through LDS in chunks of 32; after each chunk the scores go to LDS
-// and one lane per pair folds them into a running top-(k-1) list kept sorted
-// by (score desc, block asc). The own block c is appended and the row is
-// written ascending and -1 padded.
+// The selection must equal the one defined by exact scores (ties to the lower
+// block index). Scores are therefore computed in two tiers:
+//
+//  1. Fast tier on the bf16 matrix cores. Each fp64 block key is split into
+//     three bf16 planes (hi + mid + lo carries 24 significant bits, residual
+//     <= 2^-24 |kbar|); Q is exactly bf16, so the three products are exact
+//     and only the fp32 accumulation rounds. With n = 386 roundings of unit
+//     <= 2^-23, |s_fast - s| <= eps = 4.7e-5 * |q| * max_b |kbar_b| (Cauchy-
+//     Schwarz on sum |q_c kbar_c|, max over the KV head's blocks). A lane keeps
+//     a sorted top-(KM) list of (score, block) keys for its half of a row's
+//     candidates; the two halves merge and the row is certified when the
+//     k-1'th and k'th scores differ by more than 2 eps (plus the key
+//     truncation): then every exact score of the kept set exceeds every exact
+//     score left out, so the kept set is the exact one.
+//  2. Exact tier: rows that are not certified (near-ties, about 2% of rows
+//     for random data) are marked in `sel` and a second kernel re-scores each
+//     marked row in fp64 with one wave (lane per block, block keys stored
+//     transposed so the reads coalesce) and selects exactly (value
+//     descending, index ascending). fp32 inputs take this exact path for
+//     every row.
+//
+// Workgroup = 4 waves x 32 (row, head) pairs of one KV-head group inside one
+// block c (pairs pi = (row - cB) * G + hh). The bf16 planes of 32 history
+// blocks (24 KB) are streamed into LDS per chunk with buffer_load ... lds into
+// two buffers. The own block c is appended and each row is written ascending
+// and -1 padded.
 #include "moba_internal.hpp"
 
 namespace moba {
 namespace {
 
-typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kThreads = 256;
-constexpr int kPairs = 64;       // pairs per workgroup
-constexpr int kChunk = 32;       // history blocks per LDS chunk (two 16-wide MFMA tiles)
-constexpr int kSteps = kHeadDim / 4;  // 32 MFMA k-steps of 4 over d = 128
-constexpr int kScPad = kChunk + 1;
-constexpr int kListCap = kMaxTopk - 1;
+constexpr int kWaves = 4;
+constexpr int kPairs = 32 * kWaves;       // pairs per workgroup
+constexpr int kChunk = 32;                // history blocks per LDS chunk
+constexpr int kRowBytes = kHeadDim * 2;   // one bf16 plane row of one block
+constexpr int kChunkRows = 3 * kChunk;    // (block, plane) rows per chunk
+constexpr int kChunkElems = kChunkRows * kHeadDim;
+constexpr float kEpsCoef = 4.7e-5f * 1.02f;  // error bound coefficient (see above) with margin
+constexpr int kRawBufferFlags = 0x00020000;
 
-template <typename T>
-__device__ inline void load_q32(const T* p, double (&q)[kSteps]);
-template <>
-__device__ inline void load_q32<__hip_bfloat16>(const __hip_bfloat16* p, double (&q)[kSteps]) {
-  const uint4* v = reinterpret_cast<const uint4*>(p);
+__device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
+__device__ inline int swz(int row, int c) { return c ^ (row & 15); }
+
+// ---------------------------------------------------------------------------
+// Split kernel: kbar fp64 [Hkv][nh][d] -> planes bf16 [Hkv][nh][3][d],
+// per-block Euclidean norms fp32 [Hkv][nh] (rounded up) and a transposed fp64
+// copy [Hkv][d][nhp] for the exact tier.
+// ---------------------------------------------------------------------------
+__device__ inline uint16_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ inline double bf16_to_f64(uint16_t b) { return (double)__uint_as_float((uint32_t)b << 16); }
+
+__global__ __launch_bounds__(kHeadDim) void kbar_split(const double* __restrict__ kbar,
+                                                       uint16_t* __restrict__ planes,
+                                                       float* __restrict__ norms,
+                                                       double* __restrict__ kbarT, int64_t nh,
+                                                       int64_t nhp) {
+  const int64_t blk = blockIdx.x;  // over Hkv * nh
+  const int c = threadIdx.x;
+  const double x = kbar[blk * kHeadDim + c];
+  const int64_t g = blk / nh, b = blk % nh;
+  kbarT[(g * kHeadDim + c) * nhp + b] = x;  // [Hkv][d][nhp]: lane-per-block reads coalesce
+  const uint16_t hi = bf16_rne((float)x);
+  const double r1 = x - bf16_to_f64(hi);
+  const uint16_t mid = bf16_rne((float)r1);
+  const double r2 = r1 - bf16_to_f64(mid);
+  const uint16_t lo = bf16_rne((float)r2);
+  uint16_t* out = planes + blk * 3 * kHeadDim;
+  out[c] = hi;
+  out[kHeadDim + c] = mid;
+  out[2 * kHeadDim + c] = lo;
+  __shared__ double sq[kHeadDim];
+  sq[c] = x * x;
+  __syncthreads();
+  if (c == 0) {
+    double s = 0.0;
+    for (int i = 0; i < kHeadDim; ++i) s += sq[i];
+    norms[blk] = (float)(sqrt(s) * (1.0 + 1e-6));
+  }
+}
+
+// Largest block-key norm per KV head: maxnorm[g] = max_b norms[g][b].
+__global__ __launch_bounds__(256) void kbar_maxnorm(const float* __restrict__ norms,
+                                                    float* __restrict__ maxnorm, int64_t nh) {
+  __shared__ float red[256];
+  const int g = blockIdx.x;
+  float m = 0.f;
+  for (int64_t b = threadIdx.x; b < nh; b += 256) m = fmaxf(m, norms[(size_t)g * nh + b]);
+  red[threadIdx.x] = m;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (threadIdx.x < off) red[threadIdx.x] = fmaxf(red[threadIdx.x], red[threadIdx.x + off]);
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) maxnorm[g] = red[0];
+}
+
+// ---------------------------------------------------------------------------
+// Candidates travel as one sortable 32-bit key: the fp32 score mapped to an
+// order-preserving unsigned integer, its lowest `ib` bits replaced by
+// (2^ib - 1 - block) so that equal truncated scores order by lower block.
+// Keys are unique, so a descending top-KM list is a plain max/min network
+// (two integer ops per slot). Truncation lowers a score by at most 2^ib units
+// in its last place; the certification below accounts for that.
+// ---------------------------------------------------------------------------
+__device__ inline uint32_t score_key(float x, int block, int ib) {
+  const uint32_t u = __float_as_uint(x);
+  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  const uint32_t low = (1u << ib) - 1u;
+  return (k & ~low) | (low - (uint32_t)block);
+}
+__device__ inline float key_score(uint32_t k, int ib) {
+  k &= ~((1u << ib) - 1u);
+  const uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+__device__ inline int key_block(uint32_t k, int ib) {
+  const uint32_t low = (1u << ib) - 1u;
+  return (int)(low - (k & low));
+}
+
+template <int KM>
+struct KeyList {
+  uint32_t k[KM];  // descending
+  __device__ inline void init() {
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint4 u = v[i];
-    const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    for (int t = 0; t < KM; ++t) k[t] = 0u;  // below every real key
+  }
+  __device__ inline void push(uint32_t x) {
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      q[8 * i + 2 * t] = (double)__uint_as_float(w[t] << 16);
-      q[8 * i + 2 * t + 1] = (double)__uint_as_float(w[t] & 0xFFFF0000u);
+    for (int t = 0; t < KM; ++t) {
+      const uint32_t hi = k[t] > x ? k[t] : x;  // unsigned max / min
+      x = k[t] > x ? x : k[t];
+      k[t] = hi;
     }
   }
-}
-template <>
-__device__ inline void load_q32<float>(const float* p, double (&q)[kSteps]) {
-  const float4* v = reinterpret_cast<const float4*>(p);
+};
+
+// out[0..n) = the n block indices of idx[0..n) in ascending order (n <= KM).
+template <int KM>
+__device__ inline void write_sorted(const int (&idx)[KM], int n, int32_t* out) {
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    float4 u = v[i];
-    q[4 * i] = u.x; q[4 * i + 1] = u.y; q[4 * i + 2] = u.z; q[4 * i + 3] = u.w;
+  for (int a = 0; a < KM; ++a) {
+    int rank = 0;
+#pragma unroll
+    for (int b = 0; b < KM; ++b) rank += (b < n && idx[b] < idx[a]) ? 1 : 0;
+    if (a < n) out[rank] = idx[a];
   }
 }
 
-// grid.x: (block c in descending order) * tiles_per_block + tile; grid.y: KV head g.
-template <typename T>
-__global__ __launch_bounds__(kThreads) void gate_topk_kernel(
-    const T* __restrict__ Q, const double* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t N, int Hq, int G, int B, int k, int64_t n, int64_t nh, int tiles_per_block) {
-  __shared__ double kb[kSteps * kChunk * 4];     // [ks][blk][grp]: d = grp*32 + ks
-  __shared__ double sc[kPairs * kScPad];         // [pair][blk]
-  __shared__ double ls[kListCap * kPairs];       // list scores [slot][pair]
-  __shared__ int li[kListCap * kPairs];          // list blocks  [slot][pair]
+// Issue the copy of planes of blocks [cb, cb + 32) (clamped to nh) into one LDS buffer.
+__device__ inline void load_chunk(uint16_t* lds, const uint16_t* __restrict__ planes_g,
+                                  int64_t cb, int64_t nblk, int wave, int lane) {
+  const int64_t have = (nblk - cb) < kChunk ? nblk - cb : kChunk;
+  const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+      (void*)(planes_g + cb * 3 * kHeadDim), 0, (int)(have * 3 * kRowBytes), kRawBufferFlags);
+  // 96 rows of 256 B = 24 copies of 1 KB (4 rows each): 6 per wave
+#pragma unroll
+  for (int i = 0; i < 6; ++i) {
+    const int ii = wave * 6 + i;
+    const int row = 4 * ii + (lane >> 4);
+    const int c = swz(row, lane & 15);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, lds + 4 * ii * kHeadDim, 16,
+                                             (unsigned)(row * kRowBytes + 16 * c), 0, 0, 0);
+  }
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+__device__ inline void wait_chunk() {
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+}
+
+// Scores S^T (32 blocks x 32 pairs) of one chunk: three accumulation chains,
+// one per plane, summed at the end (hi + (mid + lo)).
+__device__ inline void chunk_scores(const uint16_t* lds, const bf16x8 (&q)[8], int lane,
+                                    f32x16& s) {
+  const int h = lane >> 5, lr = lane & 31;
+  f32x16 a0, a1, a2;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a0[r] = a1[r] = a2[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int c = 2 * kk + h;
+    const int r0 = 3 * lr, r1 = 3 * lr + 1, r2 = 3 * lr + 2;
+    const bf16x8 x0 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r0 * kHeadDim + 8 * swz(r0, c)));
+    const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r1 * kHeadDim + 8 * swz(r1, c)));
+    const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r2 * kHeadDim + 8 * swz(r2, c)));
+    a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[kk], a0, 0, 0, 0);
+    a1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, q[kk], a1, 0, 0, 0);
+    a2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x2, q[kk], a2, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = a0[r] + (a1[r] + a2[r]);
+}
+
+constexpr int32_t kRefine = -2;  // sel marker: this row's history needs the exact tier
+
+template <typename T>
+__device__ inline double widen(T x);
+template <>
+__device__ inline double widen<uint16_t>(uint16_t x) {
+  return (double)__uint_as_float((uint32_t)x << 16);
+}
+template <>
+__device__ inline double widen<float>(float x) {
+  return (double)x;
+}
+
+// Exact tier: one wave per 64 consecutive (row, head) pairs; each marked row
+// (or, with all_rows, every row) is re-scored in fp64 — lane b handles blocks
+// b, b+64, ... reading the transposed block keys (coalesced) against q
+// staged in LDS — and selected by (value desc, index asc): each lane keeps a
+// sorted list of its blocks (they arrive in increasing order), then KH rounds
+// of wave arg-max over the list heads pick the kept blocks. Writes the whole
+// row: kept blocks ascending, own block, -1 padding.
+template <typename T, int KM>
+__global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
+                                                  const double* __restrict__ kbarT,
+                                                  int32_t* __restrict__ sel, int64_t N, int Hq,
+                                                  int G, int B, int k, int64_t nhp, int all_rows) {
+  __shared__ double qs[kHeadDim];
+  const int lane = threadIdx.x;
+  const int KH = k - 1;
+  const int64_t nph = N * Hq;
+  const int64_t ph0 = (int64_t)blockIdx.x * 64;
+  bool mine = false;
+  {
+    const int64_t ph = ph0 + lane;
+    if (ph < nph) {
+      const int64_t r = ph / Hq, c = r / B;
+      int32_t* out = sel + ph * k;
+      if (c > KH && KH > 0) {
+        mine = all_rows || out[0] == kRefine;
+      } else if (all_rows) {  // every earlier block is taken
+        const int nsel = (int)(c < KH ? c : KH);
+        for (int a = 0; a < nsel; ++a) out[a] = a;
+        out[nsel] = (int32_t)c;
+        for (int a = nsel + 1; a < k; ++a) out[a] = -1;
+      }
+    }
+  }
+  unsigned long long todo = __ballot(mine);
+  while (todo) {
+    const int l = __ffsll((long long)todo) - 1;
+    todo &= todo - 1;
+    const int64_t ph = ph0 + l;
+    const int64_t r = ph / Hq, c = r / B;
+    const int g = (int)(ph % Hq) / G;
+    const T* qrow = Q + ph * kHeadDim;
+    qs[2 * lane] = widen<T>(qrow[2 * lane]);
+    qs[2 * lane + 1] = widen<T>(qrow[2 * lane + 1]);
+    __syncthreads();
+    double v[KM];
+    int ix[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+      v[t] = -INFINITY;
+      ix[t] = 0x7FFFFFFF;
+    }
+    const double* kt = kbarT + (int64_t)g * kHeadDim * nhp;
+    for (int64_t b = lane; b < c; b += 64) {
+      double acc = 0.0;
+#pragma unroll 16
+      for (int d = 0; d < kHeadDim; ++d) acc = fma(qs[d], kt[(int64_t)d * nhp + b], acc);
+      double x = acc;
+      int xi = (int)b;
+#pragma unroll
+      for (int t = 0; t < KM; ++t) {
+        const bool gt = x > v[t];
+        const double nv = gt ? x : v[t];
+        const int ni = gt ? xi : ix[t];
+        x = gt ? v[t] : x;
+        xi = gt ? ix[t] : xi;
+        v[t] = nv;
+        ix[t] = ni;
+      }
+    }
+    int chosen[KM];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) chosen[t] = 0x7FFFFFFF;
+    for (int rnd = 0; rnd < KH; ++rnd) {
+      const int hi = ix[0];
+      double bv = v[0];
+      int bi = hi;
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ov = __shfl_xor(bv, off);
+        const int oi = __shfl_xor(bi, off);
+        if (ov > bv || (ov == bv && oi < bi)) {
+          bv = ov;
+          bi = oi;
+        }
+      }
+      if (hi == bi) {  // the winning lane pops its head
+#pragma unroll
+        for (int t = 0; t < KM - 1; ++t) {
+          v[t] = v[t + 1];
+          ix[t] = ix[t + 1];
+        }
+        v[KM - 1] = -INFINITY;
+        ix[KM - 1] = 0x7FFFFFFF;
+      }
+#pragma unroll
+      for (int t = 0; t < KM; ++t)
+        if (t == rnd) chosen[t] = bi;
+    }
+    if (lane == 0) {
+      int32_t* out = sel + ph * k;
+      write_sorted<KM>(chosen, KH, out);
+      out[KH] = (int32_t)c;
+      for (int a = KH + 1; a < k; ++a) out[a] = -1;
+    }
+    __syncthreads();  // qs is rewritten for the next row
+  }
+}
+
+template <int KM>
+__global__ __launch_bounds__(kThreads) void gate_topk_kernel(
+    const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
+    const float* __restrict__ maxnorm, const double* __restrict__ kbar, int32_t* __restrict__ sel,
+    int64_t N, int Hq, int G, int B, int k, int64_t n, int64_t nh, int tiles_per_block) {
+  __shared__ __align__(16) uint16_t bufA[kChunkElems];
+  __shared__ __align__(16) uint16_t bufB[kChunkElems];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, lr = lane & 31;
   const int g = blockIdx.y;
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = blockIdx.x % tiles_per_block;
@@ -76,135 +344,156 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   const int64_t pair0 = (int64_t)tile * kPairs;
   if (pair0 >= npairs_c) return;
   const int KH = k - 1;
-  const int nsel = (int)(c < KH ? c : KH);  // history blocks this block's rows take
 
-  // ---- scores and running selection (only when there is a choice to make) ----
-  const bool rank = (c > KH) && (KH > 0);
-  int cnt = 0;
-  double thr = -INFINITY;
-  const int my_pair = wave * 16 + (lane & 15);  // pair a selecting lane owns (lanes < 16)
-  if (rank) {
-    double qa[kSteps];
-    {
-      const int64_t pi = pair0 + wave * 16 + (lane & 15);
-      if (pi < npairs_c) {
-        const int64_t r = row0 + pi / G;
-        const int h = g * G + (int)(pi % G);
-        load_q32<T>(Q + ((size_t)r * Hq + h) * kHeadDim + 32 * (lane >> 4), qa);
-      } else {
-#pragma unroll
-        for (int i = 0; i < kSteps; ++i) qa[i] = 0.0;
-      }
+  const int64_t pi = pair0 + wave * 32 + lr;
+  const bool valid = pi < npairs_c;
+  const int64_t r = row0 + (valid ? pi / G : 0);
+  const int hq = g * G + (int)(valid ? pi % G : 0);
+  int32_t* out = sel + ((size_t)r * Hq + hq) * k;
+  const int nsel = (int)(c < KH ? c : KH);
+
+  if (c <= KH || KH == 0) {  // every earlier block is taken: nothing to rank
+    if (valid && h == 0) {
+      for (int a = 0; a < nsel; ++a) out[a] = a;
+      out[nsel] = (int32_t)c;
+      for (int a = nsel + 1; a < k; ++a) out[a] = -1;
     }
-    const double* kbg = kbar + (size_t)g * nh * kHeadDim;
-    for (int64_t cb = 0; cb < c; cb += kChunk) {
-      __syncthreads();
-      // stage kbar[cb .. cb+32) as [ks][blk][grp]
-      {
-        const int b = tid >> 3;            // 0..31
-        const int d0 = (tid & 7) * 16;     // 16 consecutive d
-        const int64_t blk = cb + b;
-        if (blk < c) {
-          const double2* src = reinterpret_cast<const double2*>(kbg + blk * kHeadDim + d0);
-#pragma unroll
-          for (int x = 0; x < 8; ++x) {
-            double2 v = src[x];
-            int dd = d0 + 2 * x;
-            kb[((dd & 31) * kChunk + b) * 4 + (dd >> 5)] = v.x;
-            kb[(((dd + 1) & 31) * kChunk + b) * 4 + ((dd + 1) >> 5)] = v.y;
-          }
-        } else {
-#pragma unroll
-          for (int x = 0; x < 16; ++x) {
-            int dd = d0 + x;
-            kb[((dd & 31) * kChunk + b) * 4 + (dd >> 5)] = 0.0;
-          }
-        }
-      }
-      __syncthreads();
-      f64x4 acc0 = {0.0, 0.0, 0.0, 0.0};
-      f64x4 acc1 = {0.0, 0.0, 0.0, 0.0};
-      const int bl = lane & 15, grp = lane >> 4;
-#pragma unroll
-      for (int ks = 0; ks < kSteps; ++ks) {
-        double b0 = kb[(ks * kChunk + bl) * 4 + grp];
-        double b1 = kb[(ks * kChunk + 16 + bl) * 4 + grp];
-        acc0 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], b0, acc0, 0, 0, 0);
-        acc1 = __builtin_amdgcn_mfma_f64_16x16x4f64(qa[ks], b1, acc1, 0, 0, 0);
-      }
-      // D layout of v_mfma_f64_16x16x4: register r of lane l holds row (pair)
-      // l/16 + 4r, column (block) l%16
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int p = wave * 16 + grp + 4 * r;
-        sc[p * kScPad + bl] = acc0[r];
-        sc[p * kScPad + 16 + bl] = acc1[r];
-      }
-      __syncthreads();
-      if (lane < 16) {
-        const int64_t lim = (c - cb < kChunk) ? c - cb : kChunk;
-        for (int jj = 0; jj < lim; ++jj) {
-          const double s = sc[my_pair * kScPad + jj];
-          if (cnt < KH || s > thr) {
-            int pos = (cnt < KH) ? cnt : KH - 1;
-            while (pos > 0 && ls[(pos - 1) * kPairs + my_pair] < s) {
-              ls[pos * kPairs + my_pair] = ls[(pos - 1) * kPairs + my_pair];
-              li[pos * kPairs + my_pair] = li[(pos - 1) * kPairs + my_pair];
-              --pos;
-            }
-            ls[pos * kPairs + my_pair] = s;
-            li[pos * kPairs + my_pair] = (int)(cb + jj);
-            if (cnt < KH) ++cnt;
-            thr = ls[(cnt - 1) * kPairs + my_pair];
-          }
-        }
-      }
-    }
+    return;
   }
 
-  // ---- write the selection rows of this wave's 16 pairs ----
-  if (lane < 16) {
-    const int64_t pi = pair0 + my_pair;
-    if (pi < npairs_c) {
-      const int64_t r = row0 + pi / G;
-      const int h = g * G + (int)(pi % G);
-      int32_t* out = sel + ((size_t)r * Hq + h) * k;
-      if (rank) {
-        // ascending order of the kept blocks (insertion sort of <= 31 entries)
-        for (int a = 1; a < cnt; ++a) {
-          int v = li[a * kPairs + my_pair];
-          int b = a - 1;
-          while (b >= 0 && li[b * kPairs + my_pair] > v) {
-            li[(b + 1) * kPairs + my_pair] = li[b * kPairs + my_pair];
-            --b;
-          }
-          li[(b + 1) * kPairs + my_pair] = v;
-        }
-        for (int a = 0; a < cnt; ++a) out[a] = li[a * kPairs + my_pair];
-        out[cnt] = (int32_t)c;
-        for (int a = cnt + 1; a < k; ++a) out[a] = -1;
-      } else {
-        for (int a = 0; a < nsel; ++a) out[a] = a;
-        out[nsel] = (int32_t)c;
-        for (int a = nsel + 1; a < k; ++a) out[a] = -1;
-      }
+  // Q as the B operand: Q[pair][16kk + 8h .. +8]; |q|^2 from the same values
+  const uint16_t* qrow = Q + ((size_t)r * Hq + hq) * kHeadDim;
+  bf16x8 q[8];
+  float qq = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
+                          : make_uint4(0, 0, 0, 0);
+    q[kk] = as_bf16x8(u);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float x = (float)q[kk][e];
+      qq = fmaf(x, x, qq);
     }
   }
+  qq += __shfl_xor(qq, 32);
+
+  const uint16_t* planes_g = planes + (size_t)g * nh * 3 * kHeadDim;
+  const float kmax = maxnorm[g];
+  int ib = 1;  // index bits for blocks 0..c-1
+  while ((1ll << ib) < c) ++ib;
+  KeyList<KM> L;
+  L.init();
+  const int nchunks = (int)((c + kChunk - 1) / kChunk);
+  auto step = [&](int ch, uint16_t* cur, uint16_t* nxt) {
+    if (ch + 1 < nchunks) load_chunk(nxt, planes_g, (int64_t)(ch + 1) * kChunk, c, wave, lane);
+    f32x16 s;
+    chunk_scores(cur, q, lane, s);
+    const int64_t cb = (int64_t)ch * kChunk;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {  // blocks past c push key 0, which never enters
+      const int b = (int)cb + 8 * (e >> 2) + 4 * h + (e & 3);
+      L.push(b < c ? score_key(s[e], b, ib) : 0u);
+    }
+    wait_chunk();
+  };
+  load_chunk(bufA, planes_g, 0, c, wave, lane);
+  wait_chunk();
+  for (int ch = 0; ch < nchunks; ch += 2) {
+    step(ch, bufA, bufB);
+    if (ch + 1 < nchunks) step(ch + 1, bufB, bufA);
+  }
+
+  // merge the two halves of each row: both lanes end with the same list
+  uint32_t other[KM];  // the partner's list as it was, before any merging
+#pragma unroll
+  for (int t = 0; t < KM; ++t) other[t] = __shfl_xor(L.k[t], 32);
+#pragma unroll
+  for (int t = 0; t < KM; ++t) L.push(other[t]);
+
+  // certification: kept (top KH) vs best left out. Decoded scores are at most
+  // 2^ib units in the last place below the fp32 ones; the fp32 ones are within
+  // eps of the exact ones.
+  uint32_t kk_in = 0u, kk_out = 0u;
+  int idx[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) {
+    if (t == KH - 1) kk_in = L.k[t];
+    if (t == KH) kk_out = L.k[t];
+    idx[t] = key_block(L.k[t], ib);
+  }
+  const float theta = key_score(kk_in, ib), theta_n = key_score(kk_out, ib);
+  const float big = fmaxf(fabsf(theta), fabsf(theta_n));
+  const float trunc = ldexpf(big, ib - 22);  // >= 2^ib units in the last place of |score| <= big
+  const float eps = kEpsCoef * sqrtf(qq) * 1.0001f * kmax;
+  const bool certified = (theta - theta_n) > 2.f * eps + trunc + 1e-6f * big;
+  if (valid && h == 0) {
+    if (certified)
+      write_sorted<KM>(idx, KH, out);
+    else
+      out[0] = kRefine;  // completed by gate_refine
+    out[KH] = (int32_t)c;
+    for (int a = KH + 1; a < k; ++a) out[a] = -1;
+  }
+
 }
+
+template <int KM>
+hipError_t launch_km(const Prob& P, const void* Q, const double* kbar, const uint16_t* planes,
+                     const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
+                     hipStream_t s) {
+  const unsigned refine_grid = (unsigned)ceil_div(P.N * P.Hq, 64);
+  if (P.dtype == MOBA_DTYPE_F32) {
+    gate_refine<float, KM><<<refine_grid, 64, 0, s>>>((const float*)Q, kbarT, sel, P.N, P.Hq, P.G,
+                                                     P.B, P.k, nhp, 1);
+    return hipGetLastError();
+  }
+  const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
+  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
+  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, kbar, sel,
+                                                P.N, P.Hq, P.G, P.B, P.k, P.n, P.nh,
+                                                tiles_per_block);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
+  gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, sel, P.N, P.Hq,
+                                                      P.G, P.B, P.k, nhp, 0);
+  return hipGetLastError();
+}
+
+int64_t padded_nh(const Prob& P) { return ceil_div(P.nh > 0 ? P.nh : 1, 64) * 64; }
 
 }  // namespace
 
-hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, int32_t* sel,
-                            hipStream_t s) {
-  const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
-  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
-  if (P.dtype == MOBA_DTYPE_BF16)
-    gate_topk_kernel<__hip_bfloat16><<<grid, kThreads, 0, s>>>(
-        (const __hip_bfloat16*)Q, kbar, sel, P.N, P.Hq, P.G, P.B, P.k, P.n, P.nh, tiles_per_block);
-  else
-    gate_topk_kernel<float><<<grid, kThreads, 0, s>>>((const float*)Q, kbar, sel, P.N, P.Hq, P.G,
-                                                      P.B, P.k, P.n, P.nh, tiles_per_block);
-  return hipGetLastError();
+size_t gate_scratch_bytes(const Prob& P) {
+  return (size_t)P.Hkv * P.nh * (3 * kHeadDim * 2 + 4) + (size_t)P.Hkv * 4 +
+         sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P) + 1024;
+}
+
+hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, void* scratch,
+                            int32_t* sel, hipStream_t s) {
+  char* base = (char*)scratch;
+  double* kbarT = (double*)base;  // first: keeps 8-byte alignment
+  base += sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P);
+  uint16_t* planes = (uint16_t*)base;
+  base += (size_t)P.Hkv * P.nh * 3 * kHeadDim * 2;
+  float* norms = (float*)base;
+  float* maxnorm = norms + (size_t)P.Hkv * P.nh;
+  const int64_t nhp = padded_nh(P);
+  if (P.nh > 0 && P.KH > 0) {
+    kbar_split<<<(unsigned)(P.Hkv * P.nh), kHeadDim, 0, s>>>(kbar, planes, norms, kbarT, P.nh,
+                                                            nhp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(norms, maxnorm, P.nh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  // list length: the k-1 kept blocks plus the best one left out
+  const int need = P.KH + 1;
+  if (need <= 4) return launch_km<4>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 8) return launch_km<8>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 12) return launch_km<12>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 16) return launch_km<16>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
+  return launch_km<32>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
 }
 
 }  // namespace moba

@@ -68,7 +68,7 @@ int make_prob(const moba_problem_t* p, Prob* P) {
 size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t kbar, mp_part, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
+  size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
       part_lse, part_o, vt, total;
 };
 
@@ -91,6 +91,7 @@ Layout plan_ws(const Prob& P, bool full) {
   const int splits = meanpool_splits(P);
   L.kbar = take(sizeof(double) * (size_t)(P.Hkv * P.nh * P.d));
   L.mp_part = take(sizeof(double) * (size_t)splits * P.nh * P.Hkv * P.d);
+  L.gate = take(gate_scratch_bytes(P));
   if (full) {
     const BucketPlan bp = plan_bucket(P);
     L.sel = take(sizeof(int32_t) * (size_t)(P.N * P.Hq * P.k));
@@ -159,7 +160,7 @@ int run_select(const Prob& P, const void* q, const void* k, int32_t* sel, void* 
                                  meanpool_splits(P), s);
   if (e != hipSuccess) return hip_fail(e, "moba_meanpool");
   if ((rc = record(events, 1, s))) return rc;
-  e = launch_gate_topk(P, q, at<double>(ws, L.kbar), sel, s);
+  e = launch_gate_topk(P, q, at<double>(ws, L.kbar), at<void>(ws, L.gate), sel, s);
   if (e != hipSuccess) return hip_fail(e, "moba_gate_topk");
   return record(events, 2, s);
 }

@@ -56,8 +56,11 @@ hipError_t launch_meanpool(const Prob& P, const void* K, double* kbar, double* p
                            hipStream_t s);
 int meanpool_splits(const Prob& P);
 
-hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, int32_t* sel,
-                            hipStream_t s);
+// Gate + selection; `scratch` holds the bf16 split of the block keys and their
+// norms (gate_scratch_bytes).
+size_t gate_scratch_bytes(const Prob& P);
+hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, void* scratch,
+                            int32_t* sel, hipStream_t s);
 
 hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
                          const BucketBufs& b, hipStream_t s);
