@@ -111,12 +111,26 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--calibrate-copy-mib", type=int, default=0,
+                    help="only run the plain copy kernel over this many MiB (hardware-counter "
+                         "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MoBA prefill path here runs on a single "
               "MI355X (a multi-GPU split by KV-head group is described in DESIGN.md, not built).",
               file=sys.stderr)
         sys.exit(2)
+
+    if args.calibrate_copy_mib > 0:
+        nbytes = args.calibrate_copy_mib << 20
+        src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        moba.debug_copy(src, dst)
+        torch.cuda.synchronize()
+        assert torch.equal(src, dst)
+        print(json.dumps({"copy_bytes": nbytes}), flush=True)
+        return
 
     w = synth.CONFIGS[args.config]
     dtype = "bf16" if w.dtype == "bf16" else "f32"
