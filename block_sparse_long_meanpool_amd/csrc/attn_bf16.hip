@@ -57,7 +57,6 @@ constexpr int VT_ROW = KT;                  // bf16 per V^T row in LDS (128 B, s
 constexpr int KS_ELEMS = KT * KS_ROW;
 constexpr int VT_ELEMS = kHeadDim * VT_ROW;
 constexpr float kLog2e = 1.4426950408889634f;
-constexpr float kRedoSlack = 64.f;          // scores this far above the reference max force a re-run
 
 // One LDS tile buffer: a K part and a V^T part. The kernels declare each part
 // of each of the three buffers as its own __shared__ array and unroll the key
@@ -130,13 +129,13 @@ __device__ inline void wait_tile() {
   __syncthreads();
 }
 
-// Per-wave attention state for 64 queries; lane l holds query 32*qb + l%32.
+// Per-wave attention state; lane l holds query 32*qb + l%32 of each block.
 struct Wave {
   bf16x8 q[QB][8];   // B operand of S^T = K Q^T: Q[query][16kk + 8h .. +8]
   f32x16 o[QB][4];   // O^T accumulators, d-blocks of 32
-  float m[QB];       // reference max (log2 domain), fixed once set
-  float mseen[QB];   // largest scaled score seen
+  float m[QB];       // reference max (log2 domain), fixed for the whole pass
   float l[QB];       // this lane's partial row sum
+  float mx[QB];      // max-only pass: this lane's largest masked score
 };
 
 __device__ inline void wave_load_q(Wave& W, const uint16_t* const (&qrow)[QB],
@@ -159,18 +158,31 @@ __device__ inline void wave_reset(Wave& W, const float (&mstart)[QB]) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) W.o[qb][db][r] = 0.f;
     W.m[qb] = mstart[qb];
-    W.mseen[qb] = -INFINITY;
     W.l[qb] = 0.f;
+    W.mx[qb] = -INFINITY;
   }
 }
 
-// True when some valid query of this lane saw a score too far above its
-// reference max (the pass must be redone from the true maximum).
+// Weights are 2^(score - m) with m fixed by the first subtile; their sum bounds
+// every single weight. A pass is redone from the true maximum when some valid
+// query's partial sum reaches 2^64 (or is not finite), so no weight or output
+// accumulator can overflow in a pass that is kept.
+constexpr float kLMax = 18446744073709551616.f;  // 2^64
 __device__ inline bool wave_needs_redo(const Wave& W, const bool (&valid)[QB]) {
   bool r = false;
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) r |= valid[qb] && (W.mseen[qb] > W.m[qb] + kRedoSlack);
+  for (int qb = 0; qb < QB; ++qb) r |= valid[qb] && !(W.l[qb] < kLMax);
   return r;
+}
+
+// After a max-only pass: each query's true maximum scaled score (log2 domain),
+// 0 for queries with no unmasked key.
+__device__ inline void wave_true_max(const Wave& W, float sl2e, float (&m)[QB]) {
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float v = fmaxf(W.mx[qb], __shfl_xor(W.mx[qb], 32)) * sl2e;
+    m[qb] = (v == -INFINITY) ? 0.f : v;
+  }
 }
 
 // Key row (0..31) of accumulator element r in the 32x32 MFMA output layout.
@@ -193,46 +205,63 @@ __device__ inline void wave_qk(const Wave& W, Tile t, int sub, int lane, f32x16 
   }
 }
 
-// Softmax of one subtile's scores and its P.V product. Keys >= nvalid (from the
-// subtile start) are masked; when CAUSAL, also keys with key0 + key > qrow.
+// Mask one subtile's scores: keys >= nvalid (from the subtile start) and,
+// when CAUSAL, keys with key0 + key > qrow get -inf.
 template <bool CAUSAL>
-__device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int lane,
-                                 int nvalid, int64_t key0, const int64_t (&qrow)[QB], float sl2e,
-                                 bool need_mask) {
-  const int h = lane >> 5, lr = lane & 31;
-  if (need_mask) {
+__device__ inline void wave_mask(f32x16 (&s)[QB], int lane, int nvalid, int64_t key0,
+                                 const int64_t (&qrow)[QB]) {
+  const int h = lane >> 5;
 #pragma unroll
-    for (int qb = 0; qb < QB; ++qb)
+  for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int key = acc_row(r, h);
-        bool ok = key < nvalid;
-        if (CAUSAL) ok = ok && (key0 + key <= qrow[qb]);
-        if (!ok) s[qb][r] = -INFINITY;
-      }
-  }
+    for (int r = 0; r < 16; ++r) {
+      const int key = acc_row(r, h);
+      bool ok = key < nvalid;
+      if (CAUSAL) ok = ok && (key0 + key <= qrow[qb]);
+      if (!ok) s[qb][r] = -INFINITY;
+    }
+}
+
+// Fix each query's reference max from its first subtile's (masked) scores.
+__device__ inline void wave_set_reference(Wave& W, const f32x16 (&s)[QB], float sl2e) {
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     float v = s[qb][0];
 #pragma unroll
     for (int r = 1; r < 16; ++r) v = fmaxf(v, s[qb][r]);
     v = fmaxf(v, __shfl_xor(v, 32)) * sl2e;
-    W.mseen[qb] = fmaxf(W.mseen[qb], v);
-    if (W.m[qb] == -INFINITY) W.m[qb] = v;  // first unmasked keys fix the reference
+    W.m[qb] = (v == -INFINITY) ? 0.f : v;
+  }
+}
+
+// Softmax of one subtile's scores against the fixed reference max, and its
+// P.V product. MAXONLY: only track the largest masked score (no P.V).
+template <bool CAUSAL, bool MAXONLY>
+__device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int lane,
+                                 int nvalid, int64_t key0, const int64_t (&qrow)[QB], float sl2e,
+                                 bool need_mask) {
+  const int h = lane >> 5, lr = lane & 31;
+  if (need_mask) wave_mask<CAUSAL>(s, lane, nvalid, key0, qrow);
+  if (MAXONLY) {
+#pragma unroll
+    for (int qb = 0; qb < QB; ++qb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) W.mx[qb] = fmaxf(W.mx[qb], s[qb][r]);
+    return;
   }
   bf16x8 p[QB][2];
   const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
-    const float muse = (W.m[qb] == -INFINITY) ? 0.f : W.m[qb];
+    const float mneg = -W.m[qb];
     float lsum = W.l[qb];
 #pragma unroll
     for (int u = 0; u < 2; ++u)
 #pragma unroll
       for (int e = 0; e < 8; e += 2) {
         bf16x2 e2;
-        e2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e], sl2e, -muse));
-        e2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e + 1], sl2e, -muse));
+        e2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e], sl2e, mneg));
+        e2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e + 1], sl2e, mneg));
         p[qb][u][e] = e2[0];
         p[qb][u][e + 1] = e2[1];
         // the row sum adds the same rounded weights that multiply V
@@ -261,12 +290,12 @@ __device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int 
 // after the barrier that publishes tile t+1 and lands in the buffer tile t-1
 // used (every wave is past it by then). Waves whose rows start after a
 // subtile (CAUSAL) or that hold no queries skip its compute, never a barrier.
-template <bool CAUSAL, bool FULL>
+template <bool CAUSAL, bool FULL, bool MAXONLY>
 __device__ inline void run_block(Wave& W, Tile b0, Tile b1, Tile b2,
                                  const uint16_t* __restrict__ K, int64_t key0, int64_t nkeys,
                                  int Hkv, int g, const uint16_t* __restrict__ vt_col, int64_t ldv,
                                  int wave, int lane, const int64_t (&qrow)[QB], int64_t wrow_min,
-                                 int64_t wrow_max, bool wave_live, float sl2e) {
+                                 int64_t wrow_max, bool wave_live, float sl2e, bool set_m) {
   const int nt = (int)((nkeys + KT - 1) / KT);
   // FULL: every subtile has 32 keys and every wave computes (the caller checked)
   auto nvs_of = [&](int t, int sub) -> int {
@@ -288,7 +317,7 @@ __device__ inline void run_block(Wave& W, Tile b0, Tile b1, Tile b2,
     const int nv = nvs_of(t, sub);
     const int64_t k0 = key0 + (int64_t)t * KT + 32 * sub;
     const bool need_mask = nv < 32 || (CAUSAL && k0 + 31 > wrow_min);
-    wave_smpv<CAUSAL>(W, s, cur, sub, lane, nv, k0, qrow, sl2e, need_mask);
+    wave_smpv<CAUSAL, MAXONLY>(W, s, cur, sub, lane, nv, k0, qrow, sl2e, need_mask);
   };
   f32x16 sa[QB], sb[QB];
   auto step = [&](int t, Tile cur, Tile nxt, Tile spare) {
@@ -309,7 +338,16 @@ __device__ inline void run_block(Wave& W, Tile b0, Tile b1, Tile b2,
   issue(0, b0);
   wait_tile();
   if (nt > 1) issue(1, b1);
-  if (active(0, 0)) wave_qk(W, b0, 0, lane, sa);
+  if (active(0, 0)) {
+    wave_qk(W, b0, 0, lane, sa);
+    // The first subtile holds an unmasked key of every valid query: the causal
+    // block starts at or before each row, and history blocks are never empty.
+    if (!MAXONLY && set_m) {
+      const int nv = nvs_of(0, 0);
+      if (nv < 32 || (CAUSAL && key0 + 31 > wrow_min)) wave_mask<CAUSAL>(sa, lane, nv, key0, qrow);
+      wave_set_reference(W, sa, sl2e);
+    }
+  }
   for (int t = 0; t < nt; t += 3) {
     step(t, b0, b1, b2);
     if (t + 1 < nt) step(t + 1, b1, b2, b0);
@@ -366,19 +404,24 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
   const bool wave_live = (e_begin + wave * kWaveQ) < e_end;
   float mstart[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
-  for (int attempt = 0;; ++attempt) {
+  for (int qb = 0; qb < QB; ++qb) mstart[qb] = 0.f;
+  wave_reset(W, mstart);
+  if (B % KT == 0 && e_begin + kGroupQ <= e_end)
+    run_block<false, true, false>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                                  dummy_row, 0, 0, wave_live, sl2e, true);
+  else
+    run_block<false, false, false>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                                   dummy_row, 0, 0, wave_live, sl2e, true);
+  // workgroup-uniform: if some weight could have overflowed, find the true
+  // maxima with a max-only pass and redo the block from them (weights <= 1)
+  if (__syncthreads_or(wave_needs_redo(W, valid))) {
     wave_reset(W, mstart);
-    if (B % KT == 0 && e_begin + kGroupQ <= e_end)
-      run_block<false, true>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
-                             dummy_row, 0, 0, wave_live, sl2e);
-    else
-      run_block<false, false>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
-                              dummy_row, 0, 0, wave_live, sl2e);
-    // workgroup-uniform decision: re-run only if some score overran the reference max
-    if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mstart[qb] = W.mseen[qb];
+    run_block<false, false, true>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                                  dummy_row, 0, 0, wave_live, sl2e, false);
+    wave_true_max(W, sl2e, mstart);
+    wave_reset(W, mstart);
+    run_block<false, false, false>(W, tA, tB, tC, K, kbase, B, Hkv, g, vt_col, ldv, wave, lane,
+                                   dummy_row, 0, 0, wave_live, sl2e, false);
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
@@ -449,14 +492,18 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + c * Bpad;
   float mstart[QB];
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) mstart[qb] = -INFINITY;
-  for (int attempt = 0;; ++attempt) {
+  for (int qb = 0; qb < QB; ++qb) mstart[qb] = 0.f;
+  wave_reset(W, mstart);
+  run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+                                my_row, wrow_min, wrow_max, wave_live, sl2e, true);
+  if (__syncthreads_or(wave_needs_redo(W, valid))) {
     wave_reset(W, mstart);
-    run_block<true, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane, my_row,
-                    wrow_min, wrow_max, wave_live, sl2e);
-    if (attempt > 0 || !__syncthreads_or(wave_needs_redo(W, valid))) break;
-#pragma unroll
-    for (int qb = 0; qb < QB; ++qb) mstart[qb] = W.mseen[qb];
+    run_block<true, false, true>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+                                 my_row, wrow_min, wrow_max, wave_live, sl2e, false);
+    wave_true_max(W, sl2e, mstart);
+    wave_reset(W, mstart);
+    run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+                                  my_row, wrow_min, wrow_max, wave_live, sl2e, false);
   }
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
