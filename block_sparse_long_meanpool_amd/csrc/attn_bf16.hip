@@ -357,7 +357,54 @@ __device__ inline void run_block(Wave& W, Tile b0, Tile b1, Tile b2,
 }
 
 typedef _Float16 h4 __attribute__((ext_vector_type(4)));
+typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
+typedef __bf16 b8 __attribute__((ext_vector_type(8)));
+
+// Final output of one (row, head) for the 8 head-dim elements [8 c16, 8 c16 + 8):
+// the own-block result (normalised `own`, log2-sum-exp own_lse) merged with the
+// row's nhist >= 1 history partials (normalised rows po[s], log2-sum-exps
+// lse[s]) by PaperTrace "2.1.3 MoBA" eqs. (7)-(8). NH >= nhist is a
+// compile-time bound so the loads of a group of partials are all in flight
+// before their values are used; indices past nhist are clamped, so every
+// load stays inside the row's own partials.
+template <int NH>
+__device__ inline b8 merge_row(h8 own, float own_lse, const float* __restrict__ lse_src,
+                               const _Float16* __restrict__ po_src, int nhist, int c16) {
+  constexpr int GRP = 8;
+  float lse[NH];
+#pragma unroll
+  for (int s = 0; s < NH; ++s) lse[s] = lse_src[s < nhist ? s : nhist - 1];
+  float M = own_lse;
+#pragma unroll
+  for (int s = 0; s < NH; ++s) M = fmaxf(M, lse[s]);  // clamped copies repeat a real value
+  float acc[8];
+  float L = __builtin_amdgcn_exp2f(own_lse - M);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = L * (float)own[e];
+#pragma unroll
+  for (int s0 = 0; s0 < NH; s0 += GRP) {
+    if (s0 >= nhist) break;
+    h8 v[GRP];
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const int sj = s0 + j < nhist ? s0 + j : nhist - 1;
+      v[j] = *reinterpret_cast<const h8*>(po_src + (size_t)sj * kHeadDim + 8 * c16);
+    }
+#pragma unroll
+    for (int j = 0; j < GRP; ++j) {
+      const float w = s0 + j < nhist ? __builtin_amdgcn_exp2f(lse[s0 + j] - M) : 0.f;
+      L += w;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)v[j][e], acc[e]);
+    }
+  }
+  const float inv = 1.f / L;
+  b8 out;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+  return out;
+}
 
 // ----------------------------------------------------------------------------
 // History attention: one workgroup = up to 256 routed entries of one bin.
@@ -505,47 +552,70 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
                                   my_row, wrow_min, wrow_max, wave_live, sl2e, false);
   }
+  const int nhist = part_o != nullptr ? (int)(c < KH ? c : KH) : 0;  // uniform
+  if (nhist == 0) {
+    // no history: O = own-block result, straight from the accumulators
 #pragma unroll
-  for (int qb = 0; qb < QB; ++qb) {
-    float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
-    if (!valid[qb]) continue;
-    if (part_o != nullptr && KH > 0) {
-      // merge with this (row, head)'s history partials: eqs. (7)-(8)
-      const int64_t nhist = c < KH ? c : KH;
-      const int64_t ebase = ph[qb] * KH;
-      float M = W.m[qb];
-      for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
-      const float ws = __builtin_amdgcn_exp2f(W.m[qb] - M);
-      l *= ws;
+    for (int qb = 0; qb < QB; ++qb) {
+      const float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
+      if (!valid[qb]) continue;
+      const float inv = 1.f / l;
+      uint16_t* dst = O + ph[qb] * kHeadDim;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) W.o[qb][db][r] *= ws;
-      for (int64_t s = 0; s < nhist; ++s) {
-        const float wgt = __builtin_amdgcn_exp2f(part_lse[ebase + s] - M);
-        l += wgt;
-        const _Float16* src = part_o + (size_t)(ebase + s) * kHeadDim;
+        for (int r4 = 0; r4 < 4; ++r4) {
+          b4 v;
 #pragma unroll
-        for (int db = 0; db < 4; ++db)
-#pragma unroll
-          for (int r4 = 0; r4 < 4; ++r4) {
-            const h4 v = *reinterpret_cast<const h4*>(src + 32 * db + 8 * r4 + 4 * h);
-#pragma unroll
-            for (int t = 0; t < 4; ++t) W.o[qb][db][4 * r4 + t] += wgt * (float)v[t];
-          }
-      }
+          for (int t = 0; t < 4; ++t) v[t] = (__bf16)(W.o[qb][db][4 * r4 + t] * inv);
+          *reinterpret_cast<b4*>(dst + 32 * db + 8 * r4 + 4 * h) = v;
+        }
     }
+    return;
+  }
+  // Stage each wave's own-block results in the (now idle) tile buffers as
+  // normalised fp16 rows plus log2-sum-exps, then merge with 16 lanes per
+  // (row, head) so each partial row is one coalesced 256-byte read.
+  uint16_t* const wbuf = wave < 2 ? lds_k0 : wave < 4 ? lds_k1 : wave < 6 ? lds_k2 : lds_v0;
+  _Float16* const stage = reinterpret_cast<_Float16*>(wbuf) + (wave & 1) * kWaveQ * kHeadDim;
+  float* const stage_lse = reinterpret_cast<float*>(lds_v1) + wave * kWaveQ;
+#pragma unroll
+  for (int qb = 0; qb < QB; ++qb) {
+    const float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
     const float inv = 1.f / l;
-    uint16_t* dst = O + ph[qb] * kHeadDim;
+    const int j = qb * 32 + (lane & 31);
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int r4 = 0; r4 < 4; ++r4) {
-        b4 v;
+        h4 v;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) v[t] = (__bf16)(W.o[qb][db][4 * r4 + t] * inv);
-        *reinterpret_cast<b4*>(dst + 32 * db + 8 * r4 + 4 * h) = v;
+        for (int t = 0; t < 4; ++t) v[t] = (_Float16)(W.o[qb][db][4 * r4 + t] * inv);
+        *reinterpret_cast<h4*>(stage + j * kHeadDim + 32 * db + 8 * r4 + 4 * h) = v;
       }
+    if (h == 0) stage_lse[j] = W.m[qb] + __builtin_log2f(l);
+  }
+  __syncthreads();
+  const int q4 = lane >> 4, c16 = lane & 15;
+  for (int pass = 0; pass < kWaveQ / 4; ++pass) {
+    const int j = pass * 4 + q4;
+    const int64_t pi = p0 + wave * kWaveQ + j;
+    const int64_t pic = pi < npairs ? pi : npairs - 1;  // clamped: loads stay in bounds
+    const int64_t phj = (row0 + pic / G) * Hq + g * G + (int)(pic % G);
+    const h8 own = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * c16);
+    const float own_lse = stage_lse[j];
+    const float* ls = part_lse + phj * KH;
+    const _Float16* po = part_o + (size_t)(phj * KH) * kHeadDim;
+    b8 out;
+    if (nhist <= 4)
+      out = merge_row<4>(own, own_lse, ls, po, nhist, c16);
+    else if (nhist <= 8)
+      out = merge_row<8>(own, own_lse, ls, po, nhist, c16);
+    else if (nhist <= 16)
+      out = merge_row<16>(own, own_lse, ls, po, nhist, c16);
+    else
+      out = merge_row<kMaxTopk>(own, own_lse, ls, po, nhist, c16);
+    if (pi < npairs) *reinterpret_cast<b8*>(O + phj * kHeadDim + 8 * c16) = out;
   }
 }
 
