@@ -501,10 +501,17 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
   MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  const int g = blockIdx.y;
-  // heavier (later) row tiles first
-  const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
-  const int tile = tiles_per_block - 1 - (int)(blockIdx.x % tiles_per_block);
+  // Work items w = ((c' * Hkv) + g) * tiles_per_block + t' in order of
+  // blocks from the last, and inside a block heavier (later) row tiles first.
+  // Workgroup i runs on XCD i % 8 and each XCD takes a contiguous range of
+  // items, so the row tiles of one (block, KV head) share its L2 copy of K/V.
+  const int64_t items = n * Hkv * (int64_t)tiles_per_block;
+  const int64_t per = gridDim.x / 8;  // the grid is a multiple of 8
+  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= items) return;
+  const int tile = tiles_per_block - 1 - (int)(w % tiles_per_block);
+  const int g = (int)((w / tiles_per_block) % Hkv);
+  const int64_t c = n - 1 - w / ((int64_t)tiles_per_block * Hkv);
   const int64_t row0 = c * B;
   int64_t rows_c = N - row0;
   if (rows_c > B) rows_c = B;
@@ -647,8 +654,8 @@ hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, co
   const int64_t Bpad = vt_padded_block(B);
   const int64_t ldv = n * Bpad;
   const int tiles_per_block = (int)ceil_div(B * P.G, kGroupQ);
-  dim3 grid((unsigned)(n * tiles_per_block), (unsigned)P.Hkv);
-  attn_self_bf16<<<grid, kThreads, 0, s>>>(
+  const int64_t grid = ceil_div(n * tiles_per_block * P.Hkv, 8) * 8;
+  attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt,
       dense ? nullptr : (const _Float16*)part_o, dense ? nullptr : part_lse, (uint16_t*)O, P.N,
       P.Hq, P.Hkv, P.G, B, Bpad, ldv, dense ? 0 : P.KH, n, tiles_per_block, sl2e);
