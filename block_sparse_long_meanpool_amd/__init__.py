@@ -35,7 +35,9 @@ STAGES = ("meanpool", "gate_topk", "bucket", "vpack", "attn_hist", "attn_self_me
 # Every symbol include/moba.h declares.
 EXPORTS = (
     "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_prefill_ex",
-    "moba_select", "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
+    "moba_select", "moba_varlen_workspace_size", "moba_varlen_select_workspace_size",
+    "moba_prefill_varlen", "moba_select_varlen",
+    "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
 )
@@ -76,13 +78,17 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
                           "(or block_sparse_long_meanpool_amd/build.py)")
     lib = ctypes.CDLL(path)
     P = ctypes.POINTER(MobaProblem)
-    vp, sz = ctypes.c_void_p, ctypes.c_size_t
+    vp, sz, i64 = ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int64
     sig = {
         "moba_workspace_size": (sz, [P]),
         "moba_select_workspace_size": (sz, [P]),
         "moba_prefill": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_prefill_ex": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp, vp]),
         "moba_select": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
+        "moba_varlen_workspace_size": (sz, [P, i64, vp]),
+        "moba_varlen_select_workspace_size": (sz, [P, i64, vp]),
+        "moba_prefill_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_select_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_dense_workspace_size": (sz, [P]),
         "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -205,6 +211,72 @@ def select(q, k, block_size, topk, out=None, workspace=None):
     st = lib.moba_select(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), out.data_ptr(),
                          workspace.data_ptr(), workspace.numel(), _stream(q.device))
     _ok(st, "moba_select")
+    return out
+
+
+def _cu_pair(cu_seqlens, device):
+    """Host ctypes copy and device int64 tensor of the sequence offsets."""
+    if isinstance(cu_seqlens, torch.Tensor):
+        host = cu_seqlens.detach().to("cpu", torch.int64).contiguous()
+    else:
+        host = torch.tensor([int(x) for x in cu_seqlens], dtype=torch.int64)
+    if host.dim() != 1 or host.numel() < 2:
+        raise ValueError("cu_seqlens must be 1-D with nseq + 1 >= 2 entries")
+    if isinstance(cu_seqlens, torch.Tensor) and cu_seqlens.is_cuda and \
+            cu_seqlens.dtype == torch.int64 and cu_seqlens.is_contiguous():
+        dev = cu_seqlens
+    else:
+        dev = host.to(device)
+    arr = (ctypes.c_int64 * host.numel())(*host.tolist())
+    return arr, dev, host.numel() - 1
+
+
+def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, workspace=None):
+    """MoBA prefill over packed sequences: rows [cu[i], cu[i+1]) of q, k, v form
+    sequence i; blocks restart at each sequence and never cross one. Equals
+    ``prefill`` applied to every sequence on its own."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    prob = _problem_from(q, k, block_size, topk, scale)
+    cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev(out)
+    need = lib.moba_varlen_workspace_size(ctypes.byref(prob), nseq, cu_host)
+    if need == 0:
+        _ok(lib.moba_prefill_varlen(ctypes.byref(prob), nseq, cu_host, None, None, None, None,
+                                    None, None, 0, None), "moba_varlen_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib.moba_prefill_varlen(ctypes.byref(prob), nseq, cu_host, cu_dev.data_ptr(),
+                                 q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                 workspace.data_ptr(), workspace.numel(), _stream(q.device))
+    _ok(st, "moba_prefill_varlen")
+    return out
+
+
+def select_varlen(q, k, cu_seqlens, block_size, topk, out=None, workspace=None):
+    """Selected global block ids per (row, head) for packed sequences:
+    int32 [N, Hq, topk], ascending, -1 padded."""
+    lib = load_library()
+    _check_dev(q, k)
+    prob = _problem_from(q, k, block_size, topk, None)
+    cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
+    N, Hq, _ = q.shape
+    if out is None:
+        out = torch.empty((N, Hq, topk), dtype=torch.int32, device=q.device)
+    need = lib.moba_varlen_select_workspace_size(ctypes.byref(prob), nseq, cu_host)
+    if need == 0:
+        _ok(lib.moba_select_varlen(ctypes.byref(prob), nseq, cu_host, None, None, None, None,
+                                   None, 0, None), "moba_varlen_select_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib.moba_select_varlen(ctypes.byref(prob), nseq, cu_host, cu_dev.data_ptr(),
+                                q.data_ptr(), k.data_ptr(), out.data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _stream(q.device))
+    _ok(st, "moba_select_varlen")
     return out
 
 

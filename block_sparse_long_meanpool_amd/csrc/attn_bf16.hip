@@ -411,11 +411,11 @@ __device__ inline b8 merge_row(h8 own, float own_lse, const float* __restrict__ 
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
-    const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
-    const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
-    const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
-    float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad, int64_t ldv, int KH, int64_t nh,
-    float sl2e) {
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ tile_map,
+    const int32_t* __restrict__ tile_off, const int32_t* __restrict__ bin_off,
+    const int32_t* __restrict__ scalars, const uint32_t* __restrict__ entries,
+    _Float16* __restrict__ part_o, float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad,
+    int64_t ldv, int KH, int64_t nh, float sl2e) {
   MOBA_DECLARE_TILES
   // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
   // contiguous range of tiles so the tiles of one K/V block share its L2.
@@ -445,7 +445,7 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
   Wave W;
   wave_load_q(W, qrow, valid, h);
 
-  const int64_t kbase = j * B;
+  const int64_t kbase = bstart[j];  // history blocks are always full
   const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + j * Bpad;
   const int ntiles = (B + KT - 1) / KT;
   const bool wave_live = (e_begin + wave * kWaveQ) < e_end;
@@ -496,9 +496,10 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
-    const _Float16* __restrict__ part_o, const float* __restrict__ part_lse,
-    uint16_t* __restrict__ O, int64_t N, int Hq, int Hkv, int G, int64_t B, int64_t Bpad,
-    int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ blen,
+    const int32_t* __restrict__ blo, const _Float16* __restrict__ part_o,
+    const float* __restrict__ part_lse, uint16_t* __restrict__ O, int Hq, int Hkv, int G,
+    int64_t Bpad, int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
   MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   // Work items w = ((c' * Hkv) + g) * tiles_per_block + t' in order of
@@ -512,9 +513,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   const int tile = tiles_per_block - 1 - (int)(w % tiles_per_block);
   const int g = (int)((w / tiles_per_block) % Hkv);
   const int64_t c = n - 1 - w / ((int64_t)tiles_per_block * Hkv);
-  const int64_t row0 = c * B;
-  int64_t rows_c = N - row0;
-  if (rows_c > B) rows_c = B;
+  const int64_t row0 = bstart[c], rows_c = blen[c];
   const int64_t npairs = rows_c * G;
   const int64_t p0 = (int64_t)tile * kGroupQ;
   if (p0 >= npairs) return;
@@ -559,7 +558,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
                                   my_row, wrow_min, wrow_max, wave_live, sl2e, false);
   }
-  const int nhist = part_o != nullptr ? (int)(c < KH ? c : KH) : 0;  // uniform
+  const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
+  const int nhist = part_o != nullptr ? (int)(nbefore < KH ? nbefore : KH) : 0;  // uniform
   if (nhist == 0) {
     // no history: O = own-block result, straight from the accumulators
 #pragma unroll
@@ -630,35 +630,35 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
 
 int64_t vt_padded_block(int64_t B) { return ceil_div(B, KT) * KT; }
 
-hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                                 const void* Vt, const BucketBufs& b, void* part_o,
-                                 float* part_lse, hipStream_t s) {
+hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                                 const void* Q, const void* K, const void* Vt,
+                                 const BucketBufs& b, void* part_o, float* part_lse,
+                                 hipStream_t s) {
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
   const int64_t ldv = P.n * Bpad;
   const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
   attn_hist_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, b.tile_map, b.tile_off,
-      b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, Bpad, ldv, P.KH,
-      P.nh, sl2e);
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
+      b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, Bpad,
+      ldv, P.KH, P.nh, sl2e);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* Vt,
-                                 const void* part_o, const float* part_lse, void* O, bool dense,
-                                 hipStream_t s) {
+hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, const void* K,
+                                 const void* Vt, const void* part_o, const float* part_lse,
+                                 void* O, hipStream_t s) {
   const float sl2e = P.scale * kLog2e;
-  const int64_t B = dense ? P.N : P.B;
-  const int64_t n = dense ? 1 : P.n;
-  const int64_t Bpad = vt_padded_block(B);
-  const int64_t ldv = n * Bpad;
-  const int tiles_per_block = (int)ceil_div(B * P.G, kGroupQ);
-  const int64_t grid = ceil_div(n * tiles_per_block * P.Hkv, 8) * 8;
+  const int64_t Bpad = vt_padded_block(P.B);
+  const int64_t ldv = P.n * Bpad;
+  const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kGroupQ);
+  const int64_t grid = ceil_div(P.n * tiles_per_block * P.Hkv, 8) * 8;
+  const bool merge = part_o != nullptr && P.KH > 0;
   attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt,
-      dense ? nullptr : (const _Float16*)part_o, dense ? nullptr : part_lse, (uint16_t*)O, P.N,
-      P.Hq, P.Hkv, P.G, B, Bpad, ldv, dense ? 0 : P.KH, n, tiles_per_block, sl2e);
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.len, T.lo,
+      merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr, (uint16_t*)O, P.Hq,
+      P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, tiles_per_block, sl2e);
   return hipGetLastError();
 }
 

@@ -9,12 +9,13 @@
 
 namespace moba {
 
-hipError_t launch_attn_hist_bf16(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                                 const void* Vt, const BucketBufs& b, void* part_o,
-                                 float* part_lse, hipStream_t s);
-hipError_t launch_attn_self_bf16(const Prob& P, const void* Q, const void* K, const void* Vt,
-                                 const void* part_o, const float* part_lse, void* O, bool dense,
+hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                                 const void* Q, const void* K, const void* Vt,
+                                 const BucketBufs& b, void* part_o, float* part_lse,
                                  hipStream_t s);
+hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, const void* K,
+                                 const void* Vt, const void* part_o, const float* part_lse,
+                                 void* O, hipStream_t s);
 
 namespace {
 
@@ -95,7 +96,8 @@ __device__ inline void init_state(QState& S, const float* qrow, bool valid, int 
 
 __global__ __launch_bounds__(kThreads) void attn_hist_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ tile_map,
+    const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
     const uint32_t* __restrict__ entries, float* __restrict__ part_o, float* __restrict__ part_lse,
     int Hkv, int B, int KH, int64_t nh, float sl2e) {
@@ -118,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
     for (int k0 = 0; k0 < B; k0 += KT) {
       const int nv = (B - k0) < KT ? B - k0 : KT;
       __syncthreads();
-      load_tile(ks, vs, K, V, (int64_t)j * B + k0, nv, Hkv, g);
+      load_tile(ks, vs, K, V, (int64_t)bstart[j] + k0, nv, Hkv, g);
       __syncthreads();
       tile_step(S, ks, vs, sub, sl2e, [&](int t) { return t < nv; });
     }
@@ -134,17 +136,16 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
 
 __global__ __launch_bounds__(kThreads) void attn_self_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const float* __restrict__ part_o, const float* __restrict__ part_lse, float* __restrict__ O,
-    int64_t N, int Hq, int Hkv, int G, int64_t B, int KH, int64_t n, int tiles_per_block,
-    float sl2e) {
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ blen,
+    const int32_t* __restrict__ blo, const float* __restrict__ part_o,
+    const float* __restrict__ part_lse, float* __restrict__ O, int Hq, int Hkv, int G, int KH,
+    int64_t n, int tiles_per_block, float sl2e) {
   __shared__ float ks[KT * kHeadDim];
   __shared__ float vs[KT * kHeadDim];
   const int g = blockIdx.y;
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = tiles_per_block - 1 - (int)(blockIdx.x % tiles_per_block);
-  const int64_t row0 = c * B;
-  int64_t rows_c = N - row0;
-  if (rows_c > B) rows_c = B;
+  const int64_t row0 = bstart[c], rows_c = blen[c];
   const int64_t npairs = rows_c * G;
   const int64_t p0 = (int64_t)tile * kQ;
   if (p0 >= npairs) return;
@@ -169,7 +170,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
   if (!valid) return;
   float l = S.l;
   if (part_o != nullptr && KH > 0) {
-    const int64_t nhist = c < KH ? c : KH;
+    const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
+    const int64_t nhist = nbefore < KH ? nbefore : KH;
     const int64_t ebase = ph * KH;
     float M = S.m;
     for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
@@ -193,30 +195,31 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
 
 }  // namespace
 
-hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                            const void* V, const void* Vt, const BucketBufs& b, void* part_o,
-                            float* part_lse, hipStream_t s) {
-  if (P.dtype == MOBA_DTYPE_BF16) return launch_attn_hist_bf16(P, bp, Q, K, Vt, b, part_o, part_lse, s);
+hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp, const void* Q,
+                            const void* K, const void* V, const void* Vt, const BucketBufs& b,
+                            void* part_o, float* part_lse, hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16)
+    return launch_attn_hist_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s);
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   attn_hist_f32<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
-      (const float*)Q, (const float*)K, (const float*)V, b.tile_map, b.tile_off, b.bin_off,
-      b.scalars, b.entries, (float*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh, P.scale * kLog2e);
+      (const float*)Q, (const float*)K, (const float*)V, T.start, b.tile_map, b.tile_off,
+      b.bin_off, b.scalars, b.entries, (float*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh,
+      P.scale * kLog2e);
   return hipGetLastError();
 }
 
-hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
-                            const void* Vt, const void* part_o, const float* part_lse, void* O,
-                            bool dense, hipStream_t s) {
+hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const void* K,
+                            const void* V, const void* Vt, const void* part_o,
+                            const float* part_lse, void* O, hipStream_t s) {
   if (P.dtype == MOBA_DTYPE_BF16)
-    return launch_attn_self_bf16(P, Q, K, Vt, part_o, part_lse, O, dense, s);
-  const int64_t B = dense ? P.N : P.B;
-  const int64_t n = dense ? 1 : P.n;
-  const int tiles_per_block = (int)ceil_div(B * P.G, kQ);
-  dim3 grid((unsigned)(n * tiles_per_block), (unsigned)P.Hkv);
+    return launch_attn_self_bf16(P, T, Q, K, Vt, part_o, part_lse, O, s);
+  const bool merge = part_o != nullptr && P.KH > 0;
+  const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kQ);
+  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
   attn_self_f32<<<grid, kThreads, 0, s>>>(
-      (const float*)Q, (const float*)K, (const float*)V, dense ? nullptr : (const float*)part_o,
-      dense ? nullptr : part_lse, (float*)O, P.N, P.Hq, P.Hkv, P.G, B, dense ? 0 : P.KH, n,
-      tiles_per_block, P.scale * kLog2e);
+      (const float*)Q, (const float*)K, (const float*)V, T.start, T.len, T.lo,
+      merge ? (const float*)part_o : nullptr, merge ? part_lse : nullptr, (float*)O, P.Hq, P.Hkv,
+      P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e);
   return hipGetLastError();
 }
 

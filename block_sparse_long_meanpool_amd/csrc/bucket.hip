@@ -22,12 +22,14 @@ namespace {
 constexpr int kThreads = 256;
 constexpr int kScanRowGroups = 16;
 
-// Valid history entry of a selection row: block b in [0, c) at slot s < k-1.
+// Valid history entry of a selection row of block c: a block b < c at slot
+// s < k-1 (the row's own block, always its largest, and -1 pads are not).
 __device__ inline bool hist_entry(int32_t b, int64_t c) { return b >= 0 && b < c; }
 
 __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restrict__ sel,
+                                                         const int32_t* __restrict__ row_blk,
                                                          int32_t* __restrict__ chunk_base,
-                                                         int64_t N, int Hq, int G, int B, int k,
+                                                         int64_t N, int Hq, int G, int k,
                                                          int64_t nh, int rows_per_chunk,
                                                          int64_t nchunk) {
   extern __shared__ int32_t hist[];
@@ -41,7 +43,7 @@ __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restri
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
-    const int64_t c = r / B;
+    const int64_t c = row_blk[r];
     const int32_t* row = sel + ((size_t)r * Hq + h) * k;
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
@@ -133,9 +135,10 @@ __global__ __launch_bounds__(1024) void bucket_scan_bins(const int32_t* __restri
 }
 
 __global__ __launch_bounds__(kThreads) void bucket_scatter(
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ chunk_base,
-    const int32_t* __restrict__ bin_off, uint32_t* __restrict__ entries, int64_t N, int Hq, int G,
-    int B, int k, int64_t nh, int rows_per_chunk, int64_t nchunk, int words) {
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ row_blk,
+    const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ bin_off,
+    uint32_t* __restrict__ entries, int64_t N, int Hq, int G, int k, int64_t nh,
+    int rows_per_chunk, int64_t nchunk, int words) {
   extern __shared__ uint32_t bm[];  // [nh][words]
   const int g = blockIdx.y;
   const int64_t chunk = blockIdx.x;
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
-    const int64_t c = r / B;
+    const int64_t c = row_blk[r];
     const int32_t* row = sel + ((size_t)r * Hq + h) * k;
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
@@ -162,7 +165,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
-    const int64_t c = r / B;
+    const int64_t c = row_blk[r];
     const int64_t ph = (int64_t)r * Hq + h;
     const int32_t* row = sel + ph * k;
     for (int s = 0; s < KH; ++s) {
@@ -197,18 +200,12 @@ BucketPlan plan_bucket(const Prob& P) {
   bp.words = (int)ceil_div(rpc * P.G, 32);
   bp.nchunk = ceil_div(P.N, rpc);
   bp.nbins = (int64_t)P.Hkv * P.nh;
-  int64_t e = 0;
-  for (int64_t c = 0; c < P.n; ++c) {
-    int64_t rows = P.N - c * P.B;
-    if (rows > P.B) rows = P.B;
-    e += rows * (c < P.KH ? c : P.KH);
-  }
-  bp.max_entries = e * P.Hq;
+  bp.max_entries = P.hist_rows * P.Hq;
   bp.max_tiles = ceil_div(bp.max_entries, kTileQ) + bp.nbins;
   return bp;
 }
 
-hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
+hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, const int32_t* sel,
                          const BucketBufs& b, hipStream_t s) {
   if (P.nh <= 0 || P.KH <= 0) {
     // No history anywhere: empty lists.
@@ -219,7 +216,7 @@ hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel
   }
   dim3 grid((unsigned)bp.nchunk, (unsigned)P.Hkv);
   bucket_count<<<grid, kThreads, sizeof(int32_t) * P.nh, s>>>(
-      sel, b.chunk_base, P.N, P.Hq, P.G, P.B, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
+      sel, T.row_blk, b.chunk_base, P.N, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bucket_scan_cols<<<(unsigned)ceil_div(bp.nbins, 16), kThreads, 0, s>>>(b.chunk_base, b.bin_total,
@@ -229,8 +226,8 @@ hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bucket_scatter<<<grid, kThreads, sizeof(uint32_t) * P.nh * bp.words, s>>>(
-      sel, b.chunk_base, b.bin_off, b.entries, P.N, P.Hq, P.G, P.B, P.k, P.nh, bp.rows_per_chunk,
-      bp.nchunk, bp.words);
+      sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.N, P.Hq, P.G, P.k, P.nh,
+      bp.rows_per_chunk, bp.nchunk, bp.words);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (b.tile_map) {
     bucket_tile_map<<<(unsigned)bp.nbins, kThreads, 0, s>>>(b.tile_off, b.tile_map);

@@ -228,8 +228,10 @@ __device__ inline double widen<float>(float x) {
 template <typename T, int KM>
 __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
                                                   const double* __restrict__ kbarT,
+                                                  const int32_t* __restrict__ row_blk,
+                                                  const int32_t* __restrict__ blo,
                                                   int32_t* __restrict__ sel, int64_t N, int Hq,
-                                                  int G, int B, int k, int64_t nhp, int all_rows) {
+                                                  int G, int k, int64_t nhp, int all_rows) {
   __shared__ double qs[kHeadDim];
   const int lane = threadIdx.x;
   const int KH = k - 1;
@@ -239,13 +241,13 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
   {
     const int64_t ph = ph0 + lane;
     if (ph < nph) {
-      const int64_t r = ph / Hq, c = r / B;
+      const int64_t c = row_blk[ph / Hq], lo = blo[c];
       int32_t* out = sel + ph * k;
-      if (c > KH && KH > 0) {
+      if (c - lo > KH && KH > 0) {
         mine = all_rows || out[0] == kRefine;
-      } else if (all_rows) {  // every earlier block is taken
-        const int nsel = (int)(c < KH ? c : KH);
-        for (int a = 0; a < nsel; ++a) out[a] = a;
+      } else if (all_rows) {  // every earlier block of the sequence is taken
+        const int nsel = (int)(c - lo < KH ? c - lo : KH);
+        for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
         out[nsel] = (int32_t)c;
         for (int a = nsel + 1; a < k; ++a) out[a] = -1;
       }
@@ -256,7 +258,7 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     const int l = __ffsll((long long)todo) - 1;
     todo &= todo - 1;
     const int64_t ph = ph0 + l;
-    const int64_t r = ph / Hq, c = r / B;
+    const int64_t c = row_blk[ph / Hq], lo = blo[c];
     const int g = (int)(ph % Hq) / G;
     const T* qrow = Q + ph * kHeadDim;
     qs[2 * lane] = widen<T>(qrow[2 * lane]);
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
       ix[t] = 0x7FFFFFFF;
     }
     const double* kt = kbarT + (int64_t)g * kHeadDim * nhp;
-    for (int64_t b = lane; b < c; b += 64) {
+    for (int64_t b = lo + lane; b < c; b += 64) {
       double acc = 0.0;
 #pragma unroll 16
       for (int d = 0; d < kHeadDim; ++d) acc = fma(qs[d], kt[(int64_t)d * nhp + b], acc);
@@ -329,17 +331,18 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
 template <int KM>
 __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
-    const float* __restrict__ maxnorm, const double* __restrict__ kbar, int32_t* __restrict__ sel,
-    int64_t N, int Hq, int G, int B, int k, int64_t n, int64_t nh, int tiles_per_block) {
+    const float* __restrict__ maxnorm, const int32_t* __restrict__ bstart,
+    const int32_t* __restrict__ blen, const int32_t* __restrict__ blo, int32_t* __restrict__ sel,
+    int Hq, int G, int k, int64_t n, int64_t nh, int tiles_per_block) {
   __shared__ __align__(16) uint16_t bufA[kChunkElems];
   __shared__ __align__(16) uint16_t bufB[kChunkElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, lr = lane & 31;
   const int g = blockIdx.y;
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = blockIdx.x % tiles_per_block;
-  const int64_t row0 = c * B;
-  int64_t rows_c = N - row0;
-  if (rows_c > B) rows_c = B;
+  const int64_t row0 = bstart[c], rows_c = blen[c];
+  const int64_t lo = blo[c];  // candidates: blocks [lo, c) of the row's sequence
+  const int64_t nc = c - lo;
   const int64_t npairs_c = rows_c * G;
   const int64_t pair0 = (int64_t)tile * kPairs;
   if (pair0 >= npairs_c) return;
@@ -350,11 +353,11 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   const int64_t r = row0 + (valid ? pi / G : 0);
   const int hq = g * G + (int)(valid ? pi % G : 0);
   int32_t* out = sel + ((size_t)r * Hq + hq) * k;
-  const int nsel = (int)(c < KH ? c : KH);
+  const int nsel = (int)(nc < KH ? nc : KH);
 
-  if (c <= KH || KH == 0) {  // every earlier block is taken: nothing to rank
+  if (nc <= KH || KH == 0) {  // every earlier block is taken: nothing to rank
     if (valid && h == 0) {
-      for (int a = 0; a < nsel; ++a) out[a] = a;
+      for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
       out[nsel] = (int32_t)c;
       for (int a = nsel + 1; a < k; ++a) out[a] = -1;
     }
@@ -378,26 +381,27 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   }
   qq += __shfl_xor(qq, 32);
 
-  const uint16_t* planes_g = planes + (size_t)g * nh * 3 * kHeadDim;
+  // candidates by local index b - lo in [0, nc)
+  const uint16_t* planes_g = planes + ((size_t)g * nh + lo) * 3 * kHeadDim;
   const float kmax = maxnorm[g];
-  int ib = 1;  // index bits for blocks 0..c-1
-  while ((1ll << ib) < c) ++ib;
+  int ib = 1;  // index bits for local blocks 0..nc-1
+  while ((1ll << ib) < nc) ++ib;
   KeyList<KM> L;
   L.init();
-  const int nchunks = (int)((c + kChunk - 1) / kChunk);
+  const int nchunks = (int)((nc + kChunk - 1) / kChunk);
   auto step = [&](int ch, uint16_t* cur, uint16_t* nxt) {
-    if (ch + 1 < nchunks) load_chunk(nxt, planes_g, (int64_t)(ch + 1) * kChunk, c, wave, lane);
+    if (ch + 1 < nchunks) load_chunk(nxt, planes_g, (int64_t)(ch + 1) * kChunk, nc, wave, lane);
     f32x16 s;
     chunk_scores(cur, q, lane, s);
     const int64_t cb = (int64_t)ch * kChunk;
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {  // blocks past c push key 0, which never enters
+    for (int e = 0; e < 16; ++e) {  // blocks past the candidates push key 0, which never enters
       const int b = (int)cb + 8 * (e >> 2) + 4 * h + (e & 3);
-      L.push(b < c ? score_key(s[e], b, ib) : 0u);
+      L.push(b < nc ? score_key(s[e], b, ib) : 0u);
     }
     wait_chunk();
   };
-  load_chunk(bufA, planes_g, 0, c, wave, lane);
+  load_chunk(bufA, planes_g, 0, nc, wave, lane);
   wait_chunk();
   for (int ch = 0; ch < nchunks; ch += 2) {
     step(ch, bufA, bufB);
@@ -420,7 +424,7 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   for (int t = 0; t < KM; ++t) {
     if (t == KH - 1) kk_in = L.k[t];
     if (t == KH) kk_out = L.k[t];
-    idx[t] = key_block(L.k[t], ib);
+    idx[t] = (int)lo + key_block(L.k[t], ib);
   }
   const float theta = key_score(kk_in, ib), theta_n = key_score(kk_out, ib);
   const float big = fmaxf(fabsf(theta), fabsf(theta_n));
@@ -439,24 +443,24 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
 }
 
 template <int KM>
-hipError_t launch_km(const Prob& P, const void* Q, const double* kbar, const uint16_t* planes,
+hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16_t* planes,
                      const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
                      hipStream_t s) {
   const unsigned refine_grid = (unsigned)ceil_div(P.N * P.Hq, 64);
   if (P.dtype == MOBA_DTYPE_F32) {
-    gate_refine<float, KM><<<refine_grid, 64, 0, s>>>((const float*)Q, kbarT, sel, P.N, P.Hq, P.G,
-                                                     P.B, P.k, nhp, 1);
+    gate_refine<float, KM><<<refine_grid, 64, 0, s>>>((const float*)Q, kbarT, T.row_blk, T.lo, sel,
+                                                     P.N, P.Hq, P.G, P.k, nhp, 1);
     return hipGetLastError();
   }
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
   dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
-  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, kbar, sel,
-                                                P.N, P.Hq, P.G, P.B, P.k, P.n, P.nh,
+  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.start,
+                                                T.len, T.lo, sel, P.Hq, P.G, P.k, P.n, P.nh,
                                                 tiles_per_block);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
-  gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, sel, P.N, P.Hq,
-                                                      P.G, P.B, P.k, nhp, 0);
+  gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, T.row_blk, T.lo,
+                                                      sel, P.N, P.Hq, P.G, P.k, nhp, 0);
   return hipGetLastError();
 }
 
@@ -469,8 +473,8 @@ size_t gate_scratch_bytes(const Prob& P) {
          sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P) + 1024;
 }
 
-hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, void* scratch,
-                            int32_t* sel, hipStream_t s) {
+hipError_t launch_gate_topk(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
+                            void* scratch, int32_t* sel, hipStream_t s) {
   char* base = (char*)scratch;
   double* kbarT = (double*)base;  // first: keeps 8-byte alignment
   base += sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P);
@@ -489,11 +493,11 @@ hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, vo
   }
   // list length: the k-1 kept blocks plus the best one left out
   const int need = P.KH + 1;
-  if (need <= 4) return launch_km<4>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 8) return launch_km<8>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 12) return launch_km<12>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 16) return launch_km<16>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
-  return launch_km<32>(P, Q, kbar, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 4) return launch_km<4>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 8) return launch_km<8>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 12) return launch_km<12>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
+  if (need <= 16) return launch_km<16>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
+  return launch_km<32>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
 }
 
 }  // namespace moba

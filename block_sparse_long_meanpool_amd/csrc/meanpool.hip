@@ -42,10 +42,14 @@ struct Vec8<float> {
 
 // grid: (nh, col chunks, splits). Column groups of 8 elements; CW groups per
 // workgroup, R = kThreads / CW rows in flight.
+// A block shorter than B (the last one of a sequence) is never history; its
+// sums are left at zero.
 template <typename T>
 __global__ __launch_bounds__(kThreads) void meanpool_partial(const T* __restrict__ K,
-                                                             double* __restrict__ part, int64_t N,
-                                                             int B, int W8, int CW, int splits,
+                                                             const int32_t* __restrict__ bstart,
+                                                             const int32_t* __restrict__ blen,
+                                                             double* __restrict__ part, int B,
+                                                             int W8, int CW, int splits,
                                                              int64_t nh) {
   __shared__ double red[kThreads * 8];
   const int tid = threadIdx.x;
@@ -56,9 +60,11 @@ __global__ __launch_bounds__(kThreads) void meanpool_partial(const T* __restrict
   const int colg = blockIdx.y * CW + cg;
   const int s = blockIdx.z;
   const int64_t rows_per_split = (B + splits - 1) / splits;
-  const int64_t r0 = blk * B + (int64_t)s * rows_per_split;
+  const int64_t b0 = bstart[blk];
+  const int64_t r0 = b0 + (int64_t)s * rows_per_split;
   int64_t r1 = r0 + rows_per_split;
-  if (r1 > (blk + 1) * B) r1 = (blk + 1) * B;
+  if (r1 > b0 + B) r1 = b0 + B;
+  if (blen[blk] < B) r1 = r0;
   const int64_t W = (int64_t)W8 * 8;
 
   double acc[8];
@@ -133,18 +139,18 @@ int meanpool_splits(const Prob& P) {
   return (int)want;
 }
 
-hipError_t launch_meanpool(const Prob& P, const void* K, double* kbar, double* part, int splits,
-                           hipStream_t s) {
+hipError_t launch_meanpool(const Prob& P, const Blocks& T, const void* K, double* kbar,
+                           double* part, int splits, hipStream_t s) {
   if (P.nh <= 0) return hipSuccess;
   const int W8 = P.Hkv * P.d / 8;
   const int CW = W8 < kThreads ? W8 : kThreads;
   dim3 grid((unsigned)P.nh, (unsigned)ceil_div(W8, CW), (unsigned)splits);
   if (P.dtype == MOBA_DTYPE_BF16)
     meanpool_partial<__hip_bfloat16><<<grid, kThreads, 0, s>>>(
-        (const __hip_bfloat16*)K, part, P.N, P.B, W8, CW, splits, P.nh);
+        (const __hip_bfloat16*)K, T.start, T.len, part, P.B, W8, CW, splits, P.nh);
   else
-    meanpool_partial<float><<<grid, kThreads, 0, s>>>((const float*)K, part, P.N, P.B, W8, CW,
-                                                      splits, P.nh);
+    meanpool_partial<float><<<grid, kThreads, 0, s>>>((const float*)K, T.start, T.len, part, P.B,
+                                                      W8, CW, splits, P.nh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int64_t total = P.nh * P.Hkv * P.d;

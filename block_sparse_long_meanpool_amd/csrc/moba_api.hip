@@ -46,8 +46,6 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   if (p->topk > kMaxTopk) return fail(MOBA_ERR_UNSUPPORTED, "topk > 32 is not supported");
   const int G = p->num_q_heads / p->num_kv_heads;
   if (G > kMaxGroup) return fail(MOBA_ERR_UNSUPPORTED, "num_q_heads / num_kv_heads > 64");
-  const int64_t n = (p->seqlen + p->block_size - 1) / p->block_size;
-  if (n - 1 > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
   if ((double)p->seqlen * p->num_q_heads * p->topk >= 2147483648.0)
     return fail(MOBA_ERR_UNSUPPORTED, "seqlen * num_q_heads * topk must be < 2^31");
   P->N = p->seqlen;
@@ -58,25 +56,78 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   P->B = p->block_size;
   P->k = p->topk;
   P->KH = p->topk - 1;
-  P->n = n;
-  P->nh = n - 1;
   P->scale = p->scale;
   P->dtype = p->dtype;
+  // one sequence of all rows; make_prob_varlen overrides the sequence layout
+  P->nseq = 1;
+  P->n = (P->N + P->B - 1) / P->B;
+  P->nh = P->n - 1;
+  P->hist_rows = 0;
+  for (int64_t c = 0; c < P->n; ++c) {
+    const int64_t rows = P->N - c * P->B < P->B ? P->N - c * P->B : P->B;
+    P->hist_rows += rows * (c < P->KH ? c : P->KH);
+  }
+  if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
+  return MOBA_OK;
+}
+
+// Packed sequences: row offsets cu[0..nseq] on the host (cu[0] = 0,
+// nondecreasing, cu[nseq] = seqlen). Blocks restart at every sequence.
+int make_prob_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu, Prob* P) {
+  if (!cu) return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens (host) is NULL");
+  if (nseq < 1) return fail(MOBA_ERR_INVALID_ARGUMENT, "nseq must be >= 1");
+  if (!p) return fail(MOBA_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
+  if (cu[0] != 0) return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens[0] must be 0");
+  for (int64_t i = 0; i < nseq; ++i)
+    if (cu[i + 1] < cu[i]) return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens must be nondecreasing");
+  if (cu[nseq] != p->seqlen)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens[nseq] must equal seqlen");
+  int rc = make_prob(p, P);
+  if (rc) return rc;
+  if (nseq > INT32_MAX) return fail(MOBA_ERR_UNSUPPORTED, "too many sequences");
+  P->nseq = nseq;
+  P->n = 0;
+  P->hist_rows = 0;
+  for (int64_t i = 0; i < nseq; ++i) {
+    const int64_t L = cu[i + 1] - cu[i];
+    const int64_t nb = (L + P->B - 1) / P->B;
+    for (int64_t c = 0; c < nb; ++c) {
+      const int64_t rows = L - c * P->B < P->B ? L - c * P->B : P->B;
+      P->hist_rows += rows * (c < P->KH ? c : P->KH);
+    }
+    P->n += nb;
+  }
+  P->nh = P->n - 1;
+  if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
   return MOBA_OK;
 }
 
 size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 
 struct Layout {
+  size_t blk_start, blk_len, blk_lo, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
       part_lse, part_o, vt, total;
 };
 
 // Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
-size_t vt_bytes(const Prob& P, int64_t B) {
+size_t vt_bytes(const Prob& P) {
   if (P.dtype != MOBA_DTYPE_BF16) return 0;
-  const int64_t n = ceil_div(P.N, B);
-  return sizeof(uint16_t) * (size_t)P.Hkv * P.d * (size_t)(n * vt_padded_block(B));
+  return sizeof(uint16_t) * (size_t)P.Hkv * P.d * (size_t)(P.n * vt_padded_block(P.B));
+}
+
+// Block and row tables (first in every workspace).
+void take_tables(const Prob& P, Layout& L, size_t& off) {
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  L.blk_start = take(sizeof(int32_t) * (size_t)P.n);
+  L.blk_len = take(sizeof(int32_t) * (size_t)P.n);
+  L.blk_lo = take(sizeof(int32_t) * (size_t)P.n);
+  L.row_blk = take(sizeof(int32_t) * (size_t)P.N);
+  L.seq_base = take(sizeof(int32_t) * (size_t)(P.nseq + 1));
 }
 
 // Workspace layout; `full` = prefill (all stages), else select only.
@@ -88,6 +139,7 @@ Layout plan_ws(const Prob& P, bool full) {
     off = align_up(off + bytes);
     return at;
   };
+  take_tables(P, L, off);
   const int splits = meanpool_splits(P);
   L.kbar = take(sizeof(double) * (size_t)(P.Hkv * P.nh * P.d));
   L.mp_part = take(sizeof(double) * (size_t)splits * P.nh * P.Hkv * P.d);
@@ -105,7 +157,7 @@ Layout plan_ws(const Prob& P, bool full) {
     const size_t slots = (size_t)(P.N * P.Hq) * (size_t)P.KH;
     L.part_lse = take(sizeof(float) * slots);
     L.part_o = take(part_elem_bytes(P) * slots * P.d);
-    L.vt = take(vt_bytes(P, P.B));
+    L.vt = take(vt_bytes(P));
   }
   L.total = off;
   return L;
@@ -135,6 +187,16 @@ T* at(void* base, size_t off) {
   return reinterpret_cast<T*>(reinterpret_cast<char*>(base) + off);
 }
 
+Blocks tables(void* ws, const Layout& L) {
+  Blocks t{};
+  t.start = at<int32_t>(ws, L.blk_start);
+  t.len = at<int32_t>(ws, L.blk_len);
+  t.lo = at<int32_t>(ws, L.blk_lo);
+  t.row_blk = at<int32_t>(ws, L.row_blk);
+  t.seq_base = at<int32_t>(ws, L.seq_base);
+  return t;
+}
+
 BucketBufs bucket_bufs(void* ws, const Layout& L) {
   BucketBufs b{};
   b.chunk_base = at<int32_t>(ws, L.chunk_base);
@@ -153,16 +215,63 @@ int record(void* const* events, int i, hipStream_t s) {
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "hipEventRecord");
 }
 
-int run_select(const Prob& P, const void* q, const void* k, int32_t* sel, void* ws,
-               const Layout& L, hipStream_t s, void* const* events) {
+// Tables, block means, gate + top-k. cu: device row offsets or NULL.
+int run_select(const Prob& P, const int64_t* cu, const void* q, const void* k, int32_t* sel,
+               void* ws, const Layout& L, hipStream_t s, void* const* events) {
   int rc;
-  hipError_t e = launch_meanpool(P, k, at<double>(ws, L.kbar), at<double>(ws, L.mp_part),
-                                 meanpool_splits(P), s);
+  const Blocks T = tables(ws, L);
+  hipError_t e = launch_tables(P, cu, T, s);
+  if (e != hipSuccess) return hip_fail(e, "block tables");
+  e = launch_meanpool(P, T, k, at<double>(ws, L.kbar), at<double>(ws, L.mp_part),
+                      meanpool_splits(P), s);
   if (e != hipSuccess) return hip_fail(e, "moba_meanpool");
   if ((rc = record(events, 1, s))) return rc;
-  e = launch_gate_topk(P, q, at<double>(ws, L.kbar), at<void>(ws, L.gate), sel, s);
+  e = launch_gate_topk(P, T, q, at<double>(ws, L.kbar), at<void>(ws, L.gate), sel, s);
   if (e != hipSuccess) return hip_fail(e, "moba_gate_topk");
   return record(events, 2, s);
+}
+
+// The whole path on prepared problem and workspace.
+int run_prefill(const Prob& P, const int64_t* cu, const void* q, const void* k, const void* v,
+                void* o, void* workspace, const Layout& L, hipStream_t s, void* const* events) {
+  int rc;
+  if ((rc = record(events, 0, s))) return rc;
+  int32_t* sel = at<int32_t>(workspace, L.sel);
+  if ((rc = run_select(P, cu, q, k, sel, workspace, L, s, events))) return rc;
+  const Blocks T = tables(workspace, L);
+  const BucketPlan bp = plan_bucket(P);
+  const BucketBufs bb = bucket_bufs(workspace, L);
+  hipError_t e = launch_bucket(P, T, bp, sel, bb, s);
+  if (e != hipSuccess) return hip_fail(e, "moba_bucket");
+  if ((rc = record(events, 3, s))) return rc;
+  void* part_o = at<void>(workspace, L.part_o);
+  float* part_lse = at<float>(workspace, L.part_lse);
+  void* vt = at<void>(workspace, L.vt);
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    e = launch_vt_pack(P, T, v, vt, s);
+    if (e != hipSuccess) return hip_fail(e, "V pack");
+  }
+  if ((rc = record(events, 4, s))) return rc;
+  e = launch_attn_hist(P, T, bp, q, k, v, vt, bb, part_o, part_lse, s);
+  if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
+  if ((rc = record(events, 5, s))) return rc;
+  e = launch_attn_self(P, T, q, k, v, vt, part_o, part_lse, o, s);
+  if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
+  return record(events, 6, s);
+}
+
+int check_events(void* const* events) {
+  if (events)
+    for (int i = 0; i < MOBA_STAGE_EVENTS; ++i)
+      if (!events[i]) return fail(MOBA_ERR_INVALID_ARGUMENT, "stage event handle is NULL");
+  return MOBA_OK;
+}
+
+int check_cu_dev(const int64_t* cu_dev) {
+  if (!cu_dev) return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens (device) is NULL");
+  if (!aligned(cu_dev, 8))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "cu_seqlens (device) must be 8-byte aligned");
+  return MOBA_OK;
 }
 
 }  // namespace
@@ -194,32 +303,8 @@ int moba_prefill_ex(const moba_problem_t* p, const void* q, const void* k, const
   if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
   const Layout L = plan_ws(P, true);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
-  if (events)
-    for (int i = 0; i < MOBA_STAGE_EVENTS; ++i)
-      if (!events[i]) return fail(MOBA_ERR_INVALID_ARGUMENT, "stage event handle is NULL");
-  hipStream_t s = (hipStream_t)stream;
-  if ((rc = record(events, 0, s))) return rc;
-  int32_t* sel = at<int32_t>(workspace, L.sel);
-  if ((rc = run_select(P, q, k, sel, workspace, L, s, events))) return rc;
-  const BucketPlan bp = plan_bucket(P);
-  const BucketBufs bb = bucket_bufs(workspace, L);
-  hipError_t e = launch_bucket(P, bp, sel, bb, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_bucket");
-  if ((rc = record(events, 3, s))) return rc;
-  void* part_o = at<void>(workspace, L.part_o);
-  float* part_lse = at<float>(workspace, L.part_lse);
-  void* vt = at<void>(workspace, L.vt);
-  if (P.dtype == MOBA_DTYPE_BF16) {
-    e = launch_vt_pack(v, vt, P.N, P.Hkv, P.B, s);
-    if (e != hipSuccess) return hip_fail(e, "V pack");
-  }
-  if ((rc = record(events, 4, s))) return rc;
-  e = launch_attn_hist(P, bp, q, k, v, vt, bb, part_o, part_lse, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
-  if ((rc = record(events, 5, s))) return rc;
-  e = launch_attn_self(P, q, k, v, vt, part_o, part_lse, o, false, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
-  return record(events, 6, s);
+  if ((rc = check_events(events))) return rc;
+  return run_prefill(P, nullptr, q, k, v, o, workspace, L, (hipStream_t)stream, events);
 }
 
 int moba_prefill(const moba_problem_t* p, const void* q, const void* k, const void* v, void* o,
@@ -236,7 +321,49 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
   if ((rc = check_ptrs(ptrs, 3, "q, k and sel must be non-NULL"))) return rc;
   const Layout L = plan_ws(P, false);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
-  return run_select(P, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
+  return run_select(P, nullptr, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
+}
+
+size_t moba_varlen_workspace_size(const moba_problem_t* p, int64_t nseq,
+                                  const int64_t* cu_seqlens_host) {
+  Prob P;
+  if (make_prob_varlen(p, nseq, cu_seqlens_host, &P) != MOBA_OK) return 0;
+  return plan_ws(P, true).total;
+}
+
+size_t moba_varlen_select_workspace_size(const moba_problem_t* p, int64_t nseq,
+                                         const int64_t* cu_seqlens_host) {
+  Prob P;
+  if (make_prob_varlen(p, nseq, cu_seqlens_host, &P) != MOBA_OK) return 0;
+  return plan_ws(P, false).total;
+}
+
+int moba_prefill_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu_seqlens_host,
+                        const int64_t* cu_seqlens_dev, const void* q, const void* k,
+                        const void* v, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_varlen(p, nseq, cu_seqlens_host, &P);
+  if (rc) return rc;
+  if ((rc = check_cu_dev(cu_seqlens_dev))) return rc;
+  const void* ptrs[4] = {q, k, v, o};
+  if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, true);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_prefill(P, cu_seqlens_dev, q, k, v, o, workspace, L, (hipStream_t)stream, nullptr);
+}
+
+int moba_select_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu_seqlens_host,
+                       const int64_t* cu_seqlens_dev, const void* q, const void* k, int32_t* sel,
+                       void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_varlen(p, nseq, cu_seqlens_host, &P);
+  if (rc) return rc;
+  if ((rc = check_cu_dev(cu_seqlens_dev))) return rc;
+  const void* ptrs[3] = {q, k, sel};
+  if ((rc = check_ptrs(ptrs, 3, "q, k and sel must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, false);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_select(P, cu_seqlens_dev, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
 }
 
 static int dense_prob(const moba_problem_t* p, Prob* P) {
@@ -248,11 +375,19 @@ static int dense_prob(const moba_problem_t* p, Prob* P) {
   return make_prob(&d, P);
 }
 
+// Dense workspace: block tables of the one-block problem, then V^T.
+static size_t dense_ws(const Prob& P, Layout* L) {
+  size_t off = 0;
+  take_tables(P, *L, off);
+  L->vt = off;
+  return align_up(off + vt_bytes(P));
+}
+
 size_t moba_dense_workspace_size(const moba_problem_t* p) {
   Prob P;
   if (dense_prob(p, &P) != MOBA_OK) return 0;
-  const size_t t = align_up(vt_bytes(P, P.N));
-  return t > 0 ? t : kAlign;
+  Layout L{};
+  return dense_ws(P, &L);
 }
 
 int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, const void* v,
@@ -262,13 +397,18 @@ int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, con
   if (rc) return rc;
   const void* ptrs[4] = {q, k, v, o};
   if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
-  if ((rc = check_ws(workspace, ws_bytes, align_up(vt_bytes(P, P.N))))) return rc;
+  Layout L{};
+  if ((rc = check_ws(workspace, ws_bytes, dense_ws(P, &L)))) return rc;
   hipStream_t s = (hipStream_t)stream;
+  const Blocks T = tables(workspace, L);
+  hipError_t e = launch_tables(P, nullptr, T, s);
+  if (e != hipSuccess) return hip_fail(e, "block tables");
+  void* vt = at<void>(workspace, L.vt);
   if (P.dtype == MOBA_DTYPE_BF16) {
-    hipError_t e = launch_vt_pack(v, workspace, P.N, P.Hkv, P.N, s);
+    e = launch_vt_pack(P, T, v, vt, s);
     if (e != hipSuccess) return hip_fail(e, "V pack");
   }
-  hipError_t e = launch_attn_self(P, q, k, v, workspace, nullptr, nullptr, o, true, s);
+  e = launch_attn_self(P, T, q, k, v, vt, nullptr, nullptr, o, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "dense causal attention");
 }
 
@@ -294,8 +434,11 @@ int moba_debug_meanpool(const moba_problem_t* p, const void* k, double* kbar, vo
   if ((rc = check_ptrs(ptrs, 2, "k and kbar must be non-NULL"))) return rc;
   const Layout L = plan_ws(P, false);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
-  hipError_t e = launch_meanpool(P, k, kbar, at<double>(workspace, L.mp_part), meanpool_splits(P),
-                                 (hipStream_t)stream);
+  const Blocks T = tables(workspace, L);
+  hipError_t e = launch_tables(P, nullptr, T, (hipStream_t)stream);
+  if (e == hipSuccess)
+    e = launch_meanpool(P, T, k, kbar, at<double>(workspace, L.mp_part), meanpool_splits(P),
+                        (hipStream_t)stream);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "moba_meanpool");
 }
 
@@ -317,7 +460,9 @@ int moba_debug_bucket(const moba_problem_t* p, const int32_t* sel, int32_t* offs
   BucketBufs bb = bucket_bufs(workspace, L);
   bb.bin_off = offsets;
   bb.entries = entries;
-  hipError_t e = launch_bucket(P, plan_bucket(P), sel, bb, (hipStream_t)stream);
+  const Blocks T = tables(workspace, L);
+  hipError_t e = launch_tables(P, nullptr, T, (hipStream_t)stream);
+  if (e == hipSuccess) e = launch_bucket(P, T, plan_bucket(P), sel, bb, (hipStream_t)stream);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "moba_bucket");
 }
 

@@ -18,16 +18,37 @@ constexpr int64_t kMaxHist = 8192;  // history-capable blocks (bucket bitmaps li
 constexpr int kTileQ = 256;         // routed queries per history-attention tile
 constexpr int kMaxGroup = 64;       // Hq / Hkv limit
 
-// Problem with derived sizes; built and validated on the host.
+// Problem with derived sizes; built and validated on the host. The rows are
+// one sequence or several packed ones; blocks are numbered globally, each
+// sequence's blocks consecutively from its first row, and only blocks of a
+// row's own sequence are candidates for it.
 struct Prob {
-  int64_t N;
+  int64_t N;          // rows (all sequences)
   int Hq, Hkv, G, d, B, k;
-  int KH;      // history slots per (row, head) = k - 1
-  int64_t n;   // blocks = ceil(N / B)
-  int64_t nh;  // blocks that can be history = n - 1
+  int KH;             // history slots per (row, head) = k - 1
+  int64_t nseq;       // sequences
+  int64_t n;          // blocks over all sequences (a sequence's last one may be partial)
+  int64_t nh;         // blocks that can be history anywhere = n - 1
+  int64_t hist_rows;  // sum over rows of min(k - 1, blocks before the row's block in its sequence)
   float scale;
-  int dtype;   // MOBA_DTYPE_*
+  int dtype;          // MOBA_DTYPE_*
 };
+
+// Block and row tables in device memory (built by launch_tables):
+//   start[b], len[b]: first row and row count of global block b (len <= B);
+//   lo[b]: first block of b's sequence, so b's rows may select [lo[b], b);
+//   row_blk[r]: global block of row r.
+struct Blocks {
+  int32_t* start;
+  int32_t* len;
+  int32_t* lo;
+  int32_t* row_blk;
+  int32_t* seq_base;  // [nseq + 1] first block of each sequence (scratch of the build)
+};
+
+// Fill the tables; cu = device row offsets [nseq + 1] of packed sequences, or
+// NULL for one sequence of P.N rows.
+hipError_t launch_tables(const Prob& P, const int64_t* cu, const Blocks& t, hipStream_t s);
 
 // Bucketing (per KV head, history block) of the selected (row, head, slot) entries.
 struct BucketPlan {
@@ -52,36 +73,36 @@ struct BucketBufs {
 BucketPlan plan_bucket(const Prob& P);
 
 // Stage launchers (each enqueues on `s`; return hipSuccess or the launch error).
-hipError_t launch_meanpool(const Prob& P, const void* K, double* kbar, double* part, int splits,
-                           hipStream_t s);
+hipError_t launch_meanpool(const Prob& P, const Blocks& T, const void* K, double* kbar,
+                           double* part, int splits, hipStream_t s);
 int meanpool_splits(const Prob& P);
 
 // Gate + selection; `scratch` holds the bf16 split of the block keys and their
 // norms (gate_scratch_bytes).
 size_t gate_scratch_bytes(const Prob& P);
-hipError_t launch_gate_topk(const Prob& P, const void* Q, const double* kbar, void* scratch,
-                            int32_t* sel, hipStream_t s);
+hipError_t launch_gate_topk(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
+                            void* scratch, int32_t* sel, hipStream_t s);
 
-hipError_t launch_bucket(const Prob& P, const BucketPlan& bp, const int32_t* sel,
+hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, const int32_t* sel,
                          const BucketBufs& b, hipStream_t s);
 
 // bf16 kernels read V through a transposed, block-padded, key-permuted copy
 // Vt [Hkv][d][n * Bpad] (see vpack.hip); fp32 kernels read V directly.
 int64_t vt_padded_block(int64_t B);
-hipError_t launch_vt_pack(const void* V, void* Vt, int64_t N, int Hkv, int64_t B, hipStream_t s);
+hipError_t launch_vt_pack(const Prob& P, const Blocks& T, const void* V, void* Vt, hipStream_t s);
 
 // History-block attention over the bucketed entries; writes normalised partials
 // part_o [entry][d] and log2-sum-exp part_lse [entry].
-hipError_t launch_attn_hist(const Prob& P, const BucketPlan& bp, const void* Q, const void* K,
-                            const void* V, const void* Vt, const BucketBufs& b, void* part_o,
-                            float* part_lse, hipStream_t s);
+hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp, const void* Q,
+                            const void* K, const void* V, const void* Vt, const BucketBufs& b,
+                            void* part_o, float* part_lse, hipStream_t s);
 
-// Own-block causal attention fused with the merge of the history partials.
-// With dense=true: one block covering the whole sequence and no partials
-// (causal full attention); Vt must then be packed with B = N.
-hipError_t launch_attn_self(const Prob& P, const void* Q, const void* K, const void* V,
-                            const void* Vt, const void* part_o, const float* part_lse, void* O,
-                            bool dense, hipStream_t s);
+// Own-block causal attention fused with the merge of the history partials
+// (part_o == NULL: no partials, e.g. the dense baseline, whose problem is one
+// block spanning the sequence).
+hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const void* K,
+                            const void* V, const void* Vt, const void* part_o,
+                            const float* part_lse, void* O, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);

@@ -1,10 +1,11 @@
 // V layout change for the bf16 attention kernels: V [N][Hkv][d] -> per KV
 // head, a transposed, block-padded copy Vt[g][d][c * Bpad + pi(r)] holding
-// V[c*B + r][g][d]. Each block is padded to Bpad = ceil(B/64)*64 positions
-// (pads are zero) so 64-key tiles never straddle blocks, and inside every
-// 32-key group the key order is permuted by pi (swap of bits 2 and 3) so
-// that each lane's 8 keys of the P.V matrix-core operand sit in one 16-byte
-// run. One read and one write of V; no arithmetic on the values.
+// V[start(c) + r][g][d] for the rows r < len(c) of block c. Each block is
+// padded to Bpad = ceil(B/64)*64 positions (pads are zero) so 64-key tiles
+// never straddle blocks, and inside every 32-key group the key order is
+// permuted by pi (swap of bits 2 and 3) so that each lane's 8 keys of the
+// P.V matrix-core operand sit in one 16-byte run. One read and one write of
+// V; no arithmetic on the values.
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -20,22 +21,23 @@ __device__ inline int perm32(int r) {  // involution on 0..31 (and on any 32-ali
 
 // grid: (n * (Bpad / 64), Hkv)
 __global__ __launch_bounds__(kThreads) void vt_pack(const uint16_t* __restrict__ V,
-                                                    uint16_t* __restrict__ Vt, int64_t N, int Hkv,
-                                                    int64_t B, int64_t Bpad, int64_t n) {
+                                                    const int32_t* __restrict__ bstart,
+                                                    const int32_t* __restrict__ blen,
+                                                    uint16_t* __restrict__ Vt, int Hkv,
+                                                    int64_t Bpad, int64_t n) {
   __shared__ uint16_t tile[kKeys * kStride];
   const int g = blockIdx.y;
   const int64_t tiles_per_block = Bpad / kKeys;
   const int64_t c = blockIdx.x / tiles_per_block;
   const int64_t t0 = (blockIdx.x % tiles_per_block) * kKeys;  // position offset inside block
-  int64_t rows_c = N - c * B;
-  if (rows_c > B) rows_c = B;
+  const int64_t row0 = bstart[c], rows_c = blen[c];
   // load 64 key rows (zero past the block)
   {
     const int kk = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * 32;
     const int64_t r = t0 + kk;
     uint32_t w[16];
     if (r < rows_c) {
-      const uint4* src = reinterpret_cast<const uint4*>(V + ((c * B + r) * Hkv + g) * kHeadDim + d0);
+      const uint4* src = reinterpret_cast<const uint4*>(V + ((row0 + r) * Hkv + g) * kHeadDim + d0);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         uint4 u = src[i];
@@ -70,11 +72,11 @@ __global__ __launch_bounds__(kThreads) void vt_pack(const uint16_t* __restrict__
 
 }  // namespace
 
-hipError_t launch_vt_pack(const void* V, void* Vt, int64_t N, int Hkv, int64_t B, hipStream_t s) {
-  const int64_t n = ceil_div(N, B);
-  const int64_t Bpad = ceil_div(B, kKeys) * kKeys;
-  dim3 grid((unsigned)(n * (Bpad / kKeys)), (unsigned)Hkv);
-  vt_pack<<<grid, kThreads, 0, s>>>((const uint16_t*)V, (uint16_t*)Vt, N, Hkv, B, Bpad, n);
+hipError_t launch_vt_pack(const Prob& P, const Blocks& T, const void* V, void* Vt, hipStream_t s) {
+  const int64_t Bpad = ceil_div(P.B, kKeys) * kKeys;
+  dim3 grid((unsigned)(P.n * (Bpad / kKeys)), (unsigned)P.Hkv);
+  vt_pack<<<grid, kThreads, 0, s>>>((const uint16_t*)V, T.start, T.len, (uint16_t*)Vt, P.Hkv, Bpad,
+                                    P.n);
   return hipGetLastError();
 }
 

@@ -74,8 +74,11 @@ typedef struct {
 
 /*
  * Size limits of this build (MOBA_ERR_UNSUPPORTED beyond them):
- *   head_dim == 128; topk <= 32; ceil(N/B) - 1 <= 8192 history-capable blocks;
+ *   head_dim == 128; topk <= 32; ceil(N/B) - 1 <= 8192 history-capable blocks
+ *   (for packed sequences: all their blocks together minus one);
  *   N * Hq * topk < 2^31; Hq / Hkv <= 64.
+ * Value range: the bf16 path keeps normalised partial outputs in fp16, so
+ * |V| must stay below 65504.
  */
 
 /* Bytes of device workspace moba_prefill needs for *p; 0 if *p is invalid or unsupported. */
@@ -118,6 +121,36 @@ MOBA_API int moba_prefill_ex(const moba_problem_t *p, const void *q, const void 
  */
 MOBA_API int moba_select(const moba_problem_t *p, const void *q, const void *k, int32_t *sel,
                 void *workspace, size_t ws_bytes, void *stream);
+
+/*
+ * Packed variable-length batches. The N rows of q, k, v and o hold nseq
+ * sequences back to back; sequence i is rows [cu[i], cu[i+1]). Every
+ * sequence is cut into its own blocks from its first row, and a row only
+ * sees blocks of its own sequence: block means, the gate, the top-k and the
+ * attention never cross a sequence boundary (PaperTrace section 5.1: with
+ * packed documents the blocks, their summaries and the gate must share the
+ * document boundaries; section 3.1: variable-length attention kernels). The
+ * result for each sequence is exactly moba_prefill on that sequence alone.
+ *   nseq >= 1; cu_seqlens_host: HOST int64 [nseq + 1] with cu[0] = 0,
+ *     nondecreasing (empty sequences allowed), cu[nseq] = p->seqlen;
+ *   cu_seqlens_dev: the same values in DEVICE memory (8-byte aligned), read
+ *     by the kernels; the caller keeps both copies equal.
+ * The history-capable block limit applies to the blocks of all sequences
+ * together. Selections (moba_select_varlen) hold global block ids: the
+ * sequences' blocks are numbered consecutively in sequence order.
+ */
+MOBA_API size_t moba_varlen_workspace_size(const moba_problem_t *p, int64_t nseq,
+                                           const int64_t *cu_seqlens_host);
+MOBA_API size_t moba_varlen_select_workspace_size(const moba_problem_t *p, int64_t nseq,
+                                                  const int64_t *cu_seqlens_host);
+MOBA_API int moba_prefill_varlen(const moba_problem_t *p, int64_t nseq,
+                                 const int64_t *cu_seqlens_host, const int64_t *cu_seqlens_dev,
+                                 const void *q, const void *k, const void *v, void *o,
+                                 void *workspace, size_t ws_bytes, void *stream);
+MOBA_API int moba_select_varlen(const moba_problem_t *p, int64_t nseq,
+                                const int64_t *cu_seqlens_host, const int64_t *cu_seqlens_dev,
+                                const void *q, const void *k, int32_t *sel, void *workspace,
+                                size_t ws_bytes, void *stream);
 
 /*
  * Dense causal softmax attention on the same tensors (PaperTrace section 1,

@@ -172,3 +172,25 @@ def causal_full(q, k, v, rows, heads, scale=None, nthreads=0):
     if rc:
         raise ValueError(f"moba_ref_causal_full failed ({rc})")
     return o
+
+
+def prefill_varlen(q, k, v, cu, B, topk, scale=None, mode=MODE_UNION, nthreads=0):
+    """Packed sequences: rows [cu[i], cu[i+1]) form sequence i, which is cut
+    into its own blocks from its first row; its block means, gate, top-k and
+    attention see only its own rows (PaperTrace "2.1.3 MoBA", section 5.1:
+    with packed documents the blocks, their summaries and the gate share the
+    document boundaries). Each sequence is therefore evaluated on its own.
+
+    Returns (sel [N, Hq, k] with block indices counted within each sequence,
+    o [N, Hq, d] fp64).
+    """
+    N, Hq, d = q.shape
+    sel = np.full((N, Hq, topk), -1, np.int32)
+    o = np.zeros((N, Hq, d), np.float64)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b > a:
+            s_i, o_i = prefill(q[a:b], k[a:b], v[a:b], B, topk, scale=scale, mode=mode,
+                               nthreads=nthreads)
+            sel[a:b], o[a:b] = s_i, o_i
+    return sel, o

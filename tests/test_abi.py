@@ -122,3 +122,73 @@ def test_copy_rejects_bad_arguments():
     lib = moba.load_library()
     assert lib.moba_debug_copy(None, FAKE, 16, None) == 1
     assert lib.moba_debug_copy(FAKE, FAKE, 15, None) == 1
+
+
+def _cu(*xs):
+    return (ctypes.c_int64 * len(xs))(*xs)
+
+
+VARLEN_BAD = [
+    # (nseq, cu values, seqlen, expected status)
+    (2, (1, 100, 4096), 4096, moba.MOBA_ERR_INVALID_ARGUMENT),    # cu[0] != 0
+    (2, (0, 3000, 2000), 2000, moba.MOBA_ERR_INVALID_ARGUMENT),   # decreasing
+    (2, (0, 100, 4000), 4096, moba.MOBA_ERR_INVALID_ARGUMENT),    # cu[nseq] != seqlen
+    (0, (0,), 4096, moba.MOBA_ERR_INVALID_ARGUMENT),              # no sequence
+    # one long sequence past the history-block limit of the whole batch
+    (2, (0, 1 << 20, (1 << 20) + 64), (1 << 20) + 64, moba.MOBA_ERR_UNSUPPORTED),
+]
+
+
+@pytest.mark.parametrize("nseq,cu,N,code", VARLEN_BAD)
+def test_varlen_rejects_bad_offsets_before_any_hip_call(nseq, cu, N, code):
+    lib = moba.load_library()
+    bs = 64 if code == moba.MOBA_ERR_UNSUPPORTED else 256
+    p = _prob(N=N, block_size=bs)
+    c = _cu(*cu)
+    assert lib.moba_varlen_workspace_size(ctypes.byref(p), nseq, c) == 0
+    assert lib.moba_varlen_select_workspace_size(ctypes.byref(p), nseq, c) == 0
+    st = lib.moba_prefill_varlen(ctypes.byref(p), nseq, c, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 40, None)
+    assert st == code
+    assert lib.moba_select_varlen(ctypes.byref(p), nseq, c, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                  None) == code
+
+
+def test_varlen_null_offsets_and_pointers():
+    lib = moba.load_library()
+    p = _prob(N=1000)
+    c = _cu(0, 300, 300, 1000)
+    ws = lib.moba_varlen_workspace_size(ctypes.byref(p), 3, c)
+    assert ws > 0 and ws % 256 == 0
+    args = [FAKE] * 5  # cu_dev, q, k, v, o
+    assert lib.moba_prefill_varlen(ctypes.byref(p), 3, None, *args, FAKE, ws, None) == 1
+    for i in range(5):
+        for bad in (None, FAKE + 4):
+            a = list(args)
+            a[i] = bad
+            assert lib.moba_prefill_varlen(ctypes.byref(p), 3, c, *a, FAKE, ws, None) == 1
+    assert lib.moba_prefill_varlen(ctypes.byref(p), 3, c, *args, FAKE, ws - 1, None) == 3
+
+
+def test_varlen_one_sequence_sizes_match_plain():
+    """One packed sequence is the plain problem: the same workspace."""
+    lib = moba.load_library()
+    p = _prob(N=5000)
+    c = _cu(0, 5000)
+    assert lib.moba_varlen_workspace_size(ctypes.byref(p), 1, c) == lib.moba_workspace_size(
+        ctypes.byref(p))
+    assert lib.moba_varlen_select_workspace_size(ctypes.byref(p), 1, c) == \
+        lib.moba_select_workspace_size(ctypes.byref(p))
+
+
+def test_varlen_blocks_restart_per_sequence():
+    """Blocks restart at each sequence: two sequences of 300 rows with B=256 have
+    4 blocks (two of them partial), one sequence of 600 rows has 3."""
+    lib = moba.load_library()
+    p1 = _prob(N=600, Hq=1, Hkv=1, block_size=256, topk=3)
+    assert lib.moba_debug_bucket_capacity(ctypes.byref(p1)) == 256 * 1 + 88 * 2
+    a = lib.moba_varlen_workspace_size(ctypes.byref(p1), 2, _cu(0, 300, 600))
+    b = lib.moba_workspace_size(ctypes.byref(p1))
+    assert a > 0 and b > 0 and a != b
+    # empty sequences add no block
+    assert lib.moba_varlen_workspace_size(ctypes.byref(p1), 4, _cu(0, 0, 300, 300, 600)) == a

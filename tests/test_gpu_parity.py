@@ -238,3 +238,63 @@ def test_stage_events_and_copy():
     dst = torch.empty_like(src)
     moba.debug_copy(src, dst)
     assert torch.equal(src, dst)
+
+
+# ---------------------------------------------------------- packed (varlen) ---
+def _seq_base(cu, B):
+    nb = [-(-(int(cu[i + 1]) - int(cu[i])) // B) for i in range(len(cu) - 1)]
+    return np.concatenate([[0], np.cumsum(nb)]).astype(np.int64)
+
+
+VARLEN = [
+    # lengths, Hq, Hkv, B, topk, dtype
+    ([1000, 1, 0, 2500, 333, 4113], 8, 2, 256, 4, "bf16"),
+    ([64, 64, 640, 129, 1, 700], 4, 4, 64, 3, "bf16"),
+    ([5, 17, 3000, 0, 2049], 6, 3, 100, 5, "bf16"),  # B not a multiple of 64
+    ([1000, 1, 0, 2500, 333], 4, 2, 256, 4, "f32"),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,B,topk,dtype", VARLEN)
+def test_varlen_matches_each_sequence_alone(lens, Hq, Hkv, B, topk, dtype):
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N = int(cu[-1])
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + 3 * topk, dtype=dtype)
+    scale = 0.09
+    o = moba.prefill_varlen(tq, tk, tv, cu, B, topk, scale)
+    sel = moba.select_varlen(tq, tk, cu, B, topk).cpu().numpy()
+    o = to_np(o)
+    base = _seq_base(cu, B)
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        s_loc = sel[a:b].reshape(-1, topk).astype(np.int64)
+        s_loc = np.where(s_loc >= 0, s_loc - base[i], -1).astype(np.int32)
+        assert s_loc.min() >= -1 and s_loc.max() < base[i + 1] - base[i]
+        rows, heads = all_rows(b - a, Hq)
+        compare_rows(q[a:b], k[a:b], v[a:b], B, topk, scale, rows, heads, s_loc,
+                     o[a:b].reshape(-1, 128), dtype, f"varlen seq {i} ({b - a} rows)")
+
+
+def test_varlen_one_sequence_is_plain_prefill():
+    q, k, v, tq, tk, tv = small(3000, 8, 2, 256, 4, seed=21)
+    o1 = moba.prefill(tq, tk, tv, 256, 4, 0.09)
+    o2 = moba.prefill_varlen(tq, tk, tv, [0, 3000], 256, 4, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+
+
+def test_varlen_sequences_do_not_leak():
+    """Rewriting one packed sequence leaves every other sequence's output bit-identical."""
+    lens = [700, 1300, 900]
+    cu = np.cumsum([0] + lens)
+    q, k, v, tq, tk, tv = small(int(cu[-1]), 4, 2, 128, 3, seed=31)
+    o1 = moba.prefill_varlen(tq, tk, tv, cu, 128, 3, 0.09).clone()
+    tk2, tv2 = tk.clone(), tv.clone()
+    tk2[700:2000] = -tk2[700:2000]
+    tv2[700:2000] += 1.0
+    o2 = moba.prefill_varlen(tq, tk2, tv2, cu, 128, 3, 0.09)
+    torch.cuda.synchronize()
+    assert torch.equal(o1[:700], o2[:700]) and torch.equal(o1[2000:], o2[2000:])
+    assert not torch.equal(o1[700:2000], o2[700:2000])

@@ -221,6 +221,99 @@ def test_p4_brute_force(case):
     assert np.max(np.abs(o.reshape(-1, d) - bo)) < 1e-12
 
 
+# ------------------------------------------------------------ packed (varlen) ---
+def _brute_packed(q, k, v, cu, B, topk, scale):
+    """Packed rows without slicing: each row's blocks are counted from its own
+    sequence's first row, and only rows of that sequence are candidates."""
+    N, Hq, d = q.shape
+    G = Hq // k.shape[1]
+    sel_all, o_all = [], []
+    for p in range(N):
+        s = max(i for i in range(len(cu) - 1) if cu[i] <= p < cu[i + 1])
+        a = cu[s]
+        c = (p - a) // B
+        for h in range(Hq):
+            g = h // G
+            qf = [Fraction(float(x)) for x in q[p, h]]
+            scores = []
+            for i in range(c):
+                rows_i = range(a + i * B, a + (i + 1) * B)
+                mean = [sum(Fraction(float(k[j, g, t])) for j in rows_i) / B for t in range(d)]
+                scores.append(sum(x * y for x, y in zip(qf, mean)))
+            m = min(topk - 1, c)
+            best, best_sum = None, None
+            for combo in itertools.combinations(range(c), m):
+                ssum = sum((scores[i] for i in combo), Fraction(0))
+                if best is None or ssum > best_sum or (ssum == best_sum and combo < best):
+                    best, best_sum = combo, ssum
+            keys = [j for i in best for j in range(a + i * B, a + (i + 1) * B)]
+            keys += list(range(a + c * B, p + 1))
+            z = [scale * sum(float(q[p, h, t]) * float(k[j, g, t]) for t in range(d)) for j in keys]
+            mx = max(z)
+            w = [math.exp(x - mx) for x in z]
+            den = sum(w)
+            o_all.append([sum(w[i] * float(v[j, g, t]) for i, j in enumerate(keys)) / den
+                          for t in range(d)])
+            sel_all.append(list(best) + [c] + [-1] * (topk - m - 1))
+    return np.array(sel_all), np.array(o_all)
+
+
+@pytest.mark.parametrize("case", range(6))
+def test_packed_brute_force(case):
+    """Packed sequences (with empty and one-row ones) against the unsliced enumeration."""
+    rng = np.random.default_rng(500 + case)
+    B = int(rng.integers(1, 4))
+    lens = [int(x) for x in rng.integers(0, 12, size=int(rng.integers(1, 5)))]
+    lens[0] = max(lens[0], 1)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N = int(cu[-1])
+    topk = int(rng.integers(1, 5))
+    d = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(1, 3))
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=50 + case, integer=case % 2 == 0)
+    scale = float(rng.uniform(0.2, 1.5))
+    sel, o = oracle.prefill_varlen(q, k, v, cu, B, topk, scale=scale)
+    bsel, bo = _brute_packed(q, k, v, [int(x) for x in cu], B, topk, scale)
+    assert np.array_equal(sel.reshape(-1, topk), bsel)
+    assert np.max(np.abs(o.reshape(-1, d) - bo)) < 1e-12
+
+
+def test_packed_short_sequences_are_causal_attention():
+    """Sequences no longer than B are one block each: plain causal attention
+    inside each sequence (the independent causal_full routine on each slice)."""
+    B, topk, d = 16, 3, 8
+    cu = np.array([0, 5, 16, 16, 23, 39], np.int64)
+    N = int(cu[-1])
+    q, k, v = synth.random_qkv(N, 4, 2, d, seed=77)
+    sel, o = oracle.prefill_varlen(q, k, v, cu, B, topk, scale=0.4)
+    assert np.all(sel[:, :, 0] == 0) and np.all(sel[:, :, 1:] == -1)
+    for i in range(len(cu) - 1):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        r, h = oracle.all_rows(b - a, 4)
+        ref = oracle.causal_full(q[a:b], k[a:b], v[a:b], r, h, scale=0.4)
+        assert np.max(np.abs(o[a:b].reshape(-1, d) - ref)) < 1e-12
+
+
+def test_packed_sequences_do_not_leak():
+    """Changing one sequence's tokens leaves every other sequence's output bit-identical."""
+    B, topk, d = 4, 3, 8
+    cu = np.array([0, 13, 30, 41], np.int64)
+    q, k, v = synth.random_qkv(41, 2, 1, d, seed=5)
+    sel, o = oracle.prefill_varlen(q, k, v, cu, B, topk)
+    q2, k2, v2 = q.copy(), k.copy(), v.copy()
+    k2[13:30] *= -3.0
+    v2[13:30] += 1.0
+    q2[13:30] = q2[13:30][::-1]
+    sel2, o2 = oracle.prefill_varlen(q2, k2, v2, cu, B, topk)
+    for a, b in ((0, 13), (30, 41)):
+        assert np.array_equal(sel[a:b], sel2[a:b])
+        assert np.array_equal(o[a:b], o2[a:b])
+    assert not np.array_equal(o[13:30], o2[13:30])
+
+
 # ---------------------------------------------------------------------- P6 ---
 def test_p6_zero_keys_tie_to_lowest_blocks():
     """K == 0: every score and logit ties; the lowest blocks win and O is a plain mean."""
