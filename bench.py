@@ -33,14 +33,16 @@ PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 STAGES = moba.STAGES
 
 
-def pair_counts(w):
-    """Exact attended (query, key) pairs per head: own block causal + full history blocks."""
+def pair_counts(w, lens=None):
+    """Exact attended (query, key) pairs per head: own block causal + full history
+    blocks, summed over the packed sequences ``lens`` (default: one of w.N rows)."""
     KH = w.k - 1
     own = hist = 0
-    for c in range(w.n):
-        rows = min(w.B, w.N - c * w.B)
-        own += rows * (rows + 1) // 2
-        hist += rows * min(KH, c) * w.B
+    for L in (lens if lens is not None else [w.N]):
+        for c in range(-(-int(L) // w.B)):
+            rows = min(w.B, int(L) - c * w.B)
+            own += rows * (rows + 1) // 2
+            hist += rows * min(KH, c) * w.B
     return own, hist
 
 
@@ -111,6 +113,8 @@ def main():
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-varlen", action="store_true",
+                    help="skip the packed-batch leg (16 sequences, same total rows)")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel over this many MiB (hardware-counter "
                          "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
@@ -193,6 +197,29 @@ def main():
                  "speedup_moba_vs_dense": dms / ms_per_step}
         del od
 
+    varlen = None
+    if not args.no_varlen and dtype == "bf16":
+        lens = synth.packed_lengths(w.N, 16, w.seed ^ 0x5EC, max(w.B, w.N // 64), w.N * 3 // 16)
+        cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int64))
+        cu_dev = cu.to(tq.device)
+        del ws  # the packed leg gets its own workspace
+        wsv = moba.alloc_workspace(moba.varlen_workspace_size(prob, cu), tq.device)
+        moba.prefill_varlen(tq, tk, tv, cu_dev, w.B, w.k, w.scale, out=out, workspace=wsv)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(2):
+            moba.prefill_varlen(tq, tk, tv, cu_dev, w.B, w.k, w.scale, out=out, workspace=wsv)
+        e1.record()
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / 2
+        vown, vhist = pair_counts(w, lens)
+        varlen = {"workload": f"{len(lens)} packed sequences of {int(lens.min())}..{int(lens.max())} "
+                              f"rows (seeded log-uniform), {w.N} rows in all, same layer shape",
+                  "ms": vms, "tokens_per_s": w.N / (vms / 1e3),
+                  "attended_tflops": 4.0 * w.d * w.Hq * (vown + vhist) / (vms / 1e3) / 1e12}
+        del wsv
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
@@ -228,6 +255,7 @@ def main():
                      "frac": hist_tflops / PEAK_BF16_TFLOPS,
                      "traffic": read_traffic("attn_hist_c5")},
         "dense_causal": dense,
+        "varlen": varlen,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

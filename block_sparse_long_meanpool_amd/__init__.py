@@ -231,6 +231,13 @@ def _cu_pair(cu_seqlens, device):
     return arr, dev, host.numel() - 1
 
 
+def varlen_workspace_size(prob: MobaProblem, cu_seqlens) -> int:
+    """Workspace bytes of moba_prefill_varlen for sequence offsets ``cu_seqlens`` (0 if invalid)."""
+    host = [int(x) for x in (cu_seqlens.tolist() if hasattr(cu_seqlens, "tolist") else cu_seqlens)]
+    arr = (ctypes.c_int64 * len(host))(*host)
+    return load_library().moba_varlen_workspace_size(ctypes.byref(prob), len(host) - 1, arr)
+
+
 def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, workspace=None):
     """MoBA prefill over packed sequences: rows [cu[i], cu[i+1]) of q, k, v form
     sequence i; blocks restart at each sequence and never cross one. Equals

@@ -207,3 +207,13 @@ def f32_to_bf16(a: np.ndarray) -> np.ndarray:
     u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32).astype(np.uint64)
     lsb = (u >> 16) & 1
     return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
+
+
+def packed_lengths(total: int, nseq: int, seed: int, lo: int, hi: int) -> np.ndarray:
+    """Seeded sequence lengths for a packed batch: log-uniform in [lo, hi],
+    rescaled to sum to ``total`` (the last one absorbs the rounding)."""
+    rng = np.random.default_rng(seed)
+    x = np.exp(rng.uniform(np.log(lo), np.log(hi), size=nseq))
+    lens = np.maximum(1, np.floor(x / x.sum() * total)).astype(np.int64)
+    lens[-1] += total - lens.sum()
+    return lens
