@@ -29,6 +29,8 @@ MOBA_ERR_WORKSPACE_TOO_SMALL = 3
 MOBA_ERR_HIP = 4
 MOBA_DTYPE_BF16 = 0
 MOBA_DTYPE_F32 = 1
+MOBA_ROUTING_PER_HEAD = 0
+MOBA_ROUTING_SHARED = 1
 MOBA_STAGE_EVENTS = 7
 STAGES = ("meanpool", "gate_topk", "bucket", "vpack", "attn_hist", "attn_self_merge")
 
@@ -37,6 +39,7 @@ EXPORTS = (
     "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_prefill_ex",
     "moba_select", "moba_varlen_workspace_size", "moba_varlen_select_workspace_size",
     "moba_prefill_varlen", "moba_select_varlen",
+    "moba_routing_stats_workspace_size", "moba_routing_stats",
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
@@ -53,6 +56,7 @@ class MobaProblem(ctypes.Structure):
         ("topk", ctypes.c_int32),
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
+        ("routing", ctypes.c_int32),
     ]
 
 
@@ -89,6 +93,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_varlen_select_workspace_size": (sz, [P, i64, vp]),
         "moba_prefill_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_routing_stats_workspace_size": (sz, [P]),
+        "moba_routing_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_dense_workspace_size": (sz, [P]),
         "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -114,14 +120,15 @@ def _dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"q/k/v must be bfloat16 or float32, got {t.dtype}")
 
 
-def make_problem(N, Hq, Hkv, d, block_size, topk, scale=None, dtype=MOBA_DTYPE_BF16) -> MobaProblem:
+def make_problem(N, Hq, Hkv, d, block_size, topk, scale=None, dtype=MOBA_DTYPE_BF16,
+                 routing=MOBA_ROUTING_PER_HEAD) -> MobaProblem:
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     return MobaProblem(int(N), int(Hq), int(Hkv), int(d), int(block_size), int(topk),
-                       float(scale), int(dtype))
+                       float(scale), int(dtype), int(routing))
 
 
-def _problem_from(q, k, block_size, topk, scale):
+def _problem_from(q, k, block_size, topk, scale, routing=MOBA_ROUTING_PER_HEAD):
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("q must be [N, Hq, d] and k, v [N, Hkv, d]")
     N, Hq, d = q.shape
@@ -129,7 +136,7 @@ def _problem_from(q, k, block_size, topk, scale):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} vs k {tuple(k.shape)}")
     if k.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
-    return make_problem(N, Hq, k.shape[1], d, block_size, topk, scale, _dtype_code(q))
+    return make_problem(N, Hq, k.shape[1], d, block_size, topk, scale, _dtype_code(q), routing)
 
 
 def _check_dev(*ts):
@@ -161,18 +168,20 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
     return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, events=None):
+def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, events=None,
+            routing=MOBA_ROUTING_PER_HEAD):
     """MoBA prefill: O [N, Hq, d] from q [N, Hq, d], k, v [N, Hkv, d] (bf16 or fp32).
 
     ``scale`` defaults to 1/sqrt(d). ``events`` may be a list of
     ``MOBA_STAGE_EVENTS`` torch.cuda.Event (created with timing) recorded at the
-    stage boundaries on the current stream.
+    stage boundaries on the current stream. ``routing``: MOBA_ROUTING_PER_HEAD
+    or MOBA_ROUTING_SHARED (one selection per KV-head group).
     """
     lib = load_library()
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _problem_from(q, k, block_size, topk, scale)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
     if out is None:
         out = torch.empty_like(q)
     _check_dev(out)
@@ -197,11 +206,11 @@ def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, eve
     return out
 
 
-def select(q, k, block_size, topk, out=None, workspace=None):
+def select(q, k, block_size, topk, out=None, workspace=None, routing=MOBA_ROUTING_PER_HEAD):
     """Selected blocks per (row, head): int32 [N, Hq, topk], ascending, -1 padded."""
     lib = load_library()
     _check_dev(q, k)
-    prob = _problem_from(q, k, block_size, topk, None)
+    prob = _problem_from(q, k, block_size, topk, None, routing)
     N, Hq, _ = q.shape
     if out is None:
         out = torch.empty((N, Hq, topk), dtype=torch.int32, device=q.device)
@@ -238,7 +247,8 @@ def varlen_workspace_size(prob: MobaProblem, cu_seqlens) -> int:
     return load_library().moba_varlen_workspace_size(ctypes.byref(prob), len(host) - 1, arr)
 
 
-def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, workspace=None):
+def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, workspace=None,
+                   routing=MOBA_ROUTING_PER_HEAD):
     """MoBA prefill over packed sequences: rows [cu[i], cu[i+1]) of q, k, v form
     sequence i; blocks restart at each sequence and never cross one. Equals
     ``prefill`` applied to every sequence on its own."""
@@ -246,7 +256,7 @@ def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, 
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _problem_from(q, k, block_size, topk, scale)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
     cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
     if out is None:
         out = torch.empty_like(q)
@@ -285,6 +295,31 @@ def select_varlen(q, k, cu_seqlens, block_size, topk, out=None, workspace=None):
                                 workspace.numel(), _stream(q.device))
     _ok(st, "moba_select_varlen")
     return out
+
+
+def routing_stats(q, k, block_size, topk, routing=MOBA_ROUTING_PER_HEAD):
+    """Routing diagnostics from the exact gate: dict of device tensors
+    ``sel`` int32 [N, Hq, topk], ``margin`` fp32 [N, Hq] (NaN where nothing is
+    left out), ``counts`` int32 [Hkv, n] (history selections per block) and
+    ``union_size`` int32 [N, Hkv] (distinct history blocks per head group)."""
+    lib = load_library()
+    _check_dev(q, k)
+    prob = _problem_from(q, k, block_size, topk, None, routing)
+    N, Hq, _ = q.shape
+    Hkv = k.shape[1]
+    n = -(-N // block_size)
+    dev = q.device
+    sel = torch.empty((N, Hq, topk), dtype=torch.int32, device=dev)
+    margin = torch.empty((N, Hq), dtype=torch.float32, device=dev)
+    counts = torch.empty((Hkv, n), dtype=torch.int32, device=dev)
+    union = torch.empty((N, Hkv), dtype=torch.int32, device=dev)
+    need = lib.moba_routing_stats_workspace_size(ctypes.byref(prob))
+    ws = alloc_workspace(need, dev)
+    st = lib.moba_routing_stats(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), sel.data_ptr(),
+                                margin.data_ptr(), counts.data_ptr(), union.data_ptr(),
+                                ws.data_ptr(), ws.numel(), _stream(dev))
+    _ok(st, "moba_routing_stats")
+    return {"sel": sel, "margin": margin, "counts": counts, "union_size": union}
 
 
 def dense_causal(q, k, v, scale=None, out=None, workspace=None):

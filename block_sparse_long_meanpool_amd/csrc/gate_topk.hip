@@ -217,6 +217,10 @@ template <>
 __device__ inline double widen<float>(float x) {
   return (double)x;
 }
+template <>
+__device__ inline double widen<double>(double x) {
+  return x;
+}
 
 // Exact tier: one wave per 64 consecutive (row, head) pairs; each marked row
 // (or, with all_rows, every row) is re-scored in fp64 — lane b handles blocks
@@ -230,7 +234,8 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
                                                   const double* __restrict__ kbarT,
                                                   const int32_t* __restrict__ row_blk,
                                                   const int32_t* __restrict__ blo,
-                                                  int32_t* __restrict__ sel, int64_t N, int Hq,
+                                                  int32_t* __restrict__ sel,
+                                                  float* __restrict__ margin, int64_t N, int Hq,
                                                   int G, int k, int64_t nhp, int all_rows) {
   __shared__ double qs[kHeadDim];
   const int lane = threadIdx.x;
@@ -247,6 +252,7 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
         mine = all_rows || out[0] == kRefine;
       } else if (all_rows) {  // every earlier block of the sequence is taken
         const int nsel = (int)(c - lo < KH ? c - lo : KH);
+        if (margin) margin[ph] = __builtin_nanf("");  // nothing left out
         for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
         out[nsel] = (int32_t)c;
         for (int a = nsel + 1; a < k; ++a) out[a] = -1;
@@ -292,7 +298,10 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     int chosen[KM];
 #pragma unroll
     for (int t = 0; t < KM; ++t) chosen[t] = 0x7FFFFFFF;
-    for (int rnd = 0; rnd < KH; ++rnd) {
+    double last = 0.0, next = 0.0;
+    // with a margin output, one more round finds the best block left out
+    const int rounds = margin ? KH + 1 : KH;
+    for (int rnd = 0; rnd < rounds; ++rnd) {
       const int hi = ix[0];
       double bv = v[0];
       int bi = hi;
@@ -316,9 +325,12 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
       }
 #pragma unroll
       for (int t = 0; t < KM; ++t)
-        if (t == rnd) chosen[t] = bi;
+        if (t == rnd && rnd < KH) chosen[t] = bi;
+      if (rnd == KH - 1) last = bv;
+      if (rnd == KH) next = bv;
     }
     if (lane == 0) {
+      if (margin) margin[ph] = KH > 0 ? (float)(last - next) : __builtin_nanf("");
       int32_t* out = sel + ph * k;
       write_sorted<KM>(chosen, KH, out);
       out[KH] = (int32_t)c;
@@ -442,16 +454,66 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
 
 }
 
+// Group-shared routing: one selection per (row, KV head) from the summed
+// score of the group's query heads, sum_h q_h . kbar_i = (sum_h q_h) . kbar_i.
+// The group query is summed in fp64 (exact for bf16 and fp32 inputs of
+// ordinary range); Qg [N][Hkv][d].
+template <typename T>
+__global__ void group_sum_q(const T* __restrict__ Q, double* __restrict__ Qg, int64_t N, int Hkv,
+                            int G) {
+  const int64_t total = N * Hkv * kHeadDim;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t c = i % kHeadDim, rg = i / kHeadDim;  // rg = row * Hkv + g
+    const T* src = Q + (rg * G) * kHeadDim + c;         // heads g*G .. g*G+G-1 of the row
+    double acc = 0.0;
+    for (int hh = 0; hh < G; ++hh) acc += widen<T>(src[(int64_t)hh * kHeadDim]);
+    Qg[i] = acc;
+  }
+}
+
+// sel [N][Hq][k] and margin [N][Hq] from the per-(row, KV head) ones.
+__global__ void expand_group(const int32_t* __restrict__ selg, const float* __restrict__ mg,
+                             int32_t* __restrict__ sel, float* __restrict__ margin, int64_t N,
+                             int Hq, int G, int k) {
+  const int64_t total = N * Hq;
+  for (int64_t ph = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; ph < total;
+       ph += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t pg = (ph / Hq) * (Hq / G) + (ph % Hq) / G;
+    for (int a = 0; a < k; ++a) sel[ph * k + a] = selg[pg * k + a];
+    if (margin) margin[ph] = mg[pg];
+  }
+}
+
+unsigned grid_for(int64_t n) {
+  int64_t g = (n + 255) / 256;
+  if (g > 4096) g = 4096;
+  return (unsigned)(g > 0 ? g : 1);
+}
+
+// Exact tier over every row of an N x Hq_eff problem with groups of G_eff.
+template <typename T>
+hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff,
+                      const double* kbarT, int64_t nhp, int32_t* sel, float* margin,
+                      hipStream_t s) {
+  const unsigned grid = (unsigned)ceil_div(P.N * Hq_eff, 64);
+  const int need = P.KH + 1;
+#define MOBA_REFINE(KM)                                                                    \
+  gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.N,   \
+                                         Hq_eff, G_eff, P.k, nhp, 1)
+  if (need <= 4) MOBA_REFINE(4);
+  else if (need <= 8) MOBA_REFINE(8);
+  else if (need <= 12) MOBA_REFINE(12);
+  else if (need <= 16) MOBA_REFINE(16);
+  else MOBA_REFINE(32);
+#undef MOBA_REFINE
+  return hipGetLastError();
+}
+
 template <int KM>
 hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16_t* planes,
                      const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
                      hipStream_t s) {
-  const unsigned refine_grid = (unsigned)ceil_div(P.N * P.Hq, 64);
-  if (P.dtype == MOBA_DTYPE_F32) {
-    gate_refine<float, KM><<<refine_grid, 64, 0, s>>>((const float*)Q, kbarT, T.row_blk, T.lo, sel,
-                                                     P.N, P.Hq, P.G, P.k, nhp, 1);
-    return hipGetLastError();
-  }
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
   dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
   gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.start,
@@ -459,45 +521,112 @@ hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16
                                                 tiles_per_block);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
+  const unsigned refine_grid = (unsigned)ceil_div(P.N * P.Hq, 64);
   gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, T.row_blk, T.lo,
-                                                      sel, P.N, P.Hq, P.G, P.k, nhp, 0);
+                                                      sel, nullptr, P.N, P.Hq, P.G, P.k, nhp, 0);
   return hipGetLastError();
 }
 
 int64_t padded_nh(const Prob& P) { return ceil_div(P.nh > 0 ? P.nh : 1, 64) * 64; }
 
+struct GateScratch {
+  double* kbarT;
+  uint16_t* planes;
+  float* norms;
+  float* maxnorm;
+  double* qg;      // group-shared routing only
+  int32_t* selg;
+  float* marging;
+};
+
+size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+GateScratch carve(const Prob& P, void* scratch) {
+  GateScratch g{};
+  char* base = (char*)scratch;
+  g.kbarT = (double*)base;
+  base += align256(sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P));
+  g.planes = (uint16_t*)base;
+  base += align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2);
+  g.norms = (float*)base;
+  g.maxnorm = g.norms + (size_t)P.Hkv * P.nh;
+  base += align256((size_t)P.Hkv * (P.nh + 1) * 4);
+  if (P.routing == MOBA_ROUTING_SHARED) {
+    g.qg = (double*)base;
+    base += align256(sizeof(double) * (size_t)P.N * P.Hkv * kHeadDim);
+    g.selg = (int32_t*)base;
+    base += align256(sizeof(int32_t) * (size_t)P.N * P.Hkv * P.k);
+    g.marging = (float*)base;
+  }
+  return g;
+}
+
+// All of the gate: block-key split, then (per-head routing) the fast tier and
+// the exact tier for its uncertified rows, or (exact_all, fp32 inputs,
+// group-shared routing) the exact tier for every row; margin (nullable)
+// receives each row's selection margin.
+hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
+                    void* scratch, int32_t* sel, float* margin, bool exact_all, hipStream_t s) {
+  const GateScratch g = carve(P, scratch);
+  const int64_t nhp = padded_nh(P);
+  if (P.nh > 0 && P.KH > 0) {
+    kbar_split<<<(unsigned)(P.Hkv * P.nh), kHeadDim, 0, s>>>(kbar, g.planes, g.norms, g.kbarT,
+                                                            P.nh, nhp);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(g.norms, g.maxnorm, P.nh);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  if (P.routing == MOBA_ROUTING_SHARED) {
+    if (P.dtype == MOBA_DTYPE_BF16)
+      group_sum_q<uint16_t><<<grid_for(P.N * P.Hkv * kHeadDim), 256, 0, s>>>(
+          (const uint16_t*)Q, g.qg, P.N, P.Hkv, P.G);
+    else
+      group_sum_q<float><<<grid_for(P.N * P.Hkv * kHeadDim), 256, 0, s>>>(
+          (const float*)Q, g.qg, P.N, P.Hkv, P.G);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    e = refine_all<double>(P, T, g.qg, P.Hkv, 1, g.kbarT, nhp, g.selg,
+                           margin ? g.marging : nullptr, s);
+    if (e != hipSuccess) return e;
+    expand_group<<<grid_for(P.N * P.Hq), 256, 0, s>>>(g.selg, margin ? g.marging : nullptr, sel,
+                                                      margin, P.N, P.Hq, P.G, P.k);
+    return hipGetLastError();
+  }
+  if (P.dtype == MOBA_DTYPE_F32)
+    return refine_all<float>(P, T, (const float*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
+  if (exact_all)
+    return refine_all<uint16_t>(P, T, (const uint16_t*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
+  // list length: the k-1 kept blocks plus the best one left out
+  const int need = P.KH + 1;
+  if (need <= 4) return launch_km<4>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+  if (need <= 8) return launch_km<8>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+  if (need <= 12) return launch_km<12>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+  if (need <= 16) return launch_km<16>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+  return launch_km<32>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+}
+
 }  // namespace
 
 size_t gate_scratch_bytes(const Prob& P) {
-  return (size_t)P.Hkv * P.nh * (3 * kHeadDim * 2 + 4) + (size_t)P.Hkv * 4 +
-         sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P) + 1024;
+  size_t b = align256(sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P)) +
+             align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2) +
+             align256((size_t)P.Hkv * (P.nh + 1) * 4);
+  if (P.routing == MOBA_ROUTING_SHARED)
+    b += align256(sizeof(double) * (size_t)P.N * P.Hkv * kHeadDim) +
+         align256(sizeof(int32_t) * (size_t)P.N * P.Hkv * P.k) +
+         align256(sizeof(float) * (size_t)P.N * P.Hkv);
+  return b + 1024;
 }
 
 hipError_t launch_gate_topk(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
                             void* scratch, int32_t* sel, hipStream_t s) {
-  char* base = (char*)scratch;
-  double* kbarT = (double*)base;  // first: keeps 8-byte alignment
-  base += sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P);
-  uint16_t* planes = (uint16_t*)base;
-  base += (size_t)P.Hkv * P.nh * 3 * kHeadDim * 2;
-  float* norms = (float*)base;
-  float* maxnorm = norms + (size_t)P.Hkv * P.nh;
-  const int64_t nhp = padded_nh(P);
-  if (P.nh > 0 && P.KH > 0) {
-    kbar_split<<<(unsigned)(P.Hkv * P.nh), kHeadDim, 0, s>>>(kbar, planes, norms, kbarT, P.nh,
-                                                            nhp);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(norms, maxnorm, P.nh);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
-  }
-  // list length: the k-1 kept blocks plus the best one left out
-  const int need = P.KH + 1;
-  if (need <= 4) return launch_km<4>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 8) return launch_km<8>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 12) return launch_km<12>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
-  if (need <= 16) return launch_km<16>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
-  return launch_km<32>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s);
+  return run_gate(P, T, Q, kbar, scratch, sel, nullptr, false, s);
+}
+
+hipError_t launch_gate_margin(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
+                              void* scratch, int32_t* sel, float* margin, hipStream_t s) {
+  return run_gate(P, T, Q, kbar, scratch, sel, margin, true, s);
 }
 
 }  // namespace moba

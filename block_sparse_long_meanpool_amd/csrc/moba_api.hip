@@ -42,6 +42,8 @@ int make_prob(const moba_problem_t* p, Prob* P) {
     return fail(MOBA_ERR_INVALID_ARGUMENT, "scale must be finite and > 0");
   if (p->dtype != MOBA_DTYPE_BF16 && p->dtype != MOBA_DTYPE_F32)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "dtype must be MOBA_DTYPE_BF16 or MOBA_DTYPE_F32");
+  if (p->routing != MOBA_ROUTING_PER_HEAD && p->routing != MOBA_ROUTING_SHARED)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "routing must be MOBA_ROUTING_PER_HEAD or _SHARED");
   if (p->head_dim != kHeadDim) return fail(MOBA_ERR_UNSUPPORTED, "only head_dim == 128 is built");
   if (p->topk > kMaxTopk) return fail(MOBA_ERR_UNSUPPORTED, "topk > 32 is not supported");
   const int G = p->num_q_heads / p->num_kv_heads;
@@ -58,6 +60,7 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   P->KH = p->topk - 1;
   P->scale = p->scale;
   P->dtype = p->dtype;
+  P->routing = p->routing;
   // one sequence of all rows; make_prob_varlen overrides the sequence layout
   P->nseq = 1;
   P->n = (P->N + P->B - 1) / P->B;
@@ -322,6 +325,47 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
   const Layout L = plan_ws(P, false);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
   return run_select(P, nullptr, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
+}
+
+// Routing statistics: the select workspace, then room for a selection.
+static size_t stats_ws(const Prob& P, const Layout& L, size_t* sel_off) {
+  *sel_off = L.total;
+  return align_up(L.total + sizeof(int32_t) * (size_t)(P.N * P.Hq * P.k));
+}
+
+size_t moba_routing_stats_workspace_size(const moba_problem_t* p) {
+  Prob P;
+  if (make_prob(p, &P) != MOBA_OK) return 0;
+  size_t off;
+  return stats_ws(P, plan_ws(P, false), &off);
+}
+
+int moba_routing_stats(const moba_problem_t* p, const void* q, const void* k, int32_t* sel,
+                       float* margin, int32_t* counts, int32_t* union_size, void* workspace,
+                       size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  const void* ptrs[2] = {q, k};
+  if ((rc = check_ptrs(ptrs, 2, "q and k must be non-NULL"))) return rc;
+  const void* outs[4] = {sel, margin, counts, union_size};
+  for (const void* o : outs)
+    if (o && !aligned(o, 4)) return fail(MOBA_ERR_INVALID_ARGUMENT, "outputs must be 4-byte aligned");
+  const Layout L = plan_ws(P, false);
+  size_t sel_off;
+  if ((rc = check_ws(workspace, ws_bytes, stats_ws(P, L, &sel_off)))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* selw = sel ? sel : at<int32_t>(workspace, sel_off);
+  const Blocks T = tables(workspace, L);
+  hipError_t e = launch_tables(P, nullptr, T, s);
+  if (e == hipSuccess)
+    e = launch_meanpool(P, T, k, at<double>(workspace, L.kbar), at<double>(workspace, L.mp_part),
+                        meanpool_splits(P), s);
+  if (e == hipSuccess)
+    e = launch_gate_margin(P, T, q, at<double>(workspace, L.kbar), at<void>(workspace, L.gate),
+                           selw, margin, s);
+  if (e == hipSuccess) e = launch_routing_reductions(P, T, selw, counts, union_size, s);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e, "routing statistics");
 }
 
 size_t moba_varlen_workspace_size(const moba_problem_t* p, int64_t nseq,

@@ -32,6 +32,7 @@ struct Prob {
   int64_t hist_rows;  // sum over rows of min(k - 1, blocks before the row's block in its sequence)
   float scale;
   int dtype;          // MOBA_DTYPE_*
+  int routing;        // MOBA_ROUTING_*
 };
 
 // Block and row tables in device memory (built by launch_tables):
@@ -82,6 +83,15 @@ int meanpool_splits(const Prob& P);
 size_t gate_scratch_bytes(const Prob& P);
 hipError_t launch_gate_topk(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
                             void* scratch, int32_t* sel, hipStream_t s);
+// The exact tier for every row, also writing each row's selection margin
+// (last kept minus best left-out history score; NaN when nothing is left out).
+hipError_t launch_gate_margin(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
+                              void* scratch, int32_t* sel, float* margin, hipStream_t s);
+// Per-(KV head, block) history selection counts [Hkv][n] and per-(row, KV
+// head) sizes of the union of the group's history selections [N][Hkv]
+// (either output may be NULL).
+hipError_t launch_routing_reductions(const Prob& P, const Blocks& T, const int32_t* sel,
+                                     int32_t* counts, int32_t* union_size, hipStream_t s);
 
 hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, const int32_t* sel,
                          const BucketBufs& b, hipStream_t s);

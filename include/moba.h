@@ -61,6 +61,21 @@ extern "C" {
 /* Element type of Q, K, V and O. */
 typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_F32 = 1 } moba_dtype_t;
 
+/*
+ * Block routing under grouped-query attention (PaperTrace section 5.4 asks
+ * that the choice be stated: each query head routes on its own, or a head
+ * group shares one routing).
+ *   MOBA_ROUTING_PER_HEAD: every query head ranks the blocks with its own
+ *     query against its KV head's block keys (the default).
+ *   MOBA_ROUTING_SHARED: the Hq/Hkv query heads of a KV head share one
+ *     selection, ranked by the group's summed gate score
+ *     sum_h q_h . kbar_i = (sum_h q_h) . kbar_i (same ties rule); attention
+ *     still uses each head's own query. The group query is summed in fp64
+ *     (exact unless the group's values differ in magnitude by more than
+ *     2^45), and the ranking uses the exact fp64 tier for every row.
+ */
+typedef enum { MOBA_ROUTING_PER_HEAD = 0, MOBA_ROUTING_SHARED = 1 } moba_routing_t;
+
 typedef struct {
   int64_t seqlen;       /* N >= 1 */
   int32_t num_q_heads;  /* Hq >= 1 */
@@ -70,6 +85,7 @@ typedef struct {
   int32_t topk;         /* k >= 1, counting the own block; k >= ceil(N/B) = causal full attention */
   float scale;          /* finite and > 0; multiplies attention logits only (the gate is unscaled) */
   int32_t dtype;        /* moba_dtype_t of Q, K, V and O */
+  int32_t routing;      /* moba_routing_t; 0 = per head */
 } moba_problem_t;
 
 /*
@@ -151,6 +167,28 @@ MOBA_API int moba_select_varlen(const moba_problem_t *p, int64_t nseq,
                                 const int64_t *cu_seqlens_host, const int64_t *cu_seqlens_dev,
                                 const void *q, const void *k, int32_t *sel, void *workspace,
                                 size_t ws_bytes, void *stream);
+
+/*
+ * Routing diagnostics (PaperTrace section 5.4: log the gap between the
+ * k-th and (k+1)-th block scores, candidate overlap and per-block selection
+ * frequency). Runs the block means and the exact (fp64) gate for every row
+ * under p->routing, then fills whichever outputs are non-NULL (DEVICE):
+ *   sel        int32 [N][Hq][topk]: the selection, as moba_select;
+ *   margin     fp32 [N][Hq]: last kept minus best left-out history score
+ *              (gate scores, unscaled), NaN where no history block is left
+ *              out (topk == 1 or fewer earlier blocks than topk);
+ *   counts     int32 [Hkv][ceil(N/B)]: how many (row, query head) pairs of
+ *              each KV head selected each block as history;
+ *   union_size int32 [N][Hkv]: distinct history blocks selected by the query
+ *              heads of each KV head at each row (topk-1 under shared
+ *              routing once enough blocks precede the row).
+ * Workspace: moba_routing_stats_workspace_size(p) bytes.
+ */
+MOBA_API size_t moba_routing_stats_workspace_size(const moba_problem_t *p);
+MOBA_API int moba_routing_stats(const moba_problem_t *p, const void *q, const void *k,
+                                int32_t *sel, float *margin, int32_t *counts,
+                                int32_t *union_size, void *workspace, size_t ws_bytes,
+                                void *stream);
 
 /*
  * Dense causal softmax attention on the same tensors (PaperTrace section 1,

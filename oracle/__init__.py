@@ -25,6 +25,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libmoba_ref.so")
 
 MODE_UNION, MODE_TWO_BRANCH, MODE_NAIVE = 0, 1, 2
+ROUTING_PER_HEAD, ROUTING_SHARED = 0, 1
 
 
 class _Problem(ctypes.Structure):
@@ -37,6 +38,7 @@ class _Problem(ctypes.Structure):
         ("k", ctypes.c_int32),
         ("scale", ctypes.c_double),
         ("dtype", ctypes.c_int32),
+        ("routing", ctypes.c_int32),
     ]
 
 
@@ -80,12 +82,12 @@ def _dtype_code(a: np.ndarray) -> int:
     raise TypeError(f"oracle inputs must be uint16 (bf16 bits) or float32, got {a.dtype}")
 
 
-def _problem(q, k, B, topk, scale):
+def _problem(q, k, B, topk, scale, routing=ROUTING_PER_HEAD):
     N, Hq, d = q.shape
     Hkv = k.shape[1]
     if scale is None:
         scale = 1.0 / np.sqrt(d)
-    return _Problem(N, Hq, Hkv, d, B, topk, float(scale), _dtype_code(q))
+    return _Problem(N, Hq, Hkv, d, B, topk, float(scale), _dtype_code(q), int(routing))
 
 
 def _c(a, dt=None):
@@ -107,8 +109,12 @@ def block_means(k: np.ndarray, B: int) -> np.ndarray:
 
 
 def rows(q, k, v, B, topk, rows, heads, scale=None, forced_sel=None, mode=MODE_UNION,
-         want_o=True, kbar=None, nthreads=0):
+         want_o=True, kbar=None, nthreads=0, routing=ROUTING_PER_HEAD):
     """Evaluate the method on (row, head) pairs.
+
+    ``routing``: ROUTING_PER_HEAD ranks blocks with each head's own query;
+    ROUTING_SHARED ranks them once per KV-head group by the group's summed
+    gate score (PaperTrace "2.1.3 MoBA", section 5.4 on GQA routing).
 
     Returns ``(sel, o, gap)``: ``sel`` int32 [R, k] ascending and -1 padded;
     ``o`` fp64 [R, d] (None when ``want_o`` is False); ``gap`` fp64 [R, 2] with the
@@ -120,7 +126,7 @@ def rows(q, k, v, B, topk, rows, heads, scale=None, forced_sel=None, mode=MODE_U
         raise TypeError("q and k must share a dtype")
     if v is not None:
         v = _c(v)
-    pr = _problem(q, k, B, topk, scale)
+    pr = _problem(q, k, B, topk, scale, routing)
     rws = _c(np.asarray(rows), np.int64)
     hds = _c(np.asarray(heads), np.int32)
     R = rws.shape[0]
@@ -151,11 +157,12 @@ def all_rows(N, Hq):
     return r, h
 
 
-def prefill(q, k, v, B, topk, scale=None, mode=MODE_UNION, nthreads=0):
+def prefill(q, k, v, B, topk, scale=None, mode=MODE_UNION, nthreads=0, routing=ROUTING_PER_HEAD):
     """Full layer: (sel [N, Hq, k], o [N, Hq, d] fp64)."""
     N, Hq, d = q.shape
     r, h = all_rows(N, Hq)
-    sel, o, _ = rows(q, k, v, B, topk, r, h, scale=scale, mode=mode, nthreads=nthreads)
+    sel, o, _ = rows(q, k, v, B, topk, r, h, scale=scale, mode=mode, nthreads=nthreads,
+                     routing=routing)
     return sel.reshape(N, Hq, topk), o.reshape(N, Hq, d)
 
 

@@ -51,6 +51,10 @@ typedef struct {
   int32_t k;     /* top-k, counting the query's own block */
   double scale;  /* multiplies the attention logits (not the gate) */
   int32_t dtype; /* REF_BF16 or REF_F32 */
+  int32_t routing; /* 0: each query head ranks blocks with its own query;
+                      1: the query heads of a KV head share one ranking by the
+                         group's summed gate score, sum_h q_h . kbar_i
+                         (PaperTrace "2.1.3 MoBA", section 5.4 on GQA) */
 } moba_ref_problem;
 
 static inline double ld(const void *base, int dtype, int64_t i) {
@@ -70,6 +74,7 @@ static int check(const moba_ref_problem *p) {
   if (p->Hq % p->Hkv) return 1;
   if (!(p->scale > 0.0) || !isfinite(p->scale)) return 1;
   if (p->dtype != REF_BF16 && p->dtype != REF_F32) return 1;
+  if (p->routing != 0 && p->routing != 1) return 1;
   return 0;
 }
 
@@ -187,7 +192,9 @@ int moba_ref_rows(const moba_ref_problem *p, const void *Q, const void *K, const
     double *ua = (double *)malloc(sizeof(double) * (size_t)d);
     double *ub = (double *)malloc(sizeof(double) * (size_t)d);
     double *qd = (double *)malloc(sizeof(double) * (size_t)d);
-    if (!s || !picked || !hist || !in_union || !in_own || !in_hist || !z || !ua || !ub || !qd) {
+    double *qg = (double *)malloc(sizeof(double) * (size_t)d);
+    if (!s || !picked || !hist || !in_union || !in_own || !in_hist || !z || !ua || !ub || !qd ||
+        !qg) {
 #pragma omp atomic write
       err = 2;
     } else {
@@ -198,12 +205,23 @@ int moba_ref_rows(const moba_ref_problem *p, const void *Q, const void *K, const
         const int64_t c = row / B; /* the query's own block */
         const int64_t qb = (row * p->Hq + h) * d;
         for (int64_t t = 0; t < d; ++t) qd[t] = ld(Q, p->dtype, qb + t);
+        /* the gate's query: this head's, or the sum over the head group */
+        for (int64_t t = 0; t < d; ++t) {
+          if (p->routing == 1) {
+            double acc = 0.0;
+            for (int hh = 0; hh < G; ++hh)
+              acc += ld(Q, p->dtype, (row * p->Hq + (int64_t)g * G + hh) * d + t);
+            qg[t] = acc;
+          } else {
+            qg[t] = qd[t];
+          }
+        }
 
         /* Gate scores over legal history blocks 0..c-1 (eq. (3)). */
         for (int64_t i = 0; i < c; ++i) {
           double dot = 0.0;
           const double *kb = kbar + ((int64_t)g * nh + i) * d;
-          for (int64_t t = 0; t < d; ++t) dot += qd[t] * kb[t];
+          for (int64_t t = 0; t < d; ++t) dot += qg[t] * kb[t];
           s[i] = dot;
         }
         /* Selection: up to k-1 history blocks; the own block is forced. */
@@ -283,6 +301,7 @@ int moba_ref_rows(const moba_ref_problem *p, const void *Q, const void *K, const
     free(ua);
     free(ub);
     free(qd);
+    free(qg);
   }
   free(own_kbar);
   return err;

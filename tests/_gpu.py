@@ -50,17 +50,18 @@ def check_output(got_o, ref_o, dtype, what=""):
     return float(err.max()), float(err.mean())
 
 
-def compare_rows(q, k, v, B, topk, scale, rows, heads, got_sel, got_o, dtype, what=""):
+def compare_rows(q, k, v, B, topk, scale, rows, heads, got_sel, got_o, dtype, what="",
+                 routing=oracle.ROUTING_PER_HEAD):
     """Oracle on (rows, heads); selection bit-exact up to ties, O within tolerance.
 
     Rows whose selection differs on a tie are re-evaluated by the oracle with
     the GPU's selection forced, and O is checked against that.
     """
-    ref_sel, ref_o, gap = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale)
+    ref_sel, ref_o, gap = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale, routing=routing)
     tied = check_selection(got_sel, ref_sel, gap, what)
     if tied.size:
         _, forced_o, _ = oracle.rows(q, k, v, B, topk, rows[tied], heads[tied], scale=scale,
-                                     forced_sel=got_sel[tied])
+                                     forced_sel=got_sel[tied], routing=routing)
         ref_o = ref_o.copy()
         ref_o[tied] = forced_o
     return check_output(got_o, ref_o, dtype, what), tied.size

@@ -298,3 +298,80 @@ def test_varlen_sequences_do_not_leak():
     torch.cuda.synchronize()
     assert torch.equal(o1[:700], o2[:700]) and torch.equal(o1[2000:], o2[2000:])
     assert not torch.equal(o1[700:2000], o2[700:2000])
+
+
+# ------------------------------------------------ GQA shared routing, stats ---
+SHARED = [
+    # N, Hq, Hkv, B, topk, dtype
+    (3000, 8, 2, 128, 4, "bf16"),
+    (2048, 12, 3, 96, 5, "bf16"),
+    (1500, 4, 1, 64, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk,dtype", SHARED)
+def test_shared_routing_matches_oracle(N, Hq, Hkv, B, topk, dtype):
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + Hq, dtype=dtype)
+    shared = moba.MOBA_ROUTING_SHARED
+    o = moba.prefill(tq, tk, tv, B, topk, 0.09, routing=shared)
+    sel = moba.select(tq, tk, B, topk, routing=shared).cpu().numpy()
+    G = Hq // Hkv
+    for g in range(Hkv):
+        assert np.all(sel[:, g * G:(g + 1) * G] == sel[:, g * G:g * G + 1])
+    rows, heads = all_rows(N, Hq)
+    compare_rows(q, k, v, B, topk, 0.09, rows, heads, sel.reshape(-1, topk),
+                 to_np(o).reshape(-1, 128), dtype, f"shared {N},{Hq},{Hkv},{B},{topk}",
+                 routing=oracle.ROUTING_SHARED)
+
+
+def test_varlen_with_shared_routing():
+    lens = [900, 0, 1, 1700, 420]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, Hq, Hkv, B, topk = int(cu[-1]), 8, 2, 128, 4
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=91)
+    o = to_np(moba.prefill_varlen(tq, tk, tv, cu, B, topk, 0.09,
+                                  routing=moba.MOBA_ROUTING_SHARED))
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        if b == a:
+            continue
+        ref_sel, ref_o = oracle.prefill(q[a:b], k[a:b], v[a:b], B, topk, scale=0.09,
+                                        routing=oracle.ROUTING_SHARED)
+        check_output(o[a:b].reshape(-1, 128), ref_o.reshape(-1, 128), "bf16", f"seq {i}")
+
+
+@pytest.mark.parametrize("routing", [0, 1])
+def test_routing_stats(routing):
+    N, Hq, Hkv, B, topk = 2500, 8, 2, 100, 4
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=17)
+    st = moba.routing_stats(tq, tk, B, topk, routing=routing)
+    sel = st["sel"].cpu().numpy()
+    margin = st["margin"].cpu().numpy().astype(np.float64)
+    counts = st["counts"].cpu().numpy()
+    union = st["union_size"].cpu().numpy()
+    rows, heads = all_rows(N, Hq)
+    ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False, routing=routing)
+    check_selection(sel.reshape(-1, topk), ref_sel, gap, "stats sel")
+    m, g = margin.reshape(-1), gap[:, 0]
+    assert np.array_equal(np.isnan(m), np.isnan(g))
+    ok = ~np.isnan(g)
+    assert np.all(np.abs(m[ok] - g[ok]) <= 1e-6 * np.maximum(gap[ok, 1], 1e-30) + 1e-30)
+    # counts and group unions from the selection itself
+    n = -(-N // B)
+    G = Hq // Hkv
+    c_rows = np.arange(N) // B
+    ref_counts = np.zeros((Hkv, n), np.int64)
+    ref_union = np.zeros((N, Hkv), np.int64)
+    for r in range(N):
+        for g_ in range(Hkv):
+            seen = set()
+            for hh in range(G):
+                for b in sel[r, g_ * G + hh, : topk - 1]:
+                    if 0 <= b < c_rows[r]:
+                        ref_counts[g_, b] += 1
+                        seen.add(int(b))
+            ref_union[r, g_] = len(seen)
+    assert np.array_equal(counts, ref_counts)
+    assert np.array_equal(union, ref_union)
+    if routing == 1:
+        assert np.all(union <= topk - 1)

@@ -168,8 +168,9 @@ def test_p5_block_covers_sequence_is_causal_full():
 
 
 # ---------------------------------------------------------------------- P4 ---
-def _brute(q, k, v, B, topk, scale):
-    """Exact enumeration: every candidate set, Fractions for the gate, loops for attention."""
+def _brute(q, k, v, B, topk, scale, shared=False):
+    """Exact enumeration: every candidate set, Fractions for the gate, loops for attention.
+    shared: the gate query is the sum of the head group's queries."""
     N, Hq, d = q.shape
     G = Hq // k.shape[1]
     sel_all, o_all = [], []
@@ -177,7 +178,10 @@ def _brute(q, k, v, B, topk, scale):
         for h in range(Hq):
             g = h // G
             c = p // B
-            qf = [Fraction(float(x)) for x in q[p, h]]
+            if shared:
+                qf = [sum(Fraction(float(q[p, g * G + hh, t])) for hh in range(G)) for t in range(d)]
+            else:
+                qf = [Fraction(float(x)) for x in q[p, h]]
             scores = []
             for i in range(c):
                 mean = [sum(Fraction(float(k[j, g, t])) for j in range(i * B, (i + 1) * B)) / B
@@ -219,6 +223,41 @@ def test_p4_brute_force(case):
     bsel, bo = _brute(q, k, v, B, topk, scale)
     assert np.array_equal(sel.reshape(-1, topk), bsel)
     assert np.max(np.abs(o.reshape(-1, d) - bo)) < 1e-12
+
+
+# ------------------------------------------------------- GQA shared routing ---
+@pytest.mark.parametrize("case", range(6))
+def test_shared_routing_brute_force(case):
+    """One ranking per head group by the summed gate score (enumerated exactly)."""
+    rng = np.random.default_rng(700 + case)
+    B = int(rng.integers(1, 4))
+    N = int(rng.integers(4, 25))
+    topk = int(rng.integers(2, 5))
+    d = int(rng.integers(1, 4))
+    Hkv = int(rng.integers(1, 3))
+    Hq = Hkv * int(rng.integers(2, 4))
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=70 + case, integer=case % 2 == 0)
+    scale = float(rng.uniform(0.2, 1.5))
+    sel, o = oracle.prefill(q, k, v, B, topk, scale=scale, routing=oracle.ROUTING_SHARED)
+    bsel, bo = _brute(q, k, v, B, topk, scale, shared=True)
+    assert np.array_equal(sel.reshape(-1, topk), bsel)
+    assert np.max(np.abs(o.reshape(-1, d) - bo)) < 1e-12
+    G = Hq // Hkv
+    for g in range(Hkv):  # every head of a group holds the same selection
+        assert np.all(sel[:, g * G:(g + 1) * G] == sel[:, g * G:g * G + 1])
+
+
+def test_shared_routing_reduces_to_per_head():
+    """Groups of one head, or groups whose heads share one query, rank as per head."""
+    q, k, v = synth.random_qkv(96, 3, 3, 16, seed=4)
+    a = oracle.prefill(q, k, v, 8, 4)
+    b = oracle.prefill(q, k, v, 8, 4, routing=oracle.ROUTING_SHARED)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+    q1, k1, v1 = synth.random_qkv(96, 4, 1, 16, seed=6)
+    q1[:] = q1[:, :1]  # the four heads of the group carry the same query
+    a = oracle.prefill(q1, k1, v1, 8, 4)
+    b = oracle.prefill(q1, k1, v1, 8, 4, routing=oracle.ROUTING_SHARED)
+    assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
 
 
 # ------------------------------------------------------------ packed (varlen) ---
