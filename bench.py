@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-batch leg (16 sequences, same total rows)")
+    ap.add_argument("--no-shared", action="store_true",
+                    help="skip the group-shared routing leg and the routing-statistics timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel over this many MiB (hardware-counter "
                          "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
@@ -220,6 +222,28 @@ def main():
                   "attended_tflops": 4.0 * w.d * w.Hq * (vown + vhist) / (vms / 1e3) / 1e12}
         del wsv
 
+    shared = None
+    if not args.no_shared and dtype == "bf16":
+        moba.prefill(tq, tk, tv, w.B, w.k, w.scale, out=out, routing=moba.MOBA_ROUTING_SHARED)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        moba.prefill(tq, tk, tv, w.B, w.k, w.scale, out=out, routing=moba.MOBA_ROUTING_SHARED)
+        e1.record()
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1)
+        e0.record()
+        st = moba.routing_stats(tq, tk, w.B, w.k, routing=moba.MOBA_ROUTING_PER_HEAD)
+        e1.record()
+        torch.cuda.synchronize()
+        stats_ms = e0.elapsed_time(e1)
+        margin = st["margin"].float()
+        fin = margin[torch.isfinite(margin)]
+        shared = {"ms": sms, "tokens_per_s": w.N / (sms / 1e3),
+                  "routing_stats_ms": stats_ms,
+                  "median_selection_margin": float(fin.median()) if fin.numel() else None}
+        del st
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
@@ -256,6 +280,7 @@ def main():
                      "traffic": read_traffic("attn_hist_c5")},
         "dense_causal": dense,
         "varlen": varlen,
+        "shared_routing": shared,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
