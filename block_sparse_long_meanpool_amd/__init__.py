@@ -40,6 +40,7 @@ EXPORTS = (
     "moba_select", "moba_varlen_workspace_size", "moba_varlen_select_workspace_size",
     "moba_prefill_varlen", "moba_select_varlen",
     "moba_routing_stats_workspace_size", "moba_routing_stats",
+    "moba_chunk_workspace_size", "moba_prefill_chunk", "moba_select_chunk",
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
@@ -93,6 +94,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_varlen_select_workspace_size": (sz, [P, i64, vp]),
         "moba_prefill_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_chunk_workspace_size": (sz, [P, i64]),
+        "moba_prefill_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_select_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, sz, vp]),
         "moba_routing_stats_workspace_size": (sz, [P]),
         "moba_routing_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_dense_workspace_size": (sz, [P]),
@@ -294,6 +298,61 @@ def select_varlen(q, k, cu_seqlens, block_size, topk, out=None, workspace=None):
                                 q.data_ptr(), k.data_ptr(), out.data_ptr(), workspace.data_ptr(),
                                 workspace.numel(), _stream(q.device))
     _ok(st, "moba_select_varlen")
+    return out
+
+
+def _chunk_problem(q, k, block_size, topk, scale, routing):
+    if q.dim() != 3 or k.dim() != 3 or q.shape[2] != k.shape[2]:
+        raise ValueError("q must be [C, Hq, d] and k, v [N, Hkv, d]")
+    if k.dtype != q.dtype:
+        raise TypeError("q, k and v must share a dtype")
+    N, Hkv, d = k.shape
+    return make_problem(N, q.shape[1], Hkv, d, block_size, topk, scale, _dtype_code(q), routing)
+
+
+def prefill_chunk(q, k, v, block_size, topk, scale=None, out=None, workspace=None,
+                  routing=MOBA_ROUTING_PER_HEAD):
+    """Chunked prefill / decode: q [C, Hq, d] are the queries of the last C
+    positions of a sequence whose keys and values k, v [N, Hkv, d] include
+    them. Returns O [C, Hq, d], equal to those rows of ``prefill`` over the
+    whole sequence (C = 1 is one decode step)."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    prob = _chunk_problem(q, k, block_size, topk, scale, routing)
+    C = q.shape[0]
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev(out)
+    need = lib.moba_chunk_workspace_size(ctypes.byref(prob), C)
+    if need == 0:
+        _ok(lib.moba_prefill_chunk(ctypes.byref(prob), C, None, None, None, None, None, 0, None),
+            "moba_chunk_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib.moba_prefill_chunk(ctypes.byref(prob), C, q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                _stream(q.device))
+    _ok(st, "moba_prefill_chunk")
+    return out
+
+
+def select_chunk(q, k, block_size, topk, routing=MOBA_ROUTING_PER_HEAD):
+    """Selections of the last C positions (q [C, Hq, d]): int32 [C, Hq, topk]."""
+    lib = load_library()
+    _check_dev(q, k)
+    prob = _chunk_problem(q, k, block_size, topk, None, routing)
+    C, Hq, _ = q.shape
+    out = torch.empty((C, Hq, topk), dtype=torch.int32, device=q.device)
+    need = lib.moba_chunk_workspace_size(ctypes.byref(prob), C)
+    if need == 0:
+        _ok(lib.moba_select_chunk(ctypes.byref(prob), C, None, None, None, None, 0, None),
+            "moba_chunk_workspace_size")
+    ws = alloc_workspace(need, q.device)
+    st = lib.moba_select_chunk(ctypes.byref(prob), C, q.data_ptr(), k.data_ptr(), out.data_ptr(),
+                               ws.data_ptr(), ws.numel(), _stream(q.device))
+    _ok(st, "moba_select_chunk")
     return out
 
 

@@ -496,7 +496,8 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
 // ----------------------------------------------------------------------------
 __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K, const uint16_t* __restrict__ Vt,
-    const int32_t* __restrict__ bstart, const int32_t* __restrict__ blen,
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ qstart,
+    const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const _Float16* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ O, int Hq, int Hkv, int G,
     int64_t Bpad, int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
@@ -513,12 +514,14 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   const int tile = tiles_per_block - 1 - (int)(w % tiles_per_block);
   const int g = (int)((w / tiles_per_block) % Hkv);
   const int64_t c = n - 1 - w / ((int64_t)tiles_per_block * Hkv);
-  const int64_t row0 = bstart[c], rows_c = blen[c];
-  const int64_t npairs = rows_c * G;
+  // keys from the block's first row; query rows (of Q and O) and their
+  // positions (for the causal mask) from the block's query range
+  const int64_t key0 = bstart[c], qrow0 = qstart[c], pos0 = qpos[c];
+  const int64_t npairs = (int64_t)qlen[c] * G;
   const int64_t p0 = (int64_t)tile * kGroupQ;
   if (p0 >= npairs) return;
   const int64_t plast = (p0 + kGroupQ - 1 < npairs) ? p0 + kGroupQ - 1 : npairs - 1;
-  const int64_t last_row = row0 + plast / G;
+  const int64_t last_row = pos0 + plast / G;
 
   bool valid[QB];
   int64_t my_row[QB], ph[QB];
@@ -527,8 +530,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   for (int qb = 0; qb < QB; ++qb) {
     const int64_t pi = p0 + wave * kWaveQ + qb * 32 + (lane & 31);
     valid[qb] = pi < npairs;
-    my_row[qb] = valid[qb] ? row0 + pi / G : -1;
-    ph[qb] = valid[qb] ? my_row[qb] * Hq + g * G + (int)(pi % G) : 0;
+    my_row[qb] = valid[qb] ? pos0 + pi / G : -1;
+    ph[qb] = valid[qb] ? (qrow0 + pi / G) * Hq + g * G + (int)(pi % G) : 0;
     qrow[qb] = Q + ph[qb] * kHeadDim;
   }
   Wave W;
@@ -537,25 +540,25 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   const int64_t wp0 = p0 + wave * kWaveQ;
   const bool wave_live = wp0 < npairs;
   const int64_t wp1 = (wp0 + kWaveQ - 1 < npairs) ? wp0 + kWaveQ - 1 : npairs - 1;
-  const int64_t wrow_min = row0 + wp0 / G;
-  const int64_t wrow_max = row0 + wp1 / G;
+  const int64_t wrow_min = pos0 + wp0 / G;
+  const int64_t wrow_max = pos0 + wp1 / G;
 
-  const int64_t nkeys = last_row - row0 + 1;
+  const int64_t nkeys = last_row - key0 + 1;
   const int ntiles = (int)((nkeys + KT - 1) / KT);
   const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + c * Bpad;
   float mstart[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mstart[qb] = 0.f;
   wave_reset(W, mstart);
-  run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+  run_block<true, false, false>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
                                 my_row, wrow_min, wrow_max, wave_live, sl2e, true);
   if (__syncthreads_or(wave_needs_redo(W, valid))) {
     wave_reset(W, mstart);
-    run_block<true, false, true>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+    run_block<true, false, true>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
                                  my_row, wrow_min, wrow_max, wave_live, sl2e, false);
     wave_true_max(W, sl2e, mstart);
     wave_reset(W, mstart);
-    run_block<true, false, false>(W, tA, tB, tC, K, row0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
+    run_block<true, false, false>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
                                   my_row, wrow_min, wrow_max, wave_live, sl2e, false);
   }
   const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
@@ -608,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const int j = pass * 4 + q4;
     const int64_t pi = p0 + wave * kWaveQ + j;
     const int64_t pic = pi < npairs ? pi : npairs - 1;  // clamped: loads stay in bounds
-    const int64_t phj = (row0 + pic / G) * Hq + g * G + (int)(pic % G);
+    const int64_t phj = (qrow0 + pic / G) * Hq + g * G + (int)(pic % G);
     const h8 own = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * c16);
     const float own_lse = stage_lse[j];
     const float* ls = part_lse + phj * KH;
@@ -656,8 +659,8 @@ hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, 
   const int64_t grid = ceil_div(P.n * tiles_per_block * P.Hkv, 8) * 8;
   const bool merge = part_o != nullptr && P.KH > 0;
   attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
-      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.len, T.lo,
-      merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr, (uint16_t*)O, P.Hq,
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.qstart, T.qlen,
+      T.qpos, T.lo, merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr, (uint16_t*)O, P.Hq,
       P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, tiles_per_block, sl2e);
   return hipGetLastError();
 }

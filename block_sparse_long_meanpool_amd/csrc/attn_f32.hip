@@ -136,7 +136,8 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
 
 __global__ __launch_bounds__(kThreads) void attn_self_f32(
     const float* __restrict__ Q, const float* __restrict__ K, const float* __restrict__ V,
-    const int32_t* __restrict__ bstart, const int32_t* __restrict__ blen,
+    const int32_t* __restrict__ bstart, const int32_t* __restrict__ qstart,
+    const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, float* __restrict__ O, int Hq, int Hkv, int G, int KH,
     int64_t n, int tiles_per_block, float sl2e) {
@@ -145,21 +146,22 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
   const int g = blockIdx.y;
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = tiles_per_block - 1 - (int)(blockIdx.x % tiles_per_block);
-  const int64_t row0 = bstart[c], rows_c = blen[c];
-  const int64_t npairs = rows_c * G;
+  // keys from the block's first row; query rows and their positions from its query range
+  const int64_t key0 = bstart[c], qrow0 = qstart[c], pos0 = qpos[c];
+  const int64_t npairs = (int64_t)qlen[c] * G;
   const int64_t p0 = (int64_t)tile * kQ;
   if (p0 >= npairs) return;
   const int64_t plast = (p0 + kQ - 1 < npairs) ? p0 + kQ - 1 : npairs - 1;
-  const int64_t last_row = row0 + plast / G;
+  const int64_t last_row = pos0 + plast / G;
   const int qi = threadIdx.x / kSub, sub = threadIdx.x % kSub;
   const int64_t my_pi = p0 + qi;
   const bool valid = my_pi < npairs;
-  const int64_t my_row = valid ? row0 + my_pi / G : -1;
+  const int64_t my_row = valid ? pos0 + my_pi / G : -1;
   const int my_h = valid ? g * G + (int)(my_pi % G) : 0;
-  const int64_t ph = valid ? my_row * Hq + my_h : 0;
+  const int64_t ph = valid ? (qrow0 + my_pi / G) * Hq + my_h : 0;
   QState S;
   init_state(S, Q + ph * kHeadDim, valid, sub);
-  for (int64_t k0 = row0; k0 <= last_row; k0 += KT) {
+  for (int64_t k0 = key0; k0 <= last_row; k0 += KT) {
     const int64_t rem = last_row + 1 - k0;
     const int nv = rem < KT ? (int)rem : KT;
     __syncthreads();
@@ -217,7 +219,7 @@ hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kQ);
   dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
   attn_self_f32<<<grid, kThreads, 0, s>>>(
-      (const float*)Q, (const float*)K, (const float*)V, T.start, T.len, T.lo,
+      (const float*)Q, (const float*)K, (const float*)V, T.start, T.qstart, T.qlen, T.qpos, T.lo,
       merge ? (const float*)part_o : nullptr, merge ? part_lse : nullptr, (float*)O, P.Hq, P.Hkv,
       P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e);
   return hipGetLastError();

@@ -198,7 +198,7 @@ BucketPlan plan_bucket(const Prob& P) {
   if (rpc < 1) rpc = 1;
   bp.rows_per_chunk = (int)rpc;
   bp.words = (int)ceil_div(rpc * P.G, 32);
-  bp.nchunk = ceil_div(P.N, rpc);
+  bp.nchunk = ceil_div(P.Nq, rpc);
   bp.nbins = (int64_t)P.Hkv * P.nh;
   bp.max_entries = P.hist_rows * P.Hq;
   bp.max_tiles = ceil_div(bp.max_entries, kTileQ) + bp.nbins;
@@ -216,7 +216,7 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
   }
   dim3 grid((unsigned)bp.nchunk, (unsigned)P.Hkv);
   bucket_count<<<grid, kThreads, sizeof(int32_t) * P.nh, s>>>(
-      sel, T.row_blk, b.chunk_base, P.N, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
+      sel, T.row_blk, b.chunk_base, P.Nq, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bucket_scan_cols<<<(unsigned)ceil_div(bp.nbins, 16), kThreads, 0, s>>>(b.chunk_base, b.bin_total,
@@ -226,7 +226,7 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bucket_scatter<<<grid, kThreads, sizeof(uint32_t) * P.nh * bp.words, s>>>(
-      sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.N, P.Hq, P.G, P.k, P.nh,
+      sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.G, P.k, P.nh,
       bp.rows_per_chunk, bp.nchunk, bp.words);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (b.tile_map) {

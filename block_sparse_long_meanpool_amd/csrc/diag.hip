@@ -63,18 +63,18 @@ hipError_t launch_routing_reductions(const Prob& P, const Blocks& T, const int32
     e = launch_fill_i32(counts, 0, (size_t)(P.Hkv * P.n), s);
     if (e != hipSuccess) return e;
     if (P.k > 1) {
-      history_counts<<<grid_for(P.N * P.Hq), 256, 0, s>>>(sel, T.row_blk, counts, P.N, P.Hq, P.G,
+      history_counts<<<grid_for(P.Nq * P.Hq), 256, 0, s>>>(sel, T.row_blk, counts, P.Nq, P.Hq, P.G,
                                                           P.k, P.n);
       e = hipGetLastError();
     }
   }
   if (e == hipSuccess && union_size) {
     if (P.k > 1) {
-      group_union<<<grid_for(P.N * P.Hkv), 256, 0, s>>>(sel, T.row_blk, union_size, P.N, P.Hq,
+      group_union<<<grid_for(P.Nq * P.Hkv), 256, 0, s>>>(sel, T.row_blk, union_size, P.Nq, P.Hq,
                                                         P.G, P.k);
       e = hipGetLastError();
     } else {
-      e = launch_fill_i32(union_size, 0, (size_t)(P.N * P.Hkv), s);
+      e = launch_fill_i32(union_size, 0, (size_t)(P.Nq * P.Hkv), s);
     }
   }
   return e;

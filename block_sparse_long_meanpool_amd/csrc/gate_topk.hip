@@ -343,8 +343,8 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
 template <int KM>
 __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
-    const float* __restrict__ maxnorm, const int32_t* __restrict__ bstart,
-    const int32_t* __restrict__ blen, const int32_t* __restrict__ blo, int32_t* __restrict__ sel,
+    const float* __restrict__ maxnorm, const int32_t* __restrict__ qstart,
+    const int32_t* __restrict__ qlen, const int32_t* __restrict__ blo, int32_t* __restrict__ sel,
     int Hq, int G, int k, int64_t n, int64_t nh, int tiles_per_block) {
   __shared__ __align__(16) uint16_t bufA[kChunkElems];
   __shared__ __align__(16) uint16_t bufB[kChunkElems];
@@ -352,7 +352,7 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   const int g = blockIdx.y;
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = blockIdx.x % tiles_per_block;
-  const int64_t row0 = bstart[c], rows_c = blen[c];
+  const int64_t row0 = qstart[c], rows_c = qlen[c];  // query rows of block c
   const int64_t lo = blo[c];  // candidates: blocks [lo, c) of the row's sequence
   const int64_t nc = c - lo;
   const int64_t npairs_c = rows_c * G;
@@ -496,10 +496,10 @@ template <typename T>
 hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff,
                       const double* kbarT, int64_t nhp, int32_t* sel, float* margin,
                       hipStream_t s) {
-  const unsigned grid = (unsigned)ceil_div(P.N * Hq_eff, 64);
+  const unsigned grid = (unsigned)ceil_div(P.Nq * Hq_eff, 64);
   const int need = P.KH + 1;
 #define MOBA_REFINE(KM)                                                                    \
-  gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.N,   \
+  gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.Nq,  \
                                          Hq_eff, G_eff, P.k, nhp, 1)
   if (need <= 4) MOBA_REFINE(4);
   else if (need <= 8) MOBA_REFINE(8);
@@ -516,14 +516,14 @@ hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16
                      hipStream_t s) {
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
   dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
-  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.start,
-                                                T.len, T.lo, sel, P.Hq, P.G, P.k, P.n, P.nh,
+  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.qstart,
+                                                T.qlen, T.lo, sel, P.Hq, P.G, P.k, P.n, P.nh,
                                                 tiles_per_block);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
-  const unsigned refine_grid = (unsigned)ceil_div(P.N * P.Hq, 64);
+  const unsigned refine_grid = (unsigned)ceil_div(P.Nq * P.Hq, 64);
   gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, T.row_blk, T.lo,
-                                                      sel, nullptr, P.N, P.Hq, P.G, P.k, nhp, 0);
+                                                      sel, nullptr, P.Nq, P.Hq, P.G, P.k, nhp, 0);
   return hipGetLastError();
 }
 
@@ -553,9 +553,9 @@ GateScratch carve(const Prob& P, void* scratch) {
   base += align256((size_t)P.Hkv * (P.nh + 1) * 4);
   if (P.routing == MOBA_ROUTING_SHARED) {
     g.qg = (double*)base;
-    base += align256(sizeof(double) * (size_t)P.N * P.Hkv * kHeadDim);
+    base += align256(sizeof(double) * (size_t)P.Nq * P.Hkv * kHeadDim);
     g.selg = (int32_t*)base;
-    base += align256(sizeof(int32_t) * (size_t)P.N * P.Hkv * P.k);
+    base += align256(sizeof(int32_t) * (size_t)P.Nq * P.Hkv * P.k);
     g.marging = (float*)base;
   }
   return g;
@@ -579,18 +579,18 @@ hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double*
   }
   if (P.routing == MOBA_ROUTING_SHARED) {
     if (P.dtype == MOBA_DTYPE_BF16)
-      group_sum_q<uint16_t><<<grid_for(P.N * P.Hkv * kHeadDim), 256, 0, s>>>(
-          (const uint16_t*)Q, g.qg, P.N, P.Hkv, P.G);
+      group_sum_q<uint16_t><<<grid_for(P.Nq * P.Hkv * kHeadDim), 256, 0, s>>>(
+          (const uint16_t*)Q, g.qg, P.Nq, P.Hkv, P.G);
     else
-      group_sum_q<float><<<grid_for(P.N * P.Hkv * kHeadDim), 256, 0, s>>>(
-          (const float*)Q, g.qg, P.N, P.Hkv, P.G);
+      group_sum_q<float><<<grid_for(P.Nq * P.Hkv * kHeadDim), 256, 0, s>>>(
+          (const float*)Q, g.qg, P.Nq, P.Hkv, P.G);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     e = refine_all<double>(P, T, g.qg, P.Hkv, 1, g.kbarT, nhp, g.selg,
                            margin ? g.marging : nullptr, s);
     if (e != hipSuccess) return e;
-    expand_group<<<grid_for(P.N * P.Hq), 256, 0, s>>>(g.selg, margin ? g.marging : nullptr, sel,
-                                                      margin, P.N, P.Hq, P.G, P.k);
+    expand_group<<<grid_for(P.Nq * P.Hq), 256, 0, s>>>(g.selg, margin ? g.marging : nullptr, sel,
+                                                       margin, P.Nq, P.Hq, P.G, P.k);
     return hipGetLastError();
   }
   if (P.dtype == MOBA_DTYPE_F32)
@@ -613,9 +613,9 @@ size_t gate_scratch_bytes(const Prob& P) {
              align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2) +
              align256((size_t)P.Hkv * (P.nh + 1) * 4);
   if (P.routing == MOBA_ROUTING_SHARED)
-    b += align256(sizeof(double) * (size_t)P.N * P.Hkv * kHeadDim) +
-         align256(sizeof(int32_t) * (size_t)P.N * P.Hkv * P.k) +
-         align256(sizeof(float) * (size_t)P.N * P.Hkv);
+    b += align256(sizeof(double) * (size_t)P.Nq * P.Hkv * kHeadDim) +
+         align256(sizeof(int32_t) * (size_t)P.Nq * P.Hkv * P.k) +
+         align256(sizeof(float) * (size_t)P.Nq * P.Hkv);
   return b + 1024;
 }
 

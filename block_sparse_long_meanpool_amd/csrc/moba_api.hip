@@ -51,6 +51,8 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   if ((double)p->seqlen * p->num_q_heads * p->topk >= 2147483648.0)
     return fail(MOBA_ERR_UNSUPPORTED, "seqlen * num_q_heads * topk must be < 2^31");
   P->N = p->seqlen;
+  P->Nq = p->seqlen;
+  P->q0 = 0;
   P->Hq = p->num_q_heads;
   P->Hkv = p->num_kv_heads;
   P->G = G;
@@ -71,6 +73,24 @@ int make_prob(const moba_problem_t* p, Prob* P) {
     P->hist_rows += rows * (c < P->KH ? c : P->KH);
   }
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
+  return MOBA_OK;
+}
+
+// Chunk of the last q_rows positions of one sequence of p->seqlen rows: the
+// queries are rows [seqlen - q_rows, seqlen), the keys all seqlen rows.
+int make_prob_chunk(const moba_problem_t* p, int64_t q_rows, Prob* P) {
+  int rc = make_prob(p, P);
+  if (rc) return rc;
+  if (q_rows < 1 || q_rows > P->N)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "q_rows must be in [1, seqlen]");
+  P->Nq = q_rows;
+  P->q0 = P->N - q_rows;
+  P->hist_rows = 0;
+  for (int64_t c = P->q0 / P->B; c < P->n; ++c) {
+    const int64_t a = c * P->B > P->q0 ? c * P->B : P->q0;
+    const int64_t e = (c + 1) * P->B < P->N ? (c + 1) * P->B : P->N;
+    P->hist_rows += (e - a) * (c < P->KH ? c : P->KH);
+  }
   return MOBA_OK;
 }
 
@@ -108,7 +128,7 @@ int make_prob_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu, P
 size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 
 struct Layout {
-  size_t blk_start, blk_len, blk_lo, row_blk, seq_base;
+  size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
       part_lse, part_o, vt, total;
 };
@@ -129,7 +149,10 @@ void take_tables(const Prob& P, Layout& L, size_t& off) {
   L.blk_start = take(sizeof(int32_t) * (size_t)P.n);
   L.blk_len = take(sizeof(int32_t) * (size_t)P.n);
   L.blk_lo = take(sizeof(int32_t) * (size_t)P.n);
-  L.row_blk = take(sizeof(int32_t) * (size_t)P.N);
+  L.qstart = take(sizeof(int32_t) * (size_t)P.n);
+  L.qlen = take(sizeof(int32_t) * (size_t)P.n);
+  L.qpos = take(sizeof(int32_t) * (size_t)P.n);
+  L.row_blk = take(sizeof(int32_t) * (size_t)P.Nq);
   L.seq_base = take(sizeof(int32_t) * (size_t)(P.nseq + 1));
 }
 
@@ -149,7 +172,7 @@ Layout plan_ws(const Prob& P, bool full) {
   L.gate = take(gate_scratch_bytes(P));
   if (full) {
     const BucketPlan bp = plan_bucket(P);
-    L.sel = take(sizeof(int32_t) * (size_t)(P.N * P.Hq * P.k));
+    L.sel = take(sizeof(int32_t) * (size_t)(P.Nq * P.Hq * P.k));
     L.chunk_base = take(sizeof(int32_t) * (size_t)(P.Hkv * bp.nchunk * P.nh));
     L.bin_total = take(sizeof(int32_t) * (size_t)(bp.nbins + 1));
     L.bin_off = take(sizeof(int32_t) * (size_t)(bp.nbins + 1));
@@ -157,7 +180,7 @@ Layout plan_ws(const Prob& P, bool full) {
     L.scalars = take(sizeof(int32_t) * 4);
     L.tile_map = take(sizeof(int32_t) * (size_t)bp.max_tiles);
     L.entries = take(sizeof(uint32_t) * (size_t)bp.max_entries);
-    const size_t slots = (size_t)(P.N * P.Hq) * (size_t)P.KH;
+    const size_t slots = (size_t)(P.Nq * P.Hq) * (size_t)P.KH;
     L.part_lse = take(sizeof(float) * slots);
     L.part_o = take(part_elem_bytes(P) * slots * P.d);
     L.vt = take(vt_bytes(P));
@@ -195,6 +218,9 @@ Blocks tables(void* ws, const Layout& L) {
   t.start = at<int32_t>(ws, L.blk_start);
   t.len = at<int32_t>(ws, L.blk_len);
   t.lo = at<int32_t>(ws, L.blk_lo);
+  t.qstart = at<int32_t>(ws, L.qstart);
+  t.qlen = at<int32_t>(ws, L.qlen);
+  t.qpos = at<int32_t>(ws, L.qpos);
   t.row_blk = at<int32_t>(ws, L.row_blk);
   t.seq_base = at<int32_t>(ws, L.seq_base);
   return t;
@@ -330,7 +356,7 @@ int moba_select(const moba_problem_t* p, const void* q, const void* k, int32_t* 
 // Routing statistics: the select workspace, then room for a selection.
 static size_t stats_ws(const Prob& P, const Layout& L, size_t* sel_off) {
   *sel_off = L.total;
-  return align_up(L.total + sizeof(int32_t) * (size_t)(P.N * P.Hq * P.k));
+  return align_up(L.total + sizeof(int32_t) * (size_t)(P.Nq * P.Hq * P.k));
 }
 
 size_t moba_routing_stats_workspace_size(const moba_problem_t* p) {
@@ -366,6 +392,36 @@ int moba_routing_stats(const moba_problem_t* p, const void* q, const void* k, in
                            selw, margin, s);
   if (e == hipSuccess) e = launch_routing_reductions(P, T, selw, counts, union_size, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "routing statistics");
+}
+
+size_t moba_chunk_workspace_size(const moba_problem_t* p, int64_t q_rows) {
+  Prob P;
+  if (make_prob_chunk(p, q_rows, &P) != MOBA_OK) return 0;
+  return plan_ws(P, true).total;
+}
+
+int moba_prefill_chunk(const moba_problem_t* p, int64_t q_rows, const void* q, const void* k,
+                       const void* v, void* o, void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_chunk(p, q_rows, &P);
+  if (rc) return rc;
+  const void* ptrs[4] = {q, k, v, o};
+  if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, true);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_prefill(P, nullptr, q, k, v, o, workspace, L, (hipStream_t)stream, nullptr);
+}
+
+int moba_select_chunk(const moba_problem_t* p, int64_t q_rows, const void* q, const void* k,
+                      int32_t* sel, void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_chunk(p, q_rows, &P);
+  if (rc) return rc;
+  const void* ptrs[3] = {q, k, sel};
+  if ((rc = check_ptrs(ptrs, 3, "q, k and sel must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, false);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_select(P, nullptr, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
 }
 
 size_t moba_varlen_workspace_size(const moba_problem_t* p, int64_t nseq,

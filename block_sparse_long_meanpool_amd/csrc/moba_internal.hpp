@@ -23,26 +23,34 @@ constexpr int kMaxGroup = 64;       // Hq / Hkv limit
 // sequence's blocks consecutively from its first row, and only blocks of a
 // row's own sequence are candidates for it.
 struct Prob {
-  int64_t N;          // rows (all sequences)
+  int64_t N;          // key rows (all sequences)
+  int64_t Nq;         // query rows: the last Nq positions of the sequence (= N unless a chunk)
+  int64_t q0;         // position of query row 0 (= N - Nq)
   int Hq, Hkv, G, d, B, k;
   int KH;             // history slots per (row, head) = k - 1
   int64_t nseq;       // sequences
   int64_t n;          // blocks over all sequences (a sequence's last one may be partial)
   int64_t nh;         // blocks that can be history anywhere = n - 1
-  int64_t hist_rows;  // sum over rows of min(k - 1, blocks before the row's block in its sequence)
+  int64_t hist_rows;  // sum over query rows of min(k - 1, earlier blocks of the row's sequence)
   float scale;
   int dtype;          // MOBA_DTYPE_*
   int routing;        // MOBA_ROUTING_*
 };
 
 // Block and row tables in device memory (built by launch_tables):
-//   start[b], len[b]: first row and row count of global block b (len <= B);
+//   start[b], len[b]: first key row and key count of global block b (len <= B);
 //   lo[b]: first block of b's sequence, so b's rows may select [lo[b], b);
-//   row_blk[r]: global block of row r.
+//   qstart[b], qlen[b], qpos[b]: first query row, query row count and the
+//     position of that first query row inside block b (qlen may be 0);
+//   row_blk[r]: global block of query row r.
+// For a full prefill query rows are key rows: qstart = qpos = start, qlen = len.
 struct Blocks {
   int32_t* start;
   int32_t* len;
   int32_t* lo;
+  int32_t* qstart;
+  int32_t* qlen;
+  int32_t* qpos;
   int32_t* row_blk;
   int32_t* seq_base;  // [nseq + 1] first block of each sequence (scratch of the build)
 };

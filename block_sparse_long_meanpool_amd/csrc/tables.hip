@@ -57,28 +57,38 @@ __device__ inline int64_t last_le(F key, int64_t nseq, int64_t x) {
   return lo;
 }
 
+// Query rows are positions [q0, q0 + Nq) (all rows for a full prefill).
 __global__ void block_rows(const int64_t* __restrict__ cu, const int32_t* __restrict__ seq_base,
-                           int64_t nseq, int64_t N, int B, int64_t nblk,
+                           int64_t nseq, int64_t N, int B, int64_t nblk, int64_t q0, int64_t Nq,
                            int32_t* __restrict__ start, int32_t* __restrict__ len,
-                           int32_t* __restrict__ lo) {
+                           int32_t* __restrict__ lo, int32_t* __restrict__ qstart,
+                           int32_t* __restrict__ qlen, int32_t* __restrict__ qpos) {
   for (int64_t b = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; b < nblk;
        b += (int64_t)gridDim.x * blockDim.x) {
     // empty sequences share their base with the next one: the last match owns b
     const int64_t s = last_le([&](int64_t i) { return (int64_t)seq_base[i]; }, nseq, b);
     const int64_t r0 = cu_at(cu, s, N) + (b - seq_base[s]) * (int64_t)B;
     const int64_t r1 = cu_at(cu, s + 1, N);
+    const int64_t re = r1 < r0 + B ? r1 : r0 + B;  // end of the block's rows
     start[b] = (int32_t)r0;
-    len[b] = (int32_t)(r1 - r0 < B ? r1 - r0 : B);
+    len[b] = (int32_t)(re - r0);
     lo[b] = seq_base[s];
+    const int64_t a = r0 > q0 ? r0 : q0;  // first query position in the block
+    const int64_t e = re < q0 + Nq ? re : q0 + Nq;
+    qpos[b] = (int32_t)a;
+    qstart[b] = (int32_t)(a - q0);
+    qlen[b] = (int32_t)(e > a ? e - a : 0);
   }
 }
 
 __global__ void row_blocks(const int64_t* __restrict__ cu, const int32_t* __restrict__ seq_base,
-                           int64_t nseq, int64_t N, int B, int32_t* __restrict__ row_blk) {
-  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < N;
+                           int64_t nseq, int64_t N, int B, int64_t q0, int64_t Nq,
+                           int32_t* __restrict__ row_blk) {
+  for (int64_t r = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; r < Nq;
        r += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t s = last_le([&](int64_t i) { return cu_at(cu, i, N); }, nseq, r);
-    row_blk[r] = (int32_t)(seq_base[s] + (r - cu_at(cu, s, N)) / B);
+    const int64_t pos = q0 + r;
+    const int64_t s = last_le([&](int64_t i) { return cu_at(cu, i, N); }, nseq, pos);
+    row_blk[r] = (int32_t)(seq_base[s] + (pos - cu_at(cu, s, N)) / B);
   }
 }
 
@@ -94,10 +104,11 @@ hipError_t launch_tables(const Prob& P, const int64_t* cu, const Blocks& t, hipS
   seq_block_base<<<1, 1024, 0, s>>>(cu, P.nseq, P.N, P.B, t.seq_base);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  block_rows<<<grid_for(P.n), 256, 0, s>>>(cu, t.seq_base, P.nseq, P.N, P.B, P.n, t.start, t.len,
-                                          t.lo);
+  block_rows<<<grid_for(P.n), 256, 0, s>>>(cu, t.seq_base, P.nseq, P.N, P.B, P.n, P.q0, P.Nq,
+                                          t.start, t.len, t.lo, t.qstart, t.qlen, t.qpos);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  row_blocks<<<grid_for(P.N), 256, 0, s>>>(cu, t.seq_base, P.nseq, P.N, P.B, t.row_blk);
+  row_blocks<<<grid_for(P.Nq), 256, 0, s>>>(cu, t.seq_base, P.nseq, P.N, P.B, P.q0, P.Nq,
+                                           t.row_blk);
   return hipGetLastError();
 }
 

@@ -169,6 +169,28 @@ MOBA_API int moba_select_varlen(const moba_problem_t *p, int64_t nseq,
                                 size_t ws_bytes, void *stream);
 
 /*
+ * Chunked prefill and decode: the queries are the last q_rows positions of
+ * one sequence whose keys and values (all p->seqlen rows, the new ones
+ * included) are already in k and v — a KV cache. q and o hold only those
+ * q_rows rows: [q_rows][Hq][d]. Every output row equals the row at the same
+ * position of moba_prefill over the whole sequence: a row never depends on
+ * later rows, so a long prefill can be split into chunks, and q_rows = 1 is
+ * one decode step (PaperTrace section 3.1 contrasts prefill and decode;
+ * section 5.1 notes that generation needs block means kept up to date).
+ * Block means are recomputed from k on every call (no cache of them).
+ *   1 <= q_rows <= seqlen; the selection (moba_select_chunk) is
+ *   [q_rows][Hq][topk]. The workspace of moba_chunk_workspace_size serves
+ *   both calls.
+ */
+MOBA_API size_t moba_chunk_workspace_size(const moba_problem_t *p, int64_t q_rows);
+MOBA_API int moba_prefill_chunk(const moba_problem_t *p, int64_t q_rows, const void *q,
+                                const void *k, const void *v, void *o, void *workspace,
+                                size_t ws_bytes, void *stream);
+MOBA_API int moba_select_chunk(const moba_problem_t *p, int64_t q_rows, const void *q,
+                               const void *k, int32_t *sel, void *workspace, size_t ws_bytes,
+                               void *stream);
+
+/*
  * Routing diagnostics (PaperTrace section 5.4: log the gap between the
  * k-th and (k+1)-th block scores, candidate overlap and per-block selection
  * frequency). Runs the block means and the exact (fp64) gate for every row

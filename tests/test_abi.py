@@ -192,3 +192,18 @@ def test_varlen_blocks_restart_per_sequence():
     assert a > 0 and b > 0 and a != b
     # empty sequences add no block
     assert lib.moba_varlen_workspace_size(ctypes.byref(p1), 4, _cu(0, 0, 300, 300, 600)) == a
+
+
+def test_chunk_rejects_bad_row_counts():
+    lib = moba.load_library()
+    p = _prob(N=1000)
+    for bad in (0, -1, 1001):
+        assert lib.moba_chunk_workspace_size(ctypes.byref(p), bad) == 0
+        assert lib.moba_prefill_chunk(ctypes.byref(p), bad, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                      None) == 1
+    ws = lib.moba_chunk_workspace_size(ctypes.byref(p), 1000)
+    assert ws == lib.moba_workspace_size(ctypes.byref(p))  # all rows: the plain problem
+    small = lib.moba_chunk_workspace_size(ctypes.byref(p), 1)
+    assert 0 < small < ws
+    assert lib.moba_prefill_chunk(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, FAKE, small - 1,
+                                  None) == 3

@@ -375,3 +375,45 @@ def test_routing_stats(routing):
     assert np.array_equal(union, ref_union)
     if routing == 1:
         assert np.all(union <= topk - 1)
+
+
+# ------------------------------------------------- chunked prefill / decode ---
+CHUNKS = [
+    # N, Hq, Hkv, B, topk, C, dtype
+    (3000, 8, 2, 128, 4, 1, "bf16"),      # one decode step
+    (3000, 8, 2, 128, 4, 7, "bf16"),      # inside the last (partial) block
+    (3000, 8, 2, 128, 4, 300, "bf16"),    # across blocks, partial first block
+    (3000, 8, 2, 128, 4, 3000, "bf16"),   # the whole sequence
+    (2048, 4, 4, 96, 5, 200, "bf16"),     # B not a multiple of 64
+    (1500, 4, 2, 64, 3, 129, "f32"),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk,C,dtype", CHUNKS)
+def test_chunk_rows_match_full_prefill(N, Hq, Hkv, B, topk, C, dtype):
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + C, dtype=dtype)
+    qc = tq[N - C:].contiguous()
+    o = to_np(moba.prefill_chunk(qc, tk, tv, B, topk, 0.09))
+    sel = moba.select_chunk(qc, tk, B, topk).cpu().numpy()
+    rows, heads = all_rows(C, Hq)
+    rows = rows + (N - C)  # positions in the sequence
+    compare_rows(q, k, v, B, topk, 0.09, rows, heads, sel.reshape(-1, topk), o.reshape(-1, 128),
+                 dtype, f"chunk {C} of {N}")
+    full = to_np(moba.prefill(tq, tk, tv, B, topk, 0.09))[N - C:]
+    assert np.max(np.abs(full - o)) <= (1e-2 if dtype == "bf16" else 1e-5)
+
+
+def test_decode_steps():
+    """Three decode steps on a growing cache, each checked against the oracle."""
+    N0, Hq, Hkv, B, topk = 1535, 8, 2, 128, 4
+    q, k, v, tq, tk, tv = small(N0 + 3, Hq, Hkv, B, topk, seed=123)
+    for step in range(3):
+        N = N0 + step + 1  # the cache holds the new row
+        o = to_np(moba.prefill_chunk(tq[N - 1:N].contiguous(), tk[:N].contiguous(),
+                                     tv[:N].contiguous(), B, topk, 0.09))
+        sel = moba.select_chunk(tq[N - 1:N].contiguous(), tk[:N].contiguous(), B, topk)
+        rows = np.full(Hq, N - 1, np.int64)
+        heads = np.arange(Hq, dtype=np.int32)
+        compare_rows(q[:N], k[:N], v[:N], B, topk, 0.09, rows, heads,
+                     sel.cpu().numpy().reshape(-1, topk), o.reshape(-1, 128), "bf16",
+                     f"decode step {step}")
