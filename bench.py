@@ -115,6 +115,8 @@ def main():
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
                     help="skip the packed-batch leg (16 sequences, same total rows)")
+    ap.add_argument("--no-chunk", action="store_true",
+                    help="skip the decode-step and chunked-prefill legs over the same KV cache")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the group-shared routing leg and the routing-statistics timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -222,6 +224,27 @@ def main():
                   "attended_tflops": 4.0 * w.d * w.Hq * (vown + vhist) / (vms / 1e3) / 1e12}
         del wsv
 
+    chunk = None
+    if not args.no_chunk and dtype == "bf16":
+        chunk = {}
+        for C in (1, 16384):
+            qc = tq[w.N - C:].contiguous()
+            oc = torch.empty_like(qc)
+            wsc = moba.alloc_workspace(moba.chunk_workspace_size(prob, C), tq.device)
+            moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5 if C == 1 else 2
+            e0.record()
+            for _ in range(reps):
+                moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
+            e1.record()
+            torch.cuda.synchronize()
+            cms = e0.elapsed_time(e1) / reps
+            chunk["decode_step" if C == 1 else f"chunk_{C}"] = {
+                "query_rows": C, "cache_rows": w.N, "ms": cms, "tokens_per_s": C / (cms / 1e3)}
+            del wsc, oc
+
     shared = None
     if not args.no_shared and dtype == "bf16":
         moba.prefill(tq, tk, tv, w.B, w.k, w.scale, out=out, routing=moba.MOBA_ROUTING_SHARED)
@@ -281,6 +304,7 @@ def main():
         "dense_causal": dense,
         "varlen": varlen,
         "shared_routing": shared,
+        "chunked": chunk,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

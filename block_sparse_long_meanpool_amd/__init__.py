@@ -310,6 +310,11 @@ def _chunk_problem(q, k, block_size, topk, scale, routing):
     return make_problem(N, q.shape[1], Hkv, d, block_size, topk, scale, _dtype_code(q), routing)
 
 
+def chunk_workspace_size(prob: MobaProblem, q_rows: int) -> int:
+    """Workspace bytes of moba_prefill_chunk / moba_select_chunk (0 if invalid)."""
+    return load_library().moba_chunk_workspace_size(ctypes.byref(prob), int(q_rows))
+
+
 def prefill_chunk(q, k, v, block_size, topk, scale=None, out=None, workspace=None,
                   routing=MOBA_ROUTING_PER_HEAD):
     """Chunked prefill / decode: q [C, Hq, d] are the queries of the last C
