@@ -1,4 +1,4 @@
-// Routing diagnostics (PaperTrace "2.1.3 MoBA", section 5.4: log the margin
+// Routing diagnostics (PaperTrace "2.1.3 MoBA", section 5.3: log the margin
 // between the k-th and (k+1)-th block scores, the overlap of candidates and
 // how often each block is selected). The margins come from the exact gate
 // tier (run_gate with a margin output); this file holds the two reductions

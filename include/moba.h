@@ -62,7 +62,7 @@ extern "C" {
 typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_F32 = 1 } moba_dtype_t;
 
 /*
- * Block routing under grouped-query attention (PaperTrace section 5.4 asks
+ * Block routing under grouped-query attention (PaperTrace section 5.5 asks
  * that the choice be stated: each query head routes on its own, or a head
  * group shares one routing).
  *   MOBA_ROUTING_PER_HEAD: every query head ranks the blocks with its own
@@ -191,7 +191,7 @@ MOBA_API int moba_select_chunk(const moba_problem_t *p, int64_t q_rows, const vo
                                void *stream);
 
 /*
- * Routing diagnostics (PaperTrace section 5.4: log the gap between the
+ * Routing diagnostics (PaperTrace section 5.3: log the gap between the
  * k-th and (k+1)-th block scores, candidate overlap and per-block selection
  * frequency). Runs the block means and the exact (fp64) gate for every row
  * under p->routing, then fills whichever outputs are non-NULL (DEVICE):

@@ -68,6 +68,8 @@ def _load():
         lib.moba_ref_rows.restype = ctypes.c_int
         lib.moba_ref_rows.argtypes = [P, vp, vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int,
                                       vp, vp, vp, ctypes.c_int]
+        lib.moba_ref_backward.restype = ctypes.c_int
+        lib.moba_ref_backward.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp]
         lib.moba_ref_causal_full.restype = ctypes.c_int
         lib.moba_ref_causal_full.argtypes = [P, vp, vp, vp, vp, vp, ctypes.c_int64, vp, ctypes.c_int]
         _lib = lib
@@ -114,7 +116,7 @@ def rows(q, k, v, B, topk, rows, heads, scale=None, forced_sel=None, mode=MODE_U
 
     ``routing``: ROUTING_PER_HEAD ranks blocks with each head's own query;
     ROUTING_SHARED ranks them once per KV-head group by the group's summed
-    gate score (PaperTrace "2.1.3 MoBA", section 5.4 on GQA routing).
+    gate score (PaperTrace "2.1.3 MoBA", section 5.5 on GQA routing).
 
     Returns ``(sel, o, gap)``: ``sel`` int32 [R, k] ascending and -1 padded;
     ``o`` fp64 [R, d] (None when ``want_o`` is False); ``gap`` fp64 [R, 2] with the
@@ -201,3 +203,27 @@ def prefill_varlen(q, k, v, cu, B, topk, scale=None, mode=MODE_UNION, nthreads=0
                                nthreads=nthreads)
             sel[a:b], o[a:b] = s_i, o_i
     return sel, o
+
+
+def backward(q, k, v, dout, B, topk, scale=None, sel=None, routing=ROUTING_PER_HEAD):
+    """Gradients (dq [N, Hq, d], dk, dv [N, Hkv, d], fp64) of sum(dout * O) with the
+    block selection held fixed (no gradient through the hard top-k ranking):
+    the softmax-attention gradient over each row's candidate set, eqs. (4)-(6).
+    ``sel`` defaults to the oracle's own selection."""
+    q, k, v = _c(q), _c(k), _c(v)
+    N, Hq, d = q.shape
+    if sel is None:
+        r, h = all_rows(N, Hq)
+        sel, _, _ = rows(q, k, None, B, topk, r, h, want_o=False, routing=routing)
+    sel = _c(np.asarray(sel).reshape(N, Hq, topk), np.int32)
+    dout = _c(np.asarray(dout, dtype=np.float64))
+    pr = _problem(q, k, B, topk, scale, routing)
+    dq = np.empty((N, Hq, d), np.float64)
+    dk = np.empty(k.shape, np.float64)
+    dv = np.empty(k.shape, np.float64)
+    rc = _load().moba_ref_backward(ctypes.byref(pr), q.ctypes.data, k.ctypes.data, v.ctypes.data,
+                                   dout.ctypes.data, sel.ctypes.data, dq.ctypes.data,
+                                   dk.ctypes.data, dv.ctypes.data)
+    if rc:
+        raise ValueError(f"moba_ref_backward failed ({rc})")
+    return dq, dk, dv

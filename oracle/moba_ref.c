@@ -54,7 +54,7 @@ typedef struct {
   int32_t routing; /* 0: each query head ranks blocks with its own query;
                       1: the query heads of a KV head share one ranking by the
                          group's summed gate score, sum_h q_h . kbar_i
-                         (PaperTrace "2.1.3 MoBA", section 5.4 on GQA) */
+                         (PaperTrace "2.1.3 MoBA", section 5.5 on GQA) */
 } moba_ref_problem;
 
 static inline double ld(const void *base, int dtype, int64_t i) {
@@ -357,4 +357,84 @@ int moba_ref_causal_full(const moba_ref_problem *p, const void *Q, const void *K
     free(z);
   }
   return err;
+}
+
+/*
+ * Gradients of the loss L = sum over (row, head) of dO[row,head] . O[row,head]
+ * with the block selection held fixed (the hard top-k passes no gradient to
+ * the ranking, PaperTrace "2.1.3 MoBA" section 5.3; gradients reach Q, K and
+ * V only through attended pairs). For one (row, head) with candidate set I
+ * (eq. (4)): z_j = scale q.k_j, P = softmax(z) over I, o = sum_j P_j v_j;
+ *   dV_j += P_j dO,
+ *   dP_j  = dO . v_j,   D = dO . o = sum_j P_j dP_j,
+ *   dZ_j  = P_j (dP_j - D),
+ *   dq    = scale sum_j dZ_j k_j,   dK_j += scale dZ_j q.
+ * Written out over every (row, head) in fp64; the selection is taken from
+ * sel [N][Hq][k] (as moba_ref_rows returns it: history blocks < the row's
+ * block, then the own block, -1 padding). dq [N][Hq][d], dk and dv
+ * [N][Hkv][d] are overwritten. Serial: small problems only.
+ */
+int moba_ref_backward(const moba_ref_problem *p, const void *Q, const void *K, const void *V,
+                      const double *dO, const int32_t *sel, double *dq, double *dk, double *dv) {
+  if (check(p) || !Q || !K || !V || !dO || !sel || !dq || !dk || !dv) return 1;
+  const int64_t N = p->N, d = p->d, B = p->B, kk = p->k;
+  const int G = p->Hq / p->Hkv;
+  for (int64_t i = 0; i < N * p->Hq * d; ++i) dq[i] = 0.0;
+  for (int64_t i = 0; i < N * p->Hkv * d; ++i) dk[i] = dv[i] = 0.0;
+  unsigned char *member = (unsigned char *)malloc((size_t)N);
+  double *z = (double *)malloc(sizeof(double) * (size_t)N);
+  double *o = (double *)malloc(sizeof(double) * (size_t)d);
+  if (!member || !z || !o) {
+    free(member);
+    free(z);
+    free(o);
+    return 2;
+  }
+  for (int64_t row = 0; row < N; ++row) {
+    const int64_t c = row / B;
+    for (int h = 0; h < p->Hq; ++h) {
+      const int g = h / G;
+      const int32_t *sr = sel + (row * p->Hq + h) * kk;
+      for (int64_t j = 0; j < N; ++j) member[j] = (j / B == c && j <= row);
+      for (int64_t t = 0; t < kk; ++t)
+        if (sr[t] >= 0 && sr[t] < c)
+          for (int64_t j = sr[t] * B; j < (sr[t] + 1) * B; ++j) member[j] = 1;
+      const int64_t qb = (row * p->Hq + h) * d;
+      double mx = -INFINITY;
+      for (int64_t j = 0; j < N; ++j) {
+        if (!member[j]) continue;
+        double dot = 0.0;
+        for (int64_t t = 0; t < d; ++t) dot += ld(Q, p->dtype, qb + t) * ld(K, p->dtype, (j * p->Hkv + g) * d + t);
+        z[j] = p->scale * dot;
+        if (z[j] > mx) mx = z[j];
+      }
+      double l = 0.0;
+      for (int64_t j = 0; j < N; ++j)
+        if (member[j]) l += exp(z[j] - mx);
+      for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+      for (int64_t j = 0; j < N; ++j) {
+        if (!member[j]) continue;
+        z[j] = exp(z[j] - mx) / l; /* now P_j */
+        for (int64_t t = 0; t < d; ++t) o[t] += z[j] * ld(V, p->dtype, (j * p->Hkv + g) * d + t);
+      }
+      double D = 0.0;
+      for (int64_t t = 0; t < d; ++t) D += dO[qb + t] * o[t];
+      for (int64_t j = 0; j < N; ++j) {
+        if (!member[j]) continue;
+        const int64_t kvb = (j * p->Hkv + g) * d;
+        double dp = 0.0;
+        for (int64_t t = 0; t < d; ++t) dp += dO[qb + t] * ld(V, p->dtype, kvb + t);
+        const double dz = z[j] * (dp - D);
+        for (int64_t t = 0; t < d; ++t) {
+          dv[kvb + t] += z[j] * dO[qb + t];
+          dq[qb + t] += p->scale * dz * ld(K, p->dtype, kvb + t);
+          dk[kvb + t] += p->scale * dz * ld(Q, p->dtype, qb + t);
+        }
+      }
+    }
+  }
+  free(member);
+  free(z);
+  free(o);
+  return 0;
 }

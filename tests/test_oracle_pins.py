@@ -488,3 +488,54 @@ def test_gap_reports_selection_margin():
         s = kb[0, :c] @ q[r[i], 0].astype(np.float64)
         srt = np.sort(s)[::-1]
         assert abs(gap[i, 0] - (srt[1] - srt[2])) < 1e-12
+
+
+# ------------------------------------------------------------------ backward ---
+def _loss(q, k, v, dout, B, topk, scale, sel):
+    """sum(dout * O) with the selection forced (the ranking held fixed)."""
+    N, Hq, d = q.shape
+    r, h = oracle.all_rows(N, Hq)
+    _, o, _ = oracle.rows(q, k, v, B, topk, r, h, scale=scale, forced_sel=sel.reshape(-1, topk))
+    return float(np.sum(dout.reshape(-1, d) * o))
+
+
+@pytest.mark.parametrize("routing", [0, 1])
+def test_backward_matches_finite_differences(routing):
+    """Central differences of sum(dO * O) in fp64 (inputs perturbed by 2^-12,
+    exactly representable) against the analytic gradients, on entries of Q, K
+    and V in history blocks and in the own block."""
+    N, Hq, Hkv, d, B, topk, scale = 37, 4, 2, 6, 4, 3, 0.6
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=41)
+    rng = np.random.default_rng(3)
+    dout = rng.standard_normal((N, Hq, d))
+    r, h = oracle.all_rows(N, Hq)
+    sel, _, _ = oracle.rows(q, k, None, B, topk, r, h, want_o=False, routing=routing)
+    dq, dk, dv = oracle.backward(q, k, v, dout, B, topk, scale=scale, sel=sel)
+    eps = 2.0 ** -12
+    for name, arr, grad in (("q", q, dq), ("k", k, dk), ("v", v, dv)):
+        for _ in range(6):
+            idx = tuple(int(rng.integers(0, s)) for s in arr.shape)
+            a_p, a_m = arr.copy(), arr.copy()
+            a_p[idx] += eps
+            a_m[idx] -= eps
+            args_p = {"q": q, "k": k, "v": v}
+            args_m = dict(args_p)
+            args_p[name], args_m[name] = a_p, a_m
+            fd = (_loss(args_p["q"], args_p["k"], args_p["v"], dout, B, topk, scale, sel) -
+                  _loss(args_m["q"], args_m["k"], args_m["v"], dout, B, topk, scale, sel)) / (2 * eps)
+            assert abs(fd - grad[idx]) <= 1e-6 * max(1.0, abs(fd)), (name, idx, fd, grad[idx])
+
+
+def test_backward_closed_forms():
+    """Weights sum to one: the dV of a KV head sums to the dO of its query heads.
+    Constant V: every output equals that vector, so dQ and dK vanish."""
+    N, Hq, Hkv, d, B, topk = 40, 4, 2, 8, 5, 3
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=8)
+    dout = np.random.default_rng(9).standard_normal((N, Hq, d))
+    dq, dk, dv = oracle.backward(q, k, v, dout, B, topk, scale=0.5)
+    G = Hq // Hkv
+    for g in range(Hkv):
+        assert np.allclose(dv[:, g].sum(0), dout[:, g * G:(g + 1) * G].sum((0, 1)), atol=1e-12)
+    vc = np.broadcast_to(v[:1], v.shape).copy()
+    dq, dk, _ = oracle.backward(q, k, vc, dout, B, topk, scale=0.5)
+    assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
