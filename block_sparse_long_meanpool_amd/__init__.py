@@ -41,6 +41,7 @@ EXPORTS = (
     "moba_prefill_varlen", "moba_select_varlen",
     "moba_routing_stats_workspace_size", "moba_routing_stats",
     "moba_chunk_workspace_size", "moba_prefill_chunk", "moba_select_chunk",
+    "moba_prefill_train", "moba_backward_workspace_size", "moba_backward",
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
@@ -94,6 +95,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_varlen_select_workspace_size": (sz, [P, i64, vp]),
         "moba_prefill_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_prefill_train": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_backward_workspace_size": (sz, [P]),
+        "moba_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_chunk_workspace_size": (sz, [P, i64]),
         "moba_prefill_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, sz, vp]),
@@ -308,6 +312,47 @@ def _chunk_problem(q, k, block_size, topk, scale, routing):
         raise TypeError("q, k and v must share a dtype")
     N, Hkv, d = k.shape
     return make_problem(N, q.shape[1], Hkv, d, block_size, topk, scale, _dtype_code(q), routing)
+
+
+def prefill_train(q, k, v, block_size, topk, scale=None, routing=MOBA_ROUTING_PER_HEAD,
+                  workspace=None):
+    """Forward for training: (O [N, Hq, d], lse [N, Hq] fp32), lse being each
+    row's log2-sum-exp of scale*log2(e)*q.k over its keys."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    need = lib.moba_workspace_size(ctypes.byref(prob))
+    if need == 0:
+        _ok(lib.moba_prefill_train(ctypes.byref(prob), None, None, None, None, None, None, 0, None),
+            "moba_workspace_size")
+    if workspace is None:
+        workspace = alloc_workspace(need, q.device)
+    st = lib.moba_prefill_train(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                out.data_ptr(), lse.data_ptr(), workspace.data_ptr(),
+                                workspace.numel(), _stream(q.device))
+    _ok(st, "moba_prefill_train")
+    return out, lse
+
+
+def backward(q, k, v, o, lse, dout, block_size, topk, scale=None, routing=MOBA_ROUTING_PER_HEAD):
+    """Gradients (dq, dk, dv) of sum(dout * O) with the block selection held fixed."""
+    lib = load_library()
+    _check_dev(q, k, v, o, lse, dout)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = lib.moba_backward_workspace_size(ctypes.byref(prob))
+    if need == 0:
+        _ok(lib.moba_backward(ctypes.byref(prob), *([None] * 10), 0, None),
+            "moba_backward_workspace_size")
+    ws = alloc_workspace(need, q.device)
+    st = lib.moba_backward(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                           o.data_ptr(), lse.data_ptr(), dout.data_ptr(), dq.data_ptr(),
+                           dk.data_ptr(), dv.data_ptr(), ws.data_ptr(), ws.numel(),
+                           _stream(q.device))
+    _ok(st, "moba_backward")
+    return dq, dk, dv
 
 
 def chunk_workspace_size(prob: MobaProblem, q_rows: int) -> int:

@@ -370,7 +370,8 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 // load stays inside the row's own partials.
 template <int NH>
 __device__ inline b8 merge_row(h8 own, float own_lse, const float* __restrict__ lse_src,
-                               const _Float16* __restrict__ po_src, int nhist, int c16) {
+                               const _Float16* __restrict__ po_src, int nhist, int c16,
+                               float* lse_out) {
   constexpr int GRP = 8;
   float lse[NH];
 #pragma unroll
@@ -403,6 +404,7 @@ __device__ inline b8 merge_row(h8 own, float own_lse, const float* __restrict__ 
   b8 out;
 #pragma unroll
   for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
+  *lse_out = M + __builtin_log2f(L);  // the row's log2-sum-exp over all its keys
   return out;
 }
 
@@ -499,8 +501,9 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const int32_t* __restrict__ bstart, const int32_t* __restrict__ qstart,
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const _Float16* __restrict__ part_o,
-    const float* __restrict__ part_lse, uint16_t* __restrict__ O, int Hq, int Hkv, int G,
-    int64_t Bpad, int64_t ldv, int KH, int64_t n, int tiles_per_block, float sl2e) {
+    const float* __restrict__ part_lse, uint16_t* __restrict__ O, float* __restrict__ lse_out,
+    int Hq, int Hkv, int G, int64_t Bpad, int64_t ldv, int KH, int64_t n, int tiles_per_block,
+    float sl2e) {
   MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   // Work items w = ((c' * Hkv) + g) * tiles_per_block + t' in order of
@@ -569,6 +572,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     for (int qb = 0; qb < QB; ++qb) {
       const float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
       if (!valid[qb]) continue;
+      if (lse_out && h == 0) lse_out[ph[qb]] = W.m[qb] + __builtin_log2f(l);
       const float inv = 1.f / l;
       uint16_t* dst = O + ph[qb] * kHeadDim;
 #pragma unroll
@@ -617,15 +621,19 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const float* ls = part_lse + phj * KH;
     const _Float16* po = part_o + (size_t)(phj * KH) * kHeadDim;
     b8 out;
+    float lse_row;
     if (nhist <= 4)
-      out = merge_row<4>(own, own_lse, ls, po, nhist, c16);
+      out = merge_row<4>(own, own_lse, ls, po, nhist, c16, &lse_row);
     else if (nhist <= 8)
-      out = merge_row<8>(own, own_lse, ls, po, nhist, c16);
+      out = merge_row<8>(own, own_lse, ls, po, nhist, c16, &lse_row);
     else if (nhist <= 16)
-      out = merge_row<16>(own, own_lse, ls, po, nhist, c16);
+      out = merge_row<16>(own, own_lse, ls, po, nhist, c16, &lse_row);
     else
-      out = merge_row<kMaxTopk>(own, own_lse, ls, po, nhist, c16);
-    if (pi < npairs) *reinterpret_cast<b8*>(O + phj * kHeadDim + 8 * c16) = out;
+      out = merge_row<kMaxTopk>(own, own_lse, ls, po, nhist, c16, &lse_row);
+    if (pi < npairs) {
+      *reinterpret_cast<b8*>(O + phj * kHeadDim + 8 * c16) = out;
+      if (lse_out && c16 == 0) lse_out[phj] = lse_row;
+    }
   }
 }
 
@@ -651,7 +659,7 @@ hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPla
 
 hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, const void* K,
                                  const void* Vt, const void* part_o, const float* part_lse,
-                                 void* O, hipStream_t s) {
+                                 void* O, float* lse_out, hipStream_t s) {
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
   const int64_t ldv = P.n * Bpad;
@@ -660,7 +668,8 @@ hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, 
   const bool merge = part_o != nullptr && P.KH > 0;
   attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.qstart, T.qlen,
-      T.qpos, T.lo, merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr, (uint16_t*)O, P.Hq,
+      T.qpos, T.lo, merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr,
+      (uint16_t*)O, lse_out, P.Hq,
       P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, tiles_per_block, sl2e);
   return hipGetLastError();
 }

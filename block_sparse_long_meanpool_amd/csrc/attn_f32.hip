@@ -15,7 +15,7 @@ hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPla
                                  hipStream_t s);
 hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, const void* K,
                                  const void* Vt, const void* part_o, const float* part_lse,
-                                 void* O, hipStream_t s);
+                                 void* O, float* lse_out, hipStream_t s);
 
 namespace {
 
@@ -139,8 +139,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
     const int32_t* __restrict__ bstart, const int32_t* __restrict__ qstart,
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const float* __restrict__ part_o,
-    const float* __restrict__ part_lse, float* __restrict__ O, int Hq, int Hkv, int G, int KH,
-    int64_t n, int tiles_per_block, float sl2e) {
+    const float* __restrict__ part_lse, float* __restrict__ O, float* __restrict__ lse_out, int Hq,
+    int Hkv, int G, int KH, int64_t n, int tiles_per_block, float sl2e) {
   __shared__ float ks[KT * kHeadDim];
   __shared__ float vs[KT * kHeadDim];
   const int g = blockIdx.y;
@@ -171,11 +171,11 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
   }
   if (!valid) return;
   float l = S.l;
+  float M = S.m;
   if (part_o != nullptr && KH > 0) {
     const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
     const int64_t nhist = nbefore < KH ? nbefore : KH;
     const int64_t ebase = ph * KH;
-    float M = S.m;
     for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
     const float ws = __builtin_amdgcn_exp2f(S.m - M);
     l *= ws;
@@ -189,6 +189,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
       for (int cc = 0; cc < kDim; ++cc) S.o[cc] = fmaf(wgt, src[cc], S.o[cc]);
     }
   }
+  if (lse_out && sub == 0) lse_out[ph] = M + __builtin_log2f(l);  // log2-sum-exp of the row
   const float inv = 1.f / l;
   float* dst = O + ph * kHeadDim + sub * kDim;
 #pragma unroll
@@ -212,16 +213,16 @@ hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp
 
 hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const void* K,
                             const void* V, const void* Vt, const void* part_o,
-                            const float* part_lse, void* O, hipStream_t s) {
+                            const float* part_lse, void* O, float* lse_out, hipStream_t s) {
   if (P.dtype == MOBA_DTYPE_BF16)
-    return launch_attn_self_bf16(P, T, Q, K, Vt, part_o, part_lse, O, s);
+    return launch_attn_self_bf16(P, T, Q, K, Vt, part_o, part_lse, O, lse_out, s);
   const bool merge = part_o != nullptr && P.KH > 0;
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kQ);
   dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
   attn_self_f32<<<grid, kThreads, 0, s>>>(
       (const float*)Q, (const float*)K, (const float*)V, T.start, T.qstart, T.qlen, T.qpos, T.lo,
-      merge ? (const float*)part_o : nullptr, merge ? part_lse : nullptr, (float*)O, P.Hq, P.Hkv,
-      P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e);
+      merge ? (const float*)part_o : nullptr, merge ? part_lse : nullptr, (float*)O, lse_out, P.Hq,
+      P.Hkv, P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e);
   return hipGetLastError();
 }
 

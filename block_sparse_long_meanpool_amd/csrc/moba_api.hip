@@ -130,7 +130,7 @@ size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 struct Layout {
   size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
-      part_lse, part_o, vt, total;
+      part_lse, part_o, vt, delta, dq_acc, total;
 };
 
 // Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
@@ -154,6 +154,36 @@ void take_tables(const Prob& P, Layout& L, size_t& off) {
   L.qpos = take(sizeof(int32_t) * (size_t)P.n);
   L.row_blk = take(sizeof(int32_t) * (size_t)P.Nq);
   L.seq_base = take(sizeof(int32_t) * (size_t)(P.nseq + 1));
+}
+
+// Backward workspace: tables, block means, gate, selection, buckets, then the
+// fp32 row terms D = dO.O and the dq accumulator.
+Layout plan_ws_bwd(const Prob& P) {
+  Layout L{};
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    size_t at = off;
+    off = align_up(off + bytes);
+    return at;
+  };
+  take_tables(P, L, off);
+  const int splits = meanpool_splits(P);
+  L.kbar = take(sizeof(double) * (size_t)(P.Hkv * P.nh * P.d));
+  L.mp_part = take(sizeof(double) * (size_t)splits * P.nh * P.Hkv * P.d);
+  L.gate = take(gate_scratch_bytes(P));
+  const BucketPlan bp = plan_bucket(P);
+  L.sel = take(sizeof(int32_t) * (size_t)(P.Nq * P.Hq * P.k));
+  L.chunk_base = take(sizeof(int32_t) * (size_t)(P.Hkv * bp.nchunk * P.nh));
+  L.bin_total = take(sizeof(int32_t) * (size_t)(bp.nbins + 1));
+  L.bin_off = take(sizeof(int32_t) * (size_t)(bp.nbins + 1));
+  L.tile_off = take(sizeof(int32_t) * (size_t)(bp.nbins + 1));
+  L.scalars = take(sizeof(int32_t) * 4);
+  L.tile_map = take(sizeof(int32_t) * (size_t)bp.max_tiles);
+  L.entries = take(sizeof(uint32_t) * (size_t)bp.max_entries);
+  L.delta = take(sizeof(float) * (size_t)(P.Nq * P.Hq));
+  L.dq_acc = take(sizeof(float) * (size_t)(P.Nq * P.Hq) * P.d);
+  L.total = off;
+  return L;
 }
 
 // Workspace layout; `full` = prefill (all stages), else select only.
@@ -262,7 +292,8 @@ int run_select(const Prob& P, const int64_t* cu, const void* q, const void* k, i
 
 // The whole path on prepared problem and workspace.
 int run_prefill(const Prob& P, const int64_t* cu, const void* q, const void* k, const void* v,
-                void* o, void* workspace, const Layout& L, hipStream_t s, void* const* events) {
+                void* o, void* workspace, const Layout& L, hipStream_t s, void* const* events,
+                float* lse = nullptr) {
   int rc;
   if ((rc = record(events, 0, s))) return rc;
   int32_t* sel = at<int32_t>(workspace, L.sel);
@@ -284,7 +315,7 @@ int run_prefill(const Prob& P, const int64_t* cu, const void* q, const void* k, 
   e = launch_attn_hist(P, T, bp, q, k, v, vt, bb, part_o, part_lse, s);
   if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
   if ((rc = record(events, 5, s))) return rc;
-  e = launch_attn_self(P, T, q, k, v, vt, part_o, part_lse, o, s);
+  e = launch_attn_self(P, T, q, k, v, vt, part_o, part_lse, o, lse, s);
   if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
   return record(events, 6, s);
 }
@@ -392,6 +423,48 @@ int moba_routing_stats(const moba_problem_t* p, const void* q, const void* k, in
                            selw, margin, s);
   if (e == hipSuccess) e = launch_routing_reductions(P, T, selw, counts, union_size, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "routing statistics");
+}
+
+int moba_prefill_train(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                       void* o, float* lse, void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  const void* ptrs[5] = {q, k, v, o, lse};
+  if ((rc = check_ptrs(ptrs, 5, "q, k, v, o and lse must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, true);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_prefill(P, nullptr, q, k, v, o, workspace, L, (hipStream_t)stream, nullptr, lse);
+}
+
+size_t moba_backward_workspace_size(const moba_problem_t* p) {
+  Prob P;
+  if (make_prob(p, &P) != MOBA_OK) return 0;
+  return plan_ws_bwd(P).total;
+}
+
+int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, nullptr};
+  if ((rc = check_ptrs(ptrs, 9, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL")))
+    return rc;
+  const Layout L = plan_ws_bwd(P);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  int32_t* sel = at<int32_t>(workspace, L.sel);
+  if ((rc = run_select(P, nullptr, q, k, sel, workspace, L, s, nullptr))) return rc;
+  const Blocks T = tables(workspace, L);
+  const BucketPlan bp = plan_bucket(P);
+  const BucketBufs bb = bucket_bufs(workspace, L);
+  hipError_t e = launch_bucket(P, T, bp, sel, bb, s);
+  if (e != hipSuccess) return hip_fail(e, "moba_bucket");
+  e = launch_backward(P, T, bp, bb, q, k, v, o, lse, dout, dq, dk, dv,
+                      at<float>(workspace, L.delta), at<float>(workspace, L.dq_acc), s);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e, "moba_backward");
 }
 
 size_t moba_chunk_workspace_size(const moba_problem_t* p, int64_t q_rows) {
@@ -508,7 +581,7 @@ int moba_dense_causal(const moba_problem_t* p, const void* q, const void* k, con
     e = launch_vt_pack(P, T, v, vt, s);
     if (e != hipSuccess) return hip_fail(e, "V pack");
   }
-  e = launch_attn_self(P, T, q, k, v, vt, nullptr, nullptr, o, s);
+  e = launch_attn_self(P, T, q, k, v, vt, nullptr, nullptr, o, nullptr, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "dense causal attention");
 }
 

@@ -117,10 +117,20 @@ hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp
 
 // Own-block causal attention fused with the merge of the history partials
 // (part_o == NULL: no partials, e.g. the dense baseline, whose problem is one
-// block spanning the sequence).
+// block spanning the sequence). lse_out (nullable) [Nq][Hq] receives each
+// row's log2-sum-exp: P_j = 2^(scale log2(e) q.k_j - lse) over its keys.
 hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const void* K,
                             const void* V, const void* Vt, const void* part_o,
-                            const float* part_lse, void* O, hipStream_t s);
+                            const float* part_lse, void* O, float* lse_out, hipStream_t s);
+
+// Backward with the selection held fixed (bwd.hip): dq [Nq][Hq][d], dk and dv
+// [N][Hkv][d] in the input dtype from o, lse2 (the forward's lse_out) and
+// dout. delta [Nq][Hq] and dq_acc [Nq][Hq][d] (fp32) are scratch; bp/bb must
+// hold the bucketed selection of the same problem.
+hipError_t launch_backward(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                           const BucketBufs& bb, const void* q, const void* k, const void* v,
+                           const void* o, const float* lse2, const void* dout, void* dq, void* dk,
+                           void* dv, float* delta, float* dq_acc, hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);

@@ -169,6 +169,31 @@ MOBA_API int moba_select_varlen(const moba_problem_t *p, int64_t nseq,
                                 size_t ws_bytes, void *stream);
 
 /*
+ * Training: forward with saved statistics, and the backward pass.
+ *   moba_prefill_train: moba_prefill plus lse [N][Hq] fp32 (DEVICE): each
+ *     row's log2-sum-exp over its keys, lse = log2(sum_j 2^(c q.k_j)) with
+ *     c = scale * log2(e), so its attention weights are 2^(c q.k_j - lse).
+ *     Same workspace as moba_prefill.
+ *   moba_backward: gradients of sum(dout * O) — dq [N][Hq][d], dk and dv
+ *     [N][Hkv][d], in the dtype of p, overwritten — from q, k, v, the forward
+ *     output o, its lse and dout [N][Hq][d]. The block selection is held
+ *     fixed: the hard top-k passes no gradient to the ranking, so Q, K and V
+ *     get gradients only through the attended pairs (PaperTrace section
+ *     5.3); the selection is recomputed from q and k exactly as in the
+ *     forward pass. Workspace: moba_backward_workspace_size(p).
+ * Numerics: fp32 arithmetic on the vector units (not the matrix cores);
+ * weights are rebuilt from lse, and dq sums its per-block pieces with fp32
+ * atomics (so the last bits of dq may vary between runs).
+ */
+MOBA_API int moba_prefill_train(const moba_problem_t *p, const void *q, const void *k,
+                                const void *v, void *o, float *lse, void *workspace,
+                                size_t ws_bytes, void *stream);
+MOBA_API size_t moba_backward_workspace_size(const moba_problem_t *p);
+MOBA_API int moba_backward(const moba_problem_t *p, const void *q, const void *k, const void *v,
+                           const void *o, const float *lse, const void *dout, void *dq,
+                           void *dk, void *dv, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Chunked prefill and decode: the queries are the last q_rows positions of
  * one sequence whose keys and values (all p->seqlen rows, the new ones
  * included) are already in k and v — a KV cache. q and o hold only those

@@ -417,3 +417,42 @@ def test_decode_steps():
         compare_rows(q[:N], k[:N], v[:N], B, topk, 0.09, rows, heads,
                      sel.cpu().numpy().reshape(-1, topk), o.reshape(-1, 128), "bf16",
                      f"decode step {step}")
+
+
+# ------------------------------------------------------------------ backward ---
+BWD = [
+    # N, Hq, Hkv, B, topk, dtype, routing
+    (700, 4, 2, 64, 3, "f32", 0),
+    (700, 4, 2, 64, 3, "bf16", 0),
+    (900, 6, 3, 96, 4, "bf16", 0),     # B not a multiple of 64, G = 2
+    (600, 4, 1, 128, 1, "bf16", 0),    # own block only
+    (800, 8, 2, 64, 4, "bf16", 1),     # group-shared routing
+]
+
+
+def _grad_close(got, ref, dtype, what):
+    scale = max(float(np.max(np.abs(ref))), 1e-30)
+    err = np.abs(got - ref)
+    if dtype == "f32":
+        assert err.max() <= 1e-4 * scale, f"{what}: max err {err.max():.3e} vs |g| {scale:.3e}"
+    else:
+        assert err.max() <= 2e-2 * scale, f"{what}: max err {err.max():.3e} vs |g| {scale:.3e}"
+        assert err.mean() <= 2e-3 * scale, f"{what}: mean err {err.mean():.3e} vs |g| {scale:.3e}"
+    return float(err.max() / scale)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk,dtype,routing", BWD)
+def test_backward_matches_oracle(N, Hq, Hkv, B, topk, dtype, routing):
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + 5 * topk, dtype=dtype)
+    scale = 0.09
+    o, lse = moba.prefill_train(tq, tk, tv, B, topk, scale, routing=routing)
+    o_plain = moba.prefill(tq, tk, tv, B, topk, scale, routing=routing)
+    assert torch.equal(o, o_plain)
+    gen = torch.Generator(device="cpu").manual_seed(N)
+    dout = torch.randn(tq.shape, generator=gen).to(tq.dtype).to(DEV)
+    dq, dk, dv = moba.backward(tq, tk, tv, o, lse, dout, B, topk, scale, routing=routing)
+    sel = moba.select(tq, tk, B, topk, routing=routing).cpu().numpy()
+    rq, rk, rv = oracle.backward(q, k, v, to_np(dout), B, topk, scale=scale, sel=sel)
+    worst = [_grad_close(to_np(dq), rq, dtype, "dq"), _grad_close(to_np(dk), rk, dtype, "dk"),
+             _grad_close(to_np(dv), rv, dtype, "dv")]
+    print(f"backward {N},{Hq},{Hkv},{B},{topk},{dtype},{routing}: max err / max|g| {worst}")
