@@ -117,6 +117,8 @@ def main():
                     help="skip the packed-batch leg (16 sequences, same total rows)")
     ap.add_argument("--no-chunk", action="store_true",
                     help="skip the decode-step and chunked-prefill legs over the same KV cache")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip the training leg (forward with statistics + backward) on the 32K layer")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the group-shared routing leg and the routing-statistics timing")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
@@ -267,6 +269,32 @@ def main():
                   "median_selection_margin": float(fin.median()) if fin.numel() else None}
         del st
 
+    backward = None
+    if not args.no_backward and dtype == "bf16":
+        wb = synth.CONFIGS["c3"]
+        bq, bk, bv = (to_dev(a) for a in synth.make_qkv(wb, "bf16"))
+        gen = torch.Generator(device="cpu").manual_seed(1)
+        dout = torch.randn(bq.shape, generator=gen).to(torch.bfloat16).to(bq.device)
+        o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
+        moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
+        torch.cuda.synchronize()
+        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+        e0.record()
+        o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
+        e1.record()
+        moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
+        e2.record()
+        torch.cuda.synchronize()
+        fms, bms = e0.elapsed_time(e1), e1.elapsed_time(e2)
+        bown, bhist = pair_counts(wb)
+        pairs = wb.Hq * (bown + bhist)
+        backward = {"workload": f"{wb.name}: N={wb.N} Hq={wb.Hq} Hkv={wb.Hkv} d={wb.d} B={wb.B} "
+                                f"topk={wb.k}, bf16",
+                    "forward_train_ms": fms, "backward_ms": bms,
+                    "backward_tflops": 10.0 * wb.d * pairs / (bms / 1e3) / 1e12,
+                    "note": "backward on the vector units (fp32); 5 products of 2d FLOP per pair"}
+        del bq, bk, bv, dout, o_b, lse_b
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
@@ -305,6 +333,7 @@ def main():
         "varlen": varlen,
         "shared_routing": shared,
         "chunked": chunk,
+        "backward": backward,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
