@@ -29,6 +29,8 @@
 // block) list, whole block (non-causal); writes the normalised partial output
 // (fp16) and its log2-sum-exp. Own-block kernel: causal inside the block,
 // then merges its queries' history partials (eqs. (7)-(8)) and writes O.
+#include <type_traits>
+
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -549,20 +551,30 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   const int64_t nkeys = last_row - key0 + 1;
   const int ntiles = (int)((nkeys + KT - 1) / KT);
   const uint16_t* vt_col = Vt + (int64_t)g * kHeadDim * ldv + c * Bpad;
+  // Whole 64-key tiles before the workgroup's first row are unmasked for every
+  // one of its queries: they go through the unmasked engine, the rest causally.
+  const int64_t nfull = ((pos0 + p0 / G - key0 + 1) / KT) * KT;
+  auto pass = [&](auto maxonly, bool set_m) {
+    constexpr bool MO = decltype(maxonly)::value;
+    if (nfull > 0)
+      run_block<false, true, MO>(W, tA, tB, tC, K, key0, nfull, Hkv, g, vt_col, ldv, wave, lane,
+                                 my_row, 0, 0, true, sl2e, set_m);
+    if (nkeys > nfull)
+      run_block<true, false, MO>(W, tA, tB, tC, K, key0 + nfull, nkeys - nfull, Hkv, g,
+                                 vt_col + nfull, ldv, wave, lane, my_row, wrow_min, wrow_max,
+                                 wave_live, sl2e, set_m && nfull == 0);
+  };
   float mstart[QB];
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) mstart[qb] = 0.f;
   wave_reset(W, mstart);
-  run_block<true, false, false>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
-                                my_row, wrow_min, wrow_max, wave_live, sl2e, true);
+  pass(std::false_type{}, true);
   if (__syncthreads_or(wave_needs_redo(W, valid))) {
     wave_reset(W, mstart);
-    run_block<true, false, true>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
-                                 my_row, wrow_min, wrow_max, wave_live, sl2e, false);
+    pass(std::true_type{}, false);
     wave_true_max(W, sl2e, mstart);
     wave_reset(W, mstart);
-    run_block<true, false, false>(W, tA, tB, tC, K, key0, nkeys, Hkv, g, vt_col, ldv, wave, lane,
-                                  my_row, wrow_min, wrow_max, wave_live, sl2e, false);
+    pass(std::false_type{}, false);
   }
   const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
   const int nhist = part_o != nullptr ? (int)(nbefore < KH ? nbefore : KH) : 0;  // uniform
