@@ -139,10 +139,11 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ bin_off,
     uint32_t* __restrict__ entries, int64_t N, int Hq, int G, int k, int64_t nh,
     int rows_per_chunk, int64_t nchunk, int words) {
-  extern __shared__ uint32_t bm[];  // [nh][words]
+  extern __shared__ uint32_t bm[];  // [nh][words] bitmaps, then [nh][words] prefix counts
   const int g = blockIdx.y;
   const int64_t chunk = blockIdx.x;
   const int64_t nw = nh * words;
+  uint32_t* pre = bm + nw;  // pre[b][w] = entries of bin b in words 0..w-1
   for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
   __syncthreads();
   const int KH = k - 1;
@@ -159,6 +160,14 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     }
   }
   __syncthreads();
+  for (int64_t b = threadIdx.x; b < nh; b += kThreads) {
+    uint32_t run = 0;
+    for (int w = 0; w < words; ++w) {
+      pre[b * words + w] = run;
+      run += __popc(bm[b * words + w]);
+    }
+  }
+  __syncthreads();
   const int32_t* cb = chunk_base + ((size_t)g * nchunk + chunk) * nh;
   const int32_t* bo = bin_off + (size_t)g * nh;
   for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
@@ -171,9 +180,8 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
       if (!hist_entry(b, c)) continue;
-      const uint32_t* w = bm + (size_t)b * words;
-      int rank = __popc(w[pi >> 5] & ((1u << (pi & 31)) - 1u));
-      for (int q = 0; q < (pi >> 5); ++q) rank += __popc(w[q]);
+      const size_t wi = (size_t)b * words + (pi >> 5);
+      const int rank = (int)pre[wi] + __popc(bm[wi] & ((1u << (pi & 31)) - 1u));
       entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(ph * KH + s);
     }
   }
@@ -225,7 +233,7 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
   bucket_scan_bins<<<1, 1024, 0, s>>>(b.bin_total, b.bin_off, b.tile_off, b.scalars, bp.nbins,
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bucket_scatter<<<grid, kThreads, sizeof(uint32_t) * P.nh * bp.words, s>>>(
+  bucket_scatter<<<grid, kThreads, 2 * sizeof(uint32_t) * P.nh * bp.words, s>>>(
       sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.G, P.k, P.nh,
       bp.rows_per_chunk, bp.nchunk, bp.words);
   if ((e = hipGetLastError()) != hipSuccess) return e;
