@@ -9,7 +9,8 @@
 // P_j is rebuilt from the forward's per-row log2-sum-exp (lse2, such that
 // P_j = 2^(scale log2(e) q.k_j - lse2)), so no softmax statistics are
 // recomputed. fp32 vector arithmetic throughout (4 lanes per query or key,
-// 32 head-dim elements each); inputs bf16 or fp32.
+// 32 head-dim elements each); this is the path for fp32 inputs (bf16 inputs
+// take the matrix-core kernels of bwd_bf16.hip, after bwd_delta below).
 //   * dK, dV: key-stationary. One workgroup owns 64 keys of one block and
 //     one KV head and walks every query that attends to them: the block's
 //     routed history entries (the bucketed lists) and the causal rows of
@@ -354,14 +355,19 @@ hipError_t run(const Prob& P, const Blocks& Tb, const BucketPlan& bp, const Buck
 hipError_t launch_backward(const Prob& P, const Blocks& T, const BucketPlan& bp,
                            const BucketBufs& bb, const void* q, const void* k, const void* v,
                            const void* o, const float* lse2, const void* dout, void* dq, void* dk,
-                           void* dv, float* delta, float* dq_acc, hipStream_t s) {
-  if (P.dtype == MOBA_DTYPE_BF16)
-    return run<uint16_t>(P, T, bp, bb, (const uint16_t*)q, (const uint16_t*)k,
-                         (const uint16_t*)v, (const uint16_t*)o, lse2, (const uint16_t*)dout,
-                         (uint16_t*)dq, (uint16_t*)dk, (uint16_t*)dv, delta, dq_acc, s);
+                           void* dv, const BwdScratch& w, hipStream_t s) {
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    const int64_t nph = P.Nq * P.Hq;
+    bwd_delta<uint16_t><<<(unsigned)ceil_div(nph * kSub, 256), 256, 0, s>>>(
+        (const uint16_t*)o, (const uint16_t*)dout, w.delta, nph);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    return launch_backward_bf16(P, T, bp, bb, q, k, v, lse2, dout, w.delta, w.kt, w.part_dq, dq,
+                                dk, dv, s);
+  }
   return run<float>(P, T, bp, bb, (const float*)q, (const float*)k, (const float*)v,
                     (const float*)o, lse2, (const float*)dout, (float*)dq, (float*)dk, (float*)dv,
-                    delta, dq_acc, s);
+                    w.delta, w.dq_acc, s);
 }
 
 }  // namespace moba

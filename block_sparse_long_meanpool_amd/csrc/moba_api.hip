@@ -130,7 +130,7 @@ size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 struct Layout {
   size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
-      part_lse, part_o, vt, delta, dq_acc, total;
+      part_lse, part_o, vt, delta, dq_acc, part_dq, kt, total;
 };
 
 // Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
@@ -157,7 +157,8 @@ void take_tables(const Prob& P, Layout& L, size_t& off) {
 }
 
 // Backward workspace: tables, block means, gate, selection, buckets, then the
-// fp32 row terms D = dO.O and the dq accumulator.
+// fp32 row terms D = dO.O and, for fp32 inputs, the dq accumulator; for bf16
+// inputs, the per-slot dq partials and the transposed K copy.
 Layout plan_ws_bwd(const Prob& P) {
   Layout L{};
   size_t off = 0;
@@ -181,7 +182,12 @@ Layout plan_ws_bwd(const Prob& P) {
   L.tile_map = take(sizeof(int32_t) * (size_t)bp.max_tiles);
   L.entries = take(sizeof(uint32_t) * (size_t)bp.max_entries);
   L.delta = take(sizeof(float) * (size_t)(P.Nq * P.Hq));
-  L.dq_acc = take(sizeof(float) * (size_t)(P.Nq * P.Hq) * P.d);
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    L.part_dq = take(sizeof(float) * (size_t)(P.Nq * P.Hq) * P.KH * P.d);
+    L.kt = take(vt_bytes(P));
+  } else {
+    L.dq_acc = take(sizeof(float) * (size_t)(P.Nq * P.Hq) * P.d);
+  }
   L.total = off;
   return L;
 }
@@ -462,8 +468,15 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   const BucketBufs bb = bucket_bufs(workspace, L);
   hipError_t e = launch_bucket(P, T, bp, sel, bb, s);
   if (e != hipSuccess) return hip_fail(e, "moba_bucket");
-  e = launch_backward(P, T, bp, bb, q, k, v, o, lse, dout, dq, dk, dv,
-                      at<float>(workspace, L.delta), at<float>(workspace, L.dq_acc), s);
+  BwdScratch w{};
+  w.delta = at<float>(workspace, L.delta);
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    w.part_dq = at<float>(workspace, L.part_dq);
+    w.kt = at<void>(workspace, L.kt);
+  } else {
+    w.dq_acc = at<float>(workspace, L.dq_acc);
+  }
+  e = launch_backward(P, T, bp, bb, q, k, v, o, lse, dout, dq, dk, dv, w, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "moba_backward");
 }
 

@@ -123,14 +123,27 @@ hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const
                             const void* V, const void* Vt, const void* part_o,
                             const float* part_lse, void* O, float* lse_out, hipStream_t s);
 
-// Backward with the selection held fixed (bwd.hip): dq [Nq][Hq][d], dk and dv
+// Backward with the selection held fixed: dq [Nq][Hq][d], dk and dv
 // [N][Hkv][d] in the input dtype from o, lse2 (the forward's lse_out) and
-// dout. delta [Nq][Hq] and dq_acc [Nq][Hq][d] (fp32) are scratch; bp/bb must
-// hold the bucketed selection of the same problem.
+// dout; bp/bb must hold the bucketed selection of the same problem. Scratch:
+// delta [Nq][Hq] fp32 always; fp32 inputs (vector kernels, bwd.hip) use
+// dq_acc [Nq][Hq][d] fp32; bf16 inputs (matrix-core kernels, bwd_bf16.hip)
+// use kt (vt_pack layout of K) and part_dq [Nq][Hq][k-1][d] fp32.
+struct BwdScratch {
+  float* delta;
+  float* dq_acc;
+  void* kt;
+  float* part_dq;
+};
 hipError_t launch_backward(const Prob& P, const Blocks& T, const BucketPlan& bp,
                            const BucketBufs& bb, const void* q, const void* k, const void* v,
                            const void* o, const float* lse2, const void* dout, void* dq, void* dk,
-                           void* dv, float* delta, float* dq_acc, hipStream_t s);
+                           void* dv, const BwdScratch& w, hipStream_t s);
+hipError_t launch_backward_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                                const BucketBufs& bb, const void* q, const void* k, const void* v,
+                                const float* lse2, const void* dout, const float* delta,
+                                void* kt, float* part_dq, void* dq, void* dk, void* dv,
+                                hipStream_t s);
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);

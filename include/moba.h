@@ -181,9 +181,11 @@ MOBA_API int moba_select_varlen(const moba_problem_t *p, int64_t nseq,
  *     get gradients only through the attended pairs (PaperTrace section
  *     5.3); the selection is recomputed from q and k exactly as in the
  *     forward pass. Workspace: moba_backward_workspace_size(p).
- * Numerics: fp32 arithmetic on the vector units (not the matrix cores);
- * weights are rebuilt from lse, and dq sums its per-block pieces with fp32
- * atomics (so the last bits of dq may vary between runs).
+ * Numerics: weights are rebuilt from lse. bf16 inputs run on the matrix
+ * cores (fp32 accumulation, the weights P and dZ = P (dP - D) rounded to
+ * bf16 as operands); dq sums per-slot partials, so results are
+ * deterministic. fp32 inputs run in fp32 on the vector units and sum dq
+ * with atomics (the last bits of dq may vary between runs).
  */
 MOBA_API int moba_prefill_train(const moba_problem_t *p, const void *q, const void *k,
                                 const void *v, void *o, float *lse, void *workspace,

@@ -427,6 +427,8 @@ BWD = [
     (900, 6, 3, 96, 4, "bf16", 0),     # B not a multiple of 64, G = 2
     (600, 4, 1, 128, 1, "bf16", 0),    # own block only
     (800, 8, 2, 64, 4, "bf16", 1),     # group-shared routing
+    (3072, 4, 1, 512, 3, "bf16", 0),   # G = 4, several query chunks and key tiles per block
+    (2300, 4, 2, 200, 5, "bf16", 0),   # key tiles with ragged 32-key groups, partial last block
 ]
 
 
@@ -456,3 +458,17 @@ def test_backward_matches_oracle(N, Hq, Hkv, B, topk, dtype, routing):
     worst = [_grad_close(to_np(dq), rq, dtype, "dq"), _grad_close(to_np(dk), rk, dtype, "dk"),
              _grad_close(to_np(dv), rv, dtype, "dv")]
     print(f"backward {N},{Hq},{Hkv},{B},{topk},{dtype},{routing}: max err / max|g| {worst}")
+
+
+def test_backward_bf16_is_deterministic():
+    """The bf16 backward sums dq from per-slot partials (no atomics), so two
+    runs on the same inputs agree bit for bit."""
+    N, Hq, Hkv, B, topk = 1500, 4, 2, 128, 4
+    _, _, _, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=77, dtype="bf16")
+    o, lse = moba.prefill_train(tq, tk, tv, B, topk, 0.09)
+    gen = torch.Generator(device="cpu").manual_seed(3)
+    dout = torch.randn(tq.shape, generator=gen).to(tq.dtype).to(DEV)
+    a = moba.backward(tq, tk, tv, o, lse, dout, B, topk, 0.09)
+    b = moba.backward(tq, tk, tv, o, lse, dout, B, topk, 0.09)
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)
