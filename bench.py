@@ -104,6 +104,40 @@ def cpu_baseline(w, q, k, v, rows_wanted):
     }
 
 
+def backward_leg():
+    """Training leg on the 32K layer: forward with row statistics, then the
+    backward pass (each the mean of 5 calls)."""
+    wb = synth.CONFIGS["c3"]
+    bq, bk, bv = (to_dev(a) for a in synth.make_qkv(wb, "bf16"))
+    gen = torch.Generator(device="cpu").manual_seed(1)
+    dout = torch.randn(bq.shape, generator=gen).to(torch.bfloat16).to(bq.device)
+    o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
+    moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
+    torch.cuda.synchronize()
+    e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
+    reps = 5
+    e0.record()
+    for _ in range(reps):
+        o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
+    e1.record()
+    for _ in range(reps):
+        moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
+    e2.record()
+    torch.cuda.synchronize()
+    fms, bms = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
+    bown, bhist = pair_counts(wb)
+    pairs = wb.Hq * (bown + bhist)
+    backward = {"workload": f"{wb.name}: N={wb.N} Hq={wb.Hq} Hkv={wb.Hkv} d={wb.d} B={wb.B} "
+                            f"topk={wb.k}, bf16",
+                "forward_train_ms": fms, "backward_ms": bms,
+                "backward_tflops": 10.0 * wb.d * pairs / (bms / 1e3) / 1e12,
+                "note": "mean of 5 calls; matrix cores, bf16 operands, fp32 accumulation; "
+                        "the backward call recomputes the selection and its buckets; "
+                        "FLOP = 5 products of 2d per attended pair"}
+    del bq, bk, bv, dout, o_b, lse_b
+    return backward
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -121,6 +155,8 @@ def main():
                     help="skip the training leg (forward with statistics + backward) on the 32K layer")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the group-shared routing leg and the routing-statistics timing")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="only run the training leg and print its JSON object")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel over this many MiB (hardware-counter "
                          "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
@@ -140,6 +176,10 @@ def main():
         torch.cuda.synchronize()
         assert torch.equal(src, dst)
         print(json.dumps({"copy_bytes": nbytes}), flush=True)
+        return
+
+    if args.backward_only:
+        print(json.dumps({"backward": backward_leg()}), flush=True)
         return
 
     w = synth.CONFIGS[args.config]
@@ -271,34 +311,7 @@ def main():
 
     backward = None
     if not args.no_backward and dtype == "bf16":
-        wb = synth.CONFIGS["c3"]
-        bq, bk, bv = (to_dev(a) for a in synth.make_qkv(wb, "bf16"))
-        gen = torch.Generator(device="cpu").manual_seed(1)
-        dout = torch.randn(bq.shape, generator=gen).to(torch.bfloat16).to(bq.device)
-        o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
-        moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
-        torch.cuda.synchronize()
-        e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-        reps = 5
-        e0.record()
-        for _ in range(reps):
-            o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
-        e1.record()
-        for _ in range(reps):
-            moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
-        e2.record()
-        torch.cuda.synchronize()
-        fms, bms = e0.elapsed_time(e1) / reps, e1.elapsed_time(e2) / reps
-        bown, bhist = pair_counts(wb)
-        pairs = wb.Hq * (bown + bhist)
-        backward = {"workload": f"{wb.name}: N={wb.N} Hq={wb.Hq} Hkv={wb.Hkv} d={wb.d} B={wb.B} "
-                                f"topk={wb.k}, bf16",
-                    "forward_train_ms": fms, "backward_ms": bms,
-                    "backward_tflops": 10.0 * wb.d * pairs / (bms / 1e3) / 1e12,
-                    "note": "mean of 5 calls; matrix cores, bf16 operands, fp32 accumulation; "
-                            "the backward call recomputes the selection and its buckets; "
-                            "FLOP = 5 products of 2d per attended pair"}
-        del bq, bk, bv, dout, o_b, lse_b
+        backward = backward_leg()
 
     cpu = None
     if not args.no_cpu_baseline:

@@ -56,11 +56,15 @@ __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r &
 // bits 2 and 3 puts the 8 rows a lane contracts over into one 16-byte run.
 __device__ inline int perm32(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
 
-// Row-major [rows][128] bf16 tiles keep 16-byte chunk c of row r at c ^ (r & 15);
-// transposed [128][64] tiles keep chunk c of row d at c ^ (d & 7) ^ ((d >> 3) & 1).
-// Either way the 16 lanes of one ds_read_b128 cycle hit distinct bank quads.
+// Row-major [rows][128] bf16 tiles keep 16-byte chunk c of row r at
+// c ^ (r & 15): the 16 lanes of one ds_read_b128 cycle (16 rows, one chunk)
+// hit distinct bank quads. Transposed [128][64] tiles (128-byte rows, two per
+// bank line) keep chunk c of row d at c ^ ((d >> 1) & 7) ^ ((d >> 4) & 7):
+// 16 consecutive rows read at one chunk spread over all 16 bank quads, and
+// the staging writes (rows 8 apart, 32 lanes per pass) over all 8 quads of
+// their half, two lanes each.
 __device__ inline int rm_swz(int r, int c) { return c ^ (r & 15); }
-__device__ inline int tr_swz(int d, int c) { return c ^ (d & 7) ^ ((d >> 3) & 1); }
+__device__ inline int tr_swz(int d, int c) { return c ^ ((d >> 1) & 7) ^ ((d >> 4) & 7); }
 __device__ inline bf16x8 rm_read(const uint16_t* t, int r, int c) {
   return as_b8(*reinterpret_cast<const uint4*>(t + r * kD + (rm_swz(r, c) << 3)));
 }
@@ -68,12 +72,12 @@ __device__ inline bf16x8 tr_read(const uint16_t* t, int d, int c) {
   return as_b8(*reinterpret_cast<const uint4*>(t + d * 64 + (tr_swz(d, c) << 3)));
 }
 
-__device__ inline uint32_t pack_bf16(float a, float b) {
-  auto rne = [](float x) {
-    uint32_t u = __float_as_uint(x);
-    return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
-  };
-  return rne(a) | (rne(b) << 16);
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t pack_bf16(float a, float b) {  // round to nearest even
+  bf16x2 v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ inline bf16x8 to_b8(const float* x) {  // 8 consecutive values
   uint4 u;
@@ -82,6 +86,14 @@ __device__ inline bf16x8 to_b8(const float* x) {  // 8 consecutive values
   u.z = pack_bf16(x[4], x[5]);
   u.w = pack_bf16(x[6], x[7]);
   return as_b8(u);
+}
+
+// 16-byte load of element idx, or zeros when !ok. The load itself is
+// unconditional (element 0 stands in), so it stays one dwordx4 access
+// instead of being split and branched around.
+__device__ inline uint4 ld16_or_zero(const uint16_t* __restrict__ base, int64_t idx, bool ok) {
+  const uint4 u = *reinterpret_cast<const uint4*>(base + (ok ? idx : 0));
+  return ok ? u : make_uint4(0, 0, 0, 0);
 }
 
 // ===========================================================================
@@ -97,75 +109,114 @@ struct QChunk {
   uint16_t* dr;   // [64][128] dO rows
   uint16_t* qt;   // [128][64] Q^T, rows permuted per 32-group
   uint16_t* dt;   // [128][64] dO^T
-  float* lse;     // [64] log2-sum-exp (+inf: absent query)
+  float* lse;     // [64] log2-sum-exp
   float* dd;      // [64] D = dO.o
   int32_t* lim;   // [64] last visible key (relative to the block start), -1 none
 };
 
-// Source of chunk query qi: its (row, head) index ph (-1: absent) and the
-// last key of the block it sees.
+// Source of chunk query idx, as a table word: a history entry's slot code
+// (row-head * (k-1) + slot, >= 0) is stored as -2 - code, an own-block pair
+// as (r << 6) | i with r its row's offset from the block's first query row
+// and i < G <= 64 its head inside the KV head's group, an absent query as -1. The history codes are stored raw (the
+// division by k-1 happens when the chunk is staged) so nothing in the
+// compute loop waits on the entry list.
 struct QSrc {
   const uint32_t* entries;
-  int64_t e0, nhq, own0, total;
-  int KH, G, Hq, g;
-  int64_t qstart, qpos, bstart;
-  __device__ inline void at(int64_t idx, int64_t& ph, int32_t& lim) const {
-    if (idx < nhq) {
-      ph = (int64_t)(entries[e0 + idx] / (uint32_t)KH);
-      lim = 0x7FFFFFFF;  // a history query sees the whole block
-    } else if (idx < total) {
-      const int64_t pi = own0 + (idx - nhq);
-      const int64_t r = pi / G;
-      ph = (qstart + r) * Hq + (int64_t)g * G + (int)(pi % G);
-      lim = (int32_t)(qpos + r - bstart);
-    } else {
-      ph = -1;
-      lim = -1;
+  int64_t e0;
+  int nhq, own0, total;  // history entries, first own pair, all queries
+  int G;
+  // The entry id is loaded here; the word is formed only in `word`, after
+  // the chunk's compute, so the load's latency overlaps the matrix work.
+  // Branch-free (a branch here makes the compiler form the word, and wait
+  // for the load, right away): the index is clamped into the list, and a
+  // list-less launch passes a valid one-element stand-in.
+  __device__ inline uint32_t load(int idx) const {
+    const int i = idx < nhq ? idx : nhq - 1;
+    return entries[e0 + (i > 0 ? i : 0)];
+  }
+  __device__ inline int64_t word(int idx, uint32_t raw) const {
+    if (idx < nhq) return -2 - (int64_t)raw;
+    if (idx < total) {
+      const uint32_t pi = (uint32_t)(own0 + (idx - nhq));
+      const uint32_t r = pi / (uint32_t)G;
+      return ((int64_t)r << 6) | (int64_t)(pi - r * (uint32_t)G);
     }
+    return -1;
   }
 };
 
-// Per thread: 2 staging tasks of (tensor, 4 consecutive queries, 8 dims).
+// Decode a table word: row-head index (-1 absent) and last visible key.
+struct Dec {
+  int KH, Hq, qrel, head0;  // head0 = first query head of the KV head's group
+  int64_t qstart;
+};
+
+__device__ inline int64_t decode(int64_t w, const Dec& dc, int32_t& lim) {
+  if (w <= -2) {
+    lim = 0x7FFFFFFF;  // a history query sees the whole block
+    return (int64_t)((uint32_t)(-2 - w) / (uint32_t)dc.KH);
+  }
+  if (w < 0) {
+    lim = -1;
+    return -1;
+  }
+  const int r = (int)(w >> 6);  // own row: offset r, head head0 + (w & 63)
+  lim = dc.qrel + r;
+  return (dc.qstart + r) * dc.Hq + dc.head0 + (int)(w & 63);
+}
+
+// Per thread: 2 staging tasks of (tensor, 4 consecutive queries, 8 dims);
+// threads < 64 also carry one query's lse, D and key limit.
 struct Stage {
   uint4 v[2][4];
   float lse, dd;
   int32_t lim;
 };
 
-__device__ inline void stage_load(Stage& st, const QSrc& src, int64_t base,
+// Chunk query table [64] of words, filled two chunks ahead by the first 64
+// threads: the entry id is loaded before a chunk's compute, the word formed
+// and stored after it.
+struct TabFill {
+  int idx;
+  uint32_t raw;
+};
+__device__ inline void fill_load(TabFill& f, const QSrc& src, int base) {
+  f.idx = base + (int)threadIdx.x;  // every thread loads (clamped), the first 64 store
+  f.raw = src.load(f.idx);
+}
+__device__ inline void fill_store(const TabFill& f, const QSrc& src, int64_t* tab) {
+  if (threadIdx.x < kQC) tab[threadIdx.x] = src.word(f.idx, f.raw);
+}
+
+__device__ inline void stage_load(Stage& st, const int64_t* tab, const Dec& dc,
                                   const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
                                   const float* __restrict__ lse2, const float* __restrict__ delta) {
   const int tid = threadIdx.x;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    const int task = tid + k * kKThreads;  // 0..511
-    const int tensor = task >> 8, q4 = (task >> 4) & 15, c = task & 15;
-    const uint16_t* T = tensor ? dO : Q;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      int64_t ph;
-      int32_t lim;
-      src.at(base + 4 * q4 + i, ph, lim);
-      st.v[k][i] = ph >= 0 ? *reinterpret_cast<const uint4*>(T + ph * kD + 8 * c)
-                           : make_uint4(0, 0, 0, 0);
-    }
-  }
   if (tid < kQC) {
-    int64_t ph;
-    src.at(base + tid, ph, st.lim);
-    st.lse = ph >= 0 ? lse2[ph] : INFINITY;
-    st.dd = ph >= 0 ? delta[ph] : 0.f;
+    // an absent query has lim = -1, which masks all its weights, so its lse
+    // and D may be any finite values: row 0's stand in (no select on them)
+    const int64_t ph = decode(tab[tid], dc, st.lim);
+    const int64_t pc = ph >= 0 ? ph : 0;
+    st.lse = lse2[pc];
+    st.dd = delta[pc];
+  }
+  const int q4 = (tid >> 4) & 15, c = tid & 15;  // both tasks: same queries, Q then dO
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    int32_t lim;
+    const int64_t ph = decode(tab[4 * q4 + i], dc, lim);
+    st.v[0][i] = ld16_or_zero(Q, ph * kD + 8 * c, ph >= 0);
+    st.v[1][i] = ld16_or_zero(dO, ph * kD + 8 * c, ph >= 0);
   }
 }
 
 __device__ inline void stage_store(const Stage& st, QChunk b) {
   const int tid = threadIdx.x;
+  const int q4 = (tid >> 4) & 15, c = tid & 15;
 #pragma unroll
   for (int k = 0; k < 2; ++k) {
-    const int task = tid + k * kKThreads;
-    const int tensor = task >> 8, q4 = (task >> 4) & 15, c = task & 15;
-    uint16_t* rm = tensor ? b.dr : b.qr;
-    uint16_t* tr = tensor ? b.dt : b.qt;
+    uint16_t* rm = k ? b.dr : b.qr;
+    uint16_t* tr = k ? b.dt : b.qt;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int q = 4 * q4 + i;
@@ -174,17 +225,17 @@ __device__ inline void stage_store(const Stage& st, QChunk b) {
     // transposed: 8 dims x 4 consecutive (permuted) positions, 8 bytes each
     const int q0 = 4 * q4;
     const int pos = 32 * (q0 >> 5) + perm32(q0 & 31);  // positions pos..pos+3
-    const uint32_t* w0 = reinterpret_cast<const uint32_t*>(&st.v[k][0]);
-    const uint32_t* w1 = reinterpret_cast<const uint32_t*>(&st.v[k][1]);
-    const uint32_t* w2 = reinterpret_cast<const uint32_t*>(&st.v[k][2]);
-    const uint32_t* w3 = reinterpret_cast<const uint32_t*>(&st.v[k][3]);
+    const uint32_t w0[4] = {st.v[k][0].x, st.v[k][0].y, st.v[k][0].z, st.v[k][0].w};
+    const uint32_t w1[4] = {st.v[k][1].x, st.v[k][1].y, st.v[k][1].z, st.v[k][1].w};
+    const uint32_t w2[4] = {st.v[k][2].x, st.v[k][2].y, st.v[k][2].z, st.v[k][2].w};
+    const uint32_t w3[4] = {st.v[k][3].x, st.v[k][3].y, st.v[k][3].z, st.v[k][3].w};
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
       const int d = 8 * c + e;
-      const int sh = (e & 1) * 16;
-      const uint32_t a0 = (w0[e >> 1] >> sh) & 0xFFFFu, a1 = (w1[e >> 1] >> sh) & 0xFFFFu;
-      const uint32_t a2 = (w2[e >> 1] >> sh) & 0xFFFFu, a3 = (w3[e >> 1] >> sh) & 0xFFFFu;
-      uint2 out = make_uint2(a0 | (a1 << 16), a2 | (a3 << 16));
+      // byte selectors: low halves (e even) or high halves (e odd) of two words
+      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
+      const uint2 out = make_uint2(__builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel),
+                                   __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel));
       *reinterpret_cast<uint2*>(tr + d * 64 + (tr_swz(d, pos >> 3) << 3) + (pos & 7)) = out;
     }
   }
@@ -195,7 +246,7 @@ __device__ inline void stage_store(const Stage& st, QChunk b) {
   }
 }
 
-// grid: (n * ceil(B / 128), Hkv); 256 threads.
+// grid: 1D, a multiple of 8 covering Hkv * n * ceil(B / 128) items; 256 threads.
 __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
@@ -204,14 +255,21 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
     const int32_t* __restrict__ qstart, const int32_t* __restrict__ qlen,
     const int32_t* __restrict__ qpos, const int32_t* __restrict__ bin_off,
     const uint32_t* __restrict__ entries, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
-    int Hq, int Hkv, int G, int KH, int64_t nh, int tiles_per_block, float scale) {
+    int Hq, int Hkv, int G, int KH, int64_t n, int64_t nh, int tiles_per_block, float scale) {
   __shared__ __align__(16) uint16_t s_qr[2][kQC * kD], s_dr[2][kQC * kD];
   __shared__ __align__(16) uint16_t s_qt[2][kD * kQC], s_dt[2][kD * kQC];
   __shared__ __align__(16) float s_lse[2][kQC], s_dd[2][kQC];
   __shared__ __align__(16) int32_t s_lim[2][kQC];
-  const int g = blockIdx.y;
-  const int64_t b = blockIdx.x / tiles_per_block;
-  const int kt = blockIdx.x % tiles_per_block;
+  __shared__ int64_t s_tab[2][kQC];
+  // Items w = (g * n + b) * tiles_per_block + kt. Workgroup i runs on XCD
+  // i % 8 and each XCD takes a contiguous range of items, so the key tiles
+  // of one (KV head, block), which stage the same query rows, share an L2.
+  const int64_t per = gridDim.x / 8;
+  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= (int64_t)Hkv * n * tiles_per_block) return;
+  const int kt = (int)(w % tiles_per_block);
+  const int64_t b = (w / tiles_per_block) % n;
+  const int g = (int)(w / ((int64_t)tiles_per_block * n));
   const int nk = blen[b];
   if (kt * kKeysWG >= nk) return;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
@@ -226,32 +284,29 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
     const int64_t off = ((key_first + (kvalid ? key_rel : 0)) * Hkv + g) * kD + 8 * h;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
-      const uint4 zk = kvalid ? *reinterpret_cast<const uint4*>(K + off + 16 * kk)
-                              : make_uint4(0, 0, 0, 0);
-      const uint4 zv = kvalid ? *reinterpret_cast<const uint4*>(V + off + 16 * kk)
-                              : make_uint4(0, 0, 0, 0);
+      const uint4 zk = ld16_or_zero(K, off + 16 * kk, kvalid);
+      const uint4 zv = ld16_or_zero(V, off + 16 * kk, kvalid);
       kb[kk] = as_b8(zk);
       vb[kk] = as_b8(zv);
     }
+    // complete before the chunk loop, whose counter waits then only cover
+    // the staging loads
+    __builtin_amdgcn_s_waitcnt(0);
   }
 
   QSrc src;
   src.entries = entries;
   src.e0 = b < nh ? bin_off[g * nh + b] : 0;
-  src.nhq = b < nh ? bin_off[g * nh + b + 1] - src.e0 : 0;
+  src.nhq = b < nh ? (int)(bin_off[g * nh + b + 1] - src.e0) : 0;
+  const int qrel = qpos[b] - bstart[b];  // first query row's position in the block
   // own rows before this key tile see none of its keys
-  const int64_t own_all = (int64_t)qlen[b] * G;
-  const int64_t first_row = (int64_t)kt * kKeysWG - (qpos[b] - bstart[b]);  // row of key kt*128
+  const int own_all = qlen[b] * G;
+  const int first_row = kt * kKeysWG - qrel;  // own row holding key kt * 128
   src.own0 = first_row > 0 ? first_row * G : 0;
   if (src.own0 > own_all) src.own0 = own_all;
   src.total = src.nhq + (own_all - src.own0);
-  src.KH = KH;
   src.G = G;
-  src.Hq = Hq;
-  src.g = g;
-  src.qstart = qstart[b];
-  src.qpos = qpos[b];
-  src.bstart = key_first;
+  const Dec dc{KH, Hq, qrel, g * G, (int64_t)qstart[b]};
 
   f32x16 dk[4], dv[4];
 #pragma unroll
@@ -260,16 +315,37 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
     zero(dv[db]);
   }
 
-  const int nchunks = (int)((src.total + kQC - 1) / kQC);
+  const int nchunks = (src.total + kQC - 1) / kQC;
   Stage st;
+  TabFill tf{0, 0u};
+  auto buf = [&](int i) {
+    return QChunk{s_qr[i], s_dr[i], s_qt[i], s_dt[i], s_lse[i], s_dd[i], s_lim[i]};
+  };
+  // Prologue: tables of chunks 0 and 1, chunk 0 staged in LDS buffer 0, chunk
+  // 1 in flight to the registers, table of chunk 2 in slot 0.
   if (nchunks > 0) {
-    stage_load(st, src, 0, Q, dO, lse2, delta);
-    stage_store(st, QChunk{s_qr[0], s_dr[0], s_qt[0], s_dt[0], s_lse[0], s_dd[0], s_lim[0]});
+    fill_load(tf, src, 0);
+    fill_store(tf, src, s_tab[0]);
+    fill_load(tf, src, kQC);
+    fill_store(tf, src, s_tab[1]);
+    __syncthreads();
+    stage_load(st, s_tab[0], dc, Q, dO, lse2, delta);
+    stage_store(st, buf(0));
+    if (nchunks > 1) stage_load(st, s_tab[1], dc, Q, dO, lse2, delta);
+    fill_load(tf, src, 2 * kQC);
+    __syncthreads();  // slot 0 is read by everyone; buffer 0 is complete
+    fill_store(tf, src, s_tab[0]);
+    __syncthreads();
   }
-  __syncthreads();
+  // Iteration t computes chunk t from LDS buffer t & 1; then stores chunk
+  // t + 1 (loaded into registers during iteration t - 1) into buffer
+  // (t + 1) & 1, issues the loads of chunk t + 2 (table slot t & 1) and
+  // stores the table of chunk t + 3 (entry ids loaded at the start) into slot
+  // (t + 1) & 1. The staging loads thus have a whole iteration of matrix work
+  // to land in; one barrier per chunk.
   for (int t = 0; t < nchunks; ++t) {
     const int cb = t & 1;
-    if (t + 1 < nchunks) stage_load(st, src, (int64_t)(t + 1) * kQC, Q, dO, lse2, delta);
+    fill_load(tf, src, (t + 3) * kQC);  // words past the last query are -1
     const uint16_t* qr = s_qr[cb];
     const uint16_t* dr = s_dr[cb];
     const uint16_t* qt = s_qt[cb];
@@ -298,8 +374,8 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int r = 4 * j + i;
-          const bool on = kvalid && key_rel <= mv[i];
-          const float pr = on ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2e, -lv[i])) : 0.f;
+          const float x = fmaf(s[r], sl2e, -lv[i]);
+          const float pr = __builtin_amdgcn_exp2f(key_rel <= mv[i] ? x : -INFINITY);
           p[r] = pr;
           ds[r] = pr * (dp[r] - dv4[i]);
         }
@@ -315,10 +391,9 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
         }
       }
     }
-    if (t + 1 < nchunks) {
-      const int nb = cb ^ 1;
-      stage_store(st, QChunk{s_qr[nb], s_dr[nb], s_qt[nb], s_dt[nb], s_lse[nb], s_dd[nb], s_lim[nb]});
-    }
+    if (t + 1 < nchunks) stage_store(st, buf(cb ^ 1));
+    if (t + 2 < nchunks) stage_load(st, s_tab[cb], dc, Q, dO, lse2, delta);
+    fill_store(tf, src, s_tab[cb ^ 1]);
     __syncthreads();
   }
   if (!kvalid) return;
@@ -454,8 +529,8 @@ __device__ inline void load_query(const uint16_t* __restrict__ Q, const uint16_t
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const int64_t i = ph * kD + 16 * kk + 8 * h;
-    qb[kk] = as_b8(valid ? *reinterpret_cast<const uint4*>(Q + i) : make_uint4(0, 0, 0, 0));
-    ob[kk] = as_b8(valid ? *reinterpret_cast<const uint4*>(dO + i) : make_uint4(0, 0, 0, 0));
+    qb[kk] = as_b8(ld16_or_zero(Q, i, valid));
+    ob[kk] = as_b8(ld16_or_zero(dO, i, valid));
   }
 }
 
@@ -477,7 +552,11 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_hist_bf16(
     const uint32_t* __restrict__ entries, float* __restrict__ part_dq, int Hkv, int B, int KH,
     int64_t nh, int64_t Bpad, int64_t ldk, float scale) {
   MOBA_DQ_TILES
-  const int64_t w = blockIdx.x;
+  // XCD-aware order (as in the forward): each XCD takes a contiguous range
+  // of tiles, so the tiles of one K/V block share its L2. The grid is a
+  // multiple of 8.
+  const int64_t per = gridDim.x / 8;
+  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (w >= scalars[1]) return;
   const int bin = tile_map[w];
   const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
@@ -521,11 +600,17 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_self_bf16(
     const int32_t* __restrict__ qstart, const int32_t* __restrict__ qlen,
     const int32_t* __restrict__ qpos, const int32_t* __restrict__ blo,
     const float* __restrict__ part_dq, uint16_t* __restrict__ dQ, int Hq, int Hkv, int G, int KH,
-    int tiles_per_block, int64_t Bpad, int64_t ldk, float scale) {
+    int64_t n, int tiles_per_block, int64_t Bpad, int64_t ldk, float scale) {
   MOBA_DQ_TILES
-  const int g = blockIdx.y;
-  const int64_t c = blockIdx.x / tiles_per_block;
-  const int tile = blockIdx.x % tiles_per_block;
+  // Items w = (g * n + c) * tiles_per_block + tile, a contiguous range per
+  // XCD (the grid is a multiple of 8), so the row tiles of one (KV head,
+  // block) share its L2 copy of K/V.
+  const int64_t per = gridDim.x / 8;
+  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= (int64_t)Hkv * n * tiles_per_block) return;
+  const int tile = (int)(w % tiles_per_block);
+  const int64_t c = (w / tiles_per_block) % n;
+  const int g = (int)(w / ((int64_t)tiles_per_block * n));
   const int64_t npairs = (int64_t)qlen[c] * G;
   const int64_t p0 = (int64_t)tile * kTileQ;
   if (p0 >= npairs) return;
@@ -589,22 +674,23 @@ hipError_t launch_backward_bf16(const Prob& P, const Blocks& T, const BucketPlan
   if (e != hipSuccess) return e;
   const int64_t Bpad = vt_padded_block(P.B), ldk = P.n * Bpad;
   const bool hist = P.nh > 0 && P.KH > 0;
+  auto grid8 = [](int64_t items) { return (unsigned)(ceil_div(items, 8) * 8); };
   if (hist && bp.max_tiles > 0) {
-    bwd_dq_hist_bf16<<<(unsigned)bp.max_tiles, kQThreads, 0, s>>>(
+    bwd_dq_hist_bf16<<<grid8(bp.max_tiles), kQThreads, 0, s>>>(
         Q, K, V, dO, lse2, delta, (const uint16_t*)kt, T.start, bb.tile_map, bb.tile_off,
         bb.bin_off, bb.scalars, bb.entries, part_dq, P.Hkv, P.B, P.KH, P.nh, Bpad, ldk, P.scale);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   const int key_tiles = (int)ceil_div(P.B, kKeysWG);
-  bwd_dkv_bf16<<<dim3((unsigned)(P.n * key_tiles), (unsigned)P.Hkv), kKThreads, 0, s>>>(
-      Q, K, V, dO, lse2, delta, T.start, T.len, T.qstart, T.qlen, T.qpos, bb.bin_off, bb.entries,
-      (uint16_t*)dk, (uint16_t*)dv, P.Hq, P.Hkv, P.G, P.KH > 0 ? P.KH : 1, hist ? P.nh : 0,
-      key_tiles, P.scale);
+  bwd_dkv_bf16<<<grid8(P.n * key_tiles * P.Hkv), kKThreads, 0, s>>>(
+      Q, K, V, dO, lse2, delta, T.start, T.len, T.qstart, T.qlen, T.qpos, bb.bin_off,
+      hist ? bb.entries : (const uint32_t*)T.start, (uint16_t*)dk, (uint16_t*)dv, P.Hq, P.Hkv,
+      P.G, P.KH > 0 ? P.KH : 1, P.n, hist ? P.nh : 0, key_tiles, P.scale);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   const int tpb = (int)ceil_div((int64_t)P.B * P.G, kTileQ);
-  bwd_dq_self_bf16<<<dim3((unsigned)(P.n * tpb), (unsigned)P.Hkv), kQThreads, 0, s>>>(
+  bwd_dq_self_bf16<<<grid8(P.n * tpb * P.Hkv), kQThreads, 0, s>>>(
       Q, K, V, dO, lse2, delta, (const uint16_t*)kt, T.start, T.qstart, T.qlen, T.qpos, T.lo,
-      part_dq, (uint16_t*)dq, P.Hq, P.Hkv, P.G, P.KH, tpb, Bpad, ldk, P.scale);
+      part_dq, (uint16_t*)dq, P.Hq, P.Hkv, P.G, P.KH, P.n, tpb, Bpad, ldk, P.scale);
   return hipGetLastError();
 }
 
