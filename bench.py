@@ -285,7 +285,39 @@ def main():
             cms = e0.elapsed_time(e1) / reps
             chunk["decode_step" if C == 1 else f"chunk_{C}"] = {
                 "query_rows": C, "cache_rows": w.N, "ms": cms, "tokens_per_s": C / (cms / 1e3)}
+            if C == 1:
+                o_recompute = oc.clone()
             del wsc, oc
+        # the same decode step on a decode cache: append the new row (its block
+        # means only when it completes a block; its V column), then the step
+        cache = moba.DecodeCache(w.N, w.Hq, w.Hkv, w.B, w.k, w.scale, device=tq.device)
+        cache.append(tk, tv, w.N - 1)
+        qd = tq[w.N - 1:].contiguous()
+        od = torch.empty_like(qd)
+        cache.rows = w.N - 1
+        cache.append(tk, tv, w.N)
+        wsd = moba.alloc_workspace(cache.workspace_size(1), tq.device)
+
+        def cached_step():
+            cache.rows = w.N - 1
+            cache.append(tk, tv, w.N)
+            cache.prefill(qd, tk, tv, out=od, workspace=wsd)
+
+        cached_step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 20
+        e0.record()
+        for _ in range(reps):
+            cached_step()
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        chunk["decode_step_cached"] = {
+            "query_rows": 1, "cache_rows": w.N, "ms": cms, "tokens_per_s": 1 / (cms / 1e3),
+            "matches_recompute": bool(torch.equal(od, o_recompute)),
+            "note": "moba_cache_append of the new row + moba_prefill_cached"}
+        del cache, wsd, od
 
     shared = None
     if not args.no_shared and dtype == "bf16":

@@ -41,6 +41,7 @@ EXPORTS = (
     "moba_prefill_varlen", "moba_select_varlen",
     "moba_routing_stats_workspace_size", "moba_routing_stats",
     "moba_chunk_workspace_size", "moba_prefill_chunk", "moba_select_chunk",
+    "moba_cache_bytes", "moba_cache_append", "moba_cached_workspace_size", "moba_prefill_cached",
     "moba_prefill_train", "moba_backward_workspace_size", "moba_backward",
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
@@ -101,6 +102,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_chunk_workspace_size": (sz, [P, i64]),
         "moba_prefill_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, sz, vp]),
+        "moba_cache_bytes": (sz, [P, i64]),
+        "moba_cache_append": (ctypes.c_int, [P, i64, i64, vp, vp, vp, vp]),
+        "moba_cached_workspace_size": (sz, [P, i64]),
+        "moba_prefill_cached": (ctypes.c_int, [P, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_routing_stats_workspace_size": (sz, [P]),
         "moba_routing_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_dense_workspace_size": (sz, [P]),
@@ -353,6 +358,73 @@ def backward(q, k, v, o, lse, dout, block_size, topk, scale=None, routing=MOBA_R
                            _stream(q.device))
     _ok(st, "moba_backward")
     return dq, dk, dv
+
+
+class DecodeCache:
+    """Decode cache of one sequence (moba_cache_*): the block means of its full
+    blocks and the packed V copy, kept current by ``append`` as rows arrive, so
+    that ``prefill`` (a chunk or decode step) does not recompute them from the
+    whole KV cache. k and v passed to both are the KV cache tensors
+    [capacity, Hkv, d] of which the first ``rows`` are valid."""
+
+    def __init__(self, capacity, num_q_heads, num_kv_heads, block_size, topk, scale=None,
+                 dtype=MOBA_DTYPE_BF16, routing=MOBA_ROUTING_PER_HEAD, head_dim=128,
+                 device="cuda"):
+        lib = load_library()
+        self.capacity = int(capacity)
+        self.Hq, self.Hkv, self.d = num_q_heads, num_kv_heads, head_dim
+        self.block_size, self.topk, self.scale = block_size, topk, scale
+        self.dtype, self.routing = dtype, routing
+        self.rows = 0
+        prob = self._problem(1)
+        nbytes = lib.moba_cache_bytes(ctypes.byref(prob), self.capacity)
+        if nbytes == 0:
+            raise MobaError(lib.moba_cache_append(ctypes.byref(prob), self.capacity, 0, None, None,
+                                                  None, None), "moba_cache_bytes")
+        self.buf = alloc_workspace(nbytes, device)
+
+    def _problem(self, rows):
+        return make_problem(rows, self.Hq, self.Hkv, self.d, self.block_size, self.topk,
+                            self.scale, self.dtype, self.routing)
+
+    def append(self, k, v, rows):
+        """Rows [self.rows, rows) of k and v are new: update the cache."""
+        lib = load_library()
+        _check_dev(k, v)
+        if k.shape[0] != self.capacity or v.shape != k.shape:
+            raise ValueError("k and v must be the [capacity, Hkv, d] KV cache tensors")
+        prob = self._problem(rows)
+        st = lib.moba_cache_append(ctypes.byref(prob), self.capacity, self.rows, k.data_ptr(),
+                                   v.data_ptr(), self.buf.data_ptr(), _stream(k.device))
+        _ok(st, "moba_cache_append")
+        self.rows = int(rows)
+
+    def workspace_size(self, q_rows):
+        """Workspace bytes of ``prefill`` for q_rows queries at the current length."""
+        prob = self._problem(self.rows)
+        return load_library().moba_cached_workspace_size(ctypes.byref(prob), int(q_rows))
+
+    def prefill(self, q, k, v, out=None, workspace=None):
+        """O for the queries q [C, Hq, d] of the last C of the first self.rows
+        positions (as ``prefill_chunk`` over k[:rows], v[:rows])."""
+        lib = load_library()
+        _check_dev(q, k, v)
+        prob = self._problem(self.rows)
+        C = q.shape[0]
+        if out is None:
+            out = torch.empty_like(q)
+        need = lib.moba_cached_workspace_size(ctypes.byref(prob), C)
+        if need == 0:
+            _ok(lib.moba_prefill_cached(ctypes.byref(prob), self.capacity, C, None, None, None,
+                                        None, None, None, 0, None), "moba_cached_workspace_size")
+        if workspace is None:
+            workspace = alloc_workspace(need, q.device)
+        st = lib.moba_prefill_cached(ctypes.byref(prob), self.capacity, C, q.data_ptr(),
+                                     k.data_ptr(), v.data_ptr(), self.buf.data_ptr(),
+                                     out.data_ptr(), workspace.data_ptr(), workspace.numel(),
+                                     _stream(q.device))
+        _ok(st, "moba_prefill_cached")
+        return out
 
 
 def chunk_workspace_size(prob: MobaProblem, q_rows: int) -> int:

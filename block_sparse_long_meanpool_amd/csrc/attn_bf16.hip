@@ -504,15 +504,16 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const _Float16* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ O, float* __restrict__ lse_out,
-    int Hq, int Hkv, int G, int64_t Bpad, int64_t ldv, int KH, int64_t n, int tiles_per_block,
-    float sl2e) {
+    int Hq, int Hkv, int G, int64_t Bpad, int64_t ldv, int KH, int64_t n, int64_t nqb,
+    int tiles_per_block, float sl2e) {
   MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   // Work items w = ((c' * Hkv) + g) * tiles_per_block + t' in order of
-  // blocks from the last, and inside a block heavier (later) row tiles first.
-  // Workgroup i runs on XCD i % 8 and each XCD takes a contiguous range of
-  // items, so the row tiles of one (block, KV head) share its L2 copy of K/V.
-  const int64_t items = n * Hkv * (int64_t)tiles_per_block;
+  // blocks from the last (only the last nqb blocks hold query rows), and
+  // inside a block heavier (later) row tiles first. Workgroup i runs on XCD
+  // i % 8 and each XCD takes a contiguous range of items, so the row tiles of
+  // one (block, KV head) share its L2 copy of K/V.
+  const int64_t items = nqb * Hkv * (int64_t)tiles_per_block;
   const int64_t per = gridDim.x / 8;  // the grid is a multiple of 8
   const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (w >= items) return;
@@ -660,7 +661,7 @@ hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPla
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
-  const int64_t ldv = P.n * Bpad;
+  const int64_t ldv = P.vt_blocks * Bpad;
   const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
   attn_hist_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
@@ -674,15 +675,16 @@ hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, 
                                  void* O, float* lse_out, hipStream_t s) {
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
-  const int64_t ldv = P.n * Bpad;
+  const int64_t ldv = P.vt_blocks * Bpad;
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kGroupQ);
-  const int64_t grid = ceil_div(P.n * tiles_per_block * P.Hkv, 8) * 8;
+  const int64_t nqb = query_blocks(P);
+  const int64_t grid = ceil_div(nqb * tiles_per_block * P.Hkv, 8) * 8;
   const bool merge = part_o != nullptr && P.KH > 0;
   attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.qstart, T.qlen,
       T.qpos, T.lo, merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr,
       (uint16_t*)O, lse_out, P.Hq,
-      P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, tiles_per_block, sl2e);
+      P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, nqb, tiles_per_block, sl2e);
   return hipGetLastError();
 }
 

@@ -222,7 +222,8 @@ __device__ inline double widen<double>(double x) {
   return x;
 }
 
-// Exact tier: one wave per 64 consecutive (row, head) pairs; each marked row
+// Exact tier: one wave per ppw (64, or 1 for a few rows) consecutive (row,
+// head) pairs; each marked row
 // (or, with all_rows, every row) is re-scored in fp64 — lane b handles blocks
 // b, b+64, ... reading the transposed block keys (coalesced) against q
 // staged in LDS — and selected by (value desc, index asc): each lane keeps a
@@ -236,16 +237,17 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
                                                   const int32_t* __restrict__ blo,
                                                   int32_t* __restrict__ sel,
                                                   float* __restrict__ margin, int64_t N, int Hq,
-                                                  int G, int k, int64_t nhp, int all_rows) {
+                                                  int G, int k, int64_t nhp, int all_rows,
+                                                  int ppw) {
   __shared__ double qs[kHeadDim];
   const int lane = threadIdx.x;
   const int KH = k - 1;
   const int64_t nph = N * Hq;
-  const int64_t ph0 = (int64_t)blockIdx.x * 64;
+  const int64_t ph0 = (int64_t)blockIdx.x * ppw;
   bool mine = false;
   {
     const int64_t ph = ph0 + lane;
-    if (ph < nph) {
+    if (lane < ppw && ph < nph) {
       const int64_t c = row_blk[ph / Hq], lo = blo[c];
       int32_t* out = sel + ph * k;
       if (c - lo > KH && KH > 0) {
@@ -496,11 +498,13 @@ template <typename T>
 hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff,
                       const double* kbarT, int64_t nhp, int32_t* sel, float* margin,
                       hipStream_t s) {
-  const unsigned grid = (unsigned)ceil_div(P.Nq * Hq_eff, 64);
+  // a few rows: one wave per (row, head) pair so they run side by side
+  const int ppw = P.Nq <= kDecodeRows ? 1 : 64;
+  const unsigned grid = (unsigned)ceil_div(P.Nq * Hq_eff, ppw);
   const int need = P.KH + 1;
 #define MOBA_REFINE(KM)                                                                    \
   gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.Nq,  \
-                                         Hq_eff, G_eff, P.k, nhp, 1)
+                                         Hq_eff, G_eff, P.k, nhp, 1, ppw)
   if (need <= 4) MOBA_REFINE(4);
   else if (need <= 8) MOBA_REFINE(8);
   else if (need <= 12) MOBA_REFINE(12);
@@ -515,7 +519,8 @@ hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16
                      const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
                      hipStream_t s) {
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
-  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
+  // workgroups walk blocks from the last; a chunk's query rows sit in its last blocks
+  dim3 grid((unsigned)(query_blocks(P) * tiles_per_block), (unsigned)P.Hkv);
   gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.qstart,
                                                 T.qlen, T.lo, sel, P.Hq, P.G, P.k, P.n, P.nh,
                                                 tiles_per_block);
@@ -523,7 +528,8 @@ hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16
   if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
   const unsigned refine_grid = (unsigned)ceil_div(P.Nq * P.Hq, 64);
   gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, T.row_blk, T.lo,
-                                                      sel, nullptr, P.Nq, P.Hq, P.G, P.k, nhp, 0);
+                                                      sel, nullptr, P.Nq, P.Hq, P.G, P.k, nhp, 0,
+                                                      64);
   return hipGetLastError();
 }
 
@@ -595,7 +601,8 @@ hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double*
   }
   if (P.dtype == MOBA_DTYPE_F32)
     return refine_all<float>(P, T, (const float*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
-  if (exact_all)
+  // a few rows (decode): the exact tier alone, one wave per (row, head)
+  if (exact_all || P.Nq <= kDecodeRows)
     return refine_all<uint16_t>(P, T, (const uint16_t*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
   // list length: the k-1 kept blocks plus the best one left out
   const int need = P.KH + 1;

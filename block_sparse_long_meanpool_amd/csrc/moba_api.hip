@@ -67,6 +67,7 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   P->nseq = 1;
   P->n = (P->N + P->B - 1) / P->B;
   P->nh = P->n - 1;
+  P->vt_blocks = P->n;
   P->hist_rows = 0;
   for (int64_t c = 0; c < P->n; ++c) {
     const int64_t rows = P->N - c * P->B < P->B ? P->N - c * P->B : P->B;
@@ -121,6 +122,7 @@ int make_prob_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu, P
     P->n += nb;
   }
   P->nh = P->n - 1;
+  P->vt_blocks = P->n;
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
   return MOBA_OK;
 }
@@ -130,7 +132,7 @@ size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 struct Layout {
   size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
-      part_lse, part_o, vt, delta, dq_acc, part_dq, kt, total;
+      part_lse, part_o, vt, dec_part, delta, dq_acc, part_dq, kt, total;
 };
 
 // Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
@@ -192,8 +194,10 @@ Layout plan_ws_bwd(const Prob& P) {
   return L;
 }
 
-// Workspace layout; `full` = prefill (all stages), else select only.
-Layout plan_ws(const Prob& P, bool full) {
+// Workspace layout; `full` = prefill (all stages), else select only;
+// `cached` = block means and packed V come from a decode cache (no mean
+// partials, no V^T copy).
+Layout plan_ws(const Prob& P, bool full, bool cached = false) {
   Layout L{};
   size_t off = 0;
   auto take = [&](size_t bytes) {
@@ -204,7 +208,7 @@ Layout plan_ws(const Prob& P, bool full) {
   take_tables(P, L, off);
   const int splits = meanpool_splits(P);
   L.kbar = take(sizeof(double) * (size_t)(P.Hkv * P.nh * P.d));
-  L.mp_part = take(sizeof(double) * (size_t)splits * P.nh * P.Hkv * P.d);
+  L.mp_part = cached ? off : take(sizeof(double) * (size_t)splits * P.nh * P.Hkv * P.d);
   L.gate = take(gate_scratch_bytes(P));
   if (full) {
     const BucketPlan bp = plan_bucket(P);
@@ -216,13 +220,48 @@ Layout plan_ws(const Prob& P, bool full) {
     L.scalars = take(sizeof(int32_t) * 4);
     L.tile_map = take(sizeof(int32_t) * (size_t)bp.max_tiles);
     L.entries = take(sizeof(uint32_t) * (size_t)bp.max_entries);
-    const size_t slots = (size_t)(P.Nq * P.Hq) * (size_t)P.KH;
-    L.part_lse = take(sizeof(float) * slots);
-    L.part_o = take(part_elem_bytes(P) * slots * P.d);
-    L.vt = take(vt_bytes(P));
+    if (P.Nq <= kDecodeRows) {  // few rows: split-K partials instead of the tiled path
+      L.part_lse = L.part_o = L.vt = off;
+      L.dec_part = take(decode_part_bytes(P));
+    } else {
+      const size_t slots = (size_t)(P.Nq * P.Hq) * (size_t)P.KH;
+      L.part_lse = take(sizeof(float) * slots);
+      L.part_o = take(part_elem_bytes(P) * slots * P.d);
+      L.vt = cached ? off : take(vt_bytes(P));
+    }
   }
   L.total = off;
   return L;
+}
+
+// A decode cache seen by one call: means of the cache's full blocks
+// [Hkv][nhc][d] and (bf16) the packed V^T of its capacity in blocks.
+struct CacheView {
+  const double* kbar;
+  int64_t nhc;
+  const void* vt;
+  int64_t vt_blocks;
+};
+
+// Cache layout for `capacity` rows: kbar [Hkv][ncap - 1][d] fp64, then V^T
+// [Hkv][d][ncap * Bpad] for bf16.
+struct CacheLayout {
+  int64_t ncap, nhc;
+  size_t kbar, vt, total;
+};
+CacheLayout cache_layout(const Prob& P, int64_t capacity) {
+  CacheLayout C{};
+  C.ncap = (capacity + P.B - 1) / P.B;
+  C.nhc = C.ncap > 0 ? C.ncap - 1 : 0;
+  size_t off = 0;
+  C.kbar = off;
+  off = align_up(off + sizeof(double) * (size_t)P.Hkv * C.nhc * P.d);
+  C.vt = off;
+  if (P.dtype == MOBA_DTYPE_BF16)
+    off = align_up(off + sizeof(uint16_t) * (size_t)P.Hkv * P.d *
+                             (size_t)(C.ncap * vt_padded_block(P.B)));
+  C.total = off;
+  return C;
 }
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -282,13 +321,17 @@ int record(void* const* events, int i, hipStream_t s) {
 
 // Tables, block means, gate + top-k. cu: device row offsets or NULL.
 int run_select(const Prob& P, const int64_t* cu, const void* q, const void* k, int32_t* sel,
-               void* ws, const Layout& L, hipStream_t s, void* const* events) {
+               void* ws, const Layout& L, hipStream_t s, void* const* events,
+               const CacheView* cv = nullptr) {
   int rc;
   const Blocks T = tables(ws, L);
   hipError_t e = launch_tables(P, cu, T, s);
   if (e != hipSuccess) return hip_fail(e, "block tables");
-  e = launch_meanpool(P, T, k, at<double>(ws, L.kbar), at<double>(ws, L.mp_part),
-                      meanpool_splits(P), s);
+  if (cv)
+    e = launch_kbar_gather(cv->kbar, cv->nhc, at<double>(ws, L.kbar), P.nh, P.Hkv, P.d, s);
+  else
+    e = launch_meanpool(P, T, k, at<double>(ws, L.kbar), at<double>(ws, L.mp_part),
+                        meanpool_splits(P), s);
   if (e != hipSuccess) return hip_fail(e, "moba_meanpool");
   if ((rc = record(events, 1, s))) return rc;
   e = launch_gate_topk(P, T, q, at<double>(ws, L.kbar), at<void>(ws, L.gate), sel, s);
@@ -297,14 +340,23 @@ int run_select(const Prob& P, const int64_t* cu, const void* q, const void* k, i
 }
 
 // The whole path on prepared problem and workspace.
-int run_prefill(const Prob& P, const int64_t* cu, const void* q, const void* k, const void* v,
+int run_prefill(const Prob& P0, const int64_t* cu, const void* q, const void* k, const void* v,
                 void* o, void* workspace, const Layout& L, hipStream_t s, void* const* events,
-                float* lse = nullptr) {
+                float* lse = nullptr, const CacheView* cv = nullptr) {
   int rc;
+  Prob P = P0;
+  if (cv) P.vt_blocks = cv->vt_blocks;
   if ((rc = record(events, 0, s))) return rc;
   int32_t* sel = at<int32_t>(workspace, L.sel);
-  if ((rc = run_select(P, cu, q, k, sel, workspace, L, s, events))) return rc;
+  if ((rc = run_select(P, cu, q, k, sel, workspace, L, s, events, cv))) return rc;
   const Blocks T = tables(workspace, L);
+  if (P.Nq <= kDecodeRows) {  // few rows: split-K over the selected blocks
+    for (int i = 3; i <= 5; ++i)
+      if ((rc = record(events, i, s))) return rc;
+    hipError_t e = launch_decode(P, T, q, k, v, sel, at<float>(workspace, L.dec_part), o, lse, s);
+    if (e != hipSuccess) return hip_fail(e, "moba_attn (few rows)");
+    return record(events, 6, s);
+  }
   const BucketPlan bp = plan_bucket(P);
   const BucketBufs bb = bucket_bufs(workspace, L);
   hipError_t e = launch_bucket(P, T, bp, sel, bb, s);
@@ -312,9 +364,9 @@ int run_prefill(const Prob& P, const int64_t* cu, const void* q, const void* k, 
   if ((rc = record(events, 3, s))) return rc;
   void* part_o = at<void>(workspace, L.part_o);
   float* part_lse = at<float>(workspace, L.part_lse);
-  void* vt = at<void>(workspace, L.vt);
-  if (P.dtype == MOBA_DTYPE_BF16) {
-    e = launch_vt_pack(P, T, v, vt, s);
+  const void* vt = cv ? cv->vt : at<void>(workspace, L.vt);
+  if (P.dtype == MOBA_DTYPE_BF16 && !cv) {
+    e = launch_vt_pack(P, T, v, at<void>(workspace, L.vt), s);
     if (e != hipSuccess) return hip_fail(e, "V pack");
   }
   if ((rc = record(events, 4, s))) return rc;
@@ -508,6 +560,76 @@ int moba_select_chunk(const moba_problem_t* p, int64_t q_rows, const void* q, co
   const Layout L = plan_ws(P, false);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
   return run_select(P, nullptr, q, k, sel, workspace, L, (hipStream_t)stream, nullptr);
+}
+
+static int check_capacity(const Prob& P, int64_t capacity) {
+  if (capacity < P.N) return fail(MOBA_ERR_INVALID_ARGUMENT, "capacity must be >= seqlen");
+  if ((double)capacity * P.Hq * P.k >= 2147483648.0)
+    return fail(MOBA_ERR_UNSUPPORTED, "capacity * num_q_heads * topk must be < 2^31");
+  if ((capacity + P.B - 1) / P.B - 1 > kMaxHist)
+    return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks in the capacity");
+  return MOBA_OK;
+}
+
+size_t moba_cache_bytes(const moba_problem_t* p, int64_t capacity) {
+  Prob P;
+  if (make_prob(p, &P) != MOBA_OK) return 0;
+  if (capacity < 1) return 0;
+  moba_problem_t c = *p;
+  c.seqlen = capacity;
+  if (make_prob(&c, &P) != MOBA_OK) return 0;
+  return cache_layout(P, capacity).total;
+}
+
+int moba_cache_append(const moba_problem_t* p, int64_t capacity, int64_t rows_before,
+                      const void* k, const void* v, void* cache, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  if ((rc = check_capacity(P, capacity))) return rc;
+  if (rows_before < 0 || rows_before > P.N)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "rows_before must be in [0, seqlen]");
+  const void* ptrs[3] = {k, v, cache};
+  if ((rc = check_ptrs(ptrs, 3, "k, v and cache must be non-NULL"))) return rc;
+  if (!aligned(cache, kAlign)) return fail(MOBA_ERR_INVALID_ARGUMENT, "cache must be 256-byte aligned");
+  const CacheLayout C = cache_layout(P, capacity);
+  P.vt_blocks = C.ncap;
+  hipStream_t s = (hipStream_t)stream;
+  // blocks completed by rows [rows_before, N) that can be history within the capacity
+  int64_t c0 = rows_before / P.B, c1 = P.N / P.B;
+  if (c1 > C.nhc) c1 = C.nhc;
+  hipError_t e = launch_cache_means(P, k, c0, c1 - c0, at<double>(cache, C.kbar), C.nhc, s);
+  if (e != hipSuccess) return hip_fail(e, "decode cache: block means");
+  if (P.dtype == MOBA_DTYPE_BF16) {
+    e = launch_vt_pack_rows(P, v, at<void>(cache, C.vt), rows_before, P.N, s);
+    if (e != hipSuccess) return hip_fail(e, "decode cache: V pack");
+  }
+  return MOBA_OK;
+}
+
+size_t moba_cached_workspace_size(const moba_problem_t* p, int64_t q_rows) {
+  Prob P;
+  if (make_prob_chunk(p, q_rows, &P) != MOBA_OK) return 0;
+  return plan_ws(P, true, true).total;
+}
+
+int moba_prefill_cached(const moba_problem_t* p, int64_t capacity, int64_t q_rows, const void* q,
+                        const void* k, const void* v, const void* cache, void* o,
+                        void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_chunk(p, q_rows, &P);
+  if (rc) return rc;
+  if ((rc = check_capacity(P, capacity))) return rc;
+  const void* ptrs[5] = {q, k, v, o, cache};
+  if ((rc = check_ptrs(ptrs, 5, "q, k, v, o and cache must be non-NULL"))) return rc;
+  if (!aligned(cache, kAlign)) return fail(MOBA_ERR_INVALID_ARGUMENT, "cache must be 256-byte aligned");
+  const Layout L = plan_ws(P, true, true);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  const CacheLayout C = cache_layout(P, capacity);
+  const CacheView cv{at<double>(const_cast<void*>(cache), C.kbar), C.nhc,
+                     at<void>(const_cast<void*>(cache), C.vt), C.ncap};
+  return run_prefill(P, nullptr, q, k, v, o, workspace, L, (hipStream_t)stream, nullptr, nullptr,
+                     &cv);
 }
 
 size_t moba_varlen_workspace_size(const moba_problem_t* p, int64_t nseq,

@@ -35,6 +35,8 @@ struct Prob {
   float scale;
   int dtype;          // MOBA_DTYPE_*
   int routing;        // MOBA_ROUTING_*
+  int64_t vt_blocks;  // blocks of the packed V^T layout read by the bf16 kernels (n, or a
+                      // decode cache's capacity in blocks)
 };
 
 // Block and row tables in device memory (built by launch_tables):
@@ -106,8 +108,21 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
 
 // bf16 kernels read V through a transposed, block-padded, key-permuted copy
 // Vt [Hkv][d][n * Bpad] (see vpack.hip); fp32 kernels read V directly.
+// Vt rows are P.vt_blocks * Bpad long.
 int64_t vt_padded_block(int64_t B);
 hipError_t launch_vt_pack(const Prob& P, const Blocks& T, const void* V, void* Vt, hipStream_t s);
+// Pack only the 64-key tiles holding rows [r0, r1) of one sequence of P.N rows
+// (no tables needed: block c starts at c * B).
+hipError_t launch_vt_pack_rows(const Prob& P, const void* V, void* Vt, int64_t r0, int64_t r1,
+                               hipStream_t s);
+
+// Decode cache (cache.hip): fp64 means of the full blocks c0 .. c0 + count - 1
+// of one sequence into kbar [Hkv][nhc][d]; and the copy of the first nh
+// blocks' means from that layout into the [Hkv][nh][d] layout the gate reads.
+hipError_t launch_cache_means(const Prob& P, const void* K, int64_t c0, int64_t count,
+                              double* kbar, int64_t nhc, hipStream_t s);
+hipError_t launch_kbar_gather(const double* src, int64_t nhc, double* dst, int64_t nh, int Hkv,
+                              int d, hipStream_t s);
 
 // History-block attention over the bucketed entries; writes normalised partials
 // part_o [entry][d] and log2-sum-exp part_lse [entry].
@@ -145,6 +160,17 @@ hipError_t launch_backward_bf16(const Prob& P, const Blocks& T, const BucketPlan
                                 void* kt, float* part_dq, void* dq, void* dk, void* dv,
                                 hipStream_t s);
 
+// Few query rows (decode steps, small chunks): split-K attention over each
+// row's selected blocks read in place, then the merge (decode.hip). Used
+// instead of bucketing + the tiled kernels when Nq <= kDecodeRows; part holds
+// decode_part_bytes(P); lse_out (nullable) as for launch_attn_self.
+constexpr int64_t kDecodeRows = 16;
+int decode_splits(const Prob& P);
+size_t decode_part_bytes(const Prob& P);
+hipError_t launch_decode(const Prob& P, const Blocks& T, const void* q, const void* k,
+                         const void* v, const int32_t* sel, float* part, void* o, float* lse_out,
+                         hipStream_t s);
+
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);
 
@@ -152,5 +178,9 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);
 inline size_t part_elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_F32 ? 4 : 2; }
 
 inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// Blocks holding query rows, counted from the last: a chunk of one sequence
+// has its rows in the blocks from q0 / B on; otherwise every block.
+inline int64_t query_blocks(const Prob& P) { return P.nseq == 1 ? P.n - P.q0 / P.B : P.n; }
 
 }  // namespace moba

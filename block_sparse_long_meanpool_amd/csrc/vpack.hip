@@ -19,18 +19,30 @@ __device__ inline int perm32(int r) {  // involution on 0..31 (and on any 32-ali
   return (r & ~12) | ((r & 4) << 1) | ((r & 8) >> 1);
 }
 
-// grid: (n * (Bpad / 64), Hkv)
+// grid: (tiles, Hkv); tile tile0 + blockIdx.x, tiles numbered block by block
+// (Bpad / 64 per block). Block starts and lengths come from the block tables,
+// or, when bstart is NULL (one sequence of N rows), are c * B and
+// min(B, N - c * B). Vt rows are ld_blocks * Bpad long.
 __global__ __launch_bounds__(kThreads) void vt_pack(const uint16_t* __restrict__ V,
                                                     const int32_t* __restrict__ bstart,
                                                     const int32_t* __restrict__ blen,
                                                     uint16_t* __restrict__ Vt, int Hkv,
-                                                    int64_t Bpad, int64_t n) {
+                                                    int64_t Bpad, int64_t ld_blocks,
+                                                    int64_t tile0, int B, int64_t N) {
   __shared__ uint16_t tile[kKeys * kStride];
   const int g = blockIdx.y;
   const int64_t tiles_per_block = Bpad / kKeys;
-  const int64_t c = blockIdx.x / tiles_per_block;
-  const int64_t t0 = (blockIdx.x % tiles_per_block) * kKeys;  // position offset inside block
-  const int64_t row0 = bstart[c], rows_c = blen[c];
+  const int64_t tix = tile0 + blockIdx.x;
+  const int64_t c = tix / tiles_per_block;
+  const int64_t t0 = (tix % tiles_per_block) * kKeys;  // position offset inside block
+  int64_t row0, rows_c;
+  if (bstart) {
+    row0 = bstart[c];
+    rows_c = blen[c];
+  } else {
+    row0 = c * B;
+    rows_c = N - row0 < B ? N - row0 : B;
+  }
   // load 64 key rows (zero past the block)
   {
     const int kk = threadIdx.x >> 2, d0 = (threadIdx.x & 3) * 32;
@@ -62,7 +74,7 @@ __global__ __launch_bounds__(kThreads) void vt_pack(const uint16_t* __restrict__
       const int r0 = perm32(p0 & 31) + 32 * half, r1 = perm32((p0 + 1) & 31) + 32 * half;
       out[i] = (uint32_t)tile[r0 * kStride + d] | ((uint32_t)tile[r1 * kStride + d] << 16);
     }
-    const int64_t ld = n * Bpad;
+    const int64_t ld = ld_blocks * Bpad;
     uint4* dst = reinterpret_cast<uint4*>(Vt + ((int64_t)g * kHeadDim + d) * ld + c * Bpad + t0 +
                                           32 * half);
 #pragma unroll
@@ -76,7 +88,21 @@ hipError_t launch_vt_pack(const Prob& P, const Blocks& T, const void* V, void* V
   const int64_t Bpad = ceil_div(P.B, kKeys) * kKeys;
   dim3 grid((unsigned)(P.n * (Bpad / kKeys)), (unsigned)P.Hkv);
   vt_pack<<<grid, kThreads, 0, s>>>((const uint16_t*)V, T.start, T.len, (uint16_t*)Vt, P.Hkv, Bpad,
-                                    P.n);
+                                    P.vt_blocks, 0, P.B, P.N);
+  return hipGetLastError();
+}
+
+hipError_t launch_vt_pack_rows(const Prob& P, const void* V, void* Vt, int64_t r0, int64_t r1,
+                               hipStream_t s) {
+  if (r1 <= r0) return hipSuccess;
+  const int64_t Bpad = ceil_div(P.B, kKeys) * kKeys;
+  const int64_t tpb = Bpad / kKeys;
+  // tiles holding rows r0 .. r1 - 1 (whole tiles are rewritten, from all rows < N)
+  const int64_t first = (r0 / P.B) * tpb + (r0 % P.B) / kKeys;
+  const int64_t last = ((r1 - 1) / P.B) * tpb + ((r1 - 1) % P.B) / kKeys;
+  dim3 grid((unsigned)(last - first + 1), (unsigned)P.Hkv);
+  vt_pack<<<grid, kThreads, 0, s>>>((const uint16_t*)V, nullptr, nullptr, (uint16_t*)Vt, P.Hkv,
+                                    Bpad, P.vt_blocks, first, P.B, P.N);
   return hipGetLastError();
 }
 

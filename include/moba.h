@@ -204,7 +204,8 @@ MOBA_API int moba_backward(const moba_problem_t *p, const void *q, const void *k
  * later rows, so a long prefill can be split into chunks, and q_rows = 1 is
  * one decode step (PaperTrace section 3.1 contrasts prefill and decode;
  * section 5.1 notes that generation needs block means kept up to date).
- * Block means are recomputed from k on every call (no cache of them).
+ * Block means are recomputed from k on every call; a generation loop keeps
+ * them in a decode cache instead (moba_prefill_cached below).
  *   1 <= q_rows <= seqlen; the selection (moba_select_chunk) is
  *   [q_rows][Hq][topk]. The workspace of moba_chunk_workspace_size serves
  *   both calls.
@@ -216,6 +217,39 @@ MOBA_API int moba_prefill_chunk(const moba_problem_t *p, int64_t q_rows, const v
 MOBA_API int moba_select_chunk(const moba_problem_t *p, int64_t q_rows, const void *q,
                                const void *k, int32_t *sel, void *workspace, size_t ws_bytes,
                                void *stream);
+
+/*
+ * Decode cache: the state a generation loop keeps for one sequence of at
+ * most `capacity` rows, so that a chunk or decode step reads the block means
+ * and the packed V copy instead of recomputing them from the whole KV cache
+ * (PaperTrace section 5.1: generation needs the block means kept current as
+ * tokens arrive; a full block's mean never changes, so each block's mean is
+ * computed once, when the rows appended complete it).
+ *   moba_cache_bytes(p, capacity): bytes of the cache (DEVICE, 256-byte
+ *     aligned, caller-owned; no initialisation needed); p->seqlen is not
+ *     used beyond validation. 0 if the problem or capacity is invalid.
+ *     Holds fp64 means [Hkv][ceil(capacity/B) - 1][d] and, for bf16, the V
+ *     copy [Hkv][d][ceil(capacity/B) * ceil(B/64) * 64].
+ *   moba_cache_append(p, capacity, rows_before, k, v, cache, stream): k and
+ *     v (the KV cache, [capacity][Hkv][d], rows [0, p->seqlen) valid) have
+ *     gained rows [rows_before, p->seqlen); computes the means of the blocks
+ *     those rows complete and packs those rows of V into the cache. Appends
+ *     go in order: rows_before is the previous append's p->seqlen (0 for the
+ *     first); 0 <= rows_before <= p->seqlen <= capacity. No workspace.
+ *   moba_prefill_cached(p, capacity, q_rows, q, k, v, cache, o, workspace,
+ *     ws_bytes, stream): moba_prefill_chunk (same arguments and result) with
+ *     the block means and packed V taken from `cache`, which must hold every
+ *     row of k and v up to p->seqlen. Workspace:
+ *     moba_cached_workspace_size(p, q_rows) bytes.
+ * Errors as elsewhere; capacity < p->seqlen is MOBA_ERR_INVALID_ARGUMENT.
+ */
+MOBA_API size_t moba_cache_bytes(const moba_problem_t *p, int64_t capacity);
+MOBA_API int moba_cache_append(const moba_problem_t *p, int64_t capacity, int64_t rows_before,
+                               const void *k, const void *v, void *cache, void *stream);
+MOBA_API size_t moba_cached_workspace_size(const moba_problem_t *p, int64_t q_rows);
+MOBA_API int moba_prefill_cached(const moba_problem_t *p, int64_t capacity, int64_t q_rows,
+                                 const void *q, const void *k, const void *v, const void *cache,
+                                 void *o, void *workspace, size_t ws_bytes, void *stream);
 
 /*
  * Routing diagnostics (PaperTrace section 5.3: log the gap between the

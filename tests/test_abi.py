@@ -207,3 +207,47 @@ def test_chunk_rejects_bad_row_counts():
     assert 0 < small < ws
     assert lib.moba_prefill_chunk(ctypes.byref(p), 1, FAKE, FAKE, FAKE, FAKE, FAKE, small - 1,
                                   None) == 3
+
+
+def test_cache_sizes():
+    lib = moba.load_library()
+    p = _prob(N=1000, block_size=256)
+    a = lib.moba_cache_bytes(ctypes.byref(p), 1000)
+    b = lib.moba_cache_bytes(ctypes.byref(p), 5000)
+    assert 0 < a < b
+    assert lib.moba_cache_bytes(ctypes.byref(p), 0) == 0
+    # fp64 means of ceil(cap/B) - 1 blocks + bf16 V^T of ceil(cap/B) padded blocks
+    n = -(-5000 // 256)
+    expect = 8 * 2 * (n - 1) * 128 + 2 * 2 * 128 * n * 256
+    assert expect <= b <= expect + 2 * 256
+    f32 = lib.moba_cache_bytes(ctypes.byref(_prob(N=1000, block_size=256, dtype=1)), 5000)
+    assert f32 < b  # no packed V for fp32
+    cw = lib.moba_cached_workspace_size(ctypes.byref(p), 1)
+    assert 0 < cw < lib.moba_chunk_workspace_size(ctypes.byref(p), 1)
+
+
+def test_cache_append_rejects_bad_arguments():
+    lib = moba.load_library()
+    p = _prob(N=1000)
+    assert lib.moba_cache_append(ctypes.byref(p), 999, 0, FAKE, FAKE, FAKE, None) == 1  # capacity
+    assert lib.moba_cache_append(ctypes.byref(p), 2000, 1001, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moba_cache_append(ctypes.byref(p), 2000, -1, FAKE, FAKE, FAKE, None) == 1
+    for i in range(3):
+        ptrs = [FAKE, FAKE, FAKE]
+        ptrs[i] = None
+        assert lib.moba_cache_append(ctypes.byref(p), 2000, 0, *ptrs, None) == 1
+    assert lib.moba_cache_append(ctypes.byref(p), 2000, 0, FAKE, FAKE, FAKE + 16, None) == 1
+
+
+def test_prefill_cached_rejects_bad_arguments():
+    lib = moba.load_library()
+    p = _prob(N=1000)
+    ws = lib.moba_cached_workspace_size(ctypes.byref(p), 4)
+    args = lambda cap, rows, cache, n: (ctypes.byref(p), cap, rows, FAKE, FAKE, FAKE, cache, FAKE,
+                                        FAKE, n, None)
+    assert lib.moba_prefill_cached(*args(999, 4, FAKE, ws)) == 1          # capacity < seqlen
+    assert lib.moba_prefill_cached(*args(2000, 0, FAKE, ws)) == 1         # q_rows
+    assert lib.moba_prefill_cached(*args(2000, 1001, FAKE, ws)) == 1
+    assert lib.moba_prefill_cached(*args(2000, 4, None, ws)) == 1         # cache
+    assert lib.moba_prefill_cached(*args(2000, 4, FAKE + 16, ws)) == 1    # misaligned cache
+    assert lib.moba_prefill_cached(*args(2000, 4, FAKE, ws - 1)) == 3     # workspace

@@ -419,6 +419,41 @@ def test_decode_steps():
                      f"decode step {step}")
 
 
+CACHE = [
+    # capacity, Hq, Hkv, B, topk, dtype, rows appended per step
+    (2000, 4, 2, 256, 3, "bf16", [700, 1, 1, 1, 65, 1, 254, 258, 1, 255, 1]),
+    (1500, 8, 2, 96, 4, "bf16", [1, 94, 1, 1, 200, 3, 500]),  # B not a multiple of 64
+    (1200, 4, 1, 128, 3, "f32", [500, 1, 139, 1, 1]),
+]
+
+
+@pytest.mark.parametrize("cap,Hq,Hkv,B,topk,dtype,steps", CACHE)
+def test_decode_cache_matches_recompute(cap, Hq, Hkv, B, topk, dtype, steps):
+    """Appending rows to a decode cache and running the chunk on it gives the
+    rows of moba_prefill_chunk over the same prefix (bit for bit in bf16: the
+    cached means are exact fp64 sums, as are the recomputed ones); the last
+    step is also checked against the oracle."""
+    q, k, v, tq, tk, tv = small(cap, Hq, Hkv, B, topk, seed=cap + B, dtype=dtype)
+    code = moba.MOBA_DTYPE_BF16 if dtype == "bf16" else moba.MOBA_DTYPE_F32
+    cache = moba.DecodeCache(cap, Hq, Hkv, B, topk, 0.09, dtype=code, device=DEV)
+    rows = 0
+    for a in steps:
+        rows += a
+        cache.append(tk, tv, rows)
+        C = min(a, 96)
+        qc = tq[rows - C:rows].contiguous()
+        got = cache.prefill(qc, tk, tv)
+        ref = moba.prefill_chunk(qc, tk[:rows], tv[:rows], B, topk, 0.09)
+        if dtype == "bf16":
+            assert torch.equal(got, ref), f"rows {rows}"
+        else:
+            assert torch.allclose(got, ref, rtol=0, atol=1e-6), f"rows {rows}"
+    sel = moba.select_chunk(qc, tk[:rows], B, topk).cpu().numpy()
+    r, heads = all_rows(C, Hq)
+    compare_rows(q[:rows], k[:rows], v[:rows], B, topk, 0.09, r + (rows - C), heads,
+                 sel.reshape(-1, topk), to_np(got).reshape(-1, 128), dtype, f"cache {rows}")
+
+
 # ------------------------------------------------------------------ backward ---
 BWD = [
     # N, Hq, Hkv, B, topk, dtype, routing
