@@ -138,6 +138,70 @@ def backward_leg():
     return backward
 
 
+def chunk_leg(w, tq, tk, tv, prob):
+    """Chunked prefill and decode over the layer's KV cache: one decode step
+    and a 16,384-row chunk recomputing the block means, and the decode step
+    on a decode cache."""
+    chunk = {}
+    for C in (1, 16384):
+        qc = tq[w.N - C:].contiguous()
+        oc = torch.empty_like(qc)
+        wsc = moba.alloc_workspace(moba.chunk_workspace_size(prob, C), tq.device)
+        moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        reps = 5 if C == 1 else 2
+        e0.record()
+        for _ in range(reps):
+            moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
+        e1.record()
+        torch.cuda.synchronize()
+        cms = e0.elapsed_time(e1) / reps
+        chunk["decode_step" if C == 1 else f"chunk_{C}"] = {
+            "query_rows": C, "cache_rows": w.N, "ms": cms, "tokens_per_s": C / (cms / 1e3)}
+        if C == 1:
+            o_recompute = oc.clone()
+        del wsc, oc
+    # the same decode step on a decode cache: append the new row (its block
+    # means only when it completes a block; its V column), then the step
+    cache = moba.DecodeCache(w.N, w.Hq, w.Hkv, w.B, w.k, w.scale, device=tq.device)
+    cache.append(tk, tv, w.N - 1)
+    qd = tq[w.N - 1:].contiguous()
+    od = torch.empty_like(qd)
+    cache.rows = w.N - 1
+    cache.append(tk, tv, w.N)
+    wsd = moba.alloc_workspace(cache.workspace_size(1), tq.device)
+
+    def cached_step():
+        cache.rows = w.N - 1
+        cache.append(tk, tv, w.N)
+        cache.prefill(qd, tk, tv, out=od, workspace=wsd)
+
+    cached_step()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = 20
+    e0.record()
+    for _ in range(reps):
+        cached_step()
+    e1.record()
+    torch.cuda.synchronize()
+    cms = e0.elapsed_time(e1) / reps
+    # algorithmic bytes of a decode step: K and V rows of every selected block
+    # (k - 1 full history blocks and the own block up to the row) of every head
+    pos = w.N - 1
+    own = pos - (pos // w.B) * w.B + 1
+    sel_keys = (min(w.k - 1, pos // w.B) * w.B + own) * w.Hq
+    dec_bytes = sel_keys * 2 * w.d * 2
+    chunk["decode_step_cached"] = {
+        "query_rows": 1, "cache_rows": w.N, "ms": cms, "tokens_per_s": 1 / (cms / 1e3),
+        "selected_kv_bytes": dec_bytes, "step_gbps": dec_bytes / (cms / 1e3) / 1e9,
+        "matches_recompute": bool(torch.equal(od, o_recompute)),
+        "note": "moba_cache_append of the new row + moba_prefill_cached"}
+    del cache, wsd, od
+    return chunk
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -155,8 +219,9 @@ def main():
                     help="skip the training leg (forward with statistics + backward) on the 32K layer")
     ap.add_argument("--no-shared", action="store_true",
                     help="skip the group-shared routing leg and the routing-statistics timing")
-    ap.add_argument("--backward-only", action="store_true",
-                    help="only run the training leg and print its JSON object")
+    ap.add_argument("--only", choices=["backward", "chunk"], default=None,
+                    help="only run that leg (the training leg on the 32K layer, or the "
+                         "chunk / decode leg on the 1M-row cache) and print its JSON object")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel over this many MiB (hardware-counter "
                          "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
@@ -178,7 +243,7 @@ def main():
         print(json.dumps({"copy_bytes": nbytes}), flush=True)
         return
 
-    if args.backward_only:
+    if args.only == "backward":
         print(json.dumps({"backward": backward_leg()}), flush=True)
         return
 
@@ -191,6 +256,9 @@ def main():
     out = torch.empty_like(tq)
     prob = moba.make_problem(w.N, w.Hq, w.Hkv, w.d, w.B, w.k, w.scale,
                              moba.MOBA_DTYPE_BF16 if dtype == "bf16" else moba.MOBA_DTYPE_F32)
+    if args.only == "chunk":
+        print(json.dumps({"chunked": chunk_leg(w, tq, tk, tv, prob)}), flush=True)
+        return
     ws = moba.alloc_workspace(moba.workspace_size(prob), tq.device)
     print(f"[bench] {w.name}: inputs ready in {gen_s:.1f} s, workspace {ws.numel() / 2**30:.1f} GiB",
           file=sys.stderr, flush=True)
@@ -268,56 +336,7 @@ def main():
 
     chunk = None
     if not args.no_chunk and dtype == "bf16":
-        chunk = {}
-        for C in (1, 16384):
-            qc = tq[w.N - C:].contiguous()
-            oc = torch.empty_like(qc)
-            wsc = moba.alloc_workspace(moba.chunk_workspace_size(prob, C), tq.device)
-            moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5 if C == 1 else 2
-            e0.record()
-            for _ in range(reps):
-                moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale, out=oc, workspace=wsc)
-            e1.record()
-            torch.cuda.synchronize()
-            cms = e0.elapsed_time(e1) / reps
-            chunk["decode_step" if C == 1 else f"chunk_{C}"] = {
-                "query_rows": C, "cache_rows": w.N, "ms": cms, "tokens_per_s": C / (cms / 1e3)}
-            if C == 1:
-                o_recompute = oc.clone()
-            del wsc, oc
-        # the same decode step on a decode cache: append the new row (its block
-        # means only when it completes a block; its V column), then the step
-        cache = moba.DecodeCache(w.N, w.Hq, w.Hkv, w.B, w.k, w.scale, device=tq.device)
-        cache.append(tk, tv, w.N - 1)
-        qd = tq[w.N - 1:].contiguous()
-        od = torch.empty_like(qd)
-        cache.rows = w.N - 1
-        cache.append(tk, tv, w.N)
-        wsd = moba.alloc_workspace(cache.workspace_size(1), tq.device)
-
-        def cached_step():
-            cache.rows = w.N - 1
-            cache.append(tk, tv, w.N)
-            cache.prefill(qd, tk, tv, out=od, workspace=wsd)
-
-        cached_step()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        reps = 20
-        e0.record()
-        for _ in range(reps):
-            cached_step()
-        e1.record()
-        torch.cuda.synchronize()
-        cms = e0.elapsed_time(e1) / reps
-        chunk["decode_step_cached"] = {
-            "query_rows": 1, "cache_rows": w.N, "ms": cms, "tokens_per_s": 1 / (cms / 1e3),
-            "matches_recompute": bool(torch.equal(od, o_recompute)),
-            "note": "moba_cache_append of the new row + moba_prefill_cached"}
-        del cache, wsd, od
+        chunk = chunk_leg(w, tq, tk, tv, prob)
 
     shared = None
     if not args.no_shared and dtype == "bf16":
