@@ -171,6 +171,8 @@ EDGE = [
     (1000, 2, 1, 96, 3, "f32"),
     (2048, 4, 2, 128, 16, "f32"),
     (300, 2, 1, 1, 4, "f32"),
+    (16, 4, 2, 4, 3, "bf16"),        # 16 rows: the few-row path over a whole prefill
+    (13, 2, 1, 3, 4, "f32"),
 ]
 
 
@@ -252,6 +254,7 @@ VARLEN = [
     ([64, 64, 640, 129, 1, 700], 4, 4, 64, 3, "bf16"),
     ([5, 17, 3000, 0, 2049], 6, 3, 100, 5, "bf16"),  # B not a multiple of 64
     ([1000, 1, 0, 2500, 333], 4, 2, 256, 4, "f32"),
+    ([3, 0, 9, 4], 4, 2, 2, 3, "bf16"),  # 16 rows in all: the few-row path
 ]
 
 
@@ -386,6 +389,10 @@ CHUNKS = [
     (3000, 8, 2, 128, 4, 3000, "bf16"),   # the whole sequence
     (2048, 4, 4, 96, 5, 200, "bf16"),     # B not a multiple of 64
     (1500, 4, 2, 64, 3, 129, "f32"),
+    (3000, 8, 2, 128, 4, 16, "bf16"),     # the largest chunk of the few-row (split-K) path
+    (3000, 8, 2, 128, 4, 17, "bf16"),     # the smallest of the tiled path
+    (1500, 4, 2, 64, 3, 5, "f32"),        # few-row path in fp32
+    (5000, 4, 1, 1000, 3, 3, "bf16"),     # few rows, 4 splits of a block, partial last split
 ]
 
 
@@ -464,6 +471,7 @@ BWD = [
     (800, 8, 2, 64, 4, "bf16", 1),     # group-shared routing
     (3072, 4, 1, 512, 3, "bf16", 0),   # G = 4, several query chunks and key tiles per block
     (2300, 4, 2, 200, 5, "bf16", 0),   # key tiles with ragged 32-key groups, partial last block
+    (12, 2, 1, 4, 3, "bf16", 0),       # lse from the few-row forward path
 ]
 
 
