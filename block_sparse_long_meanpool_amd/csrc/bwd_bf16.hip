@@ -466,20 +466,22 @@ __device__ inline void wait_tile() {
 }
 
 // One wave's 32 queries (lane: query lr) over keys [key0, key0 + nkeys) of one
-// block, accumulating dq^T (unscaled) in acc. CAUSAL: key <= qrow.
+// block, accumulating dq^T (unscaled) in acc. CAUSAL: key <= the query's
+// position. Positions are relative to key0 (32-bit): qrel is the lane's
+// query, wmin / wmax the wave's first and last query.
 template <bool CAUSAL>
 __device__ inline void dq_block(KTile b0, KTile b1, const uint16_t* __restrict__ K,
-                                const uint16_t* __restrict__ V, int64_t key0, int64_t nkeys,
+                                const uint16_t* __restrict__ V, int64_t key0, int nkeys,
                                 int Hkv, int g, const uint16_t* __restrict__ kt_col, int64_t ldk,
                                 const bf16x8 (&qb)[8], const bf16x8 (&ob)[8], float lse, float dd,
-                                int64_t qrow, int64_t wrow_min, int64_t wrow_max, bool live,
-                                float sl2e, f32x16 (&acc)[4]) {
+                                int qrel, int wmin, int wmax, bool live, float sl2e,
+                                f32x16 (&acc)[4]) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
-  const int nt = (int)((nkeys + KT - 1) / KT);
+  const int nt = (nkeys + KT - 1) / KT;
   auto issue = [&](int t, KTile dst) {
-    const int64_t rem = nkeys - (int64_t)t * KT;
-    load_ktile(dst, K, V, key0 + (int64_t)t * KT, rem < KT ? (int)rem : KT, Hkv, g,
-               kt_col + t * KT, ldk, wave, lane);
+    const int rem = nkeys - t * KT;
+    load_ktile(dst, K, V, key0 + (int64_t)t * KT, rem < KT ? rem : KT, Hkv, g, kt_col + t * KT,
+               ldk, wave, lane);
   };
   issue(0, b0);
   wait_tile();
@@ -488,10 +490,10 @@ __device__ inline void dq_block(KTile b0, KTile b1, const uint16_t* __restrict__
     if (t + 1 < nt) issue(t + 1, (t & 1) ? b0 : b1);
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      const int64_t k0 = key0 + (int64_t)t * KT + 32 * sub;
-      const int64_t rem = key0 + nkeys - k0;
-      const int nv = rem <= 0 ? 0 : (rem < 32 ? (int)rem : 32);
-      if (!live || nv == 0 || (CAUSAL && k0 > wrow_max)) continue;
+      const int k0 = t * KT + 32 * sub;  // relative to key0
+      const int rem = nkeys - k0;
+      const int nv = rem <= 0 ? 0 : (rem < 32 ? rem : 32);
+      if (!live || nv == 0 || (CAUSAL && k0 > wmax)) continue;
       f32x16 s, dp;
       zero(s);
       zero(dp);
@@ -501,14 +503,14 @@ __device__ inline void dq_block(KTile b0, KTile b1, const uint16_t* __restrict__
         dp = mfma(rm_read(cur.v, 32 * sub + lr, 2 * kk + h), ob[kk], dp);
       }
       // lane: query; element r: key k0 + acc_row(r, h)
-      const bool need_mask = nv < 32 || (CAUSAL && k0 + 31 > wrow_min);
+      const bool need_mask = nv < 32 || (CAUSAL && k0 + 31 > wmin);
       float ds[16];
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const int key = acc_row(r, h);
-        bool on = true;
-        if (need_mask) on = key < nv && (!CAUSAL || k0 + key <= qrow);
-        const float p = on ? __builtin_amdgcn_exp2f(fmaf(s[r], sl2e, -lse)) : 0.f;
+        float x = fmaf(s[r], sl2e, -lse);
+        if (need_mask) x = (key < nv && (!CAUSAL || k0 + key <= qrel)) ? x : -INFINITY;
+        const float p = __builtin_amdgcn_exp2f(x);
         ds[r] = p * (dp[r] - dd);
       }
 #pragma unroll
@@ -633,9 +635,10 @@ __global__ __launch_bounds__(kQThreads) void bwd_dq_self_bf16(
   f32x16 acc[4];
 #pragma unroll
   for (int db = 0; db < 4; ++db) zero(acc[db]);
-  const int64_t nkeys = pos0 + plast / G - key0 + 1;
+  const int nkeys = (int)(pos0 + plast / G - key0 + 1);
   dq_block<true>(b0, b1, K, V, key0, nkeys, Hkv, g, Kt + (int64_t)g * kD * ldk + c * Bpad, ldk,
-                 qb, ob, lse, dd, qpos_me, wrow_min, wrow_max, live, scale * kLog2e, acc);
+                 qb, ob, lse, dd, (int)(qpos_me - key0), (int)(wrow_min - key0),
+                 (int)(wrow_max - key0), live, scale * kLog2e, acc);
   if (!valid) return;
   // the row's history slots: min(k - 1, earlier blocks of its sequence)
   const int64_t avail = c - blo[c];
