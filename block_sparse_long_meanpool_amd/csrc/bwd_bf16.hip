@@ -11,16 +11,18 @@
 //
 // All products are v_mfma_f32_32x32x16_bf16 (fp32 accumulation); P and dZ
 // are rounded to bf16 as matrix operands. Two kernels:
-//   * dK, dV (key-stationary): a workgroup of 4 waves owns 128 keys of one
-//     block and KV head, a wave 32 of them with its K and V rows held as
-//     matrix operands in registers. It streams every query that attends the
+//   * dK, dV (key-stationary): a workgroup of 8 waves owns 128 keys of one
+//     block and KV head, a wave 16 of them with its K and V rows held as
+//     matrix operands (16x16x32 products) in registers. It streams every query that attends the
 //     block (the bucketed history entries of (KV head, block), then the
 //     block's own causal rows for all G query heads) through LDS in chunks of
-//     64, double buffered, each chunk staged both row-major (operand of
-//     S = Q K^T and dP = dO V^T) and transposed (operand of dK^T = Q^T dZ and
-//     dV^T = dO^T P). The score layout puts one key per lane, so P and dZ
-//     feed the second pair of products straight from the accumulators.
-//     Every key's gradients are finished in one workgroup and written once.
+//     64, double buffered, copied straight from global memory into a
+//     row-major tile: the operand of S = Q K^T and dP = dO V^T is read from
+//     it directly, the transposed operand of dK^T = Q^T dZ and dV^T = dO^T P
+//     with the transpose reads of gfx950 (ds_read_b64_tr_b16). The score
+//     layout puts one key per lane, so P and dZ feed the second pair of
+//     products straight from the accumulators. Every key's gradients are
+//     finished in one workgroup and written once.
 //   * dQ (query-stationary): the tiles of the forward pass (256 routed
 //     entries of one history block, or 256 own-block (row, head) pairs);
 //     8 waves of 32 queries stream the block's K rows, V rows and a
@@ -52,9 +54,6 @@ __device__ inline void zero(f32x16& c) {
 }
 // Row (0..31) of accumulator element r of the 32x32 output, for lane half h.
 __device__ inline int acc_row(int r, int h) { return 8 * (r >> 2) + 4 * h + (r & 3); }
-// Position of row q inside its 32-group in a transposed operand: swapping
-// bits 2 and 3 puts the 8 rows a lane contracts over into one 16-byte run.
-__device__ inline int perm32(int q) { return (q & ~12) | ((q & 4) << 1) | ((q & 8) >> 1); }
 
 // Row-major [rows][128] bf16 tiles keep 16-byte chunk c of row r at
 // c ^ (r & 15): the 16 lanes of one ds_read_b128 cycle (16 rows, one chunk)
@@ -99,20 +98,15 @@ __device__ inline uint4 ld16_or_zero(const uint16_t* __restrict__ base, int64_t 
 // ===========================================================================
 // dK, dV
 // ===========================================================================
-constexpr int kKW = 4;              // waves
+constexpr int kKW = 8;              // waves
 constexpr int kKThreads = 64 * kKW;
-constexpr int kKeysWG = 32 * kKW;   // 128 keys per workgroup
+constexpr int kKeysWG = 16 * kKW;   // 128 keys per workgroup, 16 per wave
 constexpr int kQC = 64;             // queries per staged chunk
 
-struct QChunk {
-  uint16_t* qr;   // [64][128] Q rows
-  uint16_t* dr;   // [64][128] dO rows
-  uint16_t* qt;   // [128][64] Q^T, rows permuted per 32-group
-  uint16_t* dt;   // [128][64] dO^T
-  float* lse;     // [64] log2-sum-exp
-  float* dd;      // [64] D = dO.o
-  int32_t* lim;   // [64] last visible key (relative to the block start), -1 none
-};
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+__device__ inline f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Source of chunk query idx, as a table word: a history entry's slot code
 // (row-head * (k-1) + slot, >= 0) is stored as -2 - code, an own-block pair
@@ -165,14 +159,6 @@ __device__ inline int64_t decode(int64_t w, const Dec& dc, int32_t& lim) {
   return (dc.qstart + r) * dc.Hq + dc.head0 + (int)(w & 63);
 }
 
-// Per thread: 2 staging tasks of (tensor, 4 consecutive queries, 8 dims);
-// threads < 64 also carry one query's lse, D and key limit.
-struct Stage {
-  uint4 v[2][4];
-  float lse, dd;
-  int32_t lim;
-};
-
 // Chunk query table [64] of words, filled two chunks ahead by the first 64
 // threads: the entry id is loaded before a chunk's compute, the word formed
 // and stored after it.
@@ -188,66 +174,77 @@ __device__ inline void fill_store(const TabFill& f, const QSrc& src, int64_t* ta
   if (threadIdx.x < kQC) tab[threadIdx.x] = src.word(f.idx, f.raw);
 }
 
-__device__ inline void stage_load(Stage& st, const int64_t* tab, const Dec& dc,
-                                  const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
-                                  const float* __restrict__ lse2, const float* __restrict__ delta) {
-  const int tid = threadIdx.x;
-  if (tid < kQC) {
-    // an absent query has lim = -1, which masks all its weights, so its lse
-    // and D may be any finite values: row 0's stand in (no select on them)
-    const int64_t ph = decode(tab[tid], dc, st.lim);
-    const int64_t pc = ph >= 0 ? ph : 0;
-    st.lse = lse2[pc];
-    st.dd = delta[pc];
-  }
-  const int q4 = (tid >> 4) & 15, c = tid & 15;  // both tasks: same queries, Q then dO
+// One staged chunk of 64 queries in LDS.
+struct QBuf {
+  uint16_t* q;   // [64][128] Q rows, 16-byte chunk c of row r at c ^ (r & 15)
+  uint16_t* o;   // [64][128] dO rows, same layout
+  float* lse;    // [64] log2-sum-exp
+  float* dd;     // [64] D = dO.o
+  int32_t* lim;  // [64] last visible key (relative to the block start), -1 none
+};
+
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4i16 lds_v4i16;
+
+// Stage a chunk with direct global -> LDS copies (no registers in between):
+// each of the 8 waves copies 2 x 1 KB of Q rows and of dO rows (4 rows of 16
+// chunks per copy, the source chunk chosen so that the LDS position is
+// swizzled), wave 0 the 64 lse values, wave 1 the 64 D values; wave 2 writes
+// the key limits. An absent query reads row 0 (finite values; its limit -1
+// masks it).
+__device__ inline void stage(QBuf B, const int64_t* tab, const Dec& dc,
+                             const uint16_t* __restrict__ Q, const uint16_t* __restrict__ dO,
+                             const float* __restrict__ lse2, const float* __restrict__ delta) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
+    const int ii = 2 * wave + i;
+    const int r = 4 * ii + (lane >> 4);
     int32_t lim;
-    const int64_t ph = decode(tab[4 * q4 + i], dc, lim);
-    st.v[0][i] = ld16_or_zero(Q, ph * kD + 8 * c, ph >= 0);
-    st.v[1][i] = ld16_or_zero(dO, ph * kD + 8 * c, ph >= 0);
+    int64_t ph = decode(tab[r], dc, lim);
+    ph = ph >= 0 ? ph : 0;
+    const int64_t off = ph * kD + 8 * rm_swz(r, lane & 15);  // the swizzle is an involution
+    __builtin_amdgcn_global_load_lds(Q + off, (__attribute__((address_space(3))) void*)(B.q + 4 * ii * kD), 16, 0, 0);
+    __builtin_amdgcn_global_load_lds(dO + off, (__attribute__((address_space(3))) void*)(B.o + 4 * ii * kD), 16, 0, 0);
+  }
+  if (wave < 3) {
+    int32_t lim;
+    int64_t ph = decode(tab[lane], dc, lim);
+    ph = ph >= 0 ? ph : 0;
+    if (wave == 0)
+      __builtin_amdgcn_global_load_lds(lse2 + ph, (__attribute__((address_space(3))) void*)B.lse, 4, 0, 0);
+    else if (wave == 1)
+      __builtin_amdgcn_global_load_lds(delta + ph, (__attribute__((address_space(3))) void*)B.dd, 4, 0, 0);
+    else
+      B.lim[lane] = lim;
   }
 }
 
-__device__ inline void stage_store(const Stage& st, QChunk b) {
-  const int tid = threadIdx.x;
-  const int q4 = (tid >> 4) & 15, c = tid & 15;
-#pragma unroll
-  for (int k = 0; k < 2; ++k) {
-    uint16_t* rm = k ? b.dr : b.qr;
-    uint16_t* tr = k ? b.dt : b.qt;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int q = 4 * q4 + i;
-      *reinterpret_cast<uint4*>(rm + q * kD + (rm_swz(q, c) << 3)) = st.v[k][i];
-    }
-    // transposed: 8 dims x 4 consecutive (permuted) positions, 8 bytes each
-    const int q0 = 4 * q4;
-    const int pos = 32 * (q0 >> 5) + perm32(q0 & 31);  // positions pos..pos+3
-    const uint32_t w0[4] = {st.v[k][0].x, st.v[k][0].y, st.v[k][0].z, st.v[k][0].w};
-    const uint32_t w1[4] = {st.v[k][1].x, st.v[k][1].y, st.v[k][1].z, st.v[k][1].w};
-    const uint32_t w2[4] = {st.v[k][2].x, st.v[k][2].y, st.v[k][2].z, st.v[k][2].w};
-    const uint32_t w3[4] = {st.v[k][3].x, st.v[k][3].y, st.v[k][3].z, st.v[k][3].w};
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const int d = 8 * c + e;
-      // byte selectors: low halves (e even) or high halves (e odd) of two words
-      const uint32_t sel = (e & 1) ? 0x07060302u : 0x05040100u;
-      const uint2 out = make_uint2(__builtin_amdgcn_perm(w1[e >> 1], w0[e >> 1], sel),
-                                   __builtin_amdgcn_perm(w3[e >> 1], w2[e >> 1], sel));
-      *reinterpret_cast<uint2*>(tr + d * 64 + (tr_swz(d, pos >> 3) << 3) + (pos & 7)) = out;
-    }
-  }
-  if (tid < kQC) {
-    b.lse[tid] = st.lse;
-    b.dd[tid] = st.dd;
-    b.lim[tid] = st.lim;
-  }
+// A operand [16 dims][32 queries] of dK^T = Q^T dZ or dV^T = dO^T P from the
+// row-major tile by two transpose reads (ds_read_b64_tr_b16: in each group
+// of 16 lanes, lane j receives element j % 4 of the 8-byte reads of lanes
+// 4e + j / 4, e = 0..3). Group a = l / 16, lane 4e + b of it reads dims
+// 16 mb + 4b .. +3 of query row 4a + e (first read) and 16 + 4a + e
+// (second) of the 32-query step, so lane l receives dim 16 mb + l % 16 of
+// queries 4a + 0..3 and 16 + 4a + 0..3: the order in which the score
+// accumulators of two 16-query blocks hold them.
+__device__ inline bf16x8 tr_pair(const uint16_t* p0, const uint16_t* p1) {
+  const v4i16 a = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p0);
+  const v4i16 b = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16*)p1);
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(a, b, 0, 1, 2, 3, 4, 5, 6, 7));
 }
 
-// grid: 1D, a multiple of 8 covering Hkv * n * ceil(B / 128) items; 256 threads.
-__global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
+// B operand from two 16-query blocks of accumulators: queries 4a + 0..3 of
+// the first and of the second block.
+__device__ inline bf16x8 pack_pair(const f32x4& x, const f32x4& y) {
+  const float v[8] = {x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
+  return to_b8(v);
+}
+
+// grid: 1D, a multiple of 8 covering Hkv * n * ceil(B / 128) items; 512 threads.
+// Products are v_mfma_f32_16x16x32_bf16 (lane l: A[l % 16][8 (l / 16) + 0..7],
+// B[8 (l / 16) + 0..7][l % 16], C[4 (l / 16) + i][l % 16]).
+__global__ __launch_bounds__(kKThreads) void bwd_dkv_bf16(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
     const uint16_t* __restrict__ V, const uint16_t* __restrict__ dO,
     const float* __restrict__ lse2, const float* __restrict__ delta,
@@ -256,11 +253,13 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
     const int32_t* __restrict__ qpos, const int32_t* __restrict__ bin_off,
     const uint32_t* __restrict__ entries, uint16_t* __restrict__ dK, uint16_t* __restrict__ dV,
     int Hq, int Hkv, int G, int KH, int64_t n, int64_t nh, int tiles_per_block, float scale) {
-  __shared__ __align__(16) uint16_t s_qr[2][kQC * kD], s_dr[2][kQC * kD];
-  __shared__ __align__(16) uint16_t s_qt[2][kD * kQC], s_dt[2][kD * kQC];
-  __shared__ __align__(16) float s_lse[2][kQC], s_dd[2][kQC];
-  __shared__ __align__(16) int32_t s_lim[2][kQC];
-  __shared__ int64_t s_tab[2][kQC];
+  // two chunk buffers, each part its own array: the copies into one buffer
+  // visibly never alias the reads from the other
+  __shared__ __align__(16) uint16_t s_q0[kQC * kD], s_q1[kQC * kD];
+  __shared__ __align__(16) uint16_t s_o0[kQC * kD], s_o1[kQC * kD];
+  __shared__ __align__(16) float s_l0[kQC], s_l1[kQC], s_d0[kQC], s_d1[kQC];
+  __shared__ __align__(16) int32_t s_m0[kQC], s_m1[kQC];
+  __shared__ int64_t s_t0[kQC], s_t1[kQC];
   // Items w = (g * n + b) * tiles_per_block + kt. Workgroup i runs on XCD
   // i % 8 and each XCD takes a contiguous range of items, so the key tiles
   // of one (KV head, block), which stage the same query rows, share an L2.
@@ -272,25 +271,23 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
   const int g = (int)(w / ((int64_t)tiles_per_block * n));
   const int nk = blen[b];
   if (kt * kKeysWG >= nk) return;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, lr = lane & 31, h = lane >> 5;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, ln16 = lane & 15, a4 = lane >> 4;
   const int64_t key_first = bstart[b];
-  const int key_rel = kt * kKeysWG + 32 * wave + lr;  // this lane's key in the block
+  const int key_rel = kt * kKeysWG + 16 * wave + ln16;  // this lane's key in the block
   const bool kvalid = key_rel < nk;
   const float sl2e = scale * kLog2e;
 
-  // this lane's key as the B operand: dims 16kk + 8h .. +7
-  bf16x8 kb[8], vb[8];
+  // this lane's key as the B operand: dims 32 kk + 8 a4 .. +7
+  bf16x8 kb[4], vb[4];
   {
-    const int64_t off = ((key_first + (kvalid ? key_rel : 0)) * Hkv + g) * kD + 8 * h;
+    const int64_t off = ((key_first + (kvalid ? key_rel : 0)) * Hkv + g) * kD + 8 * a4;
 #pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint4 zk = ld16_or_zero(K, off + 16 * kk, kvalid);
-      const uint4 zv = ld16_or_zero(V, off + 16 * kk, kvalid);
-      kb[kk] = as_b8(zk);
-      vb[kk] = as_b8(zv);
+    for (int kk = 0; kk < 4; ++kk) {
+      kb[kk] = as_b8(ld16_or_zero(K, off + 32 * kk, kvalid));
+      vb[kk] = as_b8(ld16_or_zero(V, off + 32 * kk, kvalid));
     }
     // complete before the chunk loop, whose counter waits then only cover
-    // the staging loads
+    // the staging copies
     __builtin_amdgcn_s_waitcnt(0);
   }
 
@@ -308,109 +305,117 @@ __global__ __launch_bounds__(kKThreads, 1) void bwd_dkv_bf16(
   src.G = G;
   const Dec dc{KH, Hq, qrel, g * G, (int64_t)qstart[b]};
 
-  f32x16 dk[4], dv[4];
+  f32x4 dk[8], dv[8];  // dims 16 mb + 4 a4 + i of this lane's key
 #pragma unroll
-  for (int db = 0; db < 4; ++db) {
-    zero(dk[db]);
-    zero(dv[db]);
-  }
+  for (int mb = 0; mb < 8; ++mb)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dk[mb][i] = dv[mb][i] = 0.f;
 
-  const int nchunks = (src.total + kQC - 1) / kQC;
-  Stage st;
-  TabFill tf{0, 0u};
-  auto buf = [&](int i) {
-    return QChunk{s_qr[i], s_dr[i], s_qt[i], s_dt[i], s_lse[i], s_dd[i], s_lim[i]};
+  auto compute = [&](QBuf cur) {
+    // Per-lane element offsets inside a tile; query blocks, 32-query steps
+    // and the Q / dO tiles differ by constants (the reads' immediate
+    // offsets). The lane id goes through an empty asm statement so the
+    // offsets are rebuilt per chunk rather than hoisted out of the loop.
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int l16 = ln & 15, la = ln >> 4;
+    int rmo[4];  // row l16 (of a 16-query block), dims 32 kk + 8 la
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) rmo[kk] = l16 * kD + (rm_swz(l16, 4 * kk + la) << 3);
+    int tro[8];  // row 4 la + e, dims 16 mb + 4 bb of a 32-query step
+    {
+      const int e = l16 >> 2, bb = l16 & 3, row = 4 * la + e;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb)
+        tro[mb] = row * kD + (rm_swz(row, 2 * mb + (bb >> 1)) << 3) + (bb & 1) * 4;
+    }
+    // scores and dP of the chunk's 4 query blocks (lane: key; register i:
+    // query 16 qb + 4 la + i)
+    f32x4 sc[4], dp[4];
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[qb][i] = dp[qb][i] = 0.f;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) {
+        const int o = qb * 16 * kD + rmo[kk];
+        sc[qb] = mfma16(as_b8(*reinterpret_cast<const uint4*>(cur.q + o)), kb[kk], sc[qb]);
+        dp[qb] = mfma16(as_b8(*reinterpret_cast<const uint4*>(cur.o + o)), vb[kk], dp[qb]);
+      }
+    }
+    // P = 2^(c s - lse) (masked), dZ = P (dP - D)
+#pragma unroll
+    for (int qb = 0; qb < 4; ++qb) {
+      const int q = 16 * qb + 4 * la;
+      const float4 l4 = *reinterpret_cast<const float4*>(cur.lse + q);
+      const float4 d4 = *reinterpret_cast<const float4*>(cur.dd + q);
+      const int4 m4 = *reinterpret_cast<const int4*>(cur.lim + q);
+      const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
+      const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
+      const int mv[4] = {m4.x, m4.y, m4.z, m4.w};
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = fmaf(sc[qb][i], sl2e, -lv[i]);
+        const float pr = __builtin_amdgcn_exp2f(key_rel <= mv[i] ? x : -INFINITY);
+        sc[qb][i] = pr;
+        dp[qb][i] = pr * (dp[qb][i] - dv4[i]);
+      }
+    }
+    // dV^T += dO^T P and dK^T += Q^T dZ over two 32-query steps
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bf16x8 pb = pack_pair(sc[2 * j], sc[2 * j + 1]);
+      const bf16x8 zb = pack_pair(dp[2 * j], dp[2 * j + 1]);
+      const int rows = 32 * j * kD;
+#pragma unroll
+      for (int mb = 0; mb < 8; ++mb) {
+        const int o = rows + tro[mb];
+        dv[mb] = mfma16(tr_pair(cur.o + o, cur.o + o + 16 * kD), pb, dv[mb]);
+        dk[mb] = mfma16(tr_pair(cur.q + o, cur.q + o + 16 * kD), zb, dk[mb]);
+      }
+    }
   };
-  // Prologue: tables of chunks 0 and 1, chunk 0 staged in LDS buffer 0, chunk
-  // 1 in flight to the registers, table of chunk 2 in slot 0.
+
+  const QBuf buf0{s_q0, s_o0, s_l0, s_d0, s_m0}, buf1{s_q1, s_o1, s_l1, s_d1, s_m1};
+  const int nchunks = (src.total + kQC - 1) / kQC;
+  TabFill tf{0, 0u};
+  // Prologue: tables of chunks 0 and 1; chunk 0 staged into buffer 0.
   if (nchunks > 0) {
     fill_load(tf, src, 0);
-    fill_store(tf, src, s_tab[0]);
+    fill_store(tf, src, s_t0);
     fill_load(tf, src, kQC);
-    fill_store(tf, src, s_tab[1]);
+    fill_store(tf, src, s_t1);
     __syncthreads();
-    stage_load(st, s_tab[0], dc, Q, dO, lse2, delta);
-    stage_store(st, buf(0));
-    if (nchunks > 1) stage_load(st, s_tab[1], dc, Q, dO, lse2, delta);
-    fill_load(tf, src, 2 * kQC);
-    __syncthreads();  // slot 0 is read by everyone; buffer 0 is complete
-    fill_store(tf, src, s_tab[0]);
+    stage(buf0, s_t0, dc, Q, dO, lse2, delta);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
   }
-  // Iteration t computes chunk t from LDS buffer t & 1; then stores chunk
-  // t + 1 (loaded into registers during iteration t - 1) into buffer
-  // (t + 1) & 1, issues the loads of chunk t + 2 (table slot t & 1) and
-  // stores the table of chunk t + 3 (entry ids loaded at the start) into slot
-  // (t + 1) & 1. The staging loads thus have a whole iteration of matrix work
-  // to land in; one barrier per chunk.
-  for (int t = 0; t < nchunks; ++t) {
-    const int cb = t & 1;
-    fill_load(tf, src, (t + 3) * kQC);  // words past the last query are -1
-    const uint16_t* qr = s_qr[cb];
-    const uint16_t* dr = s_dr[cb];
-    const uint16_t* qt = s_qt[cb];
-    const uint16_t* dt = s_dt[cb];
-#pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      f32x16 s, dp;
-      zero(s);
-      zero(dp);
-#pragma unroll
-      for (int kk = 0; kk < 8; ++kk) {
-        s = mfma(rm_read(qr, 32 * sub + lr, 2 * kk + h), kb[kk], s);
-        dp = mfma(rm_read(dr, 32 * sub + lr, 2 * kk + h), vb[kk], dp);
-      }
-      // lane: key key_rel; element r: query 32 sub + acc_row(r, h)
-      float p[16], ds[16];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int q = 32 * sub + 8 * j + 4 * h;
-        const float4 l4 = *reinterpret_cast<const float4*>(&s_lse[cb][q]);
-        const float4 d4 = *reinterpret_cast<const float4*>(&s_dd[cb][q]);
-        const int4 m4 = *reinterpret_cast<const int4*>(&s_lim[cb][q]);
-        const float lv[4] = {l4.x, l4.y, l4.z, l4.w};
-        const float dv4[4] = {d4.x, d4.y, d4.z, d4.w};
-        const int mv[4] = {m4.x, m4.y, m4.z, m4.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = 4 * j + i;
-          const float x = fmaf(s[r], sl2e, -lv[i]);
-          const float pr = __builtin_amdgcn_exp2f(key_rel <= mv[i] ? x : -INFINITY);
-          p[r] = pr;
-          ds[r] = pr * (dp[r] - dv4[i]);
-        }
-      }
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const bf16x8 pb = to_b8(p + 8 * u), db8 = to_b8(ds + 8 * u);
-        const int c = 4 * sub + 2 * u + h;
-#pragma unroll
-        for (int db = 0; db < 4; ++db) {
-          dv[db] = mfma(tr_read(dt, 32 * db + lr, c), pb, dv[db]);
-          dk[db] = mfma(tr_read(qt, 32 * db + lr, c), db8, dk[db]);
-        }
-      }
-    }
-    if (t + 1 < nchunks) stage_store(st, buf(cb ^ 1));
-    if (t + 2 < nchunks) stage_load(st, s_tab[cb], dc, Q, dO, lse2, delta);
-    fill_store(tf, src, s_tab[cb ^ 1]);
+  // Iteration t: stage chunk t + 1 (table slot (t + 1) & 1) into the other
+  // buffer, load the entry ids of chunk t + 2, compute chunk t, store chunk
+  // t + 2's table into slot t & 1, wait for this wave's copies, barrier.
+  auto iter = [&](int t, QBuf cur, QBuf nxt, int64_t* tab_cur, int64_t* tab_nxt) {
+    if (t + 1 < nchunks) stage(nxt, tab_nxt, dc, Q, dO, lse2, delta);
+    fill_load(tf, src, (t + 2) * kQC);  // words past the last query are -1
+    compute(cur);
+    fill_store(tf, src, tab_cur);
+    __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
+  };
+  for (int t = 0; t < nchunks; t += 2) {
+    iter(t, buf0, buf1, s_t0, s_t1);
+    if (t + 1 < nchunks) iter(t + 1, buf1, buf0, s_t1, s_t0);
   }
   if (!kvalid) return;
-  // lane: key key_rel; element r of block db: dim 32 db + acc_row(r, h)
-  const int64_t off = ((key_first + key_rel) * Hkv + g) * kD;
+  // lane: key key_rel; register i of block mb: dim 16 mb + 4 a4 + i
+  const int64_t off = ((key_first + key_rel) * Hkv + g) * kD + 4 * a4;
 #pragma unroll
-  for (int db = 0; db < 4; ++db)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int d = 32 * db + 8 * j + 4 * h;
-      const int r = 4 * j;
-      *reinterpret_cast<uint2*>(dK + off + d) =
-          make_uint2(pack_bf16(scale * dk[db][r], scale * dk[db][r + 1]),
-                     pack_bf16(scale * dk[db][r + 2], scale * dk[db][r + 3]));
-      *reinterpret_cast<uint2*>(dV + off + d) =
-          make_uint2(pack_bf16(dv[db][r], dv[db][r + 1]), pack_bf16(dv[db][r + 2], dv[db][r + 3]));
-    }
+  for (int mb = 0; mb < 8; ++mb) {
+    *reinterpret_cast<uint2*>(dK + off + 16 * mb) =
+        make_uint2(pack_bf16(scale * dk[mb][0], scale * dk[mb][1]),
+                   pack_bf16(scale * dk[mb][2], scale * dk[mb][3]));
+    *reinterpret_cast<uint2*>(dV + off + 16 * mb) =
+        make_uint2(pack_bf16(dv[mb][0], dv[mb][1]), pack_bf16(dv[mb][2], dv[mb][3]));
+  }
 }
 
 // ===========================================================================
