@@ -43,6 +43,7 @@ EXPORTS = (
     "moba_chunk_workspace_size", "moba_prefill_chunk", "moba_select_chunk",
     "moba_cache_bytes", "moba_cache_append", "moba_cached_workspace_size", "moba_prefill_cached",
     "moba_prefill_train", "moba_backward_workspace_size", "moba_backward",
+    "moba_prefill_train_varlen", "moba_backward_varlen_workspace_size", "moba_backward_varlen",
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
@@ -99,6 +100,11 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_prefill_train": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_backward_workspace_size": (sz, [P]),
         "moba_backward": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_prefill_train_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                                     vp]),
+        "moba_backward_varlen_workspace_size": (sz, [P, i64, vp]),
+        "moba_backward_varlen": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp,
+                                                vp, vp, sz, vp]),
         "moba_chunk_workspace_size": (sz, [P, i64]),
         "moba_prefill_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, vp, sz, vp]),
         "moba_select_chunk": (ctypes.c_int, [P, i64, vp, vp, vp, vp, sz, vp]),
@@ -425,6 +431,50 @@ class DecodeCache:
                                      _stream(q.device))
         _ok(st, "moba_prefill_cached")
         return out
+
+
+def prefill_train_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None,
+                         routing=MOBA_ROUTING_PER_HEAD):
+    """``prefill_train`` over packed sequences (the layout of ``prefill_varlen``):
+    (O [N, Hq, d], lse [N, Hq] fp32)."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
+    out = torch.empty_like(q)
+    lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
+    need = lib.moba_varlen_workspace_size(ctypes.byref(prob), nseq, cu_host)
+    if need == 0:
+        _ok(lib.moba_prefill_train_varlen(ctypes.byref(prob), nseq, cu_host, *([None] * 7), 0,
+                                          None), "moba_varlen_workspace_size")
+    ws = alloc_workspace(need, q.device)
+    st = lib.moba_prefill_train_varlen(ctypes.byref(prob), nseq, cu_host, cu_dev.data_ptr(),
+                                       q.data_ptr(), k.data_ptr(), v.data_ptr(), out.data_ptr(),
+                                       lse.data_ptr(), ws.data_ptr(), ws.numel(),
+                                       _stream(q.device))
+    _ok(st, "moba_prefill_train_varlen")
+    return out, lse
+
+
+def backward_varlen(q, k, v, o, lse, dout, cu_seqlens, block_size, topk, scale=None,
+                    routing=MOBA_ROUTING_PER_HEAD):
+    """``backward`` over packed sequences: (dq, dk, dv)."""
+    lib = load_library()
+    _check_dev(q, k, v, o, lse, dout)
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    need = lib.moba_backward_varlen_workspace_size(ctypes.byref(prob), nseq, cu_host)
+    if need == 0:
+        _ok(lib.moba_backward_varlen(ctypes.byref(prob), nseq, cu_host, *([None] * 10), 0, None),
+            "moba_backward_varlen_workspace_size")
+    ws = alloc_workspace(need, q.device)
+    st = lib.moba_backward_varlen(ctypes.byref(prob), nseq, cu_host, cu_dev.data_ptr(),
+                                  q.data_ptr(), k.data_ptr(), v.data_ptr(), o.data_ptr(),
+                                  lse.data_ptr(), dout.data_ptr(), dq.data_ptr(), dk.data_ptr(),
+                                  dv.data_ptr(), ws.data_ptr(), ws.numel(), _stream(q.device))
+    _ok(st, "moba_backward_varlen")
+    return dq, dk, dv
 
 
 def chunk_workspace_size(prob: MobaProblem, q_rows: int) -> int:

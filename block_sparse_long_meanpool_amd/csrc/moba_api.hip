@@ -501,12 +501,11 @@ size_t moba_backward_workspace_size(const moba_problem_t* p) {
   return plan_ws_bwd(P).total;
 }
 
-int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v,
-                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
-                  void* workspace, size_t ws_bytes, void* stream) {
-  Prob P;
-  int rc = make_prob(p, &P);
-  if (rc) return rc;
+static int run_backward(const Prob& P, const int64_t* cu_dev, const void* q, const void* k,
+                        const void* v, const void* o, const float* lse, const void* dout,
+                        void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                        void* stream) {
+  int rc;
   const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, nullptr};
   if ((rc = check_ptrs(ptrs, 9, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL")))
     return rc;
@@ -514,7 +513,7 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
   hipStream_t s = (hipStream_t)stream;
   int32_t* sel = at<int32_t>(workspace, L.sel);
-  if ((rc = run_select(P, nullptr, q, k, sel, workspace, L, s, nullptr))) return rc;
+  if ((rc = run_select(P, cu_dev, q, k, sel, workspace, L, s, nullptr))) return rc;
   const Blocks T = tables(workspace, L);
   const BucketPlan bp = plan_bucket(P);
   const BucketBufs bb = bucket_bufs(workspace, L);
@@ -530,6 +529,51 @@ int moba_backward(const moba_problem_t* p, const void* q, const void* k, const v
   }
   e = launch_backward(P, T, bp, bb, q, k, v, o, lse, dout, dq, dk, dv, w, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "moba_backward");
+}
+
+int moba_backward(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                  const void* o, const float* lse, const void* dout, void* dq, void* dk, void* dv,
+                  void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  return run_backward(P, nullptr, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes, stream);
+}
+
+int moba_prefill_train_varlen(const moba_problem_t* p, int64_t nseq,
+                              const int64_t* cu_seqlens_host, const int64_t* cu_seqlens_dev,
+                              const void* q, const void* k, const void* v, void* o, float* lse,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  Prob P;
+  int rc = make_prob_varlen(p, nseq, cu_seqlens_host, &P);
+  if (rc) return rc;
+  if ((rc = check_cu_dev(cu_seqlens_dev))) return rc;
+  const void* ptrs[5] = {q, k, v, o, lse};
+  if ((rc = check_ptrs(ptrs, 5, "q, k, v, o and lse must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, true);
+  if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  return run_prefill(P, cu_seqlens_dev, q, k, v, o, workspace, L, (hipStream_t)stream, nullptr,
+                     lse);
+}
+
+size_t moba_backward_varlen_workspace_size(const moba_problem_t* p, int64_t nseq,
+                                           const int64_t* cu_seqlens_host) {
+  Prob P;
+  if (make_prob_varlen(p, nseq, cu_seqlens_host, &P) != MOBA_OK) return 0;
+  return plan_ws_bwd(P).total;
+}
+
+int moba_backward_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu_seqlens_host,
+                         const int64_t* cu_seqlens_dev, const void* q, const void* k,
+                         const void* v, const void* o, const float* lse, const void* dout,
+                         void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
+                         void* stream) {
+  Prob P;
+  int rc = make_prob_varlen(p, nseq, cu_seqlens_host, &P);
+  if (rc) return rc;
+  if ((rc = check_cu_dev(cu_seqlens_dev))) return rc;
+  return run_backward(P, cu_seqlens_dev, q, k, v, o, lse, dout, dq, dk, dv, workspace, ws_bytes,
+                      stream);
 }
 
 size_t moba_chunk_workspace_size(const moba_problem_t* p, int64_t q_rows) {

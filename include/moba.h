@@ -196,6 +196,26 @@ MOBA_API int moba_backward(const moba_problem_t *p, const void *q, const void *k
                            void *dk, void *dv, void *workspace, size_t ws_bytes, void *stream);
 
 /*
+ * Training on packed sequences: moba_prefill_train and moba_backward for the
+ * packed layout of moba_prefill_varlen (same nseq / cu_seqlens arguments and
+ * rules). Each sequence's result equals the single-sequence call on that
+ * sequence alone. Workspaces: moba_varlen_workspace_size (forward) and
+ * moba_backward_varlen_workspace_size (backward).
+ */
+MOBA_API int moba_prefill_train_varlen(const moba_problem_t *p, int64_t nseq,
+                                       const int64_t *cu_seqlens_host,
+                                       const int64_t *cu_seqlens_dev, const void *q,
+                                       const void *k, const void *v, void *o, float *lse,
+                                       void *workspace, size_t ws_bytes, void *stream);
+MOBA_API size_t moba_backward_varlen_workspace_size(const moba_problem_t *p, int64_t nseq,
+                                                    const int64_t *cu_seqlens_host);
+MOBA_API int moba_backward_varlen(const moba_problem_t *p, int64_t nseq,
+                                  const int64_t *cu_seqlens_host, const int64_t *cu_seqlens_dev,
+                                  const void *q, const void *k, const void *v, const void *o,
+                                  const float *lse, const void *dout, void *dq, void *dk,
+                                  void *dv, void *workspace, size_t ws_bytes, void *stream);
+
+/*
  * Chunked prefill and decode: the queries are the last q_rows positions of
  * one sequence whose keys and values (all p->seqlen rows, the new ones
  * included) are already in k and v — a KV cache. q and o hold only those

@@ -251,3 +251,27 @@ def test_prefill_cached_rejects_bad_arguments():
     assert lib.moba_prefill_cached(*args(2000, 4, None, ws)) == 1         # cache
     assert lib.moba_prefill_cached(*args(2000, 4, FAKE + 16, ws)) == 1    # misaligned cache
     assert lib.moba_prefill_cached(*args(2000, 4, FAKE, ws - 1)) == 3     # workspace
+
+
+def test_varlen_training_rejects_bad_arguments():
+    lib = moba.load_library()
+    p = _prob(N=1000)
+    cu = _cu(0, 400, 1000)
+    assert lib.moba_backward_varlen_workspace_size(ctypes.byref(p), 2, cu) > 0
+    assert lib.moba_backward_varlen_workspace_size(ctypes.byref(p), 2, _cu(0, 400, 999)) == 0
+    ws = lib.moba_backward_varlen_workspace_size(ctypes.byref(p), 2, cu)
+    # one packed sequence needs the same workspace as the plain backward
+    assert lib.moba_backward_varlen_workspace_size(ctypes.byref(p), 1, _cu(0, 1000)) == \
+        lib.moba_backward_workspace_size(ctypes.byref(p))
+    f = [FAKE] * 9
+    assert lib.moba_backward_varlen(ctypes.byref(p), 2, cu, None, *f, FAKE, ws, None) == 1
+    assert lib.moba_backward_varlen(ctypes.byref(p), 2, _cu(0, 1001, 1000), FAKE, *f, FAKE, ws,
+                                    None) == 1
+    f2 = list(f)
+    f2[6] = None  # dq
+    assert lib.moba_backward_varlen(ctypes.byref(p), 2, cu, FAKE, *f2, FAKE, ws, None) == 1
+    assert lib.moba_backward_varlen(ctypes.byref(p), 2, cu, FAKE, *f, FAKE, ws - 1, None) == 3
+    assert lib.moba_prefill_train_varlen(ctypes.byref(p), 2, cu, None, FAKE, FAKE, FAKE, FAKE,
+                                         FAKE, FAKE, 1 << 40, None) == 1
+    assert lib.moba_prefill_train_varlen(ctypes.byref(p), 2, cu, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                         None, FAKE, 1 << 40, None) == 1

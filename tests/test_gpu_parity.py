@@ -515,3 +515,42 @@ def test_backward_bf16_is_deterministic():
     b = moba.backward(tq, tk, tv, o, lse, dout, B, topk, 0.09)
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+BWD_VARLEN = [
+    # lengths, Hq, Hkv, B, topk, dtype
+    ([700, 0, 1, 1300, 513], 4, 2, 128, 3, "bf16"),
+    ([300, 900, 5], 4, 1, 96, 4, "bf16"),   # B not a multiple of 64
+    ([400, 1, 600], 2, 2, 64, 3, "f32"),
+]
+
+
+@pytest.mark.parametrize("lens,Hq,Hkv,B,topk,dtype", BWD_VARLEN)
+def test_backward_varlen_matches_each_sequence(lens, Hq, Hkv, B, topk, dtype):
+    """Training on packed sequences: the packed forward (with row statistics)
+    equals the packed inference forward, and the packed gradients equal the
+    oracle's gradients of every sequence on its own."""
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N = int(cu[-1])
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + 11, dtype=dtype)
+    scale = 0.09
+    o, lse = moba.prefill_train_varlen(tq, tk, tv, cu, B, topk, scale)
+    assert torch.equal(o, moba.prefill_varlen(tq, tk, tv, cu, B, topk, scale))
+    gen = torch.Generator(device="cpu").manual_seed(N)
+    dout = torch.randn(tq.shape, generator=gen).to(tq.dtype).to(DEV)
+    dq, dk, dv = moba.backward_varlen(tq, tk, tv, o, lse, dout, cu, B, topk, scale)
+    sel = moba.select_varlen(tq, tk, cu, B, topk).cpu().numpy()
+    rq, rk, rv = np.zeros_like(to_np(dq)), np.zeros_like(to_np(dk)), np.zeros_like(to_np(dv))
+    d_np = to_np(dout)
+    base = 0  # first global block of the sequence
+    for s in range(len(lens)):
+        a, b = int(cu[s]), int(cu[s + 1])
+        if b > a:
+            loc = sel[a:b].copy()
+            loc[loc >= 0] -= base
+            rq[a:b], rk[a:b], rv[a:b] = oracle.backward(q[a:b], k[a:b], v[a:b], d_np[a:b], B,
+                                                        topk, scale=scale, sel=loc)
+        base += -(-(b - a) // B)
+    _grad_close(to_np(dq), rq, dtype, "dq")
+    _grad_close(to_np(dk), rk, dtype, "dk")
+    _grad_close(to_np(dv), rv, dtype, "dv")
