@@ -107,7 +107,7 @@ def cpu_baseline(w, q, k, v, rows_wanted):
 def backward_leg():
     """Training leg on the 32K layer: forward with row statistics, then the
     backward pass (each the mean of 5 calls)."""
-    wb = synth.CONFIGS["c3"]
+    wb = synth.CONFIGS["mha32k_needles"]
     bq, bk, bv = (to_dev(a) for a in synth.make_qkv(wb, "bf16"))
     gen = torch.Generator(device="cpu").manual_seed(1)
     dout = torch.randn(bq.shape, generator=gen).to(torch.bfloat16).to(bq.device)
@@ -207,7 +207,7 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--config", default="c5", choices=sorted(synth.CONFIGS))
+    ap.add_argument("--config", default="llama8b_1m", choices=sorted(synth.CONFIGS))
     ap.add_argument("--cpu-rows", type=int, default=1024)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
@@ -228,7 +228,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the MoBA prefill path here runs on a single "
-              "MI355X (a multi-GPU split by KV-head group is described in DESIGN.md, not built).",
+              "MI355X (a split by KV-head group across GPUs is not built).",
               file=sys.stderr)
         sys.exit(2)
 
@@ -397,7 +397,7 @@ def main():
         "roofline": {"bound": "mfma", "kernel": "attn_hist_bf16",
                      "achieved": hist_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": hist_tflops / PEAK_BF16_TFLOPS,
-                     "traffic": read_traffic("attn_hist_c5")},
+                     "traffic": read_traffic("attn_hist_llama8b_1m")},
         "dense_causal": dense,
         "varlen": varlen,
         "shared_routing": shared,

@@ -2,13 +2,13 @@
 
 The five workloads mirror the shapes of the experiments on the pages:
 
-* ``c1`` tiny single-head layer (N=2048, B=256, k=3), fp32 masters;
-* ``c2`` the scaling-law setting at 8K (N=8192, B=512, k=3, 16 heads) —
+* ``tiny2k`` tiny single-head layer (N=2048, B=256, k=3), fp32 masters;
+* ``mha8k`` the scaling-law setting at 8K (N=8192, B=512, k=3, 16 heads) —
   MoBA paper summary (PaperTrace "2.1.3 MoBA", section 2.1, eq. (9));
-* ``c3`` the same block/top-k at 32K with long-range "needle" blocks;
-* ``c4`` the efficient-vs-naive comparison shape (32K, 1 head, B=2048, k=3) —
+* ``mha32k_needles`` the same block/top-k at 32K with long-range "needle" blocks;
+* ``coarse32k`` the efficient-vs-naive comparison shape (32K, 1 head, B=2048, k=3) —
   MoonshotAI/MoBA README, implementation details;
-* ``c5`` the Llama-3.1-8B 1M-token layer (B=4096, k=12) with 32 query heads
+* ``llama8b_1m`` the Llama-3.1-8B 1M-token layer (B=4096, k=12) with 32 query heads
   sharing 8 KV heads — agihunt summary, results section.
 
 Values come from ``synth.c`` (SplitMix64 counters + Box-Muller); the C
@@ -57,13 +57,17 @@ class Workload:
         return replace(self, **kw)
 
 
+# Workloads shaped like the pages' experiments, named by what they are:
+# a tiny single-head layer (2K rows), a 16-head layer at 8K and at 32K (the
+# latter with planted needle blocks), a single-head coarse-block layer at 32K,
+# and a Llama-3.1-8B-shaped GQA layer (32 query / 8 KV heads) at 1M rows.
 CONFIGS = {
-    "c1": Workload("c1", 2048, 1, 1, 128, 256, 3, dtype="f32", seed=SEED_BASE | 1),
-    "c2": Workload("c2", 8192, 16, 16, 128, 512, 3, seed=SEED_BASE | 2),
-    "c3": Workload("c3", 32768, 16, 16, 128, 512, 3, needle_blocks=8, needle_gain=1.5,
-                   needle_row_frac=0.01, seed=SEED_BASE | 3),
-    "c4": Workload("c4", 32768, 1, 1, 128, 2048, 3, seed=SEED_BASE | 4),
-    "c5": Workload("c5", 1048576, 32, 8, 128, 4096, 12, seed=SEED_BASE | 5),
+    "tiny2k": Workload("tiny2k", 2048, 1, 1, 128, 256, 3, dtype="f32", seed=SEED_BASE | 1),
+    "mha8k": Workload("mha8k", 8192, 16, 16, 128, 512, 3, seed=SEED_BASE | 2),
+    "mha32k_needles": Workload("mha32k_needles", 32768, 16, 16, 128, 512, 3, needle_blocks=8,
+                               needle_gain=1.5, needle_row_frac=0.01, seed=SEED_BASE | 3),
+    "coarse32k": Workload("coarse32k", 32768, 1, 1, 128, 2048, 3, seed=SEED_BASE | 4),
+    "llama8b_1m": Workload("llama8b_1m", 1048576, 32, 8, 128, 4096, 12, seed=SEED_BASE | 5),
 }
 
 

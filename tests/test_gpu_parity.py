@@ -44,7 +44,7 @@ def all_rows(N, Hq):
 
 
 # ------------------------------------------------------------------ stages ---
-@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None)])
+@pytest.mark.parametrize("name,dtype", [("tiny2k", "f32"), ("tiny2k", "bf16"), ("mha8k", None), ("coarse32k", None)])
 def test_meanpool_exact(name, dtype):
     w, q, k, v, tq, tk, tv = inputs(name, dtype)
     got = moba.debug_meanpool(tk, w.B).cpu().numpy()
@@ -62,8 +62,8 @@ def test_meanpool_irregular(N, Hkv, B):
     assert np.array_equal(got, oracle.block_means(k, B))
 
 
-@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None),
-                                        ("c3", None)])
+@pytest.mark.parametrize("name,dtype", [("tiny2k", "f32"), ("tiny2k", "bf16"), ("mha8k", None), ("coarse32k", None),
+                                        ("mha32k_needles", None)])
 def test_select_all_rows(name, dtype):
     w, q, k, v, tq, tk, tv = inputs(name, dtype)
     sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
@@ -104,7 +104,7 @@ def test_bucket_lists(N, Hq, Hkv, B, topk):
 
 
 # ---------------------------------------------------------------- prefill ---
-@pytest.mark.parametrize("name,dtype", [("c1", "f32"), ("c1", "bf16"), ("c2", None), ("c4", None)])
+@pytest.mark.parametrize("name,dtype", [("tiny2k", "f32"), ("tiny2k", "bf16"), ("mha8k", None), ("coarse32k", None)])
 def test_prefill_all_rows(name, dtype):
     w, q, k, v, tq, tk, tv = inputs(name, dtype)
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
@@ -117,12 +117,12 @@ def test_prefill_all_rows(name, dtype):
 
 
 def test_prefill_c3_sampled_and_needles():
-    w, q, k, v, tq, tk, tv = inputs("c3")
+    w, q, k, v, tq, tk, tv = inputs("mha32k_needles")
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
     rows, heads = synth.sample_rows(w, 4096)
     (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads, sel[rows, heads],
-                                    to_np(o)[rows, heads], "bf16", "c3")
+                                    to_np(o)[rows, heads], "bf16", "mha32k_needles")
     # needle rows pick needle blocks: long-range selection is exercised
     hits = 0
     for h in range(2):
@@ -133,12 +133,12 @@ def test_prefill_c3_sampled_and_needles():
             if len(legal) >= w.k - 1:
                 hits += set(sel[r, h, : w.k - 1].tolist()) <= legal
     assert hits > 0
-    print(f"c3: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied} needle rows routed {hits}")
+    print(f"mha32k_needles: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied} needle rows routed {hits}")
 
 
 @pytest.mark.timeout(1200)
 def test_prefill_c5_sampled():
-    w, q, k, v, tq, tk, tv = inputs("c5")
+    w, q, k, v, tq, tk, tv = inputs("llama8b_1m")
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     sel = moba.select(tq, tk, w.B, w.k)
     torch.cuda.synchronize()
@@ -148,12 +148,12 @@ def test_prefill_c5_sampled():
     kbar = oracle.block_means(k, w.B)
     got_o = o_np[torch.from_numpy(rows), torch.from_numpy(heads.astype(np.int64))].float().numpy()
     (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads, sel_np[rows, heads],
-                                    got_o.astype(np.float64), "bf16", "c5")
+                                    got_o.astype(np.float64), "bf16", "llama8b_1m")
     # selections on a larger seeded sample (gate only)
     r2, h2 = synth.sample_rows(w.with_(seed=w.seed ^ 0xABCDEF), 1 << 20)
     ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, r2, h2, want_o=False, kbar=kbar)
-    check_selection(sel_np[r2, h2], ref_sel, gap, "c5 sel")
-    print(f"c5: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
+    check_selection(sel_np[r2, h2], ref_sel, gap, "llama8b_1m sel")
+    print(f"llama8b_1m: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
 
 
 # ------------------------------------------------------------- edge cases ---
@@ -223,14 +223,14 @@ def test_dense_baseline_and_full_coverage(dtype):
 
 
 def test_deterministic():
-    w, q, k, v, tq, tk, tv = inputs("c2")
+    w, q, k, v, tq, tk, tv = inputs("mha8k")
     a = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     b = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_stage_events_and_copy():
-    w, q, k, v, tq, tk, tv = inputs("c2")
+    w, q, k, v, tq, tk, tv = inputs("mha8k")
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_STAGE_EVENTS)]
     moba.prefill(tq, tk, tv, w.B, w.k, w.scale, events=ev)
     torch.cuda.synchronize()
