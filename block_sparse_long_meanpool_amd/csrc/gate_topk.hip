@@ -23,12 +23,24 @@
 //     k-1'th and k'th scores differ by more than 2 eps (plus the key
 //     truncation): then every exact score of the kept set exceeds every exact
 //     score left out, so the kept set is the exact one.
-//  2. Exact tier: rows that are not certified (near-ties, about 2% of rows
-//     for random data) are marked in `sel` and a second kernel re-scores each
-//     marked row in fp64 with one wave (lane per block, block keys stored
-//     transposed so the reads coalesce) and selects exactly (value
-//     descending, index ascending). fp32 inputs take this exact path for
-//     every row.
+//  2. Exact tier: rows that are not certified (near-ties; about 0.5% of the
+//     rows of a 1M-row random layer) are marked in `sel` and a second kernel
+//     re-scores each marked row in fp64 with one wave (lane per block, block
+//     keys stored transposed so the reads coalesce) and selects exactly
+//     (value descending, index ascending). fp32 inputs take this exact path
+//     for every row.
+//
+// Group-shared routing ranks blocks by the group's summed query
+// q_g = sum_h q_h (exact in fp64 for bf16 inputs of ordinary range). Its fast
+// tier splits q_g into three bf16 planes as well and takes the six plane
+// products that reach 2^-16 of the score: hi.hi over dims 0..63 and 64..127
+// (two chains of 64), hi.mid + mid.hi (one chain of 256), hi.lo + lo.hi +
+// mid.mid (one chain of 384); s = (A + B) + (C + D). With T = sum_c
+// |q_g,c kbar_c|: A and B <= 64 u T (1 + 2^-8); C <= 256 u 2^-7 (1 + 2^-8) T
+// = 2.01 u T; D <= 384 u 3 2^-16 T = 0.02 u T; the three products left out
+// (mid.lo, lo.mid, lo.lo) <= 1.5 u T; the residuals of both splits <= u T;
+// three additions <= 3 u T. So |s_fast - s| <= 71.8 u T <= 8.56e-6 |q_g|
+// max_b |kbar_b|, and certification is as above.
 //
 // Workgroup = 4 waves x 32 (row, head) pairs of one KV-head group inside one
 // block c (pairs pi = (row - cB) * G + hh). The bf16 planes of 32 history
@@ -51,6 +63,7 @@ constexpr int kRowBytes = kHeadDim * 2;   // one bf16 plane row of one block
 constexpr int kChunkRows = 3 * kChunk;    // (block, plane) rows per chunk
 constexpr int kChunkElems = kChunkRows * kHeadDim;
 constexpr float kEpsCoef = 8.4e-6f * 1.02f;  // error bound coefficient (see above) with margin
+constexpr float kEpsCoefShared = 8.56e-6f * 1.02f;  // the same for group-shared routing
 constexpr int kRawBufferFlags = 0x00020000;
 
 __device__ inline bf16x8 as_bf16x8(uint4 u) { return __builtin_bit_cast(bf16x8, u); }
@@ -215,6 +228,35 @@ __device__ inline void chunk_scores(const uint16_t* lds, const bf16x8 (&q)[8], i
   for (int r = 0; r < 16; ++r) s[r] = (a0[r] + a0b[r]) + (a1[r] + a2[r]);
 }
 
+// Group-shared scores: the group query in three bf16 planes q[0..2] (hi,
+// mid, lo); chains and their sum as in the shared-routing bound above.
+__device__ inline void chunk_scores_shared(const uint16_t* lds, const bf16x8 (&q)[3][8], int lane,
+                                           f32x16& s) {
+  const int h = lane >> 5, lr = lane & 31;
+  f32x16 a, b, c2, d;
+#pragma unroll
+  for (int r = 0; r < 16; ++r) a[r] = b[r] = c2[r] = d[r] = 0.f;
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) {
+    const int c = 2 * kk + h;
+    const int r0 = 3 * lr, r1 = 3 * lr + 1, r2 = 3 * lr + 2;
+    const bf16x8 x0 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r0 * kHeadDim + 8 * swz(r0, c)));
+    const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r1 * kHeadDim + 8 * swz(r1, c)));
+    const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r2 * kHeadDim + 8 * swz(r2, c)));
+    if (kk < 4)
+      a = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[0][kk], a, 0, 0, 0);
+    else
+      b = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[0][kk], b, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, q[0][kk], c2, 0, 0, 0);
+    c2 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[1][kk], c2, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x2, q[0][kk], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[2][kk], d, 0, 0, 0);
+    d = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x1, q[1][kk], d, 0, 0, 0);
+  }
+#pragma unroll
+  for (int r = 0; r < 16; ++r) s[r] = (a[r] + b[r]) + (c2[r] + d[r]);
+}
+
 constexpr int32_t kRefine = -2;  // sel marker: this row's history needs the exact tier
 
 template <typename T>
@@ -240,6 +282,10 @@ __device__ inline double widen<double>(double x) {
 // sorted list of its blocks (they arrive in increasing order), then KH rounds
 // of wave arg-max over the list heads pick the kept blocks. Writes the whole
 // row: kept blocks ascending, own block, -1 padding.
+// Group-shared routing passes pairs (row, KV head) (Hq = Hkv, G = 1) and
+// gq = the group size: the scoring query is the fp64 sum of the gq query
+// heads ph * gq .. ph * gq + gq - 1 of Q, and the row (and margin) is written
+// for each of them; a pair's marker sits in its first head's row.
 template <typename T, int KM>
 __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
                                                   const double* __restrict__ kbarT,
@@ -248,7 +294,7 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
                                                   int32_t* __restrict__ sel,
                                                   float* __restrict__ margin, int64_t N, int Hq,
                                                   int G, int k, int64_t nhp, int all_rows,
-                                                  int ppw) {
+                                                  int ppw, int gq) {
   __shared__ double qs[kHeadDim];
   const int lane = threadIdx.x;
   const int KH = k - 1;
@@ -259,15 +305,17 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     const int64_t ph = ph0 + lane;
     if (lane < ppw && ph < nph) {
       const int64_t c = row_blk[ph / Hq], lo = blo[c];
-      int32_t* out = sel + ph * k;
       if (c - lo > KH && KH > 0) {
-        mine = all_rows || out[0] == kRefine;
+        mine = all_rows || sel[ph * gq * k] == kRefine;
       } else if (all_rows) {  // every earlier block of the sequence is taken
         const int nsel = (int)(c - lo < KH ? c - lo : KH);
-        if (margin) margin[ph] = __builtin_nanf("");  // nothing left out
-        for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
-        out[nsel] = (int32_t)c;
-        for (int a = nsel + 1; a < k; ++a) out[a] = -1;
+        for (int hh = 0; hh < gq; ++hh) {
+          int32_t* out = sel + (ph * gq + hh) * k;
+          if (margin) margin[ph * gq + hh] = __builtin_nanf("");  // nothing left out
+          for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
+          out[nsel] = (int32_t)c;
+          for (int a = nsel + 1; a < k; ++a) out[a] = -1;
+        }
       }
     }
   }
@@ -278,9 +326,14 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     const int64_t ph = ph0 + l;
     const int64_t c = row_blk[ph / Hq], lo = blo[c];
     const int g = (int)(ph % Hq) / G;
-    const T* qrow = Q + ph * kHeadDim;
-    qs[2 * lane] = widen<T>(qrow[2 * lane]);
-    qs[2 * lane + 1] = widen<T>(qrow[2 * lane + 1]);
+    const T* qrow = Q + ph * gq * kHeadDim;
+    double q0 = 0.0, q1 = 0.0;  // the sum of gq bf16 or fp32 values is exact in fp64
+    for (int hh = 0; hh < gq; ++hh) {
+      q0 += widen<T>(qrow[(int64_t)hh * kHeadDim + 2 * lane]);
+      q1 += widen<T>(qrow[(int64_t)hh * kHeadDim + 2 * lane + 1]);
+    }
+    qs[2 * lane] = q0;
+    qs[2 * lane + 1] = q1;
     __syncthreads();
     double v[KM];
     int ix[KM];
@@ -341,9 +394,9 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
       if (rnd == KH - 1) last = bv;
       if (rnd == KH) next = bv;
     }
-    if (lane == 0) {
-      if (margin) margin[ph] = KH > 0 ? (float)(last - next) : __builtin_nanf("");
-      int32_t* out = sel + ph * k;
+    if (lane < gq) {
+      if (margin) margin[ph * gq + lane] = KH > 0 ? (float)(last - next) : __builtin_nanf("");
+      int32_t* out = sel + (ph * gq + lane) * k;
       write_sorted<KM>(chosen, KH, out);
       out[KH] = (int32_t)c;
       for (int a = KH + 1; a < k; ++a) out[a] = -1;
@@ -352,12 +405,16 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
   }
 }
 
-template <int KM>
+// SHARED: pairs are (row, KV head) (Hq = Hkv, G = 1); the scoring query is
+// the fp64 sum of the pair's gq query heads of Q, split into three bf16
+// planes here, and the row is written for each of those heads.
+template <int KM, bool SHARED>
 __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
     const float* __restrict__ maxnorm, const int32_t* __restrict__ qstart,
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ blo, int32_t* __restrict__ sel,
-    int Hq, int G, int k, int64_t n, int64_t nh, int tiles_per_block) {
+    int Hq, int G, int gq_arg, int k, int64_t n, int64_t nh, int tiles_per_block) {
+  const int gq = SHARED ? gq_arg : 1;  // query heads per pair
   __shared__ __align__(16) uint16_t bufA[kChunkElems];
   __shared__ __align__(16) uint16_t bufB[kChunkElems];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5, lr = lane & 31;
@@ -376,34 +433,71 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   const bool valid = pi < npairs_c;
   const int64_t r = row0 + (valid ? pi / G : 0);
   const int hq = g * G + (int)(valid ? pi % G : 0);
-  int32_t* out = sel + ((size_t)r * Hq + hq) * k;
+  // the pair's rows of sel: heads (r * Hq + hq) * gq + 0 .. gq-1
+  int32_t* out = sel + ((size_t)r * Hq + hq) * gq * k;
   const int nsel = (int)(nc < KH ? nc : KH);
 
   if (nc <= KH || KH == 0) {  // every earlier block is taken: nothing to rank
     if (valid && h == 0) {
-      for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
-      out[nsel] = (int32_t)c;
-      for (int a = nsel + 1; a < k; ++a) out[a] = -1;
+      for (int hh = 0; hh < gq; ++hh) {
+        int32_t* o = out + hh * k;
+        for (int a = 0; a < nsel; ++a) o[a] = (int32_t)(lo + a);
+        o[nsel] = (int32_t)c;
+        for (int a = nsel + 1; a < k; ++a) o[a] = -1;
+      }
     }
     return;
   }
 
   // Q as the B operand: Q[pair][16kk + 8h .. +8]; |q|^2 from the same values
-  const uint16_t* qrow = Q + ((size_t)r * Hq + hq) * kHeadDim;
-  bf16x8 q[8];
+  constexpr int NP = SHARED ? 3 : 1;  // query planes
+  const uint16_t* qrow = Q + ((size_t)r * Hq + hq) * gq * kHeadDim;
+  bf16x8 q[NP][8];
   float qq = 0.f;
+  if constexpr (!SHARED) {
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) {
-    const uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
-                          : make_uint4(0, 0, 0, 0);
-    q[kk] = as_bf16x8(u);
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
+                            : make_uint4(0, 0, 0, 0);
+      q[0][kk] = as_bf16x8(u);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float x = (float)q[kk][e];
-      qq = fmaf(x, x, qq);
+      for (int e = 0; e < 8; ++e) {
+        const float x = (float)q[0][kk][e];
+        qq = fmaf(x, x, qq);
+      }
     }
+    qq += __shfl_xor(qq, 32);
+  } else {
+    // group query x = sum of the gq heads (exact in fp64), split like the block keys
+    double ss = 0.0;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      double x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = 0.0;
+      for (int hh = 0; hh < gq; ++hh) {
+        const uint4 u = valid ? *reinterpret_cast<const uint4*>(qrow + hh * kHeadDim + 16 * kk + 8 * h)
+                              : make_uint4(0, 0, 0, 0);
+        const bf16x8 b = as_bf16x8(u);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] += (double)(float)b[e];
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const uint16_t p0 = bf16_rne((float)x[e]);
+        const double r1 = x[e] - bf16_to_f64(p0);
+        const uint16_t p1 = bf16_rne((float)r1);
+        const uint16_t p2 = bf16_rne((float)(r1 - bf16_to_f64(p1)));
+        q[0][kk][e] = __builtin_bit_cast(__bf16, p0);
+        q[1][kk][e] = __builtin_bit_cast(__bf16, p1);
+        q[2][kk][e] = __builtin_bit_cast(__bf16, p2);
+        ss = fma(x[e], x[e], ss);
+      }
+    }
+    ss += __shfl_xor(ss, 32);
+    const float qn = (float)(sqrt(ss) * (1.0 + 1e-6));  // |x|, rounded up
+    qq = qn * qn;
   }
-  qq += __shfl_xor(qq, 32);
 
   // candidates by local index b - lo in [0, nc)
   const uint16_t* planes_g = planes + ((size_t)g * nh + lo) * 3 * kHeadDim;
@@ -416,7 +510,10 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   auto step = [&](int ch, uint16_t* cur, uint16_t* nxt) {
     if (ch + 1 < nchunks) load_chunk(nxt, planes_g, (int64_t)(ch + 1) * kChunk, nc, wave, lane);
     f32x16 s;
-    chunk_scores(cur, q, lane, s);
+    if constexpr (SHARED)
+      chunk_scores_shared(cur, q, lane, s);
+    else
+      chunk_scores(cur, q[0], lane, s);
     const int64_t cb = (int64_t)ch * kChunk;
 #pragma unroll
     for (int e = 0; e < 16; ++e) {  // blocks past the candidates push key 0, which never enters
@@ -453,59 +550,27 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   const float theta = key_score(kk_in, ib), theta_n = key_score(kk_out, ib);
   const float big = fmaxf(fabsf(theta), fabsf(theta_n));
   const float trunc = ldexpf(big, ib - 22);  // >= 2^ib units in the last place of |score| <= big
-  const float eps = kEpsCoef * sqrtf(qq) * 1.0001f * kmax;
+  const float eps = (SHARED ? kEpsCoefShared : kEpsCoef) * sqrtf(qq) * 1.0001f * kmax;
   const bool certified = (theta - theta_n) > 2.f * eps + trunc + 1e-6f * big;
   if (valid && h == 0) {
-    if (certified)
-      write_sorted<KM>(idx, KH, out);
-    else
-      out[0] = kRefine;  // completed by gate_refine
-    out[KH] = (int32_t)c;
-    for (int a = KH + 1; a < k; ++a) out[a] = -1;
+    if (certified) {
+      for (int hh = 0; hh < gq; ++hh) {
+        int32_t* o = out + hh * k;
+        write_sorted<KM>(idx, KH, o);
+        o[KH] = (int32_t)c;
+        for (int a = KH + 1; a < k; ++a) o[a] = -1;
+      }
+    } else {
+      out[0] = kRefine;  // gate_refine writes the pair's rows
+    }
   }
 
 }
 
-// Group-shared routing: one selection per (row, KV head) from the summed
-// score of the group's query heads, sum_h q_h . kbar_i = (sum_h q_h) . kbar_i.
-// The group query is summed in fp64 (exact for bf16 and fp32 inputs of
-// ordinary range); Qg [N][Hkv][d].
+// Exact tier over every row of an N x Hq_eff problem with groups of G_eff
+// (gq: query heads summed per pair, group-shared routing).
 template <typename T>
-__global__ void group_sum_q(const T* __restrict__ Q, double* __restrict__ Qg, int64_t N, int Hkv,
-                            int G) {
-  const int64_t total = N * Hkv * kHeadDim;
-  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < total;
-       i += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t c = i % kHeadDim, rg = i / kHeadDim;  // rg = row * Hkv + g
-    const T* src = Q + (rg * G) * kHeadDim + c;         // heads g*G .. g*G+G-1 of the row
-    double acc = 0.0;
-    for (int hh = 0; hh < G; ++hh) acc += widen<T>(src[(int64_t)hh * kHeadDim]);
-    Qg[i] = acc;
-  }
-}
-
-// sel [N][Hq][k] and margin [N][Hq] from the per-(row, KV head) ones.
-__global__ void expand_group(const int32_t* __restrict__ selg, const float* __restrict__ mg,
-                             int32_t* __restrict__ sel, float* __restrict__ margin, int64_t N,
-                             int Hq, int G, int k) {
-  const int64_t total = N * Hq;
-  for (int64_t ph = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; ph < total;
-       ph += (int64_t)gridDim.x * blockDim.x) {
-    const int64_t pg = (ph / Hq) * (Hq / G) + (ph % Hq) / G;
-    for (int a = 0; a < k; ++a) sel[ph * k + a] = selg[pg * k + a];
-    if (margin) margin[ph] = mg[pg];
-  }
-}
-
-unsigned grid_for(int64_t n) {
-  int64_t g = (n + 255) / 256;
-  if (g > 4096) g = 4096;
-  return (unsigned)(g > 0 ? g : 1);
-}
-
-// Exact tier over every row of an N x Hq_eff problem with groups of G_eff.
-template <typename T>
-hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff,
+hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff, int gq,
                       const double* kbarT, int64_t nhp, int32_t* sel, float* margin,
                       hipStream_t s) {
   // a few rows: one wave per (row, head) pair so they run side by side
@@ -514,7 +579,7 @@ hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, i
   const int need = P.KH + 1;
 #define MOBA_REFINE(KM)                                                                    \
   gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.Nq,  \
-                                         Hq_eff, G_eff, P.k, nhp, 1, ppw)
+                                         Hq_eff, G_eff, P.k, nhp, 1, ppw, gq)
   if (need <= 4) MOBA_REFINE(4);
   else if (need <= 8) MOBA_REFINE(8);
   else if (need <= 12) MOBA_REFINE(12);
@@ -524,23 +589,42 @@ hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, i
   return hipGetLastError();
 }
 
-template <int KM>
+// Fast tier then the exact tier for its uncertified rows, on bf16 Q. Per-head
+// routing: pairs (row, query head). Group-shared (SHARED): pairs (row, KV
+// head), scored with the sum of the group's G query heads.
+template <int KM, bool SHARED>
 hipError_t launch_km(const Prob& P, const Blocks& T, const void* Q, const uint16_t* planes,
                      const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
                      hipStream_t s) {
-  const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kPairs);
+  const int Hq = SHARED ? P.Hkv : P.Hq, G = SHARED ? 1 : P.G, gq = SHARED ? P.G : 1;
+  const int tiles_per_block = (int)ceil_div((int64_t)P.B * G, kPairs);
   // workgroups walk blocks from the last; a chunk's query rows sit in its last blocks
   dim3 grid((unsigned)(query_blocks(P) * tiles_per_block), (unsigned)P.Hkv);
-  gate_topk_kernel<KM><<<grid, kThreads, 0, s>>>((const uint16_t*)Q, planes, maxnorm, T.qstart,
-                                                T.qlen, T.lo, sel, P.Hq, P.G, P.k, P.n, P.nh,
-                                                tiles_per_block);
+  gate_topk_kernel<KM, SHARED><<<grid, kThreads, 0, s>>>(
+      (const uint16_t*)Q, planes, maxnorm, T.qstart, T.qlen, T.lo, sel, Hq, G, gq, P.k, P.n,
+      P.nh, tiles_per_block);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || P.nh <= 0 || P.KH <= 0) return e;
-  const unsigned refine_grid = (unsigned)ceil_div(P.Nq * P.Hq, 64);
+  const unsigned refine_grid = (unsigned)ceil_div(P.Nq * Hq, 64);
   gate_refine<uint16_t, KM><<<refine_grid, 64, 0, s>>>((const uint16_t*)Q, kbarT, T.row_blk, T.lo,
-                                                      sel, nullptr, P.Nq, P.Hq, P.G, P.k, nhp, 0,
-                                                      64);
+                                                      sel, nullptr, P.Nq, Hq, G, P.k, nhp, 0, 64,
+                                                      gq);
   return hipGetLastError();
+}
+
+template <bool SHARED>
+hipError_t launch_fast(const Prob& P, const Blocks& T, const void* Q, const uint16_t* planes,
+                       const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
+                       hipStream_t s) {
+  // list length: the k-1 kept blocks plus the best one left out
+  const int need = P.KH + 1;
+#define MOBA_FAST(KM) launch_km<KM, SHARED>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s)
+  if (need <= 4) return MOBA_FAST(4);
+  if (need <= 8) return MOBA_FAST(8);
+  if (need <= 12) return MOBA_FAST(12);
+  if (need <= 16) return MOBA_FAST(16);
+  return MOBA_FAST(32);
+#undef MOBA_FAST
 }
 
 int64_t padded_nh(const Prob& P) { return ceil_div(P.nh > 0 ? P.nh : 1, 64) * 64; }
@@ -550,9 +634,6 @@ struct GateScratch {
   uint16_t* planes;
   float* norms;
   float* maxnorm;
-  double* qg;      // group-shared routing only
-  int32_t* selg;
-  float* marging;
 };
 
 size_t align256(size_t x) { return (x + 255) / 256 * 256; }
@@ -566,21 +647,14 @@ GateScratch carve(const Prob& P, void* scratch) {
   base += align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2);
   g.norms = (float*)base;
   g.maxnorm = g.norms + (size_t)P.Hkv * P.nh;
-  base += align256((size_t)P.Hkv * (P.nh + 1) * 4);
-  if (P.routing == MOBA_ROUTING_SHARED) {
-    g.qg = (double*)base;
-    base += align256(sizeof(double) * (size_t)P.Nq * P.Hkv * kHeadDim);
-    g.selg = (int32_t*)base;
-    base += align256(sizeof(int32_t) * (size_t)P.Nq * P.Hkv * P.k);
-    g.marging = (float*)base;
-  }
   return g;
 }
 
-// All of the gate: block-key split, then (per-head routing) the fast tier and
-// the exact tier for its uncertified rows, or (exact_all, fp32 inputs,
-// group-shared routing) the exact tier for every row; margin (nullable)
-// receives each row's selection margin.
+// All of the gate: block-key split, then for bf16 inputs with many rows the
+// fast tier and the exact tier for its uncertified rows, else (exact_all,
+// fp32 inputs, a few rows) the exact tier for every row; margin (nullable)
+// receives each row's selection margin. Group-shared routing scores pairs
+// (row, KV head) with the group's summed query and writes each head's row.
 hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double* kbar,
                     void* scratch, int32_t* sel, float* margin, bool exact_all, hipStream_t s) {
   const GateScratch g = carve(P, scratch);
@@ -593,47 +667,24 @@ hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double*
     kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(g.norms, g.maxnorm, P.nh);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (P.routing == MOBA_ROUTING_SHARED) {
-    if (P.dtype == MOBA_DTYPE_BF16)
-      group_sum_q<uint16_t><<<grid_for(P.Nq * P.Hkv * kHeadDim), 256, 0, s>>>(
-          (const uint16_t*)Q, g.qg, P.Nq, P.Hkv, P.G);
-    else
-      group_sum_q<float><<<grid_for(P.Nq * P.Hkv * kHeadDim), 256, 0, s>>>(
-          (const float*)Q, g.qg, P.Nq, P.Hkv, P.G);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    e = refine_all<double>(P, T, g.qg, P.Hkv, 1, g.kbarT, nhp, g.selg,
-                           margin ? g.marging : nullptr, s);
-    if (e != hipSuccess) return e;
-    expand_group<<<grid_for(P.Nq * P.Hq), 256, 0, s>>>(g.selg, margin ? g.marging : nullptr, sel,
-                                                       margin, P.Nq, P.Hq, P.G, P.k);
-    return hipGetLastError();
-  }
+  const bool shared = P.routing == MOBA_ROUTING_SHARED;
+  const int Hq = shared ? P.Hkv : P.Hq, G = shared ? 1 : P.G, gq = shared ? P.G : 1;
   if (P.dtype == MOBA_DTYPE_F32)
-    return refine_all<float>(P, T, (const float*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
-  // a few rows (decode): the exact tier alone, one wave per (row, head)
+    return refine_all<float>(P, T, (const float*)Q, Hq, G, gq, g.kbarT, nhp, sel, margin, s);
+  // a few rows (decode): the exact tier alone, one wave per pair
   if (exact_all || P.Nq <= kDecodeRows)
-    return refine_all<uint16_t>(P, T, (const uint16_t*)Q, P.Hq, P.G, g.kbarT, nhp, sel, margin, s);
-  // list length: the k-1 kept blocks plus the best one left out
-  const int need = P.KH + 1;
-  if (need <= 4) return launch_km<4>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
-  if (need <= 8) return launch_km<8>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
-  if (need <= 12) return launch_km<12>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
-  if (need <= 16) return launch_km<16>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
-  return launch_km<32>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+    return refine_all<uint16_t>(P, T, (const uint16_t*)Q, Hq, G, gq, g.kbarT, nhp, sel, margin,
+                                s);
+  if (shared) return launch_fast<true>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
+  return launch_fast<false>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
 }
 
 }  // namespace
 
 size_t gate_scratch_bytes(const Prob& P) {
-  size_t b = align256(sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P)) +
-             align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2) +
-             align256((size_t)P.Hkv * (P.nh + 1) * 4);
-  if (P.routing == MOBA_ROUTING_SHARED)
-    b += align256(sizeof(double) * (size_t)P.Nq * P.Hkv * kHeadDim) +
-         align256(sizeof(int32_t) * (size_t)P.Nq * P.Hkv * P.k) +
-         align256(sizeof(float) * (size_t)P.Nq * P.Hkv);
-  return b + 1024;
+  return align256(sizeof(double) * (size_t)P.Hkv * kHeadDim * padded_nh(P)) +
+         align256((size_t)P.Hkv * P.nh * 3 * kHeadDim * 2) +
+         align256((size_t)P.Hkv * (P.nh + 1) * 4) + 1024;
 }
 
 hipError_t launch_gate_topk(const Prob& P, const Blocks& T, const void* Q, const double* kbar,

@@ -343,6 +343,37 @@ def test_varlen_with_shared_routing():
         check_output(o[a:b].reshape(-1, 128), ref_o.reshape(-1, 128), "bf16", f"seq {i}")
 
 
+def test_shared_fast_tier_equals_exact_tier():
+    """bf16 group-shared routing with many rows runs the certified fast tier;
+    its selection must equal the exact tier's on every row (both are exact),
+    here with 255 candidate blocks per late row."""
+    N, Hq, Hkv, B, topk = 16384, 8, 2, 64, 8
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=23)
+    shared = moba.MOBA_ROUTING_SHARED
+    fast = moba.select(tq, tk, B, topk, routing=shared).cpu().numpy()
+    exact = moba.routing_stats(tq, tk, B, topk, routing=shared)["sel"].cpu().numpy()
+    assert np.array_equal(fast, exact)
+    rng = np.random.default_rng(5)
+    rows = np.sort(rng.choice(N, 256, replace=False))
+    heads = rng.integers(0, Hq, size=rows.size)
+    ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False,
+                                  routing=oracle.ROUTING_SHARED)
+    check_selection(fast[rows, heads], ref_sel, gap, "shared fast tier")
+
+
+@pytest.mark.parametrize("kind", ["zero_k", "integer"])
+def test_shared_routing_ties_are_exact(kind):
+    """Exact ties in the group score (all-zero keys, or integer data) must go
+    to the lower block, through the fast tier's refine path."""
+    N, Hq, Hkv, B, topk = 1280, 4, 2, 32, 5
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=29, **{kind: True})
+    sel = moba.select(tq, tk, B, topk, routing=moba.MOBA_ROUTING_SHARED).cpu().numpy()
+    rows, heads = all_rows(N, Hq)
+    ref_sel, _, _ = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False,
+                                routing=oracle.ROUTING_SHARED)
+    assert np.array_equal(sel.reshape(-1, topk), ref_sel)
+
+
 @pytest.mark.parametrize("routing", [0, 1])
 def test_routing_stats(routing):
     N, Hq, Hkv, B, topk = 2500, 8, 2, 100, 4
