@@ -72,7 +72,9 @@ typedef enum { MOBA_DTYPE_BF16 = 0, MOBA_DTYPE_F32 = 1 } moba_dtype_t;
  *     sum_h q_h . kbar_i = (sum_h q_h) . kbar_i (same ties rule); attention
  *     still uses each head's own query. The group query is summed in fp64
  *     (exact unless the group's values differ in magnitude by more than
- *     2^45), and the ranking uses the exact fp64 tier for every row.
+ *     2^45); bf16 inputs are ranked by the certified matrix-core tier with
+ *     the fp64 tier for the rows it cannot certify, fp32 inputs by the fp64
+ *     tier, so the selection is the exact one either way.
  */
 typedef enum { MOBA_ROUTING_PER_HEAD = 0, MOBA_ROUTING_SHARED = 1 } moba_routing_t;
 
