@@ -363,51 +363,63 @@ typedef _Float16 h8 __attribute__((ext_vector_type(8)));
 typedef __bf16 b4 __attribute__((ext_vector_type(4)));
 typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 
-// Final output of one (row, head) for the 8 head-dim elements [8 c16, 8 c16 + 8):
-// the own-block result (normalised `own`, log2-sum-exp own_lse) merged with the
-// row's nhist >= 1 history partials (normalised rows po[s], log2-sum-exps
-// lse[s]) by PaperTrace "2.1.3 MoBA" eqs. (7)-(8). NH >= nhist is a
-// compile-time bound so the loads of a group of partials are all in flight
-// before their values are used; indices past nhist are clamped, so every
-// load stays inside the row's own partials.
-template <int NH>
-__device__ inline b8 merge_row(h8 own, float own_lse, const float* __restrict__ lse_src,
-                               const _Float16* __restrict__ po_src, int nhist, int c16,
-                               float* lse_out) {
-  constexpr int GRP = 8;
-  float lse[NH];
+// Final outputs of R (row, head) pairs for the 8 head-dim elements
+// [8 c16, 8 c16 + 8): each pair's own-block result (normalised `own`,
+// log2-sum-exp own_lse) merged with its nhist >= 1 history partials
+// (normalised rows po[s], log2-sum-exps lse[s]) by PaperTrace "2.1.3 MoBA"
+// eqs. (7)-(8). NH >= nhist is a compile-time bound so the loads of a group
+// of partials of all R pairs are in flight before their values are used;
+// indices past nhist are clamped, so every load stays inside the pair's own
+// partials.
+template <int NH, int R>
+__device__ inline void merge_rows(const h8 (&own)[R], const float (&own_lse)[R],
+                                  const float* const (&lse_src)[R],
+                                  const _Float16* const (&po_src)[R], int nhist, int c16,
+                                  b8 (&out)[R], float (&lse_out)[R]) {
+  constexpr int GRP = NH < 16 ? NH : 16;  // partial rows of a pair in flight together
+  float lse[R][NH];
 #pragma unroll
-  for (int s = 0; s < NH; ++s) lse[s] = lse_src[s < nhist ? s : nhist - 1];
-  float M = own_lse;
+  for (int i = 0; i < R; ++i)
 #pragma unroll
-  for (int s = 0; s < NH; ++s) M = fmaxf(M, lse[s]);  // clamped copies repeat a real value
-  float acc[8];
-  float L = __builtin_amdgcn_exp2f(own_lse - M);
+    for (int s = 0; s < NH; ++s) lse[i][s] = lse_src[i][s < nhist ? s : nhist - 1];
+  float M[R], L[R], acc[R][8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = L * (float)own[e];
+  for (int i = 0; i < R; ++i) {
+    M[i] = own_lse[i];
+#pragma unroll
+    for (int s = 0; s < NH; ++s) M[i] = fmaxf(M[i], lse[i][s]);  // clamped copies repeat a real value
+    L[i] = __builtin_amdgcn_exp2f(own_lse[i] - M[i]);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[i][e] = L[i] * (float)own[i][e];
+  }
 #pragma unroll
   for (int s0 = 0; s0 < NH; s0 += GRP) {
     if (s0 >= nhist) break;
-    h8 v[GRP];
+    h8 v[R][GRP];
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const int sj = s0 + j < nhist ? s0 + j : nhist - 1;
-      v[j] = *reinterpret_cast<const h8*>(po_src + (size_t)sj * kHeadDim + 8 * c16);
-    }
+    for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int j = 0; j < GRP; ++j) {
-      const float w = s0 + j < nhist ? __builtin_amdgcn_exp2f(lse[s0 + j] - M) : 0.f;
-      L += w;
+      for (int j = 0; j < GRP; ++j) {
+        const int sj = s0 + j < nhist ? s0 + j : nhist - 1;
+        v[i][j] = *reinterpret_cast<const h8*>(po_src[i] + (size_t)sj * kHeadDim + 8 * c16);
+      }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] = fmaf(w, (float)v[j][e], acc[e]);
-    }
+    for (int i = 0; i < R; ++i)
+#pragma unroll
+      for (int j = 0; j < GRP; ++j) {
+        const float w = s0 + j < nhist ? __builtin_amdgcn_exp2f(lse[i][s0 + j] - M[i]) : 0.f;
+        L[i] += w;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(w, (float)v[i][j][e], acc[i][e]);
+      }
   }
-  const float inv = 1.f / L;
-  b8 out;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) out[e] = (__bf16)(acc[e] * inv);
-  *lse_out = M + __builtin_log2f(L);  // the row's log2-sum-exp over all its keys
-  return out;
+  for (int i = 0; i < R; ++i) {
+    const float inv = 1.f / L[i];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) out[i][e] = (__bf16)(acc[i][e] * inv);
+    lse_out[i] = M[i] + __builtin_log2f(L[i]);  // the row's log2-sum-exp over all its keys
+  }
 }
 
 // ----------------------------------------------------------------------------
@@ -624,30 +636,51 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   }
   __syncthreads();
   const int q4 = lane >> 4, c16 = lane & 15;
-  for (int pass = 0; pass < kWaveQ / 4; ++pass) {
-    const int j = pass * 4 + q4;
-    const int64_t pi = p0 + wave * kWaveQ + j;
-    const int64_t pic = pi < npairs ? pi : npairs - 1;  // clamped: loads stay in bounds
-    const int64_t phj = (qrow0 + pic / G) * Hq + g * G + (int)(pic % G);
-    const h8 own = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * c16);
-    const float own_lse = stage_lse[j];
-    const float* ls = part_lse + phj * KH;
-    const _Float16* po = part_o + (size_t)(phj * KH) * kHeadDim;
-    b8 out;
-    float lse_row;
-    if (nhist <= 4)
-      out = merge_row<4>(own, own_lse, ls, po, nhist, c16, &lse_row);
-    else if (nhist <= 8)
-      out = merge_row<8>(own, own_lse, ls, po, nhist, c16, &lse_row);
-    else if (nhist <= 16)
-      out = merge_row<16>(own, own_lse, ls, po, nhist, c16, &lse_row);
-    else
-      out = merge_row<kMaxTopk>(own, own_lse, ls, po, nhist, c16, &lse_row);
-    if (pi < npairs) {
-      *reinterpret_cast<b8*>(O + phj * kHeadDim + 8 * c16) = out;
-      if (lse_out && c16 == 0) lse_out[phj] = lse_row;
+  // R passes (4 pairs each, 16 lanes per pair) merged together: two while a
+  // pair's partials fit the registers comfortably, else one
+  auto merge_passes = [&](auto nh_tag, auto r_tag) {
+    constexpr int NH = decltype(nh_tag)::value, R = decltype(r_tag)::value;
+    for (int pass = 0; pass < kWaveQ / 4; pass += R) {
+      int64_t pi[R], phj[R];
+      h8 own[R];
+      float own_lse[R];
+      const float* ls[R];
+      const _Float16* po[R];
+#pragma unroll
+      for (int i = 0; i < R; ++i) {
+        const int j = (pass + i) * 4 + q4;
+        pi[i] = p0 + wave * kWaveQ + j;
+        const int64_t pic = pi[i] < npairs ? pi[i] : npairs - 1;  // clamped: loads stay in bounds
+        phj[i] = (qrow0 + pic / G) * Hq + g * G + (int)(pic % G);
+        own[i] = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * c16);
+        own_lse[i] = stage_lse[j];
+        ls[i] = part_lse + phj[i] * KH;
+        po[i] = part_o + (size_t)(phj[i] * KH) * kHeadDim;
+      }
+      b8 out[R];
+      float lse_row[R];
+      merge_rows<NH, R>(own, own_lse, ls, po, nhist, c16, out, lse_row);
+#pragma unroll
+      for (int i = 0; i < R; ++i)
+        if (pi[i] < npairs) {
+          *reinterpret_cast<b8*>(O + phj[i] * kHeadDim + 8 * c16) = out[i];
+          if (lse_out && c16 == 0) lse_out[phj[i]] = lse_row[i];
+        }
     }
-  }
+  };
+  using one = std::integral_constant<int, 1>;
+  using two = std::integral_constant<int, 2>;
+  static_assert((kWaveQ / 4) % 2 == 0, "whole pairs of passes");
+  if (nhist <= 4)
+    merge_passes(std::integral_constant<int, 4>{}, two{});
+  else if (nhist <= 8)
+    merge_passes(std::integral_constant<int, 8>{}, two{});
+  else if (nhist <= 12)
+    merge_passes(std::integral_constant<int, 12>{}, two{});
+  else if (nhist <= 16)
+    merge_passes(std::integral_constant<int, 16>{}, one{});
+  else
+    merge_passes(std::integral_constant<int, kMaxTopk>{}, one{});
 }
 
 }  // namespace
