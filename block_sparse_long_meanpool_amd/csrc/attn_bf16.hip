@@ -614,7 +614,9 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
   }
   // Stage each wave's own-block results in the (now idle) tile buffers as
   // normalised fp16 rows plus log2-sum-exps, then merge with 16 lanes per
-  // (row, head) so each partial row is one coalesced 256-byte read.
+  // (row, head) so each partial row is one coalesced 256-byte read. Staged
+  // row j keeps its 16-byte chunk c at position c ^ (j & 15), so the stores
+  // (one chunk of 32 rows at a time) spread over the banks.
   uint16_t* const wbuf = wave < 2 ? lds_k0 : wave < 4 ? lds_k1 : wave < 6 ? lds_k2 : lds_v0;
   _Float16* const stage = reinterpret_cast<_Float16*>(wbuf) + (wave & 1) * kWaveQ * kHeadDim;
   float* const stage_lse = reinterpret_cast<float*>(lds_v1) + wave * kWaveQ;
@@ -630,7 +632,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
         h4 v;
 #pragma unroll
         for (int t = 0; t < 4; ++t) v[t] = (_Float16)(W.o[qb][db][4 * r4 + t] * inv);
-        *reinterpret_cast<h4*>(stage + j * kHeadDim + 32 * db + 8 * r4 + 4 * h) = v;
+        *reinterpret_cast<h4*>(stage + j * kHeadDim + 8 * ((4 * db + r4) ^ (j & 15)) + 4 * h) = v;
       }
     if (h == 0) stage_lse[j] = W.m[qb] + __builtin_log2f(l);
   }
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
         pi[i] = p0 + wave * kWaveQ + j;
         const int64_t pic = pi[i] < npairs ? pi[i] : npairs - 1;  // clamped: loads stay in bounds
         phj[i] = (qrow0 + pic / G) * Hq + g * G + (int)(pic % G);
-        own[i] = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * c16);
+        own[i] = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * (c16 ^ (j & 15)));
         own_lse[i] = stage_lse[j];
         ls[i] = part_lse + phj[i] * KH;
         po[i] = part_o + (size_t)(phj[i] * KH) * kHeadDim;
