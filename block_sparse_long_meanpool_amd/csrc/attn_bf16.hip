@@ -3,11 +3,11 @@
 // causal own-block branch eq. (5), merged by eqs. (7)-(8); section 3.1 steps
 // 4-5; section 5.4 on tiling queries per KV block).
 //
-// Tile engine shared by both kernels. A wavefront owns 64 queries (two
-// 32-column blocks); a workgroup of 4 waves streams one K/V block in 64-key
-// tiles through LDS (double buffered, one barrier per tile), so each K/V
-// byte read from L2 serves 256 queries and each LDS operand read feeds two
-// matrix-core ops. Tiles move global -> LDS with global_load_lds_dwordx4 (no
+// Tile engine shared by both kernels. A wavefront owns 32 queries (one
+// 32-column block; QB blocks in general); a workgroup of 8 waves streams one
+// K/V block in 64-key tiles through LDS (three buffers, one barrier per
+// tile), so each K/V byte read from L2 serves 256 queries, and two waves
+// share each SIMD. Tiles move global -> LDS with buffer_load ... lds (no
 // register staging); rows are stored with their 16-byte chunks XOR-swizzled
 // by the row index so the operand reads below are bank-conflict free.
 // Per 32-key subtile and wave:
@@ -38,6 +38,8 @@ namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 #ifndef MOBA_ATTN_QB
@@ -258,17 +260,21 @@ __device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int 
     const float mneg = -W.m[qb];
     float lsum = W.l[qb];
 #pragma unroll
-    for (int u = 0; u < 2; ++u)
+    for (int u = 0; u < 2; ++u) {
+      bf16x2 pr[4];  // weight pairs, each converted by one packed instruction
 #pragma unroll
-      for (int e = 0; e < 8; e += 2) {
-        bf16x2 e2;
-        e2[0] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e], sl2e, mneg));
-        e2[1] = (__bf16)__builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + e + 1], sl2e, mneg));
-        p[qb][u][e] = e2[0];
-        p[qb][u][e + 1] = e2[1];
+      for (int e = 0; e < 4; ++e) {
+        f32x2 f;
+        f[0] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e], sl2e, mneg));
+        f[1] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e + 1], sl2e, mneg));
+        pr[e] = __builtin_convertvector(f, bf16x2);
         // the row sum adds the same rounded weights that multiply V
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(e2, ones, lsum, false);
+        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], ones, lsum, false);
       }
+      const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
+      const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
+      p[qb][u] = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    }
     W.l[qb] = lsum;
   }
   const int csub = 4 * sub;
