@@ -208,6 +208,34 @@ def test_integer_ties_are_exact():
     assert np.array_equal(sel, ref_sel)
 
 
+def test_softmax_overflow_rerun():
+    """Spike keys past each block's first 32 keys score ~200 (log2 units) above
+    the rest, beyond the 2^64 headroom of the fixed reference maximum and
+    beyond fp32's range: the attention kernels must re-run those blocks from
+    the true maxima (history and own block alike), else weights overflow to
+    infinity."""
+    N, Hq, Hkv, B, topk = 2048, 2, 1, 128, 3
+    q, k, v, _, _, _ = small(N, Hq, Hkv, B, topk, seed=41)
+    u = np.random.default_rng(41).standard_normal(128)
+    u /= np.linalg.norm(u)
+    qf, kf = synth.bf16_to_f32(q), synth.bf16_to_f32(k)
+    qf += (35.0 * u).astype(np.float32)  # every query leans along u
+    spikes = [c * B + 40 + (7 * c) % 80 for c in range(N // B)]
+    kf[spikes] += (45.0 * u).astype(np.float32)
+    q, k = synth.f32_to_bf16(qf), synth.f32_to_bf16(kf)
+    # O is then close to single V rows: V / 4 (exact) keeps |O| < 2, where
+    # bf16's half-ulp stays below the 1e-2 bar
+    v = synth.f32_to_bf16(synth.bf16_to_f32(v) * np.float32(0.25))
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    scale = 1.0 / np.sqrt(128.0)
+    o = moba.prefill(tq, tk, tv, B, topk, scale)
+    sel = moba.select(tq, tk, B, topk).cpu().numpy()
+    assert bool(torch.isfinite(o.float()).all())
+    rows, heads = all_rows(N, Hq)
+    compare_rows(q, k, v, B, topk, scale, rows, heads, sel.reshape(-1, topk),
+                 to_np(o).reshape(-1, 128), "bf16", "spike keys")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dense_baseline_and_full_coverage(dtype):
     """k covering every block equals causal full attention, and so does the dense kernel."""
