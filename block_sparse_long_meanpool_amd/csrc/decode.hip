@@ -78,6 +78,22 @@ __device__ inline void st<float>(float* p, float x) {
   *p = x;
 }
 
+// Sum over each aligned group of 16 lanes, left in every lane of the group,
+// with DPP lane moves: swap within pairs, swap pairs within quads, mirror
+// within 8 lanes (quad i <-> quad 1 - i), mirror within 16 lanes.
+template <int CTRL>
+__device__ inline float dpp_mov(float a) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, a), CTRL, 0xF, 0xF, true));
+}
+__device__ inline float sum16(float a) {
+  a += dpp_mov<0xB1>(a);   // quad_perm [1, 0, 3, 2]
+  a += dpp_mov<0x4E>(a);   // quad_perm [2, 3, 0, 1]
+  a += dpp_mov<0x141>(a);  // row_half_mirror
+  a += dpp_mov<0x140>(a);  // row_mirror
+  return a;
+}
+
 __device__ inline float block_max(float v, float* red) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = v;
@@ -137,30 +153,47 @@ __global__ __launch_bounds__(kThreads) void decode_partial(
   }
   if (tid < kHeadDim) qs[tid] = ldf(Q + rh * kHeadDim + tid);
   __syncthreads();
-  // scores: one key per thread
-  const int64_t key = k0 + tid;
+  // scores: the lanes of a group (16 lanes for bf16, 32 for fp32) read one
+  // key row together (each its 16-byte chunk), take partial dot products and
+  // add them across the group; the group walks its keys, and its lane i keeps
+  // the score of its i-th key: key kk + (256 / group) i for group kk
+  constexpr int kVec = 16 / sizeof(T);       // elements per 16-byte load
+  constexpr int kChunks = kHeadDim / kVec;   // 16-byte chunks per row
+  constexpr int kRowsPerPass = kThreads / kChunks;
+  const int ch = tid % kChunks, kk = tid / kChunks;
+  float qv[kVec];
+#pragma unroll
+  for (int e = 0; e < kVec; ++e) qv[e] = qs[ch * kVec + e];
   float s = -INFINITY;
-  if (key < k1) {
-    const T* kr = K + (key * Hkv + g) * kHeadDim;
-    float a[4] = {0.f, 0.f, 0.f, 0.f};
-    constexpr int kVec = 16 / sizeof(T);  // elements per 16-byte load
+  int mykey = -1;  // key offset whose score this thread keeps
+#pragma unroll 4
+  for (int i = 0; i < kSplit / kRowsPerPass; ++i) {
+    const int j = kk + kRowsPerPass * i;
+    const int64_t key = k0 + j;
+    float x[kVec];
+    if (key < k1) {
+      ld16(K + (key * Hkv + g) * kHeadDim + ch * kVec, x);
+    } else {
 #pragma unroll
-    for (int d = 0; d < kHeadDim; d += kVec) {
-      float x[kVec];
-      ld16(kr + d, x);
-#pragma unroll
-      for (int e = 0; e < kVec; ++e) a[e & 3] = fmaf(qs[d + e], x[e], a[e & 3]);
+      for (int e = 0; e < kVec; ++e) x[e] = 0.f;
     }
-    s = ((a[0] + a[1]) + (a[2] + a[3])) * sl2e;
+    float a = 0.f;
+#pragma unroll
+    for (int e = 0; e < kVec; ++e) a = fmaf(qv[e], x[e], a);
+    a = sum16(a);
+    if (kChunks == 32) a += __shfl_xor(a, 16);  // fp32 rows span 32 lanes
+    if (i % kChunks == ch) {
+      mykey = j;
+      s = key < k1 ? a * sl2e : -INFINITY;
+    }
   }
   const float m = block_max(s, red);
-  const float p = key < k1 ? __builtin_amdgcn_exp2f(s - m) : 0.f;
-  ps[tid] = p;
+  const float p = s > -INFINITY ? __builtin_amdgcn_exp2f(s - m) : 0.f;
+  if (mykey >= 0) ps[mykey] = p;
   const float l = block_sum(p, red);  // also publishes ps
   // u: thread (key group kg of 16 keys, 16-byte column group cv) sums its
   // keys' V over the group's columns; the 16 key groups are added in LDS
-  constexpr int kVec = 16 / sizeof(T);  // columns per 16-byte load
-  constexpr int kColGroups = kHeadDim / kVec;
+  constexpr int kColGroups = kChunks;
   constexpr int kKeyGroups = kThreads / kColGroups;
   constexpr int kPerGroup = kSplit / kKeyGroups;
   const int cv = tid % kColGroups, kg = tid / kColGroups;

@@ -72,7 +72,7 @@ __device__ inline int swz(int row, int c) { return c ^ (row & 15); }
 // ---------------------------------------------------------------------------
 // Split kernel: kbar fp64 [Hkv][nh][d] -> planes bf16 [Hkv][nh][3][d],
 // per-block Euclidean norms fp32 [Hkv][nh] (rounded up) and a transposed fp64
-// copy [Hkv][d][nhp] for the exact tier.
+// copy [Hkv][d][nhp] for the exact tier (planes NULL: the copy only).
 // ---------------------------------------------------------------------------
 __device__ inline uint16_t bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -91,6 +91,7 @@ __global__ __launch_bounds__(kHeadDim) void kbar_split(const double* __restrict_
   const double x = kbar[blk * kHeadDim + c];
   const int64_t g = blk / nh, b = blk % nh;
   kbarT[(g * kHeadDim + c) * nhp + b] = x;  // [Hkv][d][nhp]: lane-per-block reads coalesce
+  if (!planes) return;  // the exact tier alone needs only the transposed copy
   const uint16_t hi = bf16_rne((float)x);
   const double r1 = x - bf16_to_f64(hi);
   const uint16_t mid = bf16_rne((float)r1);
@@ -408,6 +409,127 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
 // SHARED: pairs are (row, KV head) (Hq = Hkv, G = 1); the scoring query is
 // the fp64 sum of the pair's gq query heads of Q, split into three bf16
 // planes here, and the row is written for each of those heads.
+// Exact tier for a few rows (decode): a workgroup of 4 waves per (row, head)
+// pair, the pair's candidate blocks spread over its 256 lanes (lane t takes
+// blocks lo + t, lo + t + 256, ...), each lane keeping a sorted list of its
+// blocks; then KH rounds (KH + 1 with margins) of workgroup arg-max by (value
+// desc, index asc) — a shuffle reduction per wave, then over the 4 waves in
+// LDS — pick the kept blocks. Every pair is written (kept blocks ascending,
+// own block, -1 padding); group-shared pairs sum gq heads as gate_refine does.
+template <typename T, int KM>
+__global__ __launch_bounds__(256) void gate_refine_few(const T* __restrict__ Q,
+                                                       const double* __restrict__ kbarT,
+                                                       const int32_t* __restrict__ row_blk,
+                                                       const int32_t* __restrict__ blo,
+                                                       int32_t* __restrict__ sel,
+                                                       float* __restrict__ margin, int Hq, int G,
+                                                       int k, int64_t nhp, int gq) {
+  __shared__ double qs[kHeadDim];
+  __shared__ double wbest[4];
+  __shared__ int wblk[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int KH = k - 1;
+  const int64_t ph = blockIdx.x;
+  const int64_t c = row_blk[ph / Hq], lo = blo[c];
+  if (!(c - lo > KH && KH > 0)) {  // every earlier block of the sequence is taken
+    if (tid < gq) {
+      const int nsel = (int)(c - lo < KH ? c - lo : KH);
+      int32_t* out = sel + (ph * gq + tid) * k;
+      if (margin) margin[ph * gq + tid] = __builtin_nanf("");  // nothing left out
+      for (int a = 0; a < nsel; ++a) out[a] = (int32_t)(lo + a);
+      out[nsel] = (int32_t)c;
+      for (int a = nsel + 1; a < k; ++a) out[a] = -1;
+    }
+    return;
+  }
+  const int g = (int)(ph % Hq) / G;
+  if (tid < kHeadDim) {
+    const T* qrow = Q + ph * gq * kHeadDim;
+    double x = 0.0;  // the sum of gq bf16 or fp32 values is exact in fp64
+    for (int hh = 0; hh < gq; ++hh) x += widen<T>(qrow[(int64_t)hh * kHeadDim + tid]);
+    qs[tid] = x;
+  }
+  __syncthreads();
+  double v[KM];
+  int ix[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) {
+    v[t] = -INFINITY;
+    ix[t] = 0x7FFFFFFF;
+  }
+  const double* kt = kbarT + (int64_t)g * kHeadDim * nhp;
+  for (int64_t b = lo + tid; b < c; b += 256) {
+    double acc = 0.0;
+#pragma unroll 32
+    for (int d = 0; d < kHeadDim; ++d) acc = fma(qs[d], kt[(int64_t)d * nhp + b], acc);
+    double x = acc;
+    int xi = (int)b;
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+      const bool gt = x > v[t];
+      const double nv = gt ? x : v[t];
+      const int ni = gt ? xi : ix[t];
+      x = gt ? v[t] : x;
+      xi = gt ? ix[t] : xi;
+      v[t] = nv;
+      ix[t] = ni;
+    }
+  }
+  int chosen[KM];
+#pragma unroll
+  for (int t = 0; t < KM; ++t) chosen[t] = 0x7FFFFFFF;
+  double last = 0.0, next = 0.0;
+  const int rounds = margin ? KH + 1 : KH;
+  for (int rnd = 0; rnd < rounds; ++rnd) {
+    double bv = v[0];
+    int bi = ix[0];
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      if (ov > bv || (ov == bv && oi < bi)) {
+        bv = ov;
+        bi = oi;
+      }
+    }
+    if (lane == 0) {
+      wbest[wave] = bv;
+      wblk[wave] = bi;
+    }
+    __syncthreads();
+    bv = wbest[0];
+    bi = wblk[0];
+#pragma unroll
+    for (int w = 1; w < 4; ++w)
+      if (wbest[w] > bv || (wbest[w] == bv && wblk[w] < bi)) {
+        bv = wbest[w];
+        bi = wblk[w];
+      }
+    __syncthreads();  // the slots are rewritten next round
+    if (ix[0] == bi) {  // block indices are unique: exactly one lane pops its head
+#pragma unroll
+      for (int t = 0; t < KM - 1; ++t) {
+        v[t] = v[t + 1];
+        ix[t] = ix[t + 1];
+      }
+      v[KM - 1] = -INFINITY;
+      ix[KM - 1] = 0x7FFFFFFF;
+    }
+#pragma unroll
+    for (int t = 0; t < KM; ++t)
+      if (t == rnd && rnd < KH) chosen[t] = bi;
+    if (rnd == KH - 1) last = bv;
+    if (rnd == KH) next = bv;
+  }
+  if (tid < gq) {
+    if (margin) margin[ph * gq + tid] = (float)(last - next);
+    int32_t* out = sel + (ph * gq + tid) * k;
+    write_sorted<KM>(chosen, KH, out);
+    out[KH] = (int32_t)c;
+    for (int a = KH + 1; a < k; ++a) out[a] = -1;
+  }
+}
+
 template <int KM, bool SHARED>
 __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
@@ -573,13 +695,20 @@ template <typename T>
 hipError_t refine_all(const Prob& P, const Blocks& T_, const T* Q, int Hq_eff, int G_eff, int gq,
                       const double* kbarT, int64_t nhp, int32_t* sel, float* margin,
                       hipStream_t s) {
-  // a few rows: one wave per (row, head) pair so they run side by side
-  const int ppw = P.Nq <= kDecodeRows ? 1 : 64;
-  const unsigned grid = (unsigned)ceil_div(P.Nq * Hq_eff, ppw);
+  // a few rows: a workgroup of 4 waves per (row, head) pair; else one wave
+  // per 64 consecutive pairs
+  const bool few = P.Nq <= kDecodeRows;
+  const unsigned grid = (unsigned)(few ? P.Nq * Hq_eff : ceil_div(P.Nq * Hq_eff, 64));
   const int need = P.KH + 1;
-#define MOBA_REFINE(KM)                                                                    \
-  gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.Nq,  \
-                                         Hq_eff, G_eff, P.k, nhp, 1, ppw, gq)
+#define MOBA_REFINE(KM)                                                                        \
+  do {                                                                                         \
+    if (few)                                                                                   \
+      gate_refine_few<T, KM><<<grid, 256, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin,  \
+                                                  Hq_eff, G_eff, P.k, nhp, gq);              \
+    else                                                                                       \
+      gate_refine<T, KM><<<grid, 64, 0, s>>>(Q, kbarT, T_.row_blk, T_.lo, sel, margin, P.Nq, \
+                                             Hq_eff, G_eff, P.k, nhp, 1, 64, gq);            \
+  } while (0)
   if (need <= 4) MOBA_REFINE(4);
   else if (need <= 8) MOBA_REFINE(8);
   else if (need <= 12) MOBA_REFINE(12);
@@ -659,20 +788,23 @@ hipError_t run_gate(const Prob& P, const Blocks& T, const void* Q, const double*
                     void* scratch, int32_t* sel, float* margin, bool exact_all, hipStream_t s) {
   const GateScratch g = carve(P, scratch);
   const int64_t nhp = padded_nh(P);
+  // fp32 inputs, diagnostics and a few rows take the exact tier alone
+  const bool exact_only = P.dtype == MOBA_DTYPE_F32 || exact_all || P.Nq <= kDecodeRows;
   if (P.nh > 0 && P.KH > 0) {
-    kbar_split<<<(unsigned)(P.Hkv * P.nh), kHeadDim, 0, s>>>(kbar, g.planes, g.norms, g.kbarT,
-                                                            P.nh, nhp);
+    kbar_split<<<(unsigned)(P.Hkv * P.nh), kHeadDim, 0, s>>>(
+        kbar, exact_only ? nullptr : g.planes, g.norms, g.kbarT, P.nh, nhp);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(g.norms, g.maxnorm, P.nh);
-    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (!exact_only) {
+      kbar_maxnorm<<<(unsigned)P.Hkv, 256, 0, s>>>(g.norms, g.maxnorm, P.nh);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
   }
   const bool shared = P.routing == MOBA_ROUTING_SHARED;
   const int Hq = shared ? P.Hkv : P.Hq, G = shared ? 1 : P.G, gq = shared ? P.G : 1;
   if (P.dtype == MOBA_DTYPE_F32)
     return refine_all<float>(P, T, (const float*)Q, Hq, G, gq, g.kbarT, nhp, sel, margin, s);
-  // a few rows (decode): the exact tier alone, one wave per pair
-  if (exact_all || P.Nq <= kDecodeRows)
+  if (exact_only)
     return refine_all<uint16_t>(P, T, (const uint16_t*)Q, Hq, G, gq, g.kbarT, nhp, sel, margin,
                                 s);
   if (shared) return launch_fast<true>(P, T, Q, g.planes, g.maxnorm, g.kbarT, nhp, sel, s);
