@@ -200,6 +200,11 @@ __device__ inline void wave_qk(const Wave& W, Tile t, int sub, int lane, f32x16 
   for (int qb = 0; qb < QB; ++qb)
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[qb][r] = 0.f;
+  // The wave issuing these matrix ops gets the SIMD's issue priority, so
+  // they reach the matrix core ahead of the other wave's softmax work (which
+  // then fills the gaps); measured 0.6-1.4% faster than equal priority, while
+  // raising it for the P.V ops or the exponentials instead was slower.
+  __builtin_amdgcn_s_setprio(1);
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk) {
     const bf16x8 a = as_bf16x8(*reinterpret_cast<const uint4*>(k_chunk(ks, lr, 2 * kk + h)));
@@ -207,6 +212,7 @@ __device__ inline void wave_qk(const Wave& W, Tile t, int sub, int lane, f32x16 
     for (int qb = 0; qb < QB; ++qb)
       s[qb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, W.q[qb][kk], s[qb], 0, 0, 0);
   }
+  __builtin_amdgcn_s_setprio(0);
 }
 
 // Mask one subtile's scores: keys >= nvalid (from the subtile start) and,
