@@ -27,8 +27,9 @@
 //     rows of a 1M-row random layer) are marked in `sel` and a second kernel
 //     re-scores each marked row in fp64 with one wave (lane per block, block
 //     keys stored transposed so the reads coalesce) and selects exactly
-//     (value descending, index ascending). fp32 inputs take this exact path
-//     for every row.
+//     (value descending, index ascending). fp32 inputs, diagnostics and
+//     calls with a few rows (decode; one workgroup of 4 waves per pair) take
+//     this exact path for every row.
 //
 // Group-shared routing ranks blocks by the group's summed query
 // q_g = sum_h q_h (exact in fp64 for bf16 inputs of ordinary range). Its fast
@@ -275,8 +276,8 @@ __device__ inline double widen<double>(double x) {
   return x;
 }
 
-// Exact tier: one wave per ppw (64, or 1 for a few rows) consecutive (row,
-// head) pairs; each marked row
+// Exact tier: one wave per ppw consecutive (row, head) pairs (64; a few
+// rows use gate_refine_few instead); each marked row
 // (or, with all_rows, every row) is re-scored in fp64 — lane b handles blocks
 // b, b+64, ... reading the transposed block keys (coalesced) against q
 // staged in LDS — and selected by (value desc, index asc): each lane keeps a
