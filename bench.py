@@ -104,10 +104,10 @@ def cpu_baseline(w, q, k, v, rows_wanted):
     }
 
 
-def backward_leg():
-    """Training leg on the 32K layer: forward with row statistics, then the
-    backward pass (each the mean of 5 calls)."""
-    wb = synth.CONFIGS["mha32k_needles"]
+def backward_leg(name="mha32k_needles", reps=5):
+    """Training leg: forward with row statistics, then the backward pass (each
+    the mean of `reps` calls), on the 32K layer or on the 128K-row GQA layer."""
+    wb = synth.CONFIGS[name]
     bq, bk, bv = (to_dev(a) for a in synth.make_qkv(wb, "bf16"))
     gen = torch.Generator(device="cpu").manual_seed(1)
     dout = torch.randn(bq.shape, generator=gen).to(torch.bfloat16).to(bq.device)
@@ -115,7 +115,6 @@ def backward_leg():
     moba.backward(bq, bk, bv, o_b, lse_b, dout, wb.B, wb.k, wb.scale)
     torch.cuda.synchronize()
     e0, e1, e2 = (torch.cuda.Event(enable_timing=True) for _ in range(3))
-    reps = 5
     e0.record()
     for _ in range(reps):
         o_b, lse_b = moba.prefill_train(bq, bk, bv, wb.B, wb.k, wb.scale)
@@ -131,7 +130,7 @@ def backward_leg():
                             f"topk={wb.k}, bf16",
                 "forward_train_ms": fms, "backward_ms": bms,
                 "backward_tflops": 10.0 * wb.d * pairs / (bms / 1e3) / 1e12,
-                "note": "mean of 5 calls; matrix cores, bf16 operands, fp32 accumulation; "
+                "note": f"mean of {reps} calls; matrix cores, bf16 operands, fp32 accumulation; "
                         "the backward call recomputes the selection and its buckets; "
                         "FLOP = 5 products of 2d per attended pair"}
     del bq, bk, bv, dout, o_b, lse_b
@@ -244,7 +243,9 @@ def main():
         return
 
     if args.only == "backward":
-        print(json.dumps({"backward": backward_leg()}), flush=True)
+        print(json.dumps({"backward": backward_leg(),
+                          "backward_llama8b_128k": backward_leg("llama8b_128k", reps=3)}),
+              flush=True)
         return
 
     w = synth.CONFIGS[args.config]
@@ -360,9 +361,10 @@ def main():
                   "median_selection_margin": float(fin.median()) if fin.numel() else None}
         del st
 
-    backward = None
+    backward = backward_large = None
     if not args.no_backward and dtype == "bf16":
         backward = backward_leg()
+        backward_large = backward_leg("llama8b_128k", reps=3)
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -403,6 +405,7 @@ def main():
         "shared_routing": shared,
         "chunked": chunk,
         "backward": backward,
+        "backward_llama8b_128k": backward_large,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)

@@ -9,7 +9,9 @@ The five workloads mirror the shapes of the experiments on the pages:
 * ``coarse32k`` the efficient-vs-naive comparison shape (32K, 1 head, B=2048, k=3) —
   MoonshotAI/MoBA README, implementation details;
 * ``llama8b_1m`` the Llama-3.1-8B 1M-token layer (B=4096, k=12) with 32 query heads
-  sharing 8 KV heads — agihunt summary, results section.
+  sharing 8 KV heads — agihunt summary, results section;
+* ``llama8b_128k`` the same layer at 128K rows (a training-sized shape for the
+  backward pass).
 
 Values come from ``synth.c`` (SplitMix64 counters + Box-Muller); the C
 library is built by :func:`build` and loaded with ctypes.
@@ -68,6 +70,8 @@ CONFIGS = {
                                needle_gain=1.5, needle_row_frac=0.01, seed=SEED_BASE | 3),
     "coarse32k": Workload("coarse32k", 32768, 1, 1, 128, 2048, 3, seed=SEED_BASE | 4),
     "llama8b_1m": Workload("llama8b_1m", 1048576, 32, 8, 128, 4096, 12, seed=SEED_BASE | 5),
+    # the same GQA layer at 128K rows: a training-sized shape for the backward pass
+    "llama8b_128k": Workload("llama8b_128k", 131072, 32, 8, 128, 4096, 12, seed=SEED_BASE | 6),
 }
 
 
