@@ -167,6 +167,51 @@ struct KeyList {
       k[t] = hi;
     }
   }
+  // Add 16 keys at once: sort them descending with a bitonic network; then
+  // m_t = max(k[t], c[KM-1-t]) is exactly the top KM of both lists (two
+  // sorted lists, one read backwards) and is decreasing-then-increasing, so
+  // with maximal keys appended it is bitonic and one bitonic merge of P =
+  // 2^ceil(log2(KM + pads)) elements sorts it; the pads come first and are
+  // dropped. Same result as 16 push() calls, in fewer operations.
+  __device__ inline void push16(uint32_t (&c)[16]) {
+#pragma unroll
+    for (int size = 2; size <= 16; size <<= 1)
+#pragma unroll
+      for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int j = i ^ stride;
+          if (j > i) {
+            const uint32_t hi = c[i] > c[j] ? c[i] : c[j], lo = c[i] > c[j] ? c[j] : c[i];
+            const bool desc = (i & size) == 0;  // the last stage sorts all 16 descending
+            c[i] = desc ? hi : lo;
+            c[j] = desc ? lo : hi;
+          }
+        }
+    constexpr int P = KM <= 4 ? 8 : KM <= 12 ? 16 : KM <= 16 ? 32 : 64;  // room for >= 1 pad
+    constexpr int PADS = P - KM;
+    uint32_t m[P];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) {
+      const uint32_t other = KM - 1 - t < 16 ? c[KM - 1 - t] : 0u;
+      m[t] = k[t] > other ? k[t] : other;
+    }
+#pragma unroll
+    for (int t = KM; t < P; ++t) m[t] = 0xFFFFFFFFu;  // above every real key
+#pragma unroll
+    for (int stride = P >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint32_t hi = m[i] > m[j] ? m[i] : m[j], lo = m[i] > m[j] ? m[j] : m[i];
+          m[i] = hi;
+          m[j] = lo;
+        }
+      }
+#pragma unroll
+    for (int t = 0; t < KM; ++t) k[t] = m[PADS + t];
+  }
 };
 
 // out[0..n) = the n block indices of idx[0..n) in ascending order (n <= KM).
@@ -638,11 +683,13 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
     else
       chunk_scores(cur, q[0], lane, s);
     const int64_t cb = (int64_t)ch * kChunk;
+    uint32_t c[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {  // blocks past the candidates push key 0, which never enters
+    for (int e = 0; e < 16; ++e) {  // blocks past the candidates give key 0, which never enters
       const int b = (int)cb + 8 * (e >> 2) + 4 * h + (e & 3);
-      L.push(b < nc ? score_key(s[e], b, ib) : 0u);
+      c[e] = b < nc ? score_key(s[e], b, ib) : 0u;
     }
+    L.push16(c);
     wait_chunk();
   };
   load_chunk(bufA, planes_g, 0, nc, wave, lane);
