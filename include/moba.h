@@ -91,7 +91,7 @@ typedef struct {
 } moba_problem_t;
 
 /*
- * Size limits of this build (MOBA_ERR_UNSUPPORTED beyond them):
+ * Size limits of this library (MOBA_ERR_UNSUPPORTED beyond them):
  *   head_dim == 128; topk <= 32; ceil(N/B) - 1 <= 8192 history-capable blocks
  *   (for packed sequences: all their blocks together minus one);
  *   N * Hq * topk < 2^31; Hq / Hkv <= 64.
