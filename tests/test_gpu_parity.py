@@ -116,7 +116,7 @@ def test_prefill_all_rows(name, dtype):
     print(f"{name} {dtype or w.dtype}: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
 
 
-def test_prefill_c3_sampled_and_needles():
+def test_prefill_mha32k_needles_sampled():
     w, q, k, v, tq, tk, tv = inputs("mha32k_needles")
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
@@ -137,7 +137,7 @@ def test_prefill_c3_sampled_and_needles():
 
 
 @pytest.mark.timeout(1200)
-def test_prefill_c5_sampled():
+def test_prefill_llama8b_1m_sampled():
     w, q, k, v, tq, tk, tv = inputs("llama8b_1m")
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
     sel = moba.select(tq, tk, w.B, w.k)
