@@ -84,6 +84,81 @@ def read_traffic(kernel_tag):
     return float(fields["hbm_bytes_per_launch"]) if cur == src else None
 
 
+def _best_ms(fn, reps=5):
+    """Best of ``reps`` calls of ``fn`` timed by events on torch's current
+    stream (the stream the binding launches on)."""
+    fn()
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        fn()
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        best = ms if best is None else min(best, ms)
+    return best
+
+
+def measured_peaks():
+    """Measured denominators beside the published ones: the matrix-core
+    issue-rate probe (four waves per workgroup, 2, 3 or 6 workgroups per
+    compute unit, the best of the three), the read-only stream probe over
+    2 GiB (4, 8 or 16 workgroups per compute unit, the best) and the plain
+    copy kernel over 2 GiB (read + write bytes)."""
+    best_tf, shape = 0.0, None
+    for per_cu in (2, 3, 6):
+        wgs = 256 * per_cu
+        iters = 16384 * 512 // wgs
+        out = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+        ms = _best_ms(lambda: moba.debug_mfma_peak(out, iters))
+        if not bool((out == 16.0 * iters).all()):
+            raise RuntimeError("matrix-core probe: checksum mismatch")
+        tf = wgs * 4 * iters * 4 * 32768 / (ms / 1e3) / 1e12
+        if tf > best_tf:
+            best_tf, shape = tf, f"{wgs} workgroups x 4 waves x {iters} rounds of 4 ops"
+        del out
+    nbytes = 2 << 30
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    ms = _best_ms(lambda: moba.debug_copy(src, dst))
+    if not torch.equal(src, dst):
+        raise RuntimeError("copy probe: wrong result")
+    copy_gbps = 2 * nbytes / (ms / 1e3) / 1e9
+    del dst
+    best_rd, rd_shape = 0.0, None
+    for per_cu in (4, 8, 16):
+        out = torch.empty(256 * per_cu * 256, dtype=torch.int32, device="cuda")
+        ms = _best_ms(lambda: moba.debug_read_peak(src, out))
+        # src holds 2^29 words of 1: their XOR is 0
+        if int(np.bitwise_xor.reduce(out.cpu().numpy())) != 0:
+            raise RuntimeError("read probe: checksum mismatch")
+        gbps = nbytes / (ms / 1e3) / 1e9
+        if gbps > best_rd:
+            best_rd, rd_shape = gbps, f"{256 * per_cu} workgroups x 256 threads"
+        del out
+    del src
+    return {"mfma_bf16_tflops": best_tf, "mfma_probe": shape,
+            "hbm_read_gbps": best_rd,
+            "hbm_read_probe": f"2 GiB read once, 16-byte loads, four in flight per thread, "
+                              f"{rd_shape}",
+            "hbm_copy_gbps": copy_gbps,
+            "hbm_copy_probe": "16-byte grid-stride copy of 2 GiB; bytes = read + write"}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, q, k, v, rows_wanted):
     import oracle  # the fp64 oracle: this leg only
     rows, heads = synth.sample_rows(w, 4096)
@@ -98,6 +173,8 @@ def cpu_baseline(w, q, k, v, rows_wanted):
     tok_s = (len(rows) / w.Hq) / (t2 - t1)
     return {
         "value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
+        "cpu_model": _cpu_model(),
+        "extrapolated_layer_hours": w.N / tok_s / 3600.0,
         "sample": (f"{len(rows)} seeded (row, head) pairs of the same layer spread over all blocks; "
                    f"value = pairs/{w.Hq} per second of the fp64 dense-masked row evaluation; the "
                    f"one-time fp64 block means took {t1 - t0:.2f} s and are not in the rate"),
@@ -221,6 +298,8 @@ def main():
     ap.add_argument("--only", choices=["backward", "chunk"], default=None,
                     help="only run that leg (the training leg on the 32K layer, or the "
                          "chunk / decode leg on the 1M-row cache) and print its JSON object")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured matrix-core and HBM-stream denominators")
     ap.add_argument("--calibrate-copy-mib", type=int, default=0,
                     help="only run the plain copy kernel over this many MiB (hardware-counter "
                          "calibration of FETCH_SIZE / WRITE_SIZE) and exit")
@@ -366,6 +445,8 @@ def main():
         backward = backward_leg()
         backward_large = backward_leg("llama8b_128k", reps=3)
 
+    peaks = None if args.no_peaks else measured_peaks()
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
@@ -395,10 +476,17 @@ def main():
         "meanpool_frac_of_hbm_peak": mp_bytes / (stage_ms["meanpool"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
         "bucket_gbps": bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9,
         "bucket_frac_of_hbm_peak": bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9 / PEAK_HBM_GBPS,
+        "measured_peaks": peaks,
+        "meanpool_frac_of_measured_read": (mp_bytes / (stage_ms["meanpool"] / 1e3) / 1e9
+                                           / peaks["hbm_read_gbps"]) if peaks else None,
+        "bucket_frac_of_measured_copy": (bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9
+                                         / peaks["hbm_copy_gbps"]) if peaks else None,
         "routed_entries": entries,
         "roofline": {"bound": "mfma", "kernel": "attn_hist_bf16",
                      "achieved": hist_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": hist_tflops / PEAK_BF16_TFLOPS,
+                     "frac_of_measured_peak": (hist_tflops / peaks["mfma_bf16_tflops"]
+                                               if peaks else None),
                      "traffic": read_traffic("attn_hist_llama8b_1m")},
         "dense_causal": dense,
         "varlen": varlen,

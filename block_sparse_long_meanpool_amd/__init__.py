@@ -47,6 +47,7 @@ EXPORTS = (
     "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
+    "moba_debug_read_peak", "moba_debug_mfma_peak",
 )
 
 
@@ -122,6 +123,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_debug_bucket_capacity": (sz, [P]),
         "moba_debug_bucket": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "moba_debug_copy": (ctypes.c_int, [vp, vp, sz, vp]),
+        "moba_debug_read_peak": (ctypes.c_int, [vp, sz, ctypes.c_int32, vp, vp]),
+        "moba_debug_mfma_peak": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32, vp, vp]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -609,3 +612,32 @@ def debug_copy(src, dst):
     st = lib.moba_debug_copy(src.data_ptr(), dst.data_ptr(), nbytes, _stream(src.device))
     _ok(st, "moba_debug_copy")
     return dst
+
+
+def debug_read_peak(src, out):
+    """Read-only HBM stream probe over all bytes of ``src``; ``out`` is an
+    int32 device tensor of ``workgroups * 256`` values whose XOR equals the
+    XOR of every 32-bit word of ``src``."""
+    lib = load_library()
+    _check_dev(src, out)
+    if out.dtype != torch.int32 or out.numel() % 256:
+        raise ValueError("out must be an int32 tensor of workgroups * 256 values")
+    nbytes = src.numel() * src.element_size()
+    st = lib.moba_debug_read_peak(src.data_ptr(), nbytes, out.numel() // 256, out.data_ptr(),
+                                  _stream(src.device))
+    _ok(st, "moba_debug_read_peak")
+    return out
+
+
+def debug_mfma_peak(out, iters):
+    """Matrix-core issue-rate probe: ``out`` is a float32 device tensor of
+    ``workgroups * 256`` values (one per lane); each comes back as exactly
+    ``16 * iters``. FLOP per call = ``workgroups * 4 * iters * 4 * 32768``."""
+    lib = load_library()
+    _check_dev(out)
+    if out.dtype != torch.float32 or out.numel() % 256 or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor of workgroups * 256 values")
+    st = lib.moba_debug_mfma_peak(out.numel() // 256, int(iters), out.data_ptr(),
+                                  _stream(out.device))
+    _ok(st, "moba_debug_mfma_peak")
+    return out

@@ -826,4 +826,23 @@ int moba_debug_copy(const void* src, void* dst, size_t bytes, void* stream) {
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "copy");
 }
 
+int moba_debug_read_peak(const void* src, size_t bytes, int32_t workgroups, uint32_t* out,
+                         void* stream) {
+  if (!src || !out) return fail(MOBA_ERR_INVALID_ARGUMENT, "src and out must be non-NULL");
+  if (!aligned(src, 16) || bytes % 16 || !aligned(out, 4))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "read probe needs a 16-byte aligned src and size");
+  if (workgroups < 1 || workgroups > (1 << 20))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workgroups must lie in [1, 2^20]");
+  hipError_t e = launch_read_probe(src, bytes, workgroups, out, (hipStream_t)stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e, "read probe");
+}
+
+int moba_debug_mfma_peak(int32_t workgroups, int32_t iters, float* out, void* stream) {
+  if (!out || !aligned(out, 4)) return fail(MOBA_ERR_INVALID_ARGUMENT, "out must be a non-NULL float pointer");
+  if (workgroups < 1 || workgroups > (1 << 20) || iters < 1 || iters > (1 << 20))
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "workgroups and iters must lie in [1, 2^20]");
+  hipError_t e = launch_mfma_probe(workgroups, iters, out, (hipStream_t)stream);
+  return e == hipSuccess ? MOBA_OK : hip_fail(e, "mfma probe");
+}
+
 }  // extern "C"

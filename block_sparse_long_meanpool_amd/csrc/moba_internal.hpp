@@ -173,6 +173,9 @@ hipError_t launch_decode(const Prob& P, const Blocks& T, const void* q, const vo
 
 hipError_t launch_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, size_t count, hipStream_t s);
+hipError_t launch_mfma_probe(int workgroups, int iters, float* out, hipStream_t s);
+hipError_t launch_read_probe(const void* src, size_t bytes, int workgroups, uint32_t* out,
+                             hipStream_t s);
 
 // Element type of the partial outputs of history attention.
 inline size_t part_elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_F32 ? 4 : 2; }

@@ -322,7 +322,23 @@ MOBA_API const char *moba_last_error(void);
  *     ((row*Hq + head)*(topk-1) + slot), slot = position in the sel row.
  *     Lists are ordered by (row, head). workspace as for moba_prefill.
  *   moba_debug_copy: plain device copy of `bytes` bytes (a traffic calibration
- *     kernel for hardware counters).
+ *     kernel for hardware counters, and the HBM stream probe: it moves
+ *     2 * bytes through HBM per call). src and dst: device, 16-byte aligned,
+ *     non-overlapping; bytes a multiple of 16.
+ *   moba_debug_read_peak: read-only HBM stream probe (the measured
+ *     denominator for read-bound stages): `workgroups` workgroups of 256
+ *     threads read all `bytes` of src (device, 16-byte aligned, bytes a
+ *     multiple of 16) once, 16 bytes per load, four loads in flight per
+ *     thread; out: device, workgroups * 256 uint32 values whose XOR equals
+ *     the XOR of every 32-bit word of src. workgroups in [1, 2^20], else
+ *     MOBA_ERR_INVALID_ARGUMENT; nothing is allocated.
+ *   moba_debug_mfma_peak: matrix-core issue-rate probe, the measured
+ *     denominator beside the published bf16 peak. `workgroups` workgroups of
+ *     four waves each run `iters` rounds of four v_mfma_f32_32x32x16_bf16 per
+ *     wave on register operands: FLOP per call = workgroups * 4 * iters * 4 *
+ *     32768. out: device fp32, workgroups * 256 values, one per lane, each
+ *     exactly 16 * iters (a checksum that every op ran). workgroups and iters
+ *     in [1, 2^20], else MOBA_ERR_INVALID_ARGUMENT; nothing is allocated.
  */
 MOBA_API int moba_debug_meanpool(const moba_problem_t *p, const void *k, double *kbar, void *workspace,
                         size_t ws_bytes, void *stream);
@@ -330,6 +346,9 @@ MOBA_API size_t moba_debug_bucket_capacity(const moba_problem_t *p);
 MOBA_API int moba_debug_bucket(const moba_problem_t *p, const int32_t *sel, int32_t *offsets,
                       uint32_t *entries, void *workspace, size_t ws_bytes, void *stream);
 MOBA_API int moba_debug_copy(const void *src, void *dst, size_t bytes, void *stream);
+MOBA_API int moba_debug_read_peak(const void *src, size_t bytes, int32_t workgroups, uint32_t *out,
+                                  void *stream);
+MOBA_API int moba_debug_mfma_peak(int32_t workgroups, int32_t iters, float *out, void *stream);
 
 #ifdef __cplusplus
 }

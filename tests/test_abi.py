@@ -124,6 +124,25 @@ def test_copy_rejects_bad_arguments():
     assert lib.moba_debug_copy(FAKE, FAKE, 15, None) == 1
 
 
+def test_read_probe_rejects_bad_arguments():
+    lib = moba.load_library()
+    assert lib.moba_debug_read_peak(None, 16, 1, FAKE, None) == 1
+    assert lib.moba_debug_read_peak(FAKE, 16, 1, None, None) == 1
+    assert lib.moba_debug_read_peak(FAKE, 15, 1, FAKE, None) == 1
+    assert lib.moba_debug_read_peak(FAKE + 4, 16, 1, FAKE, None) == 1
+    assert lib.moba_debug_read_peak(FAKE, 16, 0, FAKE, None) == 1
+    assert lib.moba_debug_read_peak(FAKE, 16, (1 << 20) + 1, FAKE, None) == 1
+
+
+def test_mfma_probe_rejects_bad_arguments():
+    lib = moba.load_library()
+    assert lib.moba_debug_mfma_peak(1, 1, None, None) == 1
+    assert lib.moba_debug_mfma_peak(0, 1, FAKE, None) == 1
+    assert lib.moba_debug_mfma_peak(1, 0, FAKE, None) == 1
+    assert lib.moba_debug_mfma_peak((1 << 20) + 1, 1, FAKE, None) == 1
+    assert lib.moba_debug_mfma_peak(1, (1 << 20) + 1, FAKE, None) == 1
+
+
 def _cu(*xs):
     return (ctypes.c_int64 * len(xs))(*xs)
 

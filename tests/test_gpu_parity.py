@@ -613,3 +613,27 @@ def test_backward_varlen_matches_each_sequence(lens, Hq, Hkv, B, topk, dtype):
     _grad_close(to_np(dq), rq, dtype, "dq")
     _grad_close(to_np(dk), rk, dtype, "dk")
     _grad_close(to_np(dv), rv, dtype, "dv")
+
+
+def test_mfma_probe_runs_every_op():
+    """The matrix-core probe's per-lane checksum is exactly 16 * iters when
+    every one of its ops ran (operands 0.125, sums exact in fp32)."""
+    for wgs, iters in ((3, 1), (512, 100), (1, 1 << 20)):
+        out = torch.full((wgs * 256,), -1.0, dtype=torch.float32, device=DEV)
+        moba.debug_mfma_peak(out, iters)
+        torch.cuda.synchronize()
+        assert bool((out == 16.0 * iters).all()), (wgs, iters)
+
+
+def test_read_probe_sees_every_word():
+    """The read probe's outputs XOR to the XOR of every 32-bit word of its
+    input, for sizes that leave ragged last rounds and for more workgroups
+    than rounds."""
+    g = np.random.default_rng(7)
+    for words, wgs in ((4, 1), (4 * 1024 * 3 + 8, 2), (4 * 1000, 64), (1 << 22, 37)):
+        host = g.integers(-2**31, 2**31, size=words, dtype=np.int64).astype(np.int32)
+        src = torch.from_numpy(host).to(DEV)
+        out = torch.zeros(wgs * 256, dtype=torch.int32, device=DEV)
+        moba.debug_read_peak(src, out)
+        got = np.bitwise_xor.reduce(out.cpu().numpy())
+        assert got == np.bitwise_xor.reduce(host), (words, wgs)
