@@ -27,6 +27,20 @@ int hip_fail(hipError_t e, const char* where) {
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
+// The bf16 kernels read the packed V^T (and, in the backward, K^T) of one
+// KV head through a buffer resource whose per-lane byte offsets are 32-bit:
+// head-dim row d starts at d * ldv elements with ldv = blocks * Bpad, so the
+// last row's 64-key tile must end below 2^32 bytes. Beyond that the offsets
+// would wrap and read the wrong rows, so such problems are refused.
+int check_vt_extent(const Prob& P, int64_t blocks) {
+  if (P.dtype != MOBA_DTYPE_BF16) return MOBA_OK;
+  const double ldv = (double)blocks * (double)vt_padded_block(P.B);
+  if (2.0 * ((kHeadDim - 1) * ldv + 64.0) >= 4294967296.0)
+    return fail(MOBA_ERR_UNSUPPORTED,
+                "bf16: ceil(N/B) * ceil(B/64) * 64 must stay below 16,909,320 rows of packed V");
+  return MOBA_OK;
+}
+
 // Checks the problem; fills *P. Returns MOBA_OK or an error code (with text).
 int make_prob(const moba_problem_t* p, Prob* P) {
   if (!p) return fail(MOBA_ERR_INVALID_ARGUMENT, "problem pointer is NULL");
@@ -74,7 +88,7 @@ int make_prob(const moba_problem_t* p, Prob* P) {
     P->hist_rows += rows * (c < P->KH ? c : P->KH);
   }
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
-  return MOBA_OK;
+  return check_vt_extent(*P, P->n);
 }
 
 // Chunk of the last q_rows positions of one sequence of p->seqlen rows: the
@@ -124,7 +138,7 @@ int make_prob_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu, P
   P->nh = P->n - 1;
   P->vt_blocks = P->n;
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
-  return MOBA_OK;
+  return check_vt_extent(*P, P->n);
 }
 
 size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
@@ -612,7 +626,7 @@ static int check_capacity(const Prob& P, int64_t capacity) {
     return fail(MOBA_ERR_UNSUPPORTED, "capacity * num_q_heads * topk must be < 2^31");
   if ((capacity + P.B - 1) / P.B - 1 > kMaxHist)
     return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks in the capacity");
-  return MOBA_OK;
+  return check_vt_extent(P, (capacity + P.B - 1) / P.B);
 }
 
 size_t moba_cache_bytes(const moba_problem_t* p, int64_t capacity) {

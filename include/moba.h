@@ -94,7 +94,10 @@ typedef struct {
  * Size limits of this library (MOBA_ERR_UNSUPPORTED beyond them):
  *   head_dim == 128; topk <= 32; ceil(N/B) - 1 <= 8192 history-capable blocks
  *   (for packed sequences: all their blocks together minus one);
- *   N * Hq * topk < 2^31; Hq / Hkv <= 64.
+ *   N * Hq * topk < 2^31; Hq / Hkv <= 64; bf16 only: ceil(N/B) * ceil(B/64) * 64
+ *   < 16,909,320 (a KV head's packed V^T is addressed with 32-bit byte
+ *   offsets; for packed sequences the blocks of all sequences count, for a
+ *   decode cache its capacity does).
  * Value range: the bf16 path keeps normalised partial outputs in fp16, so
  * |V| must stay below 65504.
  */

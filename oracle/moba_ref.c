@@ -143,8 +143,11 @@ static void branch_stats(const moba_ref_problem *p, const double *q, const void 
  *
  *  kbar        block keys from moba_ref_block_means, or NULL to compute them here.
  *  forced_sel  NULL, or [nrows][k] selections to use instead of the gate's
- *              ranking (entries >= 0 and < the row's own block are taken as the
- *              history set; the own block is always added).
+ *              ranking: entries b with 0 <= b < the row's own block c are
+ *              the history set, a repeated entry counting once and at most
+ *              k-1 of them kept in the given order; -1, the own block and
+ *              later blocks are skipped; the own block is always attended
+ *              causally.
  *  sel_out     [nrows][k]: selected blocks ascending (history, then own block),
  *              padded with -1. May be NULL.
  *  o_out       [nrows][d] fp64 output. May be NULL.
@@ -372,69 +375,130 @@ int moba_ref_causal_full(const moba_ref_problem *p, const void *Q, const void *K
  * Written out over every (row, head) in fp64; the selection is taken from
  * sel [N][Hq][k] (as moba_ref_rows returns it: history blocks < the row's
  * block, then the own block, -1 padding). dq [N][Hq][d], dk and dv
- * [N][Hkv][d] are overwritten. Serial: small problems only.
+ * [N][Hkv][d] are overwritten.
+ *
+ * Every sum runs in the order of the plain loop nest "for row, for head, for
+ * key j": dq of a (row, head) adds its keys in ascending j, and dK_j / dV_j
+ * add the contributions of the (row, head) pairs in ascending (row, head).
+ * Rows are processed in chunks: the per-pair quantities of a chunk (P_j and
+ * dZ_j for its attended keys) are computed in parallel over pairs, then each
+ * key's dK / dV rows take the chunk's contributions in (row, head) order, in
+ * parallel over keys — the same additions in the same order as the serial
+ * nest, so the result does not depend on the thread count.
  */
+enum { BWD_CHUNK_ROWS = 32 };
+
 int moba_ref_backward(const moba_ref_problem *p, const void *Q, const void *K, const void *V,
                       const double *dO, const int32_t *sel, double *dq, double *dk, double *dv) {
   if (check(p) || !Q || !K || !V || !dO || !sel || !dq || !dk || !dv) return 1;
   const int64_t N = p->N, d = p->d, B = p->B, kk = p->k;
+  const int64_t Hq = p->Hq;
   const int G = p->Hq / p->Hkv;
   for (int64_t i = 0; i < N * p->Hq * d; ++i) dq[i] = 0.0;
   for (int64_t i = 0; i < N * p->Hkv * d; ++i) dk[i] = dv[i] = 0.0;
-  unsigned char *member = (unsigned char *)malloc((size_t)N);
-  double *z = (double *)malloc(sizeof(double) * (size_t)N);
-  double *o = (double *)malloc(sizeof(double) * (size_t)d);
-  if (!member || !z || !o) {
+  const int64_t npair = BWD_CHUNK_ROWS * Hq;
+  /* per pair of a chunk: membership and P_j, dZ_j over all N keys */
+  unsigned char *member = (unsigned char *)malloc((size_t)(npair * N));
+  double *pw = (double *)malloc(sizeof(double) * (size_t)(npair * N));
+  double *dzw = (double *)malloc(sizeof(double) * (size_t)(npair * N));
+  /* the inputs widened to fp64 once (exact) */
+  const int64_t nq = N * Hq * d, nk = N * p->Hkv * d;
+  double *Qd = (double *)malloc(sizeof(double) * (size_t)nq);
+  double *Kd = (double *)malloc(sizeof(double) * (size_t)nk);
+  double *Vd = (double *)malloc(sizeof(double) * (size_t)nk);
+  if (!member || !pw || !dzw || !Qd || !Kd || !Vd) {
     free(member);
-    free(z);
-    free(o);
+    free(pw);
+    free(dzw);
+    free(Qd);
+    free(Kd);
+    free(Vd);
     return 2;
   }
-  for (int64_t row = 0; row < N; ++row) {
-    const int64_t c = row / B;
-    for (int h = 0; h < p->Hq; ++h) {
-      const int g = h / G;
-      const int32_t *sr = sel + (row * p->Hq + h) * kk;
-      for (int64_t j = 0; j < N; ++j) member[j] = (j / B == c && j <= row);
-      for (int64_t t = 0; t < kk; ++t)
-        if (sr[t] >= 0 && sr[t] < c)
-          for (int64_t j = sr[t] * B; j < (sr[t] + 1) * B; ++j) member[j] = 1;
-      const int64_t qb = (row * p->Hq + h) * d;
-      double mx = -INFINITY;
-      for (int64_t j = 0; j < N; ++j) {
-        if (!member[j]) continue;
-        double dot = 0.0;
-        for (int64_t t = 0; t < d; ++t) dot += ld(Q, p->dtype, qb + t) * ld(K, p->dtype, (j * p->Hkv + g) * d + t);
-        z[j] = p->scale * dot;
-        if (z[j] > mx) mx = z[j];
+  for (int64_t i = 0; i < nq; ++i) Qd[i] = ld(Q, p->dtype, i);
+  for (int64_t i = 0; i < nk; ++i) {
+    Kd[i] = ld(K, p->dtype, i);
+    Vd[i] = ld(V, p->dtype, i);
+  }
+  int err = 0;
+  for (int64_t r0 = 0; r0 < N && !err; r0 += BWD_CHUNK_ROWS) {
+    const int64_t r1 = r0 + BWD_CHUNK_ROWS < N ? r0 + BWD_CHUNK_ROWS : N;
+    const int64_t pairs = (r1 - r0) * Hq;
+    /* phase 1: softmax weights, D, dZ and dq of each (row, head) of the chunk */
+#pragma omp parallel
+    {
+      double *o = (double *)malloc(sizeof(double) * (size_t)d);
+      if (!o) {
+#pragma omp atomic write
+        err = 2;
+      } else {
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t pi = 0; pi < pairs; ++pi) {
+          const int64_t row = r0 + pi / Hq;
+          const int h = (int)(pi % Hq), g = h / G;
+          const int64_t c = row / B;
+          unsigned char *mem = member + pi * N;
+          double *z = pw + pi * N, *dz = dzw + pi * N;
+          const int32_t *sr = sel + (row * Hq + h) * kk;
+          for (int64_t j = 0; j < N; ++j) mem[j] = (j / B == c && j <= row);
+          for (int64_t t = 0; t < kk; ++t)
+            if (sr[t] >= 0 && sr[t] < c)
+              for (int64_t j = sr[t] * B; j < (sr[t] + 1) * B; ++j) mem[j] = 1;
+          const int64_t qb = (row * Hq + h) * d;
+          double mx = -INFINITY;
+          for (int64_t j = 0; j < N; ++j) {
+            if (!mem[j]) continue;
+            double dot = 0.0;
+            for (int64_t t = 0; t < d; ++t)
+              dot += Qd[qb + t] * Kd[(j * p->Hkv + g) * d + t];
+            z[j] = p->scale * dot;
+            if (z[j] > mx) mx = z[j];
+          }
+          double l = 0.0;
+          for (int64_t j = 0; j < N; ++j)
+            if (mem[j]) l += exp(z[j] - mx);
+          for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
+          for (int64_t j = 0; j < N; ++j) {
+            if (!mem[j]) continue;
+            z[j] = exp(z[j] - mx) / l; /* now P_j */
+            for (int64_t t = 0; t < d; ++t) o[t] += z[j] * Vd[(j * p->Hkv + g) * d + t];
+          }
+          double D = 0.0;
+          for (int64_t t = 0; t < d; ++t) D += dO[qb + t] * o[t];
+          for (int64_t j = 0; j < N; ++j) {
+            if (!mem[j]) continue;
+            const int64_t kvb = (j * p->Hkv + g) * d;
+            double dp = 0.0;
+            for (int64_t t = 0; t < d; ++t) dp += dO[qb + t] * Vd[kvb + t];
+            dz[j] = z[j] * (dp - D);
+            for (int64_t t = 0; t < d; ++t) dq[qb + t] += p->scale * dz[j] * Kd[kvb + t];
+          }
+        }
       }
-      double l = 0.0;
-      for (int64_t j = 0; j < N; ++j)
-        if (member[j]) l += exp(z[j] - mx);
-      for (int64_t t = 0; t < d; ++t) o[t] = 0.0;
-      for (int64_t j = 0; j < N; ++j) {
-        if (!member[j]) continue;
-        z[j] = exp(z[j] - mx) / l; /* now P_j */
-        for (int64_t t = 0; t < d; ++t) o[t] += z[j] * ld(V, p->dtype, (j * p->Hkv + g) * d + t);
-      }
-      double D = 0.0;
-      for (int64_t t = 0; t < d; ++t) D += dO[qb + t] * o[t];
-      for (int64_t j = 0; j < N; ++j) {
-        if (!member[j]) continue;
-        const int64_t kvb = (j * p->Hkv + g) * d;
-        double dp = 0.0;
-        for (int64_t t = 0; t < d; ++t) dp += dO[qb + t] * ld(V, p->dtype, kvb + t);
-        const double dz = z[j] * (dp - D);
+      free(o);
+    }
+    if (err) break;
+    /* phase 2: each key's dV and dK rows, the chunk's pairs in (row, head) order */
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < N; ++j) {
+      for (int64_t pi = 0; pi < pairs; ++pi) {
+        if (!member[pi * N + j]) continue;
+        const int64_t row = r0 + pi / Hq;
+        const int h = (int)(pi % Hq), g = h / G;
+        const int64_t qb = (row * Hq + h) * d, kvb = (j * p->Hkv + g) * d;
+        const double pj = pw[pi * N + j], dzj = dzw[pi * N + j];
         for (int64_t t = 0; t < d; ++t) {
-          dv[kvb + t] += z[j] * dO[qb + t];
-          dq[qb + t] += p->scale * dz * ld(K, p->dtype, kvb + t);
-          dk[kvb + t] += p->scale * dz * ld(Q, p->dtype, qb + t);
+          dv[kvb + t] += pj * dO[qb + t];
+          dk[kvb + t] += p->scale * dzj * Qd[qb + t];
         }
       }
     }
   }
   free(member);
-  free(z);
-  free(o);
-  return 0;
+  free(pw);
+  free(dzw);
+  free(Qd);
+  free(Kd);
+  free(Vd);
+  return err;
 }

@@ -59,6 +59,9 @@ BAD = [
     (dict(N=1 << 20, block_size=64), moba.MOBA_ERR_UNSUPPORTED),
     (dict(N=1 << 24, Hq=64, Hkv=64, block_size=4096, topk=3), moba.MOBA_ERR_UNSUPPORTED),
     (dict(Hq=128, Hkv=1), moba.MOBA_ERR_UNSUPPORTED),
+    # bf16: the packed V^T rows of a KV head would pass 2^32 bytes of 32-bit
+    # buffer offsets (N * Hq * topk is still below 2^31)
+    (dict(N=20_000_000, Hq=8, Hkv=8, block_size=4096, topk=12), moba.MOBA_ERR_UNSUPPORTED),
 ]
 
 FAKE = 1 << 20  # a non-NULL, aligned address that is never dereferenced: every case fails first
@@ -294,3 +297,22 @@ def test_varlen_training_rejects_bad_arguments():
                                          FAKE, FAKE, 1 << 40, None) == 1
     assert lib.moba_prefill_train_varlen(ctypes.byref(p), 2, cu, FAKE, FAKE, FAKE, FAKE, FAKE,
                                          None, FAKE, 1 << 40, None) == 1
+
+
+def test_packed_v_extent_limit():
+    """bf16 problems are accepted up to the 32-bit offset range of the packed
+    V^T rows (ceil(N/B) * ceil(B/64) * 64 < 16,909,320) and refused past it;
+    fp32 problems do not read the packed copy and keep the larger range."""
+    lib = moba.load_library()
+    ok = _prob(N=16_777_216, Hq=1, Hkv=1, block_size=4096, topk=2)
+    assert lib.moba_workspace_size(ctypes.byref(ok)) > 0
+    big = _prob(N=16_912_384, Hq=1, Hkv=1, block_size=4096, topk=2)
+    assert lib.moba_workspace_size(ctypes.byref(big)) == 0
+    assert lib.moba_prefill(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 40, None) == 2
+    assert b"16,909,320" in lib.moba_last_error()
+    big32 = _prob(N=16_912_384, Hq=1, Hkv=1, block_size=4096, topk=2, dtype=1)
+    assert lib.moba_workspace_size(ctypes.byref(big32)) > 0
+    # the decode cache's capacity is held to the same limit
+    small = _prob(N=4096, Hq=1, Hkv=1, block_size=4096, topk=2)
+    assert lib.moba_cache_bytes(ctypes.byref(small), 16_777_216) > 0
+    assert lib.moba_cache_bytes(ctypes.byref(small), 16_912_384) == 0

@@ -69,7 +69,8 @@ def test_select_all_rows(name, dtype):
     sel = moba.select(tq, tk, w.B, w.k).cpu().numpy()
     rows, heads = all_rows(w.N, w.Hq)
     ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, rows, heads, want_o=False)
-    check_selection(sel.reshape(-1, w.k), ref_sel, gap, name)
+    check_selection(sel.reshape(-1, w.k), ref_sel, gap, name,
+                    ctx=(q, k, w.B, rows, heads, oracle.ROUTING_PER_HEAD))
 
 
 def _bucket_reference(sel, Hkv, B):
@@ -104,7 +105,9 @@ def test_bucket_lists(N, Hq, Hkv, B, topk):
 
 
 # ---------------------------------------------------------------- prefill ---
-@pytest.mark.parametrize("name,dtype", [("tiny2k", "f32"), ("tiny2k", "bf16"), ("mha8k", None), ("coarse32k", None)])
+@pytest.mark.timeout(600)
+@pytest.mark.parametrize("name,dtype", [("tiny2k", "f32"), ("tiny2k", "bf16"), ("mha8k", None), ("coarse32k", None),
+                                        ("mha32k_needles", None)])
 def test_prefill_all_rows(name, dtype):
     w, q, k, v, tq, tk, tv = inputs(name, dtype)
     o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale)
@@ -152,7 +155,8 @@ def test_prefill_llama8b_1m_sampled():
     # selections on a larger seeded sample (gate only)
     r2, h2 = synth.sample_rows(w.with_(seed=w.seed ^ 0xABCDEF), 1 << 20)
     ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, r2, h2, want_o=False, kbar=kbar)
-    check_selection(sel_np[r2, h2], ref_sel, gap, "llama8b_1m sel")
+    check_selection(sel_np[r2, h2], ref_sel, gap, "llama8b_1m sel",
+                    ctx=(q, k, w.B, r2, h2, oracle.ROUTING_PER_HEAD))
     print(f"llama8b_1m: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
 
 
@@ -386,7 +390,8 @@ def test_shared_fast_tier_equals_exact_tier():
     heads = rng.integers(0, Hq, size=rows.size)
     ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False,
                                   routing=oracle.ROUTING_SHARED)
-    check_selection(fast[rows, heads], ref_sel, gap, "shared fast tier")
+    check_selection(fast[rows, heads], ref_sel, gap, "shared fast tier",
+                    ctx=(q, k, B, rows, heads, oracle.ROUTING_SHARED))
 
 
 @pytest.mark.parametrize("kind", ["zero_k", "integer"])
@@ -413,7 +418,8 @@ def test_routing_stats(routing):
     union = st["union_size"].cpu().numpy()
     rows, heads = all_rows(N, Hq)
     ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False, routing=routing)
-    check_selection(sel.reshape(-1, topk), ref_sel, gap, "stats sel")
+    check_selection(sel.reshape(-1, topk), ref_sel, gap, "stats sel",
+                    ctx=(q, k, B, rows, heads, routing))
     m, g = margin.reshape(-1), gap[:, 0]
     assert np.array_equal(np.isnan(m), np.isnan(g))
     ok = ~np.isnan(g)

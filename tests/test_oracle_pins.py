@@ -539,3 +539,143 @@ def test_backward_closed_forms():
     vc = np.broadcast_to(v[:1], v.shape).copy()
     dq, dk, _ = oracle.backward(q, k, vc, dout, B, topk, scale=0.5)
     assert np.max(np.abs(dq)) < 1e-12 and np.max(np.abs(dk)) < 1e-12
+
+
+# ------------------------------------------------------- forced selection ---
+def _forced_history(row_sel, c, topk):
+    """The history set a forced selection row stands for: entries that are
+    earlier blocks of the row (0 <= b < c), first occurrence only, at most
+    topk - 1 of them in the given order; -1 pads, the own block and future
+    blocks are no history (PaperTrace "2.1.3 MoBA", section 2: the own block is
+    always attended causally and never ranked; section 5 lists forcing the
+    candidate set as a diagnostic)."""
+    out = []
+    for b in row_sel:
+        b = int(b)
+        if 0 <= b < c and b not in out and len(out) < topk - 1:
+            out.append(b)
+    return out
+
+
+def _forced_mask(N, Hq, B, rows, heads, fsel, topk, own_whole=False):
+    """Boolean attention mask [Hq, N, N] of the forced candidate sets (rows
+    outside `rows` keep only themselves so every softmax row is defined)."""
+    m = np.zeros((Hq, N, N), bool)
+    m[:, np.arange(N), np.arange(N)] = True
+    for r, h, fs in zip(rows, heads, fsel):
+        c = int(r) // B
+        m[h, r, :] = False
+        for b in _forced_history(fs, c, topk):
+            m[h, r, b * B:(b + 1) * B] = True
+        hi = min(N, (c + 1) * B) if own_whole else int(r) + 1
+        m[h, r, c * B:hi] = True
+    return m
+
+
+def _forced_cases(N, Hq, B, topk, seed):
+    """(rows, heads, forced rows) exercising every rule of forced selection."""
+    rng = np.random.default_rng(seed)
+    rows, heads, fsel = [], [], []
+    for r in range(N):
+        c = r // B
+        for h in range(Hq):
+            kind = (r * Hq + h) % 6
+            if kind == 0:    # a random subset of earlier blocks, reversed order
+                hist = list(rng.permutation(c)[: topk - 1])[::-1] if c else []
+                row = hist + [-1] * (topk - len(hist))
+            elif kind == 1:  # one earlier block repeated, then -1
+                b = int(rng.integers(0, c)) if c else -1
+                row = [b] * min(3, topk) + [-1] * (topk - min(3, topk))
+            elif kind == 2:  # the own block first, then earlier blocks
+                row = [c] + list(range(min(c, topk - 1)))
+                row = (row + [-1] * topk)[:topk]
+            elif kind == 3:  # future blocks and -1 mixed with one earlier block
+                row = [c + 1, -1, (c - 1) if c else -7, c + 5] + [-1] * topk
+                row = row[:topk]
+            elif kind == 4:  # every earlier block, more than topk - 1 of them
+                row = (list(range(c))[::-1] + [-1] * topk)[:topk]
+            else:            # nothing forced: own block only
+                row = [-1] * topk
+            rows.append(r)
+            heads.append(h)
+            fsel.append(row)
+    return np.array(rows, np.int64), np.array(heads, np.int32), np.array(fsel, np.int32)
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,d,B,topk,seed", [(48, 2, 1, 8, 6, 4, 1), (40, 4, 2, 4, 5, 3, 2),
+                                                     (64, 3, 3, 8, 8, 5, 3)])
+def test_forced_selection_matches_masked_softmax(N, Hq, Hkv, d, B, topk, seed):
+    """Forced mode attends exactly the forced history blocks plus the causal own
+    block, against torch's fp64 attention with that mask built here."""
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=seed)
+    scale = 0.41
+    rows, heads, fsel = _forced_cases(N, Hq, B, topk, seed)
+    sel, o, gap = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale, forced_sel=fsel)
+    ref = _sdpa_rows(q, k, v, _forced_mask(N, Hq, B, rows, heads, fsel, topk), scale)
+    assert np.max(np.abs(o - ref[rows, heads])) < 1e-12
+    # the returned selection is the forced history ascending, then the own block
+    for i in range(len(rows)):
+        c = int(rows[i]) // B
+        hist = sorted(_forced_history(fsel[i], c, topk))
+        assert list(sel[i]) == hist + [c] + [-1] * (topk - len(hist) - 1)
+    assert np.all(np.isnan(gap))
+    # the two-branch form (eqs. (7)-(8)) agrees under forcing too
+    _, o2, _ = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale, forced_sel=fsel,
+                           mode=oracle.MODE_TWO_BRANCH)
+    assert np.max(np.abs(o2 - o)) < 1e-12
+
+
+def test_forced_selection_is_discriminating():
+    """The forced-mode pin above fails for the plausible wrong forced paths: a
+    path that ignores the forced rows (natural ranking), one that takes the own
+    block whole instead of causally, and one that drops repeated entries'
+    later distinct blocks would all be off by far more than its tolerance."""
+    N, Hq, Hkv, d, B, topk = 48, 2, 1, 8, 6, 4
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=1)
+    scale = 0.41
+    rows, heads, fsel = _forced_cases(N, Hq, B, topk, 1)
+    ref = _sdpa_rows(q, k, v, _forced_mask(N, Hq, B, rows, heads, fsel, topk), scale)[rows, heads]
+    # (a) ignoring forced_sel: the natural selection differs on many rows
+    nat_sel, o_nat, _ = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale)
+    differs = np.abs(o_nat - ref).max(axis=1) > 1e-3
+    assert differs.sum() > len(rows) // 4
+    # the forced lowest-scoring choices really are off the natural ranking
+    low = []
+    for i in range(len(rows)):
+        c = int(rows[i]) // B
+        if c > topk - 1:
+            s = q[rows[i], heads[i]].astype(np.float64) @ oracle.block_means(k, B)[0, :c].T
+            low.append(sorted(np.argsort(s, kind="stable")[: topk - 1].tolist()))
+    assert len(low) > 0
+    # (b) own block whole (future keys of the block leak in)
+    whole = _sdpa_rows(q, k, v, _forced_mask(N, Hq, B, rows, heads, fsel, topk, own_whole=True),
+                       scale)[rows, heads]
+    not_last = (rows % B) != B - 1
+    assert np.all(np.abs(whole - ref).max(axis=1)[not_last] > 1e-6)
+    # (c) the own block listed inside forced_sel must not count as history
+    #     (it would then be attended whole): rows of kind 2 carry it first
+    kind2 = ((rows * Hq + heads) % 6 == 2) & not_last
+    assert kind2.any()
+    assert np.all(np.abs(whole - ref).max(axis=1)[kind2] > 1e-6)
+
+
+def test_forced_selection_equal_to_natural_reproduces_it():
+    """Forcing the oracle's own selection gives its own output bit for bit, and
+    forcing the lowest-scoring blocks gives the masked softmax of those."""
+    N, Hq, Hkv, d, B, topk = 72, 2, 2, 8, 8, 3
+    q, k, v = synth.random_qkv(N, Hq, Hkv, d, seed=9)
+    r, h = oracle.all_rows(N, Hq)
+    sel, o, _ = oracle.rows(q, k, v, B, topk, r, h, scale=0.3)
+    _, of, _ = oracle.rows(q, k, v, B, topk, r, h, scale=0.3, forced_sel=sel)
+    assert np.array_equal(o, of)
+    kb = oracle.block_means(k, B)
+    worst = np.full((len(r), topk), -1, np.int32)
+    for i in range(len(r)):
+        c = int(r[i]) // B
+        s = q[r[i], h[i]].astype(np.float64) @ kb[h[i] // (Hq // Hkv), :c].T
+        worst[i, : min(c, topk - 1)] = np.argsort(s, kind="stable")[: topk - 1]
+    sel_w, o_w, _ = oracle.rows(q, k, v, B, topk, r, h, scale=0.3, forced_sel=worst)
+    ref = _sdpa_rows(q, k, v, _forced_mask(N, Hq, B, r, h, worst, topk), 0.3)[r, h]
+    assert np.max(np.abs(o_w - ref)) < 1e-12
+    has_choice = (r // B) > topk - 1
+    assert np.all(np.any(sel_w[has_choice] != sel[has_choice], axis=1))
