@@ -393,7 +393,7 @@ def main():
 
     varlen = None
     if not args.no_varlen and dtype == "bf16":
-        lens = synth.packed_lengths(w.N, 16, w.seed ^ 0x5EC, max(w.B, w.N // 64), w.N * 3 // 16)
+        lens = synth.packed_layer_lengths(w)
         cu = torch.from_numpy(np.concatenate([[0], np.cumsum(lens)]).astype(np.int64))
         cu_dev = cu.to(tq.device)
         del ws  # the packed leg gets its own workspace

@@ -217,6 +217,12 @@ def f32_to_bf16(a: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + lsb) >> 16).astype(np.uint16)
 
 
+def packed_layer_lengths(w: Workload, nseq: int = 16) -> np.ndarray:
+    """The packed batch of a workload's layer: ``nseq`` seeded log-uniform
+    lengths between max(B, N/64) and 3N/16 rows, summing to N."""
+    return packed_lengths(w.N, nseq, w.seed ^ 0x5EC, max(w.B, w.N // 64), w.N * 3 // 16)
+
+
 def packed_lengths(total: int, nseq: int, seed: int, lo: int, hi: int) -> np.ndarray:
     """Seeded sequence lengths for a packed batch: log-uniform in [lo, hi],
     rescaled to sum to ``total`` (the last one absorbs the rounding)."""

@@ -39,13 +39,13 @@ def _swaps_inside_tie_band(got_sel, ref_sel, gap, q, k, B, rows, heads, routing)
     Hq, Hkv = q.shape[1], k.shape[1]
     G = Hq // Hkv
     kbar = oracle.block_means(k, B)
-    qf = q.astype(np.float64) if q.dtype != np.uint16 else _bf16_bits_to_f64(q)
     ok = np.zeros(len(rows), bool)
     for i in range(len(rows)):
         r, h = int(rows[i]), int(heads[i])
         c = r // B
         g = h // G
-        qg = qf[r, g * G:(g + 1) * G].sum(axis=0) if routing == oracle.ROUTING_SHARED else qf[r, h]
+        qr = q[r].astype(np.float64) if q.dtype != np.uint16 else _bf16_bits_to_f64(q[r])
+        qg = qr[g * G:(g + 1) * G].sum(axis=0) if routing == oracle.ROUTING_SHARED else qr[h]
         hg = {int(b) for b in got_sel[i] if 0 <= b < c}
         hr = {int(b) for b in ref_sel[i] if 0 <= b < c}
         if len(hg) != len(hr) or c not in set(int(b) for b in got_sel[i]):

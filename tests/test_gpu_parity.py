@@ -160,6 +160,117 @@ def test_prefill_llama8b_1m_sampled():
     print(f"llama8b_1m: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
 
 
+# ------------------------------------- the benchmarked legs at their shapes ---
+def _seq_samples(L, B, Hq, count, seed):
+    """(rows, heads) inside one sequence of L rows: its first and last row, then
+    rows cycling over its blocks at the block's first row, its last row, then
+    seeded offsets; heads seeded."""
+    rng = np.random.default_rng(seed)
+    n = -(-L // B)
+    rows = [0, L - 1]
+    r = 0
+    while len(rows) < count:
+        c = r % n
+        lo, hi = c * B, min(L, (c + 1) * B) - 1
+        rows.append(lo if r < n else hi if r < 2 * n else int(rng.integers(lo, hi + 1)))
+        r += 1
+    rows = np.array(rows[:count], np.int64)
+    return rows, rng.integers(0, Hq, size=count).astype(np.int32)
+
+
+@pytest.mark.timeout(1200)
+def test_varlen_llama8b_1m_sampled():
+    """The packed-batch leg exactly as benchmarked: 16 seeded sequences of the
+    1M-row layer (B = 4096, k = 12, 32/8 heads); 256 (row, head) pairs per
+    sequence, its first and last row among them, against the oracle run on
+    that sequence alone."""
+    w, q, k, v, tq, tk, tv = inputs("llama8b_1m")
+    lens = synth.packed_layer_lengths(w)
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    o = moba.prefill_varlen(tq, tk, tv, cu, w.B, w.k, w.scale)
+    sel = moba.select_varlen(tq, tk, cu, w.B, w.k)
+    torch.cuda.synchronize()
+    base = _seq_base(cu, w.B)
+    worst, tied_all = 0.0, 0
+    for i in range(len(lens)):
+        a, b = int(cu[i]), int(cu[i + 1])
+        rows, heads = _seq_samples(b - a, w.B, w.Hq, 256, seed=1000 + i)
+        gi = torch.from_numpy(rows + a)
+        hi = torch.from_numpy(heads.astype(np.int64))
+        s_loc = sel[gi, hi].cpu().numpy().astype(np.int64)
+        s_loc = np.where(s_loc >= 0, s_loc - base[i], -1).astype(np.int32)
+        got_o = o[gi, hi].float().cpu().numpy().astype(np.float64)
+        (mx, mean), tied = compare_rows(q[a:b], k[a:b], v[a:b], w.B, w.k, w.scale, rows, heads,
+                                        s_loc, got_o, "bf16", f"packed seq {i} ({b - a} rows)")
+        worst, tied_all = max(worst, mx), tied_all + tied
+    print(f"llama8b_1m packed: max|dO| {worst:.2e} tie-excused rows {tied_all}")
+
+
+@pytest.mark.timeout(1200)
+def test_shared_routing_llama8b_1m_sampled():
+    """The group-shared routing leg as benchmarked (the 1M-row layer, heads of
+    a KV head share the ranking by their summed gate score): O on the 4096
+    seeded (row, head) pairs, the selection on 2^20 more."""
+    w, q, k, v, tq, tk, tv = inputs("llama8b_1m")
+    shared = moba.MOBA_ROUTING_SHARED
+    o = moba.prefill(tq, tk, tv, w.B, w.k, w.scale, routing=shared)
+    sel = moba.select(tq, tk, w.B, w.k, routing=shared)
+    torch.cuda.synchronize()
+    sel_np = sel.cpu().numpy()
+    del sel
+    rows, heads = synth.sample_rows(w, 4096)
+    got_o = o[torch.from_numpy(rows), torch.from_numpy(heads.astype(np.int64))]
+    got_o = got_o.float().cpu().numpy().astype(np.float64)
+    del o
+    kbar = oracle.block_means(k, w.B)
+    (mx, mean), tied = compare_rows(q, k, v, w.B, w.k, w.scale, rows, heads, sel_np[rows, heads],
+                                    got_o, "bf16", "llama8b_1m shared",
+                                    routing=oracle.ROUTING_SHARED)
+    r2, h2 = synth.sample_rows(w.with_(seed=w.seed ^ 0x5A5A5A), 1 << 20)
+    ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, r2, h2, want_o=False, kbar=kbar,
+                                  routing=oracle.ROUTING_SHARED)
+    check_selection(sel_np[r2, h2], ref_sel, gap, "llama8b_1m shared sel",
+                    ctx=(q, k, w.B, r2, h2, oracle.ROUTING_SHARED))
+    print(f"llama8b_1m shared: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
+
+
+@pytest.mark.timeout(1200)
+def test_chunk_and_decode_llama8b_1m():
+    """The chunk / decode leg as benchmarked, over the 1M-row layer as its KV
+    cache: a decode step (the last row, every head) and a 16,384-row chunk
+    (1024 seeded pairs), recomputing the block means, and the decode step on a
+    decode cache, all against the oracle at those positions."""
+    w, q, k, v, tq, tk, tv = inputs("llama8b_1m")
+    kbar = oracle.block_means(k, w.B)
+    for C in (1, 16384):
+        qc = tq[w.N - C:].contiguous()
+        oc = moba.prefill_chunk(qc, tk, tv, w.B, w.k, w.scale)
+        sc = moba.select_chunk(qc, tk, w.B, w.k)
+        torch.cuda.synchronize()
+        if C == 1:
+            loc = np.zeros(w.Hq, np.int64)
+            heads = np.arange(w.Hq, dtype=np.int32)
+        else:
+            rng = np.random.default_rng(4)
+            loc = np.concatenate([[0, C - 1], rng.integers(0, C, size=1022)]).astype(np.int64)
+            heads = rng.integers(0, w.Hq, size=loc.size).astype(np.int32)
+        li, hi = torch.from_numpy(loc), torch.from_numpy(heads.astype(np.int64))
+        got_o = oc[li, hi].float().cpu().numpy().astype(np.float64)
+        got_s = sc[li, hi].cpu().numpy()
+        compare_rows(q, k, v, w.B, w.k, w.scale, loc + (w.N - C), heads, got_s, got_o, "bf16",
+                     f"llama8b_1m chunk of {C}")
+        if C == 1:
+            o_step = oc
+        del oc, sc
+    cache = moba.DecodeCache(w.N, w.Hq, w.Hkv, w.B, w.k, w.scale, device=tq.device)
+    cache.append(tk, tv, w.N - 1)
+    cache.append(tk, tv, w.N)
+    od = cache.prefill(tq[w.N - 1:].contiguous(), tk, tv)
+    torch.cuda.synchronize()
+    assert torch.equal(od, o_step)
+    del cache
+
+
 # ------------------------------------------------------------- edge cases ---
 EDGE = [
     # N, Hq, Hkv, B, topk, dtype
@@ -537,6 +648,7 @@ BWD = [
     (3072, 4, 1, 512, 3, "bf16", 0),   # G = 4, several query chunks and key tiles per block
     (2300, 4, 2, 200, 5, "bf16", 0),   # key tiles with ragged 32-key groups, partial last block
     (12, 2, 1, 4, 3, "bf16", 0),       # lse from the few-row forward path
+    (12288, 4, 1, 4096, 12, "bf16", 0),  # the 1M-token layer's block shape (B = 4096, k = 12, G = 4)
 ]
 
 
@@ -551,6 +663,7 @@ def _grad_close(got, ref, dtype, what):
     return float(err.max() / scale)
 
 
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("N,Hq,Hkv,B,topk,dtype,routing", BWD)
 def test_backward_matches_oracle(N, Hq, Hkv, B, topk, dtype, routing):
     q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + 5 * topk, dtype=dtype)
