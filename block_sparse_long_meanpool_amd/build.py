@@ -26,9 +26,18 @@ FLAGS = [
 ]
 
 
+# Per-file code generation options. The wide-wave history kernel keeps its
+# score accumulators in arch VGPRs (the softmax reads them directly) instead of
+# the accumulation registers the compiler would otherwise pick for every
+# matrix op once the kernel uses them.
+FILE_FLAGS = {
+    "attn_hist_bf16.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+    cmd = [HIPCC, *FLAGS, *FILE_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"hipcc failed for {src}:\n{r.stderr}")

@@ -202,7 +202,9 @@ hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp
                             const void* K, const void* V, const void* Vt, const BucketBufs& b,
                             void* part_o, float* part_lse, hipStream_t s) {
   if (P.dtype == MOBA_DTYPE_BF16)
-    return launch_attn_hist_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s);
+    return attn_hist_q64_supported(P)
+               ? launch_attn_hist_q64_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s)
+               : launch_attn_hist_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s);
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
   attn_hist_f32<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
       (const float*)Q, (const float*)K, (const float*)V, T.start, b.tile_map, b.tile_off,

@@ -124,6 +124,19 @@ hipError_t launch_cache_means(const Prob& P, const void* K, int64_t c0, int64_t 
 hipError_t launch_kbar_gather(const double* src, int64_t nhc, double* dst, int64_t nh, int Hkv,
                               int d, hipStream_t s);
 
+// bf16 history attention kernels: the 64-query-per-wave engine
+// (attn_hist_bf16.hip) for block sizes that are multiples of 256, the
+// 32-query engine (attn_bf16.hip) otherwise.
+bool attn_hist_q64_supported(const Prob& P);
+hipError_t launch_attn_hist_q64_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                                     const void* Q, const void* K, const void* Vt,
+                                     const BucketBufs& b, void* part_o, float* part_lse,
+                                     hipStream_t s);
+hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
+                                 const void* Q, const void* K, const void* Vt,
+                                 const BucketBufs& b, void* part_o, float* part_lse,
+                                 hipStream_t s);
+
 // History-block attention over the bucketed entries; writes normalised partials
 // part_o [entry][d] and log2-sum-exp part_lse [entry].
 hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp, const void* Q,
