@@ -156,13 +156,17 @@ __device__ inline void qk_plain(const Wave& W, const uint16_t* ks, int sub, int 
 }
 
 // The softmax of one subtile is 16 units (qb, u, e), unit = 8 qb + 4 u + e:
-// two scores -> two weights 2^(s sl2e - m) -> one bf16 pair, added to the
-// row sum as rounded (the same weights multiply V). A unit has five stages,
-// each reading only what an earlier stage wrote:
+// two scores -> two weights 2^(s sl2e - m) -> one bf16 pair for the P.V
+// product, and the fp32 weights added to the row sum (the bf16 rounding of
+// the weights is unbiased, so the normalisation does not need the rounded
+// values; a bf16 dot instruction for the sum would stall the wave's matrix
+// ops). A unit has five stages, each reading only what an earlier stage
+// wrote:
 //   F0: t0 = s0 sl2e - m      F1E0: t1 = s1 sl2e - m, e0 = 2^t0
-//   E1: e1 = 2^t1             C: pair = bf16(e0, e1)      D: lsum += pair . 1
+//   E1: e1 = 2^t1             C: pair = bf16(e0, e1), e01 = e0 + e1
+//   D: lsum += e01
 struct Unit {
-  float t0, t1, e0, e1;
+  float t0, t1, e0, e1, e01;
 };
 // Pins a value to this point of the instruction stream: an empty statement
 // that the compiler must treat as reading and rewriting the register, so the
@@ -192,18 +196,18 @@ __device__ inline void st_e1(Unit& x) {
   x.e1 = __builtin_amdgcn_exp2f(x.t1);
   pin(x.e1);
 }
-__device__ inline void st_c(const Unit& x, int u, bf16x2 (&pr)[2][2][4]) {
+__device__ inline void st_c(Unit& x, int u, bf16x2 (&pr)[2][2][4]) {
   f32x2 f;
   f[0] = x.e0;
   f[1] = x.e1;
   bf16x2 p = __builtin_convertvector(f, bf16x2);
   pin(p);
   pr[u >> 3][(u >> 2) & 1][u & 3] = p;
+  x.e01 = x.e0 + x.e1;
+  pin(x.e01);
 }
-__device__ inline void st_d(int u, const bf16x2 (&pr)[2][2][4], float (&lsum)[2]) {
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
-  lsum[u >> 3] =
-      __builtin_amdgcn_fdot2_f32_bf16(pr[u >> 3][(u >> 2) & 1][u & 3], ones, lsum[u >> 3], false);
+__device__ inline void st_d(const Unit& x, int u, float (&lsum)[2]) {
+  lsum[u >> 3] += x.e01;
   pin(lsum[u >> 3]);
 }
 __device__ inline bf16x8 gather_p(const bf16x2 (&pr)[4]) {
@@ -224,7 +228,7 @@ __device__ inline void softmax_plain(Wave& W, const f32x16 (&s)[2], float sl2e,
     st_f1e0(s, W, u, sl2e, x);
     st_e1(x);
     st_c(x, u, pr);
-    st_d(u, pr, lsum);
+    st_d(x, u, lsum);
   }
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
@@ -300,15 +304,15 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
       if ((slot & 1) == 0) {
         st_f0(sc, W, v, sl2e, x[v]);
         if (v >= 1) st_e1(x[v - 1]);
-        if (v >= 2) st_d(v - 2, pr, lsum);
+        if (v >= 2) st_d(x[v - 2], v - 2, lsum);
       } else {
         st_f1e0(sc, W, v, sl2e, x[v]);
         if (v >= 1) st_c(x[v - 1], v - 1, pr);
         if (slot == 31) {
           st_e1(x[15]);
           st_c(x[15], 15, pr);
-          st_d(14, pr, lsum);
-          st_d(15, pr, lsum);
+          st_d(x[14], 14, lsum);
+          st_d(x[15], 15, lsum);
         }
       }
     }
