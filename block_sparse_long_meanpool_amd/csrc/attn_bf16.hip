@@ -260,7 +260,6 @@ __device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int 
     return;
   }
   bf16x8 p[QB][2];
-  const bf16x2 ones = {(__bf16)1.f, (__bf16)1.f};
 #pragma unroll
   for (int qb = 0; qb < QB; ++qb) {
     const float mneg = -W.m[qb];
@@ -274,8 +273,9 @@ __device__ inline void wave_smpv(Wave& W, f32x16 (&s)[QB], Tile t, int sub, int 
         f[0] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e], sl2e, mneg));
         f[1] = __builtin_amdgcn_exp2f(fmaf(s[qb][8 * u + 2 * e + 1], sl2e, mneg));
         pr[e] = __builtin_convertvector(f, bf16x2);
-        // the row sum adds the same rounded weights that multiply V
-        lsum = __builtin_amdgcn_fdot2_f32_bf16(pr[e], ones, lsum, false);
+        // the row sum adds the fp32 weights (their bf16 rounding is unbiased;
+        // a bf16 dot instruction here would stall the SIMD's matrix ops)
+        lsum += f[0] + f[1];
       }
       const bf16x4 lo = __builtin_shufflevector(pr[0], pr[1], 0, 1, 2, 3);
       const bf16x4 hi = __builtin_shufflevector(pr[2], pr[3], 0, 1, 2, 3);
