@@ -19,10 +19,13 @@
 // output 128 accumulation registers.
 //
 // K and V^T move global -> LDS in 64-key tiles through four buffers
-// (buffer_load ... lds, no register staging): tile t+3 is issued right after
-// the barrier that publishes tile t+1, into the buffer tile t-1 occupied, so
-// two tiles are always in flight. K rows keep their 16-byte chunks
-// XOR-swizzled by row and V^T rows by d, so every operand read is
+// (buffer_load ... lds, no register staging). One barrier per tile, placed
+// inside the tile's second subtile once the wave has read the tile's last
+// V^T chunk: after it, the tile's buffer is refilled with the tile four
+// ahead, so two tiles are always in flight, and the barrier sits between
+// matrix ops instead of at a point where the matrix pipe has drained. K rows
+// keep their 16-byte chunks XOR-swizzled by row and V^T rows by d, so every
+// operand read is
 // bank-conflict free. V^T comes from vt_pack: per KV head [d][block-padded
 // keys], keys permuted inside each 32-key group (bits 2 and 3 swapped) so a
 // lane's 8 weights of the P operand meet one 16-byte V^T chunk.
@@ -77,42 +80,56 @@ struct Tile {
   uint16_t* v;  // [kHeadDim][VT_ROW]
 };
 
-// Copies of one tile: keys [key0, key0 + 64) of K (row stride krow elements)
-// and V^T columns [col0, col0 + 64) of every d row (row stride ldv). Each
-// wave copies 4 KB of K (16 rows) and 4 KB of V^T (32 d rows), 1 KB per
-// buffer_load ... lds. The caller waits and synchronises.
-__device__ inline void load_tile(Tile t, const uint16_t* __restrict__ kbase, int64_t krow,
-                                 const uint16_t* __restrict__ vbase, int64_t ldv, int wave,
-                                 int lane) {
-  const __amdgpu_buffer_rsrc_t kr = __builtin_amdgcn_make_buffer_rsrc(
-      (void*)kbase, 0, (int)(((int64_t)(KT - 1) * krow + kHeadDim) * 2), kRawBufferFlags);
-  const __amdgpu_buffer_rsrc_t vr = __builtin_amdgcn_make_buffer_rsrc(
+// The copies of one tile: keys [key0, key0 + 64) of K (row stride krow
+// elements) and V^T columns [col0, col0 + 64) of every d row (row stride
+// ldv). Each wave makes 8 copies of 1 KB (64 lanes x 16 B), copy i < 4: four
+// K rows, copy i >= 4: eight V^T rows; rows keep the LDS swizzle. The buffer
+// resources are rebased per tile on the scalar side, so the per-lane offsets
+// are loop invariant.
+struct TileSrc {
+  __amdgpu_buffer_rsrc_t kr, vr;
+};
+__device__ inline TileSrc tile_src(const uint16_t* __restrict__ kbase, int64_t krow,
+                                   const uint16_t* __restrict__ vbase, int64_t ldv) {
+  TileSrc t;
+  t.kr = __builtin_amdgcn_make_buffer_rsrc((void*)kbase, 0,
+                                           (int)(((int64_t)(KT - 1) * krow + kHeadDim) * 2),
+                                           kRawBufferFlags);
+  t.vr = __builtin_amdgcn_make_buffer_rsrc(
       (void*)vbase, 0, (int)(uint32_t)(((int64_t)(kHeadDim - 1) * ldv + KT) * 2), kRawBufferFlags);
-#pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
+  return t;
+}
+__device__ inline void copy_part(Tile dst, const TileSrc& src, int64_t krow, int64_t ldv, int i,
+                                 int wave, int lane) {
+  if (i < kCopies) {
     const int ii = wave * kCopies + i;  // 4 K rows per copy
     const int r = 4 * ii + (lane >> 4);
     const int c = k_swz(r, lane & 15);  // the swizzle is an involution in c
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(kr, t.k + 4 * ii * KS_ROW, 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.kr, dst.k + 4 * ii * KS_ROW, 16,
                                              (unsigned)((r * krow + 8 * c) * 2), 0, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < kCopies; ++i) {
-    const int ii = wave * kCopies + i;  // 8 V^T rows per copy
+  } else {
+    const int ii = wave * kCopies + (i - kCopies);  // 8 V^T rows per copy
     const int d = 8 * ii + (lane >> 3);
     const int c = vt_swz(d, lane & 7);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(vr, t.v + 8 * ii * VT_ROW, 16,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(src.vr, dst.v + 8 * ii * VT_ROW, 16,
                                              (unsigned)((d * ldv + 8 * c) * 2), 0, 0, 0);
   }
 }
+__device__ inline void load_tile(Tile dst, const TileSrc& src, int64_t krow, int64_t ldv,
+                                 int wave, int lane) {
+#pragma unroll
+  for (int i = 0; i < 2 * kCopies; ++i) copy_part(dst, src, krow, ldv, i, wave, lane);
+}
 
-// Wait until at most `left` of this wave's tile copies are outstanding, then
-// a workgroup barrier: every wave's copies of the older tiles have landed.
+// Wait until at most `left` of this wave's tile copies are outstanding and
+// its LDS reads have completed, then a workgroup barrier: every wave's copies
+// of the older tiles have landed and no wave still reads a buffer that is
+// about to be refilled.
 template <int left>
 __device__ inline void wait_tiles() {
   static_assert(left == 0 || left == kCopies * 2 || left == kCopies * 4, "");
-  // s_waitcnt: vmcnt = left (bits 3:0 and 15:14), expcnt and lgkmcnt not waited on
-  constexpr int imm = (left & 15) | ((left >> 4) << 14) | (7 << 4) | (15 << 8);
+  // s_waitcnt: vmcnt = left (bits 3:0 and 15:14), expcnt not waited on, lgkmcnt 0
+  constexpr int imm = (left & 15) | ((left >> 4) << 14) | (7 << 4) | (0 << 8);
   __builtin_amdgcn_s_waitcnt(imm);
   __builtin_amdgcn_s_barrier();
 }
@@ -272,11 +289,21 @@ constexpr Slot kSlots[32] = {
     {12, -1, -1, -1}, {13, -1, -1, -1}, {14, -1, -1, -1}, {15, -1, -1, -1},
 };
 
-template <bool QK, bool SM, bool PREF>
+// Tile hand-over at slot 26 of a tile's second iteration (SYNC): by then
+// this wave has read the tile's last V^T chunk, so after a barrier (with the
+// wave's own copies of the tile two ahead landed first) the tile's buffer
+// takes the tile four ahead, whose eight copies are issued over slots 26-31.
+//   SYNC 0: none; 1: wait (one tile's copies may stay in flight), barrier,
+//   copies; 2: wait the same, barrier; 3: wait for all copies, barrier.
+constexpr int8_t kCopySlot[8] = {26, 26, 27, 28, 28, 29, 30, 31};
+
+template <bool QK, bool SM, bool PREF, int SYNC = 0>
 __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16_t* vp, int sp,
                                const uint16_t* vn, int sv, f32x16 (&sn)[2],
                                const f32x16 (&sc)[2], const bf16x8 (&pc)[2][2],
-                               bf16x8 (&pn)[2][2], bf16x8 (&vpre)[3], float sl2e, int lane) {
+                               bf16x8 (&pn)[2][2], bf16x8 (&vpre)[3], float sl2e, int lane,
+                               Tile fresh = Tile{}, const TileSrc* fsrc = nullptr,
+                               int64_t krow = 0, int64_t ldv = 0, int wave = 0) {
   const f32x16 zero = {};
   bf16x8 av[8], ak[8];
   av[0] = vpre[0];
@@ -288,6 +315,15 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
 #pragma unroll
   for (int slot = 0; slot < 32; ++slot) {
     const Slot S = kSlots[slot];
+    if (SYNC && slot == 26) {
+      if (SYNC <= 2) wait_tiles<kCopies * 2>();
+      if (SYNC == 3) wait_tiles<0>();
+    }
+    if (SYNC == 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i)
+        if (kCopySlot[i] == slot) copy_part(fresh, *fsrc, krow, ldv, i, wave, lane);
+    }
     if (QK && S.rk >= 0) ak[S.rk] = read_k(kq, sq, S.rk, lane);
     if (S.rv >= 0) av[S.rv] = read_v(vp, sp, S.rv, lane);
     if (PREF && slot >= 26 && (slot & 1) == 0)
@@ -330,7 +366,8 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
 
 // The whole block for one workgroup: keys [key0, key0 + B) of K and the
 // matching V^T columns, B a multiple of 256, weights against W.m (set from
-// the first subtile when set_m).
+// the first subtile when set_m). Tile t sits in buffer t % 4; tiles 0-3 are
+// copied up front, tile t+4 right after the hand-over barrier in step t.
 __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, int64_t krow,
                                  const uint16_t* __restrict__ vbase, int64_t ldv, int B,
                                  float sl2e, bool set_m, int wave, int lane, uint16_t* k0,
@@ -338,15 +375,17 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
                                  uint16_t* v1, uint16_t* v2, uint16_t* v3) {
   const Tile T0{k0, v0}, T1{k1, v1}, T2{k2, v2}, T3{k3, v3};
   const int nt = B / KT;  // a multiple of 4
-  auto issue = [&](int t, Tile dst) {
-    load_tile(dst, kbase + (int64_t)t * KT * krow, krow, vbase + (int64_t)t * KT, ldv, wave, lane);
+  auto src_of = [&](int t) {
+    return tile_src(kbase + (int64_t)t * KT * krow, krow, vbase + (int64_t)t * KT, ldv);
   };
   f32x16 sa[2], sb[2];
   bf16x8 pa[2][2], pb[2][2], vpre[3];
-  issue(0, T0);
-  issue(1, T1);
-  issue(2, T2);
-  wait_tiles<kCopies * 4>();
+  {
+    const Tile T[4] = {T0, T1, T2, T3};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) load_tile(T[t], src_of(t), krow, ldv, wave, lane);
+  }
+  wait_tiles<kCopies * 4>();  // tiles 0 and 1
   qk_plain(W, T0.k, 0, lane, sa);
   qk_plain(W, T0.k, 1, lane, sb);
   if (set_m) {
@@ -361,19 +400,19 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
   softmax_plain(W, sa, sl2e, pa);
 #pragma unroll
   for (int i = 0; i < 3; ++i) vpre[i] = read_v(T0.v, 0, i, lane);
-  // Tile t: the output updates of subtiles 2t and 2t+1 (tile t), the scores
-  // of tile t+1, the weights of subtiles 2t+1 and 2t+2. Position tag: 0
-  // while tile t+3 exists (wait for tile t+1 with t+2 in flight, copy t+3),
-  // 1 for t = nt-3 (wait with t+2 in flight), 2 for t = nt-2 (wait for
-  // everything), 3 for the final tile (no wait, no scores of a next tile).
-  auto step = [&](int t, Tile cur, Tile nxt, Tile fresh, auto tag) {
-    constexpr int LAST = decltype(tag)::value;
-    if (LAST <= 1) wait_tiles<kCopies * 2>();
-    if (LAST == 2) wait_tiles<0>();
-    if (LAST == 0) issue(t + 3, fresh);
-    if (LAST < 3) {
+  // Step t: the output updates of subtiles 2t and 2t+1 (tile t), the scores
+  // of tile t+1, the weights of subtiles 2t+1 and 2t+2. Tag: 0 while tile
+  // t+4 exists (hand-over with its copies), 1 for t = nt-4 and 2 for t =
+  // nt-3 (hand-over publishing tile t+2, nothing new to copy), 3 for t =
+  // nt-2 (no hand-over), 4 for the final tile (no scores of a next tile).
+  auto step = [&](int t, Tile cur, Tile nxt, auto tag) {
+    constexpr int TAG = decltype(tag)::value;
+    if (TAG <= 3) {
       iterate<true, true, true>(W, nxt.k, 0, cur.v, 0, cur.v, 1, sa, sb, pa, pb, vpre, sl2e, lane);
-      iterate<true, true, true>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e, lane);
+      constexpr int SYNC = TAG == 0 ? 1 : TAG == 1 ? 2 : TAG == 2 ? 3 : 0;
+      const TileSrc fs = src_of(TAG == 0 ? t + 4 : 0);
+      iterate<true, true, true, SYNC>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e,
+                                      lane, cur, &fs, krow, ldv, wave);
     } else {
       iterate<false, true, true>(W, nxt.k, 0, cur.v, 0, cur.v, 1, sa, sb, pa, pb, vpre, sl2e, lane);
       iterate<false, false, false>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e,
@@ -383,16 +422,16 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
   using L0 = std::integral_constant<int, 0>;
   int t = 0;
   for (; t + 4 < nt; t += 4) {
-    step(t, T0, T1, T3, L0{});
-    step(t + 1, T1, T2, T0, L0{});
-    step(t + 2, T2, T3, T1, L0{});
-    step(t + 3, T3, T0, T2, L0{});
+    step(t, T0, T1, L0{});
+    step(t + 1, T1, T2, L0{});
+    step(t + 2, T2, T3, L0{});
+    step(t + 3, T3, T0, L0{});
   }
   // the last four tiles (t = nt - 4)
-  step(t, T0, T1, T3, L0{});
-  step(t + 1, T1, T2, T0, std::integral_constant<int, 1>{});
-  step(t + 2, T2, T3, T1, std::integral_constant<int, 2>{});
-  step(t + 3, T3, T0, T2, std::integral_constant<int, 3>{});
+  step(t, T0, T1, std::integral_constant<int, 1>{});
+  step(t + 1, T1, T2, std::integral_constant<int, 2>{});
+  step(t + 2, T2, T3, std::integral_constant<int, 3>{});
+  step(t + 3, T3, T0, std::integral_constant<int, 4>{});
   __syncthreads();  // every wave is done with the buffers before they are reused
 }
 
@@ -403,7 +442,8 @@ __device__ inline void block_max(const Wave& W, const uint16_t* __restrict__ kba
                                  int lane, uint16_t* k0, uint16_t* v0, float (&mx)[2]) {
   const Tile T0{k0, v0};
   for (int t = 0; t < B / KT; ++t) {
-    load_tile(T0, kbase + (int64_t)t * KT * krow, krow, vbase + (int64_t)t * KT, ldv, wave, lane);
+    load_tile(T0, tile_src(kbase + (int64_t)t * KT * krow, krow, vbase + (int64_t)t * KT, ldv),
+              krow, ldv, wave, lane);
     wait_tiles<0>();
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
