@@ -33,14 +33,22 @@
 // Softmax: weights are 2^(s - m) with m, per query, the largest score of the
 // first subtile (every query has 32 unmasked keys there). The output
 // accumulators are never rescaled; if some later score exceeds m by enough
-// that a row sum reaches 2^64, the workgroup finds the true maxima with a
-// score-only pass and redoes the block from them (never for ordinary data;
-// the result is the same up to rounding). Each normalised partial is stored
-// in fp16 with its log2-sum-exp in fp32, at the entry's slot.
+// that a row sum reaches 2^64, the tile is listed and a second kernel
+// recomputes it from the true maxima found by a score-only pass (never for
+// ordinary data; the result is the same up to rounding). Each normalised
+// partial is stored in fp16 with its log2-sum-exp in fp32, at the entry's
+// slot.
+//
+// Workgroups are persistent (one per compute unit) and walk their XCD's
+// history tiles; the K/V tile stream and the Q rows of the next history tile
+// are fetched during the current tile's last steps, so the pipeline does not
+// drain between tiles.
 //
 // Used when the block size is a multiple of 256 (whole groups of four tiles:
 // every tile full, static buffer roles in an unrolled loop); other block
 // sizes take the 32-query engine of attn_bf16.hip.
+#include <algorithm>
+
 #include "moba_internal.hpp"
 
 namespace moba {
@@ -127,7 +135,7 @@ __device__ inline void load_tile(Tile dst, const TileSrc& src, int64_t krow, int
 // about to be refilled.
 template <int left>
 __device__ inline void wait_tiles() {
-  static_assert(left == 0 || left == kCopies * 2 || left == kCopies * 4, "");
+  static_assert(left == 0 || left == kCopies * 2 || left == kCopies * 4 || left == 63, "");
   // s_waitcnt: vmcnt = left (bits 3:0 and 15:14), expcnt not waited on, lgkmcnt 0
   constexpr int imm = (left & 15) | ((left >> 4) << 14) | (7 << 4) | (0 << 8);
   __builtin_amdgcn_s_waitcnt(imm);
@@ -289,15 +297,14 @@ constexpr Slot kSlots[32] = {
     {12, -1, -1, -1}, {13, -1, -1, -1}, {14, -1, -1, -1}, {15, -1, -1, -1},
 };
 
-// Tile hand-over at slot 26 of a tile's second iteration (SYNC): by then
-// this wave has read the tile's last V^T chunk, so after a barrier (with the
-// wave's own copies of the tile two ahead landed first) the tile's buffer
-// takes the tile four ahead, whose eight copies are issued over slots 26-31.
-//   SYNC 0: none; 1: wait (one tile's copies may stay in flight), barrier,
-//   copies; 2: wait the same, barrier; 3: wait for all copies, barrier.
+// Tile hand-over at slot 26 of a tile's second iteration: by then this wave
+// has read the tile's last V^T chunk, so after a barrier (with this wave's
+// copies older than the last WAITK landed first; WAITK 63: no wait on
+// copies) the tile's buffer may take another tile (COPY), whose eight copies
+// are issued over slots 26-31. WAITK < 0: no hand-over.
 constexpr int8_t kCopySlot[8] = {26, 26, 27, 28, 28, 29, 30, 31};
 
-template <bool QK, bool SM, bool PREF, int SYNC = 0>
+template <bool QK, bool SM, bool PREF, int WAITK = -1, bool COPY = false>
 __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16_t* vp, int sp,
                                const uint16_t* vn, int sv, f32x16 (&sn)[2],
                                const f32x16 (&sc)[2], const bf16x8 (&pc)[2][2],
@@ -315,11 +322,8 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
 #pragma unroll
   for (int slot = 0; slot < 32; ++slot) {
     const Slot S = kSlots[slot];
-    if (SYNC && slot == 26) {
-      if (SYNC <= 2) wait_tiles<kCopies * 2>();
-      if (SYNC == 3) wait_tiles<0>();
-    }
-    if (SYNC == 1) {
+    if (WAITK >= 0 && slot == 26) wait_tiles<(WAITK >= 0 ? WAITK : 0)>();
+    if (COPY) {
 #pragma unroll
       for (int i = 0; i < 8; ++i)
         if (kCopySlot[i] == slot) copy_part(fresh, *fsrc, krow, ldv, i, wave, lane);
@@ -364,28 +368,65 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
   }
 }
 
+// The wave's Q rows (B operand of the scores): lane l holds the row of
+// entry ev[qb] (query l % 32 of block qb; row = entry / KH), chunks
+// 16 kk + 8 h; rows of invalid entries are zero.
+__device__ inline void load_q(Wave& W, const uint16_t* __restrict__ Q, const uint32_t* ev,
+                              const bool* valid, int KH, int lane) {
+  const int h = lane >> 5;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) {
+    const uint16_t* qrow = Q + (int64_t)(ev[qb] / (uint32_t)KH) * kHeadDim;
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 u = valid[qb] ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
+                                : make_uint4(0, 0, 0, 0);
+      W.q[qb][kk] = as_bf16x8(u);
+    }
+  }
+}
+
 // The whole block for one workgroup: keys [key0, key0 + B) of K and the
 // matching V^T columns, B a multiple of 256, weights against W.m (set from
-// the first subtile when set_m). Tile t sits in buffer t % 4; tiles 0-3 are
-// copied up front, tile t+4 right after the hand-over barrier in step t.
+// the first subtile when set_m). Tile t sits in buffer t % 4; tile t+4 is
+// copied right after the hand-over barrier in step t.
+//   STREAM = false: tiles 0-3 are copied here first.
+//   STREAM = true (persistent workgroups): on entry tiles 0-2 of this block
+//     and the wave's Q rows have been requested by the caller (or by the
+//     previous block's pass); tile 3 is copied here once every wave is past
+//     the previous block. The last steps hand the freed buffers 0-2 to tiles
+//     0-2 of the next block (nkbase, nvbase) and, once no score remains to
+//     be made, request the next block's Q rows (entries nev, nvalid) into W.q.
+template <bool STREAM>
 __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, int64_t krow,
                                  const uint16_t* __restrict__ vbase, int64_t ldv, int B,
                                  float sl2e, bool set_m, int wave, int lane, uint16_t* k0,
                                  uint16_t* k1, uint16_t* k2, uint16_t* k3, uint16_t* v0,
-                                 uint16_t* v1, uint16_t* v2, uint16_t* v3) {
+                                 uint16_t* v1, uint16_t* v2, uint16_t* v3,
+                                 const uint16_t* __restrict__ nkbase = nullptr,
+                                 const uint16_t* __restrict__ nvbase = nullptr,
+                                 const uint16_t* __restrict__ Q = nullptr,
+                                 const uint32_t* nev = nullptr, const bool* nvalid = nullptr,
+                                 int KH = 1) {
   const Tile T0{k0, v0}, T1{k1, v1}, T2{k2, v2}, T3{k3, v3};
   const int nt = B / KT;  // a multiple of 4
   auto src_of = [&](int t) {
     return tile_src(kbase + (int64_t)t * KT * krow, krow, vbase + (int64_t)t * KT, ldv);
   };
+  auto nsrc_of = [&](int t) {
+    return tile_src(nkbase + (int64_t)t * KT * krow, krow, nvbase + (int64_t)t * KT, ldv);
+  };
   f32x16 sa[2], sb[2];
   bf16x8 pa[2][2], pb[2][2], vpre[3];
-  {
+  if (STREAM) {
+    wait_tiles<0>();  // tiles 0-2 and the Q rows; every wave is past the previous block
+    load_tile(T3, src_of(3), krow, ldv, wave, lane);
+  } else {
     const Tile T[4] = {T0, T1, T2, T3};
 #pragma unroll
     for (int t = 0; t < 4; ++t) load_tile(T[t], src_of(t), krow, ldv, wave, lane);
+    wait_tiles<kCopies * 4>();  // tiles 0 and 1
   }
-  wait_tiles<kCopies * 4>();  // tiles 0 and 1
   qk_plain(W, T0.k, 0, lane, sa);
   qk_plain(W, T0.k, 1, lane, sb);
   if (set_m) {
@@ -402,18 +443,23 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
   for (int i = 0; i < 3; ++i) vpre[i] = read_v(T0.v, 0, i, lane);
   // Step t: the output updates of subtiles 2t and 2t+1 (tile t), the scores
   // of tile t+1, the weights of subtiles 2t+1 and 2t+2. Tag: 0 while tile
-  // t+4 exists (hand-over with its copies), 1 for t = nt-4 and 2 for t =
-  // nt-3 (hand-over publishing tile t+2, nothing new to copy), 3 for t =
-  // nt-2 (no hand-over), 4 for the final tile (no scores of a next tile).
+  // t+4 exists (hand-over with its copies); 1 for t = nt-4 and 2 for t =
+  // nt-3 (hand-over publishing tile t+2; STREAM: copies of the next block's
+  // tile 0, 1); 3 for t = nt-2 (STREAM: hand-over with the copies of the
+  // next block's tile 2); 4 for the final tile (no scores of a next tile;
+  // STREAM: the next block's Q rows are requested first).
   auto step = [&](int t, Tile cur, Tile nxt, auto tag) {
     constexpr int TAG = decltype(tag)::value;
     if (TAG <= 3) {
       iterate<true, true, true>(W, nxt.k, 0, cur.v, 0, cur.v, 1, sa, sb, pa, pb, vpre, sl2e, lane);
-      constexpr int SYNC = TAG == 0 ? 1 : TAG == 1 ? 2 : TAG == 2 ? 3 : 0;
-      const TileSrc fs = src_of(TAG == 0 ? t + 4 : 0);
-      iterate<true, true, true, SYNC>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e,
-                                      lane, cur, &fs, krow, ldv, wave);
+      constexpr int WAITK = TAG <= 1 ? kCopies * 2 : TAG == 2 ? (STREAM ? kCopies * 2 : 0)
+                                                              : (STREAM ? 63 : -1);
+      constexpr bool COPY = TAG == 0 || STREAM;
+      const TileSrc fs = TAG == 0 ? src_of(t + 4) : STREAM ? nsrc_of(TAG - 1) : src_of(0);
+      iterate<true, true, true, WAITK, COPY>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa,
+                                             vpre, sl2e, lane, cur, &fs, krow, ldv, wave);
     } else {
+      if (STREAM) load_q(W, Q, nev, nvalid, KH, lane);
       iterate<false, true, true>(W, nxt.k, 0, cur.v, 0, cur.v, 1, sa, sb, pa, pb, vpre, sl2e, lane);
       iterate<false, false, false>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e,
                                    lane);
@@ -432,7 +478,7 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
   step(t + 1, T1, T2, std::integral_constant<int, 2>{});
   step(t + 2, T2, T3, std::integral_constant<int, 3>{});
   step(t + 3, T3, T0, std::integral_constant<int, 4>{});
-  __syncthreads();  // every wave is done with the buffers before they are reused
+  if (!STREAM) __syncthreads();  // every wave is done with the buffers before they are reused
 }
 
 // Score-only pass for the rare re-run: the largest score of each query over
@@ -461,82 +507,61 @@ __device__ inline void block_max(const Wave& W, const uint16_t* __restrict__ kba
 }  // namespace
 
 // ----------------------------------------------------------------------------
-// History attention: one workgroup = up to 256 routed entries of one bin.
+// History attention. A history tile is up to 256 routed entries of one bin
+// (KV head g, history block j): the entries [e_begin, e_end) of the bin's
+// list, attended over the whole block.
 // ----------------------------------------------------------------------------
-__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
-                          amdgpu_waves_per_eu(1, 1))) void
-attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
-                   const uint16_t* __restrict__ Vt, const int32_t* __restrict__ bstart,
-                   const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
-                   const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
-                   const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
-                   float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad, int64_t ldv,
-                   int KH, int64_t nh, float sl2e) {
-  __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS], lds_k2[KS_ELEMS],
-      lds_k3[KS_ELEMS];
-  __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS], lds_v2[VT_ELEMS],
-      lds_v3[VT_ELEMS];
-  // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
-  // contiguous range of tiles so the tiles of one K/V block share its L2.
-  // The grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
-  const int64_t per = gridDim.x / 8;
-  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (w >= scalars[1]) return;
-  const int tid = threadIdx.x, lane = tid & 63, h = lane >> 5;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+struct HistTile {
+  int64_t e_begin, e_end;
+  const uint16_t* kbase;  // K rows of block j, KV head g
+  const uint16_t* vbase;  // V^T columns of block j, KV head g
+};
+
+__device__ inline HistTile hist_tile(int64_t w, const uint16_t* __restrict__ K,
+                                     const uint16_t* __restrict__ Vt,
+                                     const int32_t* __restrict__ bstart,
+                                     const int32_t* __restrict__ tile_map,
+                                     const int32_t* __restrict__ tile_off,
+                                     const int32_t* __restrict__ bin_off, int Hkv, int64_t Bpad,
+                                     int64_t ldv, int64_t nh) {
+  HistTile t;
   const int bin = tile_map[w];
-  const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
-  const int64_t e_end = bin_off[bin + 1];
+  t.e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
+  t.e_end = bin_off[bin + 1];
   const int g = (int)(bin / nh);
   const int64_t j = bin % nh;
+  t.kbase = K + (bstart[j] * (int64_t)Hkv + g) * kHeadDim;  // history blocks are full
+  t.vbase = Vt + (int64_t)g * kHeadDim * ldv + j * Bpad;
+  return t;
+}
 
-  uint32_t ev[2];
-  bool valid[2];
-  Wave W;
+// The two entries of this lane (query l % 32 of each 32-query block of its
+// wave) and whether they exist.
+__device__ inline void tile_entries(const HistTile& t, const uint32_t* __restrict__ entries,
+                                    int wave, int lane, uint32_t (&ev)[2], bool (&valid)[2]) {
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const int64_t e = e_begin + wave * kWaveQ + qb * 32 + (lane & 31);
-    valid[qb] = e < e_end;
+    const int64_t e = t.e_begin + wave * kWaveQ + qb * 32 + (lane & 31);
+    valid[qb] = e < t.e_end;
     ev[qb] = valid[qb] ? entries[e] : 0u;
-    const uint16_t* qrow = Q + (int64_t)(ev[qb] / (uint32_t)KH) * kHeadDim;
-#pragma unroll
-    for (int kk = 0; kk < 8; ++kk) {
-      const uint4 u = valid[qb] ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
-                                : make_uint4(0, 0, 0, 0);
-      W.q[qb][kk] = as_bf16x8(u);
-    }
   }
-  const uint16_t* kbase = K + (bstart[j] * (int64_t)Hkv + g) * kHeadDim;  // history blocks are full
-  const int64_t krow = (int64_t)Hkv * kHeadDim;
-  const uint16_t* vbase = Vt + (int64_t)g * kHeadDim * ldv + j * Bpad;
-  auto reset = [&]() {
+}
+
+__device__ inline void reset_acc(Wave& W) {
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb)
+  for (int qb = 0; qb < 2; ++qb)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) W.o[qb][db][r] = 0.f;
-    W.l[0] = W.l[1] = 0.f;
-  };
-  // First pass with reference maxima from the first subtile; if some weight
-  // could have overflowed (workgroup-uniform decision), find the true maxima
-  // with a score-only pass and redo the block from them (weights <= 1). One
-  // copy of the pipelined engine serves both passes.
-  bool set_m = true;
-  for (;;) {
-    reset();
-    run_block(W, kbase, krow, vbase, ldv, B, sl2e, set_m, wave, lane, lds_k0, lds_k1, lds_k2,
-              lds_k3, lds_v0, lds_v1, lds_v2, lds_v3);
-    bool redo = false;
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) redo |= valid[qb] && !(W.l[qb] < kLMax);
-    if (!__syncthreads_or(redo) || !set_m) break;
-    float mx[2] = {-INFINITY, -INFINITY};
-    block_max(W, kbase, krow, vbase, ldv, B, wave, lane, lds_k0, lds_v0, mx);
-#pragma unroll
-    for (int qb = 0; qb < 2; ++qb) W.m[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32)) * sl2e;
-    set_m = false;
-  }
+      for (int r = 0; r < 16; ++r) W.o[qb][db][r] = 0.f;
+  W.l[0] = W.l[1] = 0.f;
+}
+
+// Normalised partial outputs (fp16) and log2-sum-exps of the valid entries.
+__device__ inline void store_partials(const Wave& W, const uint32_t (&ev)[2],
+                                      const bool (&valid)[2], _Float16* __restrict__ part_o,
+                                      float* __restrict__ part_lse, int lane) {
+  const int h = lane >> 5;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
     const float l = W.l[qb] + __shfl_xor(W.l[qb], 32);
@@ -556,6 +581,130 @@ attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   }
 }
 
+// True when some valid query's row sum reached 2^64 (or is not finite): its
+// weights, taken against the first subtile's maximum, may have overflowed.
+__device__ inline bool wave_overflow(const Wave& W, const bool (&valid)[2]) {
+  bool r = false;
+#pragma unroll
+  for (int qb = 0; qb < 2; ++qb) r |= valid[qb] && !(W.l[qb] < kLMax);
+  return r;
+}
+
+// Persistent workgroups, one per compute unit: workgroup i runs on XCD i % 8
+// and each XCD walks a contiguous range of history tiles, its 32 workgroups
+// taking every 32nd tile, so the tiles in flight on an XCD share the K/V
+// blocks in its L2. While a tile's last steps run, the next tile's first
+// three K/V tiles and its Q rows are already being fetched. A tile whose
+// weights could have overflowed is appended to redo_list (counter
+// scalars[2]) and recomputed by attn_hist_q64_redo_bf16.
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void
+attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                   const uint16_t* __restrict__ Vt, const int32_t* __restrict__ bstart,
+                   const int32_t* __restrict__ tile_map, const int32_t* __restrict__ tile_off,
+                   const int32_t* __restrict__ bin_off, int32_t* __restrict__ scalars,
+                   const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
+                   float* __restrict__ part_lse, int32_t* __restrict__ redo_list, int Hkv, int B,
+                   int64_t Bpad, int64_t ldv, int KH, int64_t nh, float sl2e) {
+  __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS], lds_k2[KS_ELEMS],
+      lds_k3[KS_ELEMS];
+  __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS], lds_v2[VT_ELEMS],
+      lds_v3[VT_ELEMS];
+  const int64_t total = scalars[1];
+  const int64_t nloc = gridDim.x / 8;  // workgroups per XCD (the grid is a multiple of 8)
+  const int64_t per = (total + 7) / 8;
+  const int64_t lo = (blockIdx.x % 8) * per;
+  const int64_t hi = lo + per < total ? lo + per : total;
+  int64_t w = lo + blockIdx.x / 8;
+  if (w >= hi) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t krow = (int64_t)Hkv * kHeadDim;
+  auto tile_of = [&](int64_t x) {
+    return hist_tile(x, K, Vt, bstart, tile_map, tile_off, bin_off, Hkv, Bpad, ldv, nh);
+  };
+  HistTile cur = tile_of(w);
+  uint32_t ev[2];
+  bool valid[2];
+  tile_entries(cur, entries, wave, lane, ev, valid);
+  Wave W;
+  load_q(W, Q, ev, valid, KH, lane);
+  load_tile(Tile{lds_k0, lds_v0}, tile_src(cur.kbase, krow, cur.vbase, ldv), krow, ldv, wave, lane);
+  load_tile(Tile{lds_k1, lds_v1},
+            tile_src(cur.kbase + KT * krow, krow, cur.vbase + KT, ldv), krow, ldv, wave, lane);
+  load_tile(Tile{lds_k2, lds_v2},
+            tile_src(cur.kbase + 2 * KT * krow, krow, cur.vbase + 2 * KT, ldv), krow, ldv, wave,
+            lane);
+  for (;;) {
+    const int64_t wn = w + nloc;
+    const bool has_next = wn < hi;
+    // without a next tile the last steps re-request this tile's first K/V
+    // tiles and Q rows (unused), which keeps them free of branches
+    const HistTile nxt = has_next ? tile_of(wn) : cur;
+    uint32_t evn[2];
+    bool validn[2];
+    tile_entries(nxt, entries, wave, lane, evn, validn);
+    reset_acc(W);
+    run_block<true>(W, cur.kbase, krow, cur.vbase, ldv, B, sl2e, true, wave, lane, lds_k0, lds_k1,
+                    lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3, nxt.kbase, nxt.vbase, Q, evn,
+                    validn, KH);
+    // workgroup-uniform, so each tile is listed at most once
+    if (__syncthreads_or(wave_overflow(W, valid)) && tid == 0)
+      redo_list[atomicAdd(&scalars[2], 1)] = (int32_t)w;
+    store_partials(W, ev, valid, part_o, part_lse, lane);
+    if (!has_next) break;
+    w = wn;
+    cur = nxt;
+    ev[0] = evn[0];
+    ev[1] = evn[1];
+    valid[0] = validn[0];
+    valid[1] = validn[1];
+  }
+  __builtin_amdgcn_s_waitcnt(0);  // the last re-requested copies land before the LDS is released
+}
+
+// Recomputation of the tiles the persistent kernel listed: a score-only
+// pass finds each query's true maximum and the block is redone from it
+// (weights <= 1). Normally the list is empty and every workgroup returns at
+// once.
+__global__ __attribute__((amdgpu_flat_work_group_size(kThreads, kThreads),
+                          amdgpu_waves_per_eu(1, 1))) void
+attn_hist_q64_redo_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ K,
+                        const uint16_t* __restrict__ Vt, const int32_t* __restrict__ bstart,
+                        const int32_t* __restrict__ tile_map,
+                        const int32_t* __restrict__ tile_off,
+                        const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
+                        const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
+                        float* __restrict__ part_lse, const int32_t* __restrict__ redo_list,
+                        int Hkv, int B, int64_t Bpad, int64_t ldv, int KH, int64_t nh,
+                        float sl2e) {
+  __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS], lds_k2[KS_ELEMS],
+      lds_k3[KS_ELEMS];
+  __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS], lds_v2[VT_ELEMS],
+      lds_v3[VT_ELEMS];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t krow = (int64_t)Hkv * kHeadDim;
+  const int64_t count = scalars[2];
+  for (int64_t i = blockIdx.x; i < count; i += gridDim.x) {
+    const HistTile cur =
+        hist_tile(redo_list[i], K, Vt, bstart, tile_map, tile_off, bin_off, Hkv, Bpad, ldv, nh);
+    uint32_t ev[2];
+    bool valid[2];
+    tile_entries(cur, entries, wave, lane, ev, valid);
+    Wave W;
+    load_q(W, Q, ev, valid, KH, lane);
+    float mx[2] = {-INFINITY, -INFINITY};
+    block_max(W, cur.kbase, krow, cur.vbase, ldv, B, wave, lane, lds_k0, lds_v0, mx);
+#pragma unroll
+    for (int qb = 0; qb < 2; ++qb) W.m[qb] = fmaxf(mx[qb], __shfl_xor(mx[qb], 32)) * sl2e;
+    reset_acc(W);
+    run_block<false>(W, cur.kbase, krow, cur.vbase, ldv, B, sl2e, false, wave, lane, lds_k0,
+                     lds_k1, lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3);
+    store_partials(W, ev, valid, part_o, part_lse, lane);
+  }
+}
+
 bool attn_hist_q64_supported(const Prob& P) { return P.B % 256 == 0; }
 
 hipError_t launch_attn_hist_q64_bf16(const Prob& P, const Blocks& T, const BucketPlan& bp,
@@ -566,11 +715,18 @@ hipError_t launch_attn_hist_q64_bf16(const Prob& P, const Blocks& T, const Bucke
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
   const int64_t ldv = P.vt_blocks * Bpad;
-  const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
+  // one workgroup per compute unit (256 on MI355X), fewer for small problems
+  const int64_t grid = std::min<int64_t>(256, ceil_div(bp.max_tiles, 8) * 8);
   attn_hist_q64_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
-      b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, Bpad,
-      ldv, P.KH, P.nh, sl2e);
+      b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, b.redo, P.Hkv,
+      P.B, Bpad, ldv, P.KH, P.nh, sl2e);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  attn_hist_q64_redo_bf16<<<64, kThreads, 0, s>>>(
+      (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
+      b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, b.redo, P.Hkv,
+      P.B, Bpad, ldv, P.KH, P.nh, sl2e);
   return hipGetLastError();
 }
 

@@ -131,6 +131,8 @@ __global__ __launch_bounds__(1024) void bucket_scan_bins(const int32_t* __restri
     tile_off[nbins] = carry[1];
     scalars[0] = carry[0];
     scalars[1] = carry[1];
+    scalars[2] = 0;  // history tiles listed for recomputation
+    scalars[3] = 0;
   }
 }
 

@@ -146,7 +146,7 @@ size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
 struct Layout {
   size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
   size_t kbar, mp_part, gate, sel, chunk_base, bin_total, bin_off, tile_off, scalars, tile_map, entries,
-      part_lse, part_o, vt, dec_part, delta, dq_acc, part_dq, kt, total;
+      redo, part_lse, part_o, vt, dec_part, delta, dq_acc, part_dq, kt, total;
 };
 
 // Bytes of the packed V^T copy the bf16 kernels read (0 for fp32).
@@ -239,6 +239,7 @@ Layout plan_ws(const Prob& P, bool full, bool cached = false) {
       L.dec_part = take(decode_part_bytes(P));
     } else {
       const size_t slots = (size_t)(P.Nq * P.Hq) * (size_t)P.KH;
+      L.redo = take(sizeof(int32_t) * (size_t)bp.max_tiles);
       L.part_lse = take(sizeof(float) * slots);
       L.part_o = take(part_elem_bytes(P) * slots * P.d);
       L.vt = cached ? off : take(vt_bytes(P));
@@ -324,6 +325,7 @@ BucketBufs bucket_bufs(void* ws, const Layout& L) {
   b.tile_map = at<int32_t>(ws, L.tile_map);
   b.scalars = at<int32_t>(ws, L.scalars);
   b.entries = at<uint32_t>(ws, L.entries);
+  b.redo = L.redo ? at<int32_t>(ws, L.redo) : nullptr;
   return b;
 }
 

@@ -77,8 +77,9 @@ struct BucketBufs {
   int32_t* bin_off;     // [nbins + 1]
   int32_t* tile_off;    // [nbins + 1]
   int32_t* tile_map;    // [max_tiles]
-  int32_t* scalars;     // [4]: total entries, total tiles
+  int32_t* scalars;     // [4]: total entries, total tiles, tiles listed in redo, unused
   uint32_t* entries;    // [max_entries]
+  int32_t* redo;        // [max_tiles] history tiles to recompute (bf16 history attention)
 };
 
 BucketPlan plan_bucket(const Prob& P);
