@@ -44,7 +44,8 @@ EXPORTS = (
     "moba_cache_bytes", "moba_cache_append", "moba_cached_workspace_size", "moba_prefill_cached",
     "moba_prefill_train", "moba_backward_workspace_size", "moba_backward",
     "moba_prefill_train_varlen", "moba_backward_varlen_workspace_size", "moba_backward_varlen",
-    "moba_dense_workspace_size", "moba_dense_causal", "moba_status_string",
+    "moba_dense_workspace_size", "moba_dense_causal", "moba_noalloc_max_workspace",
+    "moba_prefill_noalloc", "moba_status_string",
     "moba_last_error",
     "moba_debug_meanpool", "moba_debug_bucket_capacity", "moba_debug_bucket", "moba_debug_copy",
     "moba_debug_read_peak", "moba_debug_mfma_peak",
@@ -115,6 +116,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_prefill_cached": (ctypes.c_int, [P, i64, i64, vp, vp, vp, vp, vp, vp, sz, vp]),
         "moba_routing_stats_workspace_size": (sz, [P]),
         "moba_routing_stats": (ctypes.c_int, [P, vp, vp, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_noalloc_max_workspace": (sz, []),
+        "moba_prefill_noalloc": (ctypes.c_int, [P, vp, vp, vp, vp, vp]),
         "moba_dense_workspace_size": (sz, [P]),
         "moba_dense_causal": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
         "moba_status_string": (ctypes.c_char_p, [ctypes.c_int]),
@@ -225,6 +228,26 @@ def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, eve
                              out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                              _stream(q.device), ev_arr)
     _ok(st, "moba_prefill")
+    return out
+
+
+def prefill_noalloc(q, k, v, block_size, topk, scale=None, out=None,
+                    routing=MOBA_ROUTING_PER_HEAD):
+    """``prefill`` through the allocation-free entry point: the library's own
+    fixed device scratch (``moba_noalloc_max_workspace()`` bytes per GPU)
+    serves as the workspace, so the call allocates nothing (``out`` may be
+    given to avoid the output allocation too)."""
+    lib = load_library()
+    _check_dev(q, k, v)
+    if v.shape != k.shape or v.dtype != k.dtype:
+        raise ValueError("v must match k in shape and dtype")
+    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    if out is None:
+        out = torch.empty_like(q)
+    _check_dev(out)
+    st = lib.moba_prefill_noalloc(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
+                                  out.data_ptr(), _stream(q.device))
+    _ok(st, "moba_prefill_noalloc")
     return out
 
 

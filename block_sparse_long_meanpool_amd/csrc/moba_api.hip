@@ -2,6 +2,7 @@
 // the launch sequence of the five stages on the caller's stream. The
 // operation and every entry point are specified in include/moba.h.
 #include <climits>
+#include <mutex>
 #include <cmath>
 #include <cstdio>
 #include <cstring>
@@ -497,6 +498,57 @@ int moba_routing_stats(const moba_problem_t* p, const void* q, const void* k, in
                            selw, margin, s);
   if (e == hipSuccess) e = launch_routing_reductions(P, T, selw, counts, union_size, s);
   return e == hipSuccess ? MOBA_OK : hip_fail(e, "routing statistics");
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free prefill: the workspace is a fixed device array of this
+// library (one per GPU, held until the process ends) instead of a caller
+// buffer. Its device address is looked up once per device.
+// ---------------------------------------------------------------------------
+}  // extern "C"
+
+namespace {
+constexpr size_t kScratchBytes = (size_t)512 << 20;  // 512 MiB per device
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[64] = {};  // per device id, from hipGetSymbolAddress
+
+int scratch_for_current_device(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= 64) return fail(MOBA_ERR_UNSUPPORTED, "device id >= 64");
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOBA_OK;
+}
+}  // namespace
+
+extern "C" {
+
+size_t moba_noalloc_max_workspace(void) { return kScratchBytes; }
+
+int moba_prefill_noalloc(const moba_problem_t* p, const void* q, const void* k, const void* v,
+                         void* o, void* stream) {
+  Prob P;
+  int rc = make_prob(p, &P);
+  if (rc) return rc;
+  const void* ptrs[4] = {q, k, v, o};
+  if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
+  const Layout L = plan_ws(P, true);
+  if (L.total > kScratchBytes)
+    return fail(MOBA_ERR_UNSUPPORTED,
+                "problem needs more workspace than the library's 512 MiB allocation-free scratch");
+  void* ws = nullptr;
+  if ((rc = scratch_for_current_device(&ws))) return rc;
+  return run_prefill(P, nullptr, q, k, v, o, ws, L, (hipStream_t)stream, nullptr);
 }
 
 int moba_prefill_train(const moba_problem_t* p, const void* q, const void* k, const void* v,

@@ -308,6 +308,24 @@ MOBA_API size_t moba_dense_workspace_size(const moba_problem_t *p);
 MOBA_API int moba_dense_causal(const moba_problem_t *p, const void *q, const void *k, const void *v,
                                void *o, void *workspace, size_t ws_bytes, void *stream);
 
+/*
+ * Allocation-free prefill, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): moba_prefill with the workspace taken from a fixed device
+ * array of the library (moba_noalloc_max_workspace() bytes, 512 MiB, one
+ * per GPU, held until the process ends) instead of a caller buffer. Nothing
+ * is allocated or freed by the call.
+ *   q, k, v, o: as moba_prefill; stream: the caller's HIP stream.
+ * Returns MOBA_ERR_UNSUPPORTED, before any HIP call, when
+ * moba_workspace_size(p) exceeds the array. All calls on one GPU share its
+ * array: calls that overlap on one GPU (other streams, or another host
+ * thread) race and must be serialised by the caller. The array's contents on
+ * entry are ignored (every kernel writes what it later reads).
+ */
+MOBA_API size_t moba_noalloc_max_workspace(void);
+MOBA_API int moba_prefill_noalloc(const moba_problem_t *p, const void *q, const void *k,
+                                  const void *v, void *o, void *stream);
+
 /* Static text for a status code. */
 MOBA_API const char *moba_status_string(int status);
 

@@ -316,3 +316,17 @@ def test_packed_v_extent_limit():
     small = _prob(N=4096, Hq=1, Hkv=1, block_size=4096, topk=2)
     assert lib.moba_cache_bytes(ctypes.byref(small), 16_777_216) > 0
     assert lib.moba_cache_bytes(ctypes.byref(small), 16_912_384) == 0
+
+
+def test_noalloc_refuses_problems_beyond_its_scratch():
+    """The allocation-free entry point checks the workspace its problem needs
+    against its fixed scratch array before any HIP call."""
+    lib = moba.load_library()
+    assert lib.moba_noalloc_max_workspace() == 512 << 20
+    big = _prob(N=1 << 20, Hq=32, Hkv=8, block_size=4096, topk=12)
+    assert lib.moba_workspace_size(ctypes.byref(big)) > lib.moba_noalloc_max_workspace()
+    assert lib.moba_prefill_noalloc(ctypes.byref(big), FAKE, FAKE, FAKE, FAKE, None) == 2
+    assert b"512 MiB" in lib.moba_last_error()
+    bad = _prob(N=0)
+    assert lib.moba_prefill_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == 1
+    assert lib.moba_prefill_noalloc(ctypes.byref(_prob()), FAKE, None, FAKE, FAKE, None) == 1
