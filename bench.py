@@ -349,7 +349,9 @@ def main():
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_STAGE_EVENTS)]
+    nev = moba.stage_events(prob)
+    passes = (nev - 5) // 2  # attention passes over groups of KV heads
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)]
            for _ in range(args.steps)]
     for ev in evs:
         for e in ev:
@@ -361,8 +363,13 @@ def main():
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     ms_per_step = elapsed * 1e3 / args.steps
-    stage_ms = {s: float(np.mean([ev[i].elapsed_time(ev[i + 1]) for ev in evs]))
-                for i, s in enumerate(STAGES)}
+    # the four stages before attention, then history attention and own-block
+    # attention + merge, each summed over the attention passes
+    spans = {s: [(i, i + 1)] for i, s in enumerate(STAGES[:4])}
+    spans["attn_hist"] = [(4 + 2 * i, 5 + 2 * i) for i in range(passes)]
+    spans["attn_self_merge"] = [(5 + 2 * i, 6 + 2 * i) for i in range(passes)]
+    stage_ms = {s: float(np.mean([sum(ev[a].elapsed_time(ev[b]) for a, b in spans[s])
+                                  for ev in evs])) for s in STAGES}
     event_ms = float(np.mean([ev[0].elapsed_time(ev[-1]) for ev in evs]))
     print(f"[bench] {args.steps} steps: {ms_per_step:.2f} ms/step, stages {stage_ms}",
           file=sys.stderr, flush=True)
@@ -482,7 +489,10 @@ def main():
         "bucket_frac_of_measured_copy": (bk_bytes / (stage_ms["bucket"] / 1e3) / 1e9
                                          / peaks["hbm_copy_gbps"]) if peaks else None,
         "routed_entries": entries,
-        "roofline": {"bound": "mfma", "kernel": "attn_hist_bf16",
+        "attention_passes": passes,
+        # per launch: 1/passes of the history FLOP over the mean per-pass
+        # duration, which is the same ratio as the totals
+        "roofline": {"bound": "mfma", "kernel": "attn_hist_q64_bf16",
                      "achieved": hist_tflops, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                      "frac": hist_tflops / PEAK_BF16_TFLOPS,
                      "frac_of_measured_peak": (hist_tflops / peaks["mfma_bf16_tflops"]

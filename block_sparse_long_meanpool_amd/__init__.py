@@ -31,12 +31,15 @@ MOBA_DTYPE_BF16 = 0
 MOBA_DTYPE_F32 = 1
 MOBA_ROUTING_PER_HEAD = 0
 MOBA_ROUTING_SHARED = 1
-MOBA_STAGE_EVENTS = 7
+# Stage events: [0] start, [1..4] after these four stages, then per attention
+# pass i: [5 + 2i] after its history attention, [6 + 2i] after its own-block
+# attention with the merge (``stage_events(prob)`` events in all).
 STAGES = ("meanpool", "gate_topk", "bucket", "vpack", "attn_hist", "attn_self_merge")
 
 # Every symbol include/moba.h declares.
 EXPORTS = (
-    "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_prefill_ex",
+    "moba_workspace_size", "moba_select_workspace_size", "moba_prefill", "moba_stage_events",
+    "moba_prefill_ex",
     "moba_select", "moba_varlen_workspace_size", "moba_varlen_select_workspace_size",
     "moba_prefill_varlen", "moba_select_varlen",
     "moba_routing_stats_workspace_size", "moba_routing_stats",
@@ -63,6 +66,7 @@ class MobaProblem(ctypes.Structure):
         ("scale", ctypes.c_float),
         ("dtype", ctypes.c_int32),
         ("routing", ctypes.c_int32),
+        ("kv_heads_per_pass", ctypes.c_int32),
     ]
 
 
@@ -93,6 +97,7 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         "moba_workspace_size": (sz, [P]),
         "moba_select_workspace_size": (sz, [P]),
         "moba_prefill": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp]),
+        "moba_stage_events": (sz, [P]),
         "moba_prefill_ex": (ctypes.c_int, [P, vp, vp, vp, vp, vp, sz, vp, vp]),
         "moba_select": (ctypes.c_int, [P, vp, vp, vp, vp, sz, vp]),
         "moba_varlen_workspace_size": (sz, [P, i64, vp]),
@@ -146,14 +151,22 @@ def _dtype_code(t: torch.Tensor) -> int:
 
 
 def make_problem(N, Hq, Hkv, d, block_size, topk, scale=None, dtype=MOBA_DTYPE_BF16,
-                 routing=MOBA_ROUTING_PER_HEAD) -> MobaProblem:
+                 routing=MOBA_ROUTING_PER_HEAD, kv_heads_per_pass=0) -> MobaProblem:
+    """``kv_heads_per_pass``: KV heads per attention pass (0 = the library's
+    choice); the workspace holds the history partials of one pass."""
     if scale is None:
         scale = 1.0 / (d ** 0.5)
     return MobaProblem(int(N), int(Hq), int(Hkv), int(d), int(block_size), int(topk),
-                       float(scale), int(dtype), int(routing))
+                       float(scale), int(dtype), int(routing), int(kv_heads_per_pass))
 
 
-def _problem_from(q, k, block_size, topk, scale, routing=MOBA_ROUTING_PER_HEAD):
+def stage_events(prob: MobaProblem) -> int:
+    """Number of stage events ``prefill`` records for ``prob`` (0 if invalid)."""
+    return load_library().moba_stage_events(ctypes.byref(prob))
+
+
+def _problem_from(q, k, block_size, topk, scale, routing=MOBA_ROUTING_PER_HEAD,
+                  kv_heads_per_pass=0):
     if q.dim() != 3 or k.dim() != 3:
         raise ValueError("q must be [N, Hq, d] and k, v [N, Hkv, d]")
     N, Hq, d = q.shape
@@ -161,7 +174,8 @@ def _problem_from(q, k, block_size, topk, scale, routing=MOBA_ROUTING_PER_HEAD):
         raise ValueError(f"shape mismatch: q {tuple(q.shape)} vs k {tuple(k.shape)}")
     if k.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
-    return make_problem(N, Hq, k.shape[1], d, block_size, topk, scale, _dtype_code(q), routing)
+    return make_problem(N, Hq, k.shape[1], d, block_size, topk, scale, _dtype_code(q), routing,
+                        kv_heads_per_pass)
 
 
 def _check_dev(*ts):
@@ -194,19 +208,21 @@ def alloc_workspace(nbytes: int, device) -> torch.Tensor:
 
 
 def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, events=None,
-            routing=MOBA_ROUTING_PER_HEAD):
+            routing=MOBA_ROUTING_PER_HEAD, kv_heads_per_pass=0):
     """MoBA prefill: O [N, Hq, d] from q [N, Hq, d], k, v [N, Hkv, d] (bf16 or fp32).
 
     ``scale`` defaults to 1/sqrt(d). ``events`` may be a list of
-    ``MOBA_STAGE_EVENTS`` torch.cuda.Event (created with timing) recorded at the
-    stage boundaries on the current stream. ``routing``: MOBA_ROUTING_PER_HEAD
-    or MOBA_ROUTING_SHARED (one selection per KV-head group).
+    ``stage_events(prob)`` torch.cuda.Event (created with timing) recorded at
+    the stage boundaries on the current stream. ``routing``:
+    MOBA_ROUTING_PER_HEAD or MOBA_ROUTING_SHARED (one selection per KV-head
+    group). ``kv_heads_per_pass``: KV heads per attention pass (0 = the
+    library's choice); the output does not depend on it.
     """
     lib = load_library()
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    prob = _problem_from(q, k, block_size, topk, scale, routing, kv_heads_per_pass)
     if out is None:
         out = torch.empty_like(q)
     _check_dev(out)
@@ -218,12 +234,13 @@ def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, eve
         workspace = alloc_workspace(need, q.device)
     ev_arr = None
     if events is not None:
-        if len(events) != MOBA_STAGE_EVENTS:
-            raise ValueError(f"need {MOBA_STAGE_EVENTS} events")
+        nev = lib.moba_stage_events(ctypes.byref(prob))
+        if len(events) != nev:
+            raise ValueError(f"need {nev} events")
         for e in events:
             if not e.cuda_event:  # torch creates the HIP event on first record
                 e.record()
-        ev_arr = (ctypes.c_void_p * MOBA_STAGE_EVENTS)(*[e.cuda_event for e in events])
+        ev_arr = (ctypes.c_void_p * nev)(*[e.cuda_event for e in events])
     st = lib.moba_prefill_ex(ctypes.byref(prob), q.data_ptr(), k.data_ptr(), v.data_ptr(),
                              out.data_ptr(), workspace.data_ptr(), workspace.numel(),
                              _stream(q.device), ev_arr)
@@ -232,7 +249,7 @@ def prefill(q, k, v, block_size, topk, scale=None, out=None, workspace=None, eve
 
 
 def prefill_noalloc(q, k, v, block_size, topk, scale=None, out=None,
-                    routing=MOBA_ROUTING_PER_HEAD):
+                    routing=MOBA_ROUTING_PER_HEAD, kv_heads_per_pass=0):
     """``prefill`` through the allocation-free entry point: the library's own
     fixed device scratch (``moba_noalloc_max_workspace()`` bytes per GPU)
     serves as the workspace, so the call allocates nothing (``out`` may be
@@ -241,7 +258,7 @@ def prefill_noalloc(q, k, v, block_size, topk, scale=None, out=None,
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    prob = _problem_from(q, k, block_size, topk, scale, routing, kv_heads_per_pass)
     if out is None:
         out = torch.empty_like(q)
     _check_dev(out)
@@ -293,7 +310,7 @@ def varlen_workspace_size(prob: MobaProblem, cu_seqlens) -> int:
 
 
 def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, workspace=None,
-                   routing=MOBA_ROUTING_PER_HEAD):
+                   routing=MOBA_ROUTING_PER_HEAD, kv_heads_per_pass=0):
     """MoBA prefill over packed sequences: rows [cu[i], cu[i+1]) of q, k, v form
     sequence i; blocks restart at each sequence and never cross one. Equals
     ``prefill`` applied to every sequence on its own."""
@@ -301,7 +318,7 @@ def prefill_varlen(q, k, v, cu_seqlens, block_size, topk, scale=None, out=None, 
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    prob = _problem_from(q, k, block_size, topk, scale, routing, kv_heads_per_pass)
     cu_host, cu_dev, nseq = _cu_pair(cu_seqlens, q.device)
     if out is None:
         out = torch.empty_like(q)
@@ -342,13 +359,14 @@ def select_varlen(q, k, cu_seqlens, block_size, topk, out=None, workspace=None):
     return out
 
 
-def _chunk_problem(q, k, block_size, topk, scale, routing):
+def _chunk_problem(q, k, block_size, topk, scale, routing, kv_heads_per_pass=0):
     if q.dim() != 3 or k.dim() != 3 or q.shape[2] != k.shape[2]:
         raise ValueError("q must be [C, Hq, d] and k, v [N, Hkv, d]")
     if k.dtype != q.dtype:
         raise TypeError("q, k and v must share a dtype")
     N, Hkv, d = k.shape
-    return make_problem(N, q.shape[1], Hkv, d, block_size, topk, scale, _dtype_code(q), routing)
+    return make_problem(N, q.shape[1], Hkv, d, block_size, topk, scale, _dtype_code(q), routing,
+                        kv_heads_per_pass)
 
 
 def prefill_train(q, k, v, block_size, topk, scale=None, routing=MOBA_ROUTING_PER_HEAD,
@@ -509,7 +527,7 @@ def chunk_workspace_size(prob: MobaProblem, q_rows: int) -> int:
 
 
 def prefill_chunk(q, k, v, block_size, topk, scale=None, out=None, workspace=None,
-                  routing=MOBA_ROUTING_PER_HEAD):
+                  routing=MOBA_ROUTING_PER_HEAD, kv_heads_per_pass=0):
     """Chunked prefill / decode: q [C, Hq, d] are the queries of the last C
     positions of a sequence whose keys and values k, v [N, Hkv, d] include
     them. Returns O [C, Hq, d], equal to those rows of ``prefill`` over the
@@ -518,7 +536,7 @@ def prefill_chunk(q, k, v, block_size, topk, scale=None, out=None, workspace=Non
     _check_dev(q, k, v)
     if v.shape != k.shape or v.dtype != k.dtype:
         raise ValueError("v must match k in shape and dtype")
-    prob = _chunk_problem(q, k, block_size, topk, scale, routing)
+    prob = _chunk_problem(q, k, block_size, topk, scale, routing, kv_heads_per_pass)
     C = q.shape[0]
     if out is None:
         out = torch.empty_like(q)

@@ -443,14 +443,17 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
     const int32_t* __restrict__ tile_off, const int32_t* __restrict__ bin_off,
     const int32_t* __restrict__ scalars, const uint32_t* __restrict__ entries,
     _Float16* __restrict__ part_o, float* __restrict__ part_lse, int Hkv, int B, int64_t Bpad,
-    int64_t ldv, int KH, int64_t nh, float sl2e) {
+    int64_t ldv, int KH, int64_t nh, float sl2e, int Hq, int Hs, int h0, int64_t bin0,
+    int64_t bin1) {
   MOBA_DECLARE_TILES
   // XCD-aware order: workgroup i runs on XCD i % 8; each XCD takes a
   // contiguous range of tiles so the tiles of one K/V block share its L2.
   // The grid is a multiple of 8, so this is a bijection on [0, gridDim.x).
+  // The tiles are those of this attention pass's bins [bin0, bin1).
   const int64_t per = gridDim.x / 8;
-  const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
-  if (w >= scalars[1]) return;
+  const int64_t first = tile_off[bin0];
+  const int64_t w = first + (blockIdx.x % 8) * per + blockIdx.x / 8;
+  if (w >= tile_off[bin1]) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
   const int bin = tile_map[w];
   const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
@@ -467,7 +470,9 @@ __global__ __launch_bounds__(kThreads) void attn_hist_bf16(
     const int64_t e = e_begin + wave * kWaveQ + qb * 32 + (lane & 31);
     valid[qb] = e < e_end;
     ev[qb] = valid[qb] ? entries[e] : 0u;
-    qrow[qb] = Q + (int64_t)(ev[qb] / (uint32_t)KH) * kHeadDim;
+    // e / KH = row * Hs + (head - h0) over the pass's heads; Q row = row * Hq + head
+    const uint32_t pr = ev[qb] / (uint32_t)KH;
+    qrow[qb] = Q + ((int64_t)pr + (int64_t)(pr / (uint32_t)Hs) * (Hq - Hs) + h0) * kHeadDim;
     dummy_row[qb] = 0;
   }
   Wave W;
@@ -529,21 +534,23 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
     const int32_t* __restrict__ blo, const _Float16* __restrict__ part_o,
     const float* __restrict__ part_lse, uint16_t* __restrict__ O, float* __restrict__ lse_out,
     int Hq, int Hkv, int G, int64_t Bpad, int64_t ldv, int KH, int64_t n, int64_t nqb,
-    int tiles_per_block, float sl2e) {
+    int tiles_per_block, float sl2e, int g0, int gs) {
   MOBA_DECLARE_TILES
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, h = lane >> 5;
-  // Work items w = ((c' * Hkv) + g) * tiles_per_block + t' in order of
-  // blocks from the last (only the last nqb blocks hold query rows), and
-  // inside a block heavier (later) row tiles first. Workgroup i runs on XCD
-  // i % 8 and each XCD takes a contiguous range of items, so the row tiles of
-  // one (block, KV head) share its L2 copy of K/V.
-  const int64_t items = nqb * Hkv * (int64_t)tiles_per_block;
+  // Work items w = ((c' * gs) + g - g0) * tiles_per_block + t' over this
+  // attention pass's KV heads [g0, g0 + gs), in order of blocks from the last
+  // (only the last nqb blocks hold query rows), and inside a block heavier
+  // (later) row tiles first. Workgroup i runs on XCD i % 8 and each XCD takes
+  // a contiguous range of items, so the row tiles of one (block, KV head)
+  // share its L2 copy of K/V.
+  const int64_t items = nqb * gs * (int64_t)tiles_per_block;
   const int64_t per = gridDim.x / 8;  // the grid is a multiple of 8
   const int64_t w = (blockIdx.x % 8) * per + blockIdx.x / 8;
   if (w >= items) return;
   const int tile = tiles_per_block - 1 - (int)(w % tiles_per_block);
-  const int g = (int)((w / tiles_per_block) % Hkv);
-  const int64_t c = n - 1 - w / ((int64_t)tiles_per_block * Hkv);
+  const int g = g0 + (int)((w / tiles_per_block) % gs);
+  const int64_t c = n - 1 - w / ((int64_t)tiles_per_block * gs);
+  const int Hs = gs * G, h0 = g0 * G;  // the pass's query heads, for its partials
   // keys from the block's first row; query rows (of Q and O) and their
   // positions (for the causal mask) from the block's query range
   const int64_t key0 = bstart[c], qrow0 = qstart[c], pos0 = qpos[c];
@@ -666,10 +673,12 @@ __global__ __launch_bounds__(kThreads) void attn_self_bf16(
         pi[i] = p0 + wave * kWaveQ + j;
         const int64_t pic = pi[i] < npairs ? pi[i] : npairs - 1;  // clamped: loads stay in bounds
         phj[i] = (qrow0 + pic / G) * Hq + g * G + (int)(pic % G);
+        // the pass's partial slots of this (row, head)
+        const int64_t pslot = ((qrow0 + pic / G) * Hs + (g * G - h0) + (int)(pic % G)) * KH;
         own[i] = *reinterpret_cast<const h8*>(stage + j * kHeadDim + 8 * (c16 ^ (j & 15)));
         own_lse[i] = stage_lse[j];
-        ls[i] = part_lse + phj[i] * KH;
-        po[i] = part_o + (size_t)(phj[i] * KH) * kHeadDim;
+        ls[i] = part_lse + pslot;
+        po[i] = part_o + (size_t)pslot * kHeadDim;
       }
       b8 out[R];
       float lse_row[R];
@@ -709,11 +718,12 @@ hipError_t launch_attn_hist_bf16(const Prob& P, const Blocks& T, const BucketPla
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
   const int64_t ldv = P.vt_blocks * Bpad;
-  const int64_t grid = ceil_div(bp.max_tiles, 8) * 8;
+  const int64_t grid = ceil_div(pass_max_tiles(P), 8) * 8;
   attn_hist_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
       b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, P.Hkv, P.B, Bpad,
-      ldv, P.KH, P.nh, sl2e);
+      ldv, P.KH, P.nh, sl2e, P.Hq, pass_heads(P), pass_h0(P), (int64_t)P.g0 * P.nh,
+      (int64_t)(P.g0 + P.gs) * P.nh);
   return hipGetLastError();
 }
 
@@ -725,13 +735,13 @@ hipError_t launch_attn_self_bf16(const Prob& P, const Blocks& T, const void* Q, 
   const int64_t ldv = P.vt_blocks * Bpad;
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kGroupQ);
   const int64_t nqb = query_blocks(P);
-  const int64_t grid = ceil_div(nqb * tiles_per_block * P.Hkv, 8) * 8;
+  const int64_t grid = ceil_div(nqb * tiles_per_block * P.gs, 8) * 8;
   const bool merge = part_o != nullptr && P.KH > 0;
   attn_self_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, T.qstart, T.qlen,
       T.qpos, T.lo, merge ? (const _Float16*)part_o : nullptr, merge ? part_lse : nullptr,
       (uint16_t*)O, lse_out, P.Hq,
-      P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, nqb, tiles_per_block, sl2e);
+      P.Hkv, P.G, Bpad, ldv, merge ? P.KH : 0, P.n, nqb, tiles_per_block, sl2e, P.g0, P.gs);
   return hipGetLastError();
 }
 

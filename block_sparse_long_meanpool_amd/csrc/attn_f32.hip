@@ -100,11 +100,13 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
     const int32_t* __restrict__ tile_off,
     const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
     const uint32_t* __restrict__ entries, float* __restrict__ part_o, float* __restrict__ part_lse,
-    int Hkv, int B, int KH, int64_t nh, float sl2e) {
+    int Hkv, int B, int KH, int64_t nh, float sl2e, int Hq, int Hs, int h0, int64_t bin0,
+    int64_t bin1) {
   __shared__ float ks[KT * kHeadDim];
   __shared__ float vs[KT * kHeadDim];
-  const int64_t w = blockIdx.x;
-  if (w >= scalars[1]) return;
+  // the tiles of this attention pass's bins [bin0, bin1)
+  const int64_t w = tile_off[bin0] + blockIdx.x;
+  if (w >= tile_off[bin1]) return;
   const int bin = tile_map[w];
   const int64_t e_begin = bin_off[bin] + (w - tile_off[bin]) * (int64_t)kTileQ;
   const int64_t e_end = bin_off[bin + 1];
@@ -115,8 +117,10 @@ __global__ __launch_bounds__(kThreads) void attn_hist_f32(
     const int64_t my_e = base + qi;
     const bool valid = my_e < e_end;
     const uint32_t ev = valid ? entries[my_e] : 0u;
+    // ev / KH = row * Hs + (head - h0) over the pass's heads; Q row = row * Hq + head
+    const int64_t pr = ev / (uint32_t)KH;
     QState S;
-    init_state(S, Q + (int64_t)(ev / (uint32_t)KH) * kHeadDim, valid, sub);
+    init_state(S, Q + (pr + (pr / Hs) * (Hq - Hs) + h0) * kHeadDim, valid, sub);
     for (int k0 = 0; k0 < B; k0 += KT) {
       const int nv = (B - k0) < KT ? B - k0 : KT;
       __syncthreads();
@@ -140,10 +144,10 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ qpos,
     const int32_t* __restrict__ blo, const float* __restrict__ part_o,
     const float* __restrict__ part_lse, float* __restrict__ O, float* __restrict__ lse_out, int Hq,
-    int Hkv, int G, int KH, int64_t n, int tiles_per_block, float sl2e) {
+    int Hkv, int G, int KH, int64_t n, int tiles_per_block, float sl2e, int g0, int gs) {
   __shared__ float ks[KT * kHeadDim];
   __shared__ float vs[KT * kHeadDim];
-  const int g = blockIdx.y;
+  const int g = g0 + (int)blockIdx.y;  // this attention pass's KV heads [g0, g0 + gs)
   const int64_t c = n - 1 - (int64_t)(blockIdx.x / tiles_per_block);
   const int tile = tiles_per_block - 1 - (int)(blockIdx.x % tiles_per_block);
   // keys from the block's first row; query rows and their positions from its query range
@@ -175,7 +179,8 @@ __global__ __launch_bounds__(kThreads) void attn_self_f32(
   if (part_o != nullptr && KH > 0) {
     const int64_t nbefore = c - blo[c];  // earlier blocks of the row's sequence
     const int64_t nhist = nbefore < KH ? nbefore : KH;
-    const int64_t ebase = ph * KH;
+    // the pass's partial slots of this (row, head)
+    const int64_t ebase = ((qrow0 + my_pi / G) * (gs * G) + (my_h - g0 * G)) * KH;
     for (int64_t s = 0; s < nhist; ++s) M = fmaxf(M, part_lse[ebase + s]);
     const float ws = __builtin_amdgcn_exp2f(S.m - M);
     l *= ws;
@@ -206,10 +211,11 @@ hipError_t launch_attn_hist(const Prob& P, const Blocks& T, const BucketPlan& bp
                ? launch_attn_hist_q64_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s)
                : launch_attn_hist_bf16(P, T, bp, Q, K, Vt, b, part_o, part_lse, s);
   if (P.nh <= 0 || P.KH <= 0 || bp.max_tiles <= 0) return hipSuccess;
-  attn_hist_f32<<<(unsigned)bp.max_tiles, kThreads, 0, s>>>(
+  attn_hist_f32<<<(unsigned)pass_max_tiles(P), kThreads, 0, s>>>(
       (const float*)Q, (const float*)K, (const float*)V, T.start, b.tile_map, b.tile_off,
       b.bin_off, b.scalars, b.entries, (float*)part_o, part_lse, P.Hkv, P.B, P.KH, P.nh,
-      P.scale * kLog2e);
+      P.scale * kLog2e, P.Hq, pass_heads(P), pass_h0(P), (int64_t)P.g0 * P.nh,
+      (int64_t)(P.g0 + P.gs) * P.nh);
   return hipGetLastError();
 }
 
@@ -220,11 +226,11 @@ hipError_t launch_attn_self(const Prob& P, const Blocks& T, const void* Q, const
     return launch_attn_self_bf16(P, T, Q, K, Vt, part_o, part_lse, O, lse_out, s);
   const bool merge = part_o != nullptr && P.KH > 0;
   const int tiles_per_block = (int)ceil_div((int64_t)P.B * P.G, kQ);
-  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.Hkv);
+  dim3 grid((unsigned)(P.n * tiles_per_block), (unsigned)P.gs);
   attn_self_f32<<<grid, kThreads, 0, s>>>(
       (const float*)Q, (const float*)K, (const float*)V, T.start, T.qstart, T.qlen, T.qpos, T.lo,
       merge ? (const float*)part_o : nullptr, merge ? part_lse : nullptr, (float*)O, lse_out, P.Hq,
-      P.Hkv, P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e);
+      P.Hkv, P.G, merge ? P.KH : 0, P.n, tiles_per_block, P.scale * kLog2e, P.g0, P.gs);
   return hipGetLastError();
 }
 

@@ -368,15 +368,26 @@ __device__ inline void iterate(Wave& W, const uint16_t* kq, int sq, const uint16
   }
 }
 
+// Where an attention pass's entries point: e / KH = row * Hs + (head - h0)
+// over the pass's Hs query heads from h0; the Q (and O) row of that (row,
+// head) is row * Hq + head.
+struct PassHeads {
+  int KH, Hq, Hs, h0;
+};
+__device__ inline int64_t entry_qrow(uint32_t e, const PassHeads& ph) {
+  const uint32_t pr = e / (uint32_t)ph.KH;
+  return (int64_t)pr + (int64_t)(pr / (uint32_t)ph.Hs) * (ph.Hq - ph.Hs) + ph.h0;
+}
+
 // The wave's Q rows (B operand of the scores): lane l holds the row of
-// entry ev[qb] (query l % 32 of block qb; row = entry / KH), chunks
-// 16 kk + 8 h; rows of invalid entries are zero.
+// entry ev[qb] (query l % 32 of block qb), chunks 16 kk + 8 h; rows of
+// invalid entries are zero.
 __device__ inline void load_q(Wave& W, const uint16_t* __restrict__ Q, const uint32_t* ev,
-                              const bool* valid, int KH, int lane) {
+                              const bool* valid, const PassHeads& ph, int lane) {
   const int h = lane >> 5;
 #pragma unroll
   for (int qb = 0; qb < 2; ++qb) {
-    const uint16_t* qrow = Q + (int64_t)(ev[qb] / (uint32_t)KH) * kHeadDim;
+    const uint16_t* qrow = Q + entry_qrow(ev[qb], ph) * kHeadDim;
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) {
       const uint4 u = valid[qb] ? *reinterpret_cast<const uint4*>(qrow + 16 * kk + 8 * h)
@@ -407,7 +418,7 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
                                  const uint16_t* __restrict__ nvbase = nullptr,
                                  const uint16_t* __restrict__ Q = nullptr,
                                  const uint32_t* nev = nullptr, const bool* nvalid = nullptr,
-                                 int KH = 1) {
+                                 PassHeads ph = PassHeads{1, 1, 1, 0}) {
   const Tile T0{k0, v0}, T1{k1, v1}, T2{k2, v2}, T3{k3, v3};
   const int nt = B / KT;  // a multiple of 4
   auto src_of = [&](int t) {
@@ -459,7 +470,7 @@ __device__ inline void run_block(Wave& W, const uint16_t* __restrict__ kbase, in
       iterate<true, true, true, WAITK, COPY>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa,
                                              vpre, sl2e, lane, cur, &fs, krow, ldv, wave);
     } else {
-      if (STREAM) load_q(W, Q, nev, nvalid, KH, lane);
+      if (STREAM) load_q(W, Q, nev, nvalid, ph, lane);
       iterate<false, true, true>(W, nxt.k, 0, cur.v, 0, cur.v, 1, sa, sb, pa, pb, vpre, sl2e, lane);
       iterate<false, false, false>(W, nxt.k, 1, cur.v, 1, nxt.v, 0, sb, sa, pb, pa, vpre, sl2e,
                                    lane);
@@ -605,16 +616,19 @@ attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
                    const int32_t* __restrict__ bin_off, int32_t* __restrict__ scalars,
                    const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
                    float* __restrict__ part_lse, int32_t* __restrict__ redo_list, int Hkv, int B,
-                   int64_t Bpad, int64_t ldv, int KH, int64_t nh, float sl2e) {
+                   int64_t Bpad, int64_t ldv, int64_t nh, float sl2e, PassHeads ph, int64_t bin0,
+                   int64_t bin1) {
   __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS], lds_k2[KS_ELEMS],
       lds_k3[KS_ELEMS];
   __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS], lds_v2[VT_ELEMS],
       lds_v3[VT_ELEMS];
-  const int64_t total = scalars[1];
+  // this attention pass's tiles: those of its bins [bin0, bin1)
+  const int64_t first = tile_off[bin0];
+  const int64_t total = tile_off[bin1] - first;
   const int64_t nloc = gridDim.x / 8;  // workgroups per XCD (the grid is a multiple of 8)
   const int64_t per = (total + 7) / 8;
-  const int64_t lo = (blockIdx.x % 8) * per;
-  const int64_t hi = lo + per < total ? lo + per : total;
+  const int64_t lo = first + (blockIdx.x % 8) * per;
+  const int64_t hi = lo + per < first + total ? lo + per : first + total;
   int64_t w = lo + blockIdx.x / 8;
   if (w >= hi) return;
   const int tid = threadIdx.x, lane = tid & 63;
@@ -628,7 +642,7 @@ attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
   bool valid[2];
   tile_entries(cur, entries, wave, lane, ev, valid);
   Wave W;
-  load_q(W, Q, ev, valid, KH, lane);
+  load_q(W, Q, ev, valid, ph, lane);
   load_tile(Tile{lds_k0, lds_v0}, tile_src(cur.kbase, krow, cur.vbase, ldv), krow, ldv, wave, lane);
   load_tile(Tile{lds_k1, lds_v1},
             tile_src(cur.kbase + KT * krow, krow, cur.vbase + KT, ldv), krow, ldv, wave, lane);
@@ -647,7 +661,7 @@ attn_hist_q64_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ 
     reset_acc(W);
     run_block<true>(W, cur.kbase, krow, cur.vbase, ldv, B, sl2e, true, wave, lane, lds_k0, lds_k1,
                     lds_k2, lds_k3, lds_v0, lds_v1, lds_v2, lds_v3, nxt.kbase, nxt.vbase, Q, evn,
-                    validn, KH);
+                    validn, ph);
     // workgroup-uniform, so each tile is listed at most once
     if (__syncthreads_or(wave_overflow(W, valid)) && tid == 0)
       redo_list[atomicAdd(&scalars[2], 1)] = (int32_t)w;
@@ -676,8 +690,8 @@ attn_hist_q64_redo_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restri
                         const int32_t* __restrict__ bin_off, const int32_t* __restrict__ scalars,
                         const uint32_t* __restrict__ entries, _Float16* __restrict__ part_o,
                         float* __restrict__ part_lse, const int32_t* __restrict__ redo_list,
-                        int Hkv, int B, int64_t Bpad, int64_t ldv, int KH, int64_t nh,
-                        float sl2e) {
+                        int Hkv, int B, int64_t Bpad, int64_t ldv, int64_t nh, float sl2e,
+                        PassHeads ph) {
   __shared__ __align__(16) uint16_t lds_k0[KS_ELEMS], lds_k1[KS_ELEMS], lds_k2[KS_ELEMS],
       lds_k3[KS_ELEMS];
   __shared__ __align__(16) uint16_t lds_v0[VT_ELEMS], lds_v1[VT_ELEMS], lds_v2[VT_ELEMS],
@@ -693,7 +707,7 @@ attn_hist_q64_redo_bf16(const uint16_t* __restrict__ Q, const uint16_t* __restri
     bool valid[2];
     tile_entries(cur, entries, wave, lane, ev, valid);
     Wave W;
-    load_q(W, Q, ev, valid, KH, lane);
+    load_q(W, Q, ev, valid, ph, lane);
     float mx[2] = {-INFINITY, -INFINITY};
     block_max(W, cur.kbase, krow, cur.vbase, ldv, B, wave, lane, lds_k0, lds_v0, mx);
 #pragma unroll
@@ -715,18 +729,25 @@ hipError_t launch_attn_hist_q64_bf16(const Prob& P, const Blocks& T, const Bucke
   const float sl2e = P.scale * kLog2e;
   const int64_t Bpad = vt_padded_block(P.B);
   const int64_t ldv = P.vt_blocks * Bpad;
+  const PassHeads ph{P.KH, P.Hq, pass_heads(P), pass_h0(P)};
   // one workgroup per compute unit (256 on MI355X), fewer for small problems
-  const int64_t grid = std::min<int64_t>(256, ceil_div(bp.max_tiles, 8) * 8);
+  const int64_t grid = std::min<int64_t>(256, ceil_div(pass_max_tiles(P), 8) * 8);
+  // the redo list starts empty in every attention pass (the bucketing clears
+  // it for the first)
+  if (P.g0 > 0) {
+    hipError_t e = launch_fill_i32(b.scalars + 2, 0, 1, s);
+    if (e != hipSuccess) return e;
+  }
   attn_hist_q64_bf16<<<(unsigned)grid, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
       b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, b.redo, P.Hkv,
-      P.B, Bpad, ldv, P.KH, P.nh, sl2e);
+      P.B, Bpad, ldv, P.nh, sl2e, ph, (int64_t)P.g0 * P.nh, (int64_t)(P.g0 + P.gs) * P.nh);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   attn_hist_q64_redo_bf16<<<64, kThreads, 0, s>>>(
       (const uint16_t*)Q, (const uint16_t*)K, (const uint16_t*)Vt, T.start, b.tile_map,
       b.tile_off, b.bin_off, b.scalars, b.entries, (_Float16*)part_o, part_lse, b.redo, P.Hkv,
-      P.B, Bpad, ldv, P.KH, P.nh, sl2e);
+      P.B, Bpad, ldv, P.nh, sl2e, ph);
   return hipGetLastError();
 }
 

@@ -3,9 +3,12 @@
 // KV block they read so that one contiguous K/V block serves a batch of
 // queries; section 5.4 on the sort / prefix-sum / reorder this costs).
 //
-// Bins are (KV head g, history block b). An entry is the flat selection index
-// e = (row * Hq + head) * (k - 1) + slot, which is also where history
-// attention writes that query's partial result. The lists come out ordered by
+// Bins are (KV head g, history block b). An entry is the index of the
+// query's history slot among the partial results of its attention pass (the
+// group of kvpp KV heads holding g, query heads h0 .. h0 + Hs - 1):
+// e = (row * Hs + head - h0) * (k - 1) + slot, which is where history
+// attention writes that query's partial result (one pass of all heads:
+// e = (row * Hq + head) * (k - 1) + slot). The lists come out ordered by
 // (row, head) within each bin, independently of scheduling:
 //   1. count:   per chunk of rows (one KV-head group) an LDS histogram;
 //   2. scan:    exclusive scan of the counts down the chunks of every bin,
@@ -139,10 +142,14 @@ __global__ __launch_bounds__(1024) void bucket_scan_bins(const int32_t* __restri
 __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ row_blk,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ bin_off,
-    uint32_t* __restrict__ entries, int64_t N, int Hq, int G, int k, int64_t nh,
-    int rows_per_chunk, int64_t nchunk, int words) {
+    uint32_t* __restrict__ entries, int64_t N, int Hq, int Hkv, int G, int k, int64_t nh,
+    int rows_per_chunk, int64_t nchunk, int words, int kvpp) {
   extern __shared__ uint32_t bm[];  // [nh][words] bitmaps, then [nh][words] prefix counts
   const int g = blockIdx.y;
+  // the attention pass of KV head g: query heads [h0, h0 + Hs)
+  const int g0 = (g / kvpp) * kvpp;
+  const int h0 = g0 * G;
+  const int64_t Hs = (int64_t)(Hkv - g0 < kvpp ? Hkv - g0 : kvpp) * G;
   const int64_t chunk = blockIdx.x;
   const int64_t nw = nh * words;
   uint32_t* pre = bm + nw;  // pre[b][w] = entries of bin b in words 0..w-1
@@ -177,14 +184,14 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     if (r >= N) break;
     const int h = g * G + pi % G;
     const int64_t c = row_blk[r];
-    const int64_t ph = (int64_t)r * Hq + h;
-    const int32_t* row = sel + ph * k;
+    const int32_t* row = sel + ((int64_t)r * Hq + h) * k;
+    const int64_t pslot = ((int64_t)r * Hs + (h - h0)) * KH;
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
       if (!hist_entry(b, c)) continue;
       const size_t wi = (size_t)b * words + (pi >> 5);
       const int rank = (int)pre[wi] + __popc(bm[wi] & ((1u << (pi & 31)) - 1u));
-      entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(ph * KH + s);
+      entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(pslot + s);
     }
   }
 }
@@ -236,8 +243,8 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   bucket_scatter<<<grid, kThreads, 2 * sizeof(uint32_t) * P.nh * bp.words, s>>>(
-      sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.G, P.k, P.nh,
-      bp.rows_per_chunk, bp.nchunk, bp.words);
+      sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.Hkv, P.G, P.k, P.nh,
+      bp.rows_per_chunk, bp.nchunk, bp.words, P.kvpp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (b.tile_map) {
     bucket_tile_map<<<(unsigned)bp.nbins, kThreads, 0, s>>>(b.tile_off, b.tile_map);

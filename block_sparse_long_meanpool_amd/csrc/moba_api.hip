@@ -4,6 +4,7 @@
 #include <climits>
 #include <mutex>
 #include <cmath>
+#include <algorithm>
 #include <cstdio>
 #include <cstring>
 #include <string>
@@ -27,6 +28,24 @@ int hip_fail(hipError_t e, const char* where) {
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// KV heads per attention pass: as asked, else the largest group whose
+// history partials fit kPassPartialBytes (at least one KV head).
+constexpr double kPassPartialBytes = 16.0 * (1u << 30);
+int passes_kvpp(const Prob& P, int asked) {
+  if (asked > 0) return asked;
+  const double per_kv = (double)P.hist_rows * P.G *
+                        ((double)part_elem_bytes(P) * P.d + sizeof(float));
+  const double fit = per_kv > 0 ? std::floor(kPassPartialBytes / per_kv) : (double)P.Hkv;
+  return fit < 1 ? 1 : fit > P.Hkv ? P.Hkv : (int)fit;
+}
+int num_passes(const Prob& P) { return (int)ceil_div(P.Hkv, P.kvpp); }
+Prob pass_of(const Prob& P, int i) {
+  Prob Q = P;
+  Q.g0 = i * P.kvpp;
+  Q.gs = P.Hkv - Q.g0 < P.kvpp ? P.Hkv - Q.g0 : P.kvpp;
+  return Q;
+}
 
 // The bf16 kernels read the packed V^T (and, in the backward, K^T) of one
 // KV head through a buffer resource whose per-lane byte offsets are 32-bit:
@@ -59,6 +78,8 @@ int make_prob(const moba_problem_t* p, Prob* P) {
     return fail(MOBA_ERR_INVALID_ARGUMENT, "dtype must be MOBA_DTYPE_BF16 or MOBA_DTYPE_F32");
   if (p->routing != MOBA_ROUTING_PER_HEAD && p->routing != MOBA_ROUTING_SHARED)
     return fail(MOBA_ERR_INVALID_ARGUMENT, "routing must be MOBA_ROUTING_PER_HEAD or _SHARED");
+  if (p->kv_heads_per_pass < 0 || p->kv_heads_per_pass > p->num_kv_heads)
+    return fail(MOBA_ERR_INVALID_ARGUMENT, "kv_heads_per_pass must be in [0, num_kv_heads]");
   if (p->head_dim != kHeadDim) return fail(MOBA_ERR_UNSUPPORTED, "only head_dim == 128 is built");
   if (p->topk > kMaxTopk) return fail(MOBA_ERR_UNSUPPORTED, "topk > 32 is not supported");
   const int G = p->num_q_heads / p->num_kv_heads;
@@ -83,11 +104,14 @@ int make_prob(const moba_problem_t* p, Prob* P) {
   P->n = (P->N + P->B - 1) / P->B;
   P->nh = P->n - 1;
   P->vt_blocks = P->n;
+  P->g0 = 0;
+  P->gs = P->Hkv;
   P->hist_rows = 0;
   for (int64_t c = 0; c < P->n; ++c) {
     const int64_t rows = P->N - c * P->B < P->B ? P->N - c * P->B : P->B;
     P->hist_rows += rows * (c < P->KH ? c : P->KH);
   }
+  P->kvpp = passes_kvpp(*P, p->kv_heads_per_pass);
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
   return check_vt_extent(*P, P->n);
 }
@@ -107,6 +131,7 @@ int make_prob_chunk(const moba_problem_t* p, int64_t q_rows, Prob* P) {
     const int64_t e = (c + 1) * P->B < P->N ? (c + 1) * P->B : P->N;
     P->hist_rows += (e - a) * (c < P->KH ? c : P->KH);
   }
+  P->kvpp = passes_kvpp(*P, p->kv_heads_per_pass);
   return MOBA_OK;
 }
 
@@ -138,11 +163,13 @@ int make_prob_varlen(const moba_problem_t* p, int64_t nseq, const int64_t* cu, P
   }
   P->nh = P->n - 1;
   P->vt_blocks = P->n;
+  P->kvpp = passes_kvpp(*P, p->kv_heads_per_pass);
   if (P->nh > kMaxHist) return fail(MOBA_ERR_UNSUPPORTED, "more than 8192 history blocks");
   return check_vt_extent(*P, P->n);
 }
 
 size_t elem_bytes(const Prob& P) { return P.dtype == MOBA_DTYPE_BF16 ? 2 : 4; }
+
 
 struct Layout {
   size_t blk_start, blk_len, blk_lo, qstart, qlen, qpos, row_blk, seq_base;
@@ -239,7 +266,8 @@ Layout plan_ws(const Prob& P, bool full, bool cached = false) {
       L.part_lse = L.part_o = L.vt = off;
       L.dec_part = take(decode_part_bytes(P));
     } else {
-      const size_t slots = (size_t)(P.Nq * P.Hq) * (size_t)P.KH;
+      // history partials of one attention pass (kvpp KV heads)
+      const size_t slots = (size_t)P.Nq * (size_t)(P.kvpp * P.G) * (size_t)P.KH;
       L.redo = take(sizeof(int32_t) * (size_t)bp.max_tiles);
       L.part_lse = take(sizeof(float) * slots);
       L.part_o = take(part_elem_bytes(P) * slots * P.d);
@@ -368,11 +396,12 @@ int run_prefill(const Prob& P0, const int64_t* cu, const void* q, const void* k,
   if ((rc = run_select(P, cu, q, k, sel, workspace, L, s, events, cv))) return rc;
   const Blocks T = tables(workspace, L);
   if (P.Nq <= kDecodeRows) {  // few rows: split-K over the selected blocks
-    for (int i = 3; i <= 5; ++i)
+    const int nev = 5 + 2 * num_passes(P);
+    for (int i = 3; i < nev - 1; ++i)
       if ((rc = record(events, i, s))) return rc;
     hipError_t e = launch_decode(P, T, q, k, v, sel, at<float>(workspace, L.dec_part), o, lse, s);
     if (e != hipSuccess) return hip_fail(e, "moba_attn (few rows)");
-    return record(events, 6, s);
+    return record(events, nev - 1, s);
   }
   const BucketPlan bp = plan_bucket(P);
   const BucketBufs bb = bucket_bufs(workspace, L);
@@ -387,17 +416,23 @@ int run_prefill(const Prob& P0, const int64_t* cu, const void* q, const void* k,
     if (e != hipSuccess) return hip_fail(e, "V pack");
   }
   if ((rc = record(events, 4, s))) return rc;
-  e = launch_attn_hist(P, T, bp, q, k, v, vt, bb, part_o, part_lse, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
-  if ((rc = record(events, 5, s))) return rc;
-  e = launch_attn_self(P, T, q, k, v, vt, part_o, part_lse, o, lse, s);
-  if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
-  return record(events, 6, s);
+  // attention passes over groups of kvpp KV heads; the partials of one pass
+  // live in the workspace at a time
+  for (int i = 0; i < num_passes(P); ++i) {
+    const Prob Pi = pass_of(P, i);
+    e = launch_attn_hist(Pi, T, bp, q, k, v, vt, bb, part_o, part_lse, s);
+    if (e != hipSuccess) return hip_fail(e, "moba_attn (history)");
+    if ((rc = record(events, 5 + 2 * i, s))) return rc;
+    e = launch_attn_self(Pi, T, q, k, v, vt, part_o, part_lse, o, lse, s);
+    if (e != hipSuccess) return hip_fail(e, "moba_attn (own block) + moba_merge");
+    if ((rc = record(events, 6 + 2 * i, s))) return rc;
+  }
+  return MOBA_OK;
 }
 
-int check_events(void* const* events) {
+int check_events(const Prob& P, void* const* events) {
   if (events)
-    for (int i = 0; i < MOBA_STAGE_EVENTS; ++i)
+    for (int i = 0; i < 5 + 2 * num_passes(P); ++i)
       if (!events[i]) return fail(MOBA_ERR_INVALID_ARGUMENT, "stage event handle is NULL");
   return MOBA_OK;
 }
@@ -422,6 +457,12 @@ size_t moba_workspace_size(const moba_problem_t* p) {
   return plan_ws(P, true).total;
 }
 
+size_t moba_stage_events(const moba_problem_t* p) {
+  Prob P;
+  if (make_prob(p, &P) != MOBA_OK) return 0;
+  return (size_t)(5 + 2 * num_passes(P));
+}
+
 size_t moba_select_workspace_size(const moba_problem_t* p) {
   Prob P;
   if (make_prob(p, &P) != MOBA_OK) return 0;
@@ -438,7 +479,7 @@ int moba_prefill_ex(const moba_problem_t* p, const void* q, const void* k, const
   if ((rc = check_ptrs(ptrs, 4, "q, k, v and o must be non-NULL"))) return rc;
   const Layout L = plan_ws(P, true);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
-  if ((rc = check_events(events))) return rc;
+  if ((rc = check_events(P, events))) return rc;
   return run_prefill(P, nullptr, q, k, v, o, workspace, L, (hipStream_t)stream, events);
 }
 
@@ -566,14 +607,18 @@ int moba_prefill_train(const moba_problem_t* p, const void* q, const void* k, co
 size_t moba_backward_workspace_size(const moba_problem_t* p) {
   Prob P;
   if (make_prob(p, &P) != MOBA_OK) return 0;
+  P.kvpp = P.Hkv;
   return plan_ws_bwd(P).total;
 }
 
-static int run_backward(const Prob& P, const int64_t* cu_dev, const void* q, const void* k,
+static int run_backward(const Prob& P0, const int64_t* cu_dev, const void* q, const void* k,
                         const void* v, const void* o, const float* lse, const void* dout,
                         void* dq, void* dk, void* dv, void* workspace, size_t ws_bytes,
                         void* stream) {
   int rc;
+  // the backward kernels take the bucket lists of all heads in one pass
+  Prob P = P0;
+  P.kvpp = P.Hkv;
   const void* ptrs[10] = {q, k, v, o, lse, dout, dq, dk, dv, nullptr};
   if ((rc = check_ptrs(ptrs, 9, "q, k, v, o, lse, dout, dq, dk and dv must be non-NULL")))
     return rc;
@@ -877,6 +922,7 @@ int moba_debug_bucket(const moba_problem_t* p, const int32_t* sel, int32_t* offs
   if ((rc = check_ptrs(ptrs, 3, "sel, offsets and entries must be non-NULL"))) return rc;
   const Layout L = plan_ws(P, true);
   if ((rc = check_ws(workspace, ws_bytes, L.total))) return rc;
+  P.kvpp = P.Hkv;  // entries numbered over all heads: ((row * Hq + head) * (k - 1) + slot)
   BucketBufs bb = bucket_bufs(workspace, L);
   bb.bin_off = offsets;
   bb.entries = entries;

@@ -37,7 +37,22 @@ struct Prob {
   int routing;        // MOBA_ROUTING_*
   int64_t vt_blocks;  // blocks of the packed V^T layout read by the bf16 kernels (n, or a
                       // decode cache's capacity in blocks)
+  int kvpp;           // KV heads per attention pass (1..Hkv)
+  int g0, gs;         // this attention pass: KV heads [g0, g0 + gs) (whole problem: 0, Hkv)
 };
+
+// History partial results are indexed per attention pass: the history slot s
+// of (row r, query head h) of the pass holding h is
+//   ((r * Hs + (h - h0)) * KH + s),  h0 = g0 * G, Hs = gs * G,
+// for the pass of h's KV head. These give a pass's h0 and Hs.
+inline int pass_h0(const Prob& P) { return P.g0 * P.G; }
+inline int pass_heads(const Prob& P) { return P.gs * P.G; }
+// Bound on the history tiles of an attention pass (its bins' lists in
+// tiles of kTileQ entries).
+inline int64_t pass_max_tiles(const Prob& P) {
+  const int64_t entries = P.hist_rows * (int64_t)pass_heads(P);
+  return (entries + kTileQ - 1) / kTileQ + (int64_t)P.gs * P.nh;
+}
 
 // Block and row tables in device memory (built by launch_tables):
 //   start[b], len[b]: first key row and key count of global block b (len <= B);

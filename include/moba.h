@@ -88,7 +88,22 @@ typedef struct {
   float scale;          /* finite and > 0; multiplies attention logits only (the gate is unscaled) */
   int32_t dtype;        /* moba_dtype_t of Q, K, V and O */
   int32_t routing;      /* moba_routing_t; 0 = per head */
+  int32_t kv_heads_per_pass; /* 0: the library's choice; else 1..Hkv (see below) */
 } moba_problem_t;
+
+/*
+ * Attention passes. After the selection, the history and own-block
+ * attention (with the merge) run in passes over groups of
+ * kv_heads_per_pass KV heads and their query heads; the workspace holds the
+ * history partial results (one per selected history block, fp16 + fp32 in
+ * bf16 problems, fp32 in fp32 ones) of one pass only. With 0 the library
+ * takes the largest group whose partials fit 16 GiB (at least one KV head):
+ * for the 1M-token, 32/8-head, k = 12 layer that is one KV head per pass,
+ * ~12 GB of partials instead of ~96 GB. The result does not depend on the
+ * pass size. Values outside [0, Hkv] give MOBA_ERR_INVALID_ARGUMENT. The
+ * backward entry points and moba_debug_bucket ignore the field (one pass
+ * over all heads).
+ */
 
 /*
  * Size limits of this library (MOBA_ERR_UNSUPPORTED beyond them):
@@ -122,15 +137,19 @@ MOBA_API size_t moba_select_workspace_size(const moba_problem_t *p);
 MOBA_API int moba_prefill(const moba_problem_t *p, const void *q, const void *k, const void *v, void *o,
                  void *workspace, size_t ws_bytes, void *stream);
 
-/* Stage boundaries that moba_prefill_ex can time. */
-#define MOBA_STAGE_EVENTS 7
+/*
+ * Number of stage events moba_prefill_ex records for *p: 5 + 2 x (attention
+ * passes); 0 if *p is invalid or unsupported.
+ */
+MOBA_API size_t moba_stage_events(const moba_problem_t *p);
 
 /*
  * moba_prefill with optional per-stage timing: if `events` is not NULL it
- * points to MOBA_STAGE_EVENTS caller-created hipEvent_t handles, recorded on
- * `stream` before the first stage and after each of: meanpool, gate_topk,
- * bucket, the V layout pack (bf16 only; empty for fp32), history attention,
- * own-block attention with merge. Otherwise identical to moba_prefill.
+ * points to moba_stage_events(p) caller-created hipEvent_t handles, recorded
+ * on `stream`: [0] before the first stage, then after each of [1] meanpool,
+ * [2] gate_topk, [3] bucket, [4] the V layout pack (bf16 only; empty for
+ * fp32), and for pass i: [5 + 2i] history attention, [6 + 2i] own-block
+ * attention with merge. Otherwise identical to moba_prefill.
  */
 MOBA_API int moba_prefill_ex(const moba_problem_t *p, const void *q, const void *k, const void *v, void *o,
                     void *workspace, size_t ws_bytes, void *stream, void *const *events);

@@ -36,10 +36,11 @@ def test_status_strings():
 
 
 def _prob(**kw):
-    base = dict(N=4096, Hq=8, Hkv=2, d=128, block_size=256, topk=3, scale=0.088, dtype=0)
+    base = dict(N=4096, Hq=8, Hkv=2, d=128, block_size=256, topk=3, scale=0.088, dtype=0, kvpp=0)
     base.update(kw)
     return moba.make_problem(base["N"], base["Hq"], base["Hkv"], base["d"], base["block_size"],
-                             base["topk"], base["scale"], base["dtype"])
+                             base["topk"], base["scale"], base["dtype"],
+                             kv_heads_per_pass=base["kvpp"])
 
 
 BAD = [
@@ -62,6 +63,8 @@ BAD = [
     # bf16: the packed V^T rows of a KV head would pass 2^32 bytes of 32-bit
     # buffer offsets (N * Hq * topk is still below 2^31)
     (dict(N=20_000_000, Hq=8, Hkv=8, block_size=4096, topk=12), moba.MOBA_ERR_UNSUPPORTED),
+    (dict(kvpp=-1), moba.MOBA_ERR_INVALID_ARGUMENT),
+    (dict(kvpp=3), moba.MOBA_ERR_INVALID_ARGUMENT),  # more than the 2 KV heads
 ]
 
 FAKE = 1 << 20  # a non-NULL, aligned address that is never dereferenced: every case fails first
@@ -330,3 +333,29 @@ def test_noalloc_refuses_problems_beyond_its_scratch():
     bad = _prob(N=0)
     assert lib.moba_prefill_noalloc(ctypes.byref(bad), FAKE, FAKE, FAKE, FAKE, None) == 1
     assert lib.moba_prefill_noalloc(ctypes.byref(_prob()), FAKE, None, FAKE, FAKE, None) == 1
+
+
+def test_attention_passes_cap_the_workspace():
+    """History partials are held for one attention pass (group of KV heads)
+    at a time: on the 1M-token 32/8-head k = 12 layer the library's choice is
+    one KV head per pass, eight passes, and the workspace stays under 20 GB
+    where one pass over all heads needs over 94 GiB of partials."""
+    lib = moba.load_library()
+    layer = dict(N=1 << 20, Hq=32, Hkv=8, block_size=4096, topk=12)
+    auto = _prob(**layer)
+    one = _prob(kvpp=1, **layer)
+    whole = _prob(kvpp=8, **layer)
+    ws_auto = lib.moba_workspace_size(ctypes.byref(auto))
+    assert ws_auto == lib.moba_workspace_size(ctypes.byref(one))
+    assert 0 < ws_auto < 20e9
+    assert lib.moba_workspace_size(ctypes.byref(whole)) > 94 * 2**30
+    assert lib.moba_stage_events(ctypes.byref(auto)) == 5 + 2 * 8
+    assert lib.moba_stage_events(ctypes.byref(whole)) == 7
+    assert lib.moba_stage_events(ctypes.byref(_prob(kvpp=3, **layer))) == 5 + 2 * 3
+    assert lib.moba_stage_events(ctypes.byref(_prob(kvpp=9, **layer))) == 0
+    # small problems keep one pass; the partials shrink with the pass size
+    assert lib.moba_stage_events(ctypes.byref(_prob())) == 7
+    per_kv = 4096 * 4 * 2 * (128 * 2 + 4)  # rows x G x (k-1) slots x (fp16 d + fp32)
+    full = lib.moba_workspace_size(ctypes.byref(_prob(kvpp=2)))
+    half = lib.moba_workspace_size(ctypes.byref(_prob(kvpp=1)))
+    assert full - half == per_kv

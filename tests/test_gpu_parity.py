@@ -377,7 +377,8 @@ def test_deterministic():
 
 def test_stage_events_and_copy():
     w, q, k, v, tq, tk, tv = inputs("mha8k")
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(moba.MOBA_STAGE_EVENTS)]
+    prob = moba.make_problem(w.N, w.Hq, w.Hkv, w.d, w.B, w.k, w.scale)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(moba.stage_events(prob))]
     moba.prefill(tq, tk, tv, w.B, w.k, w.scale, events=ev)
     torch.cuda.synchronize()
     times = [ev[i].elapsed_time(ev[i + 1]) for i in range(len(ev) - 1)]
@@ -386,6 +387,64 @@ def test_stage_events_and_copy():
     dst = torch.empty_like(src)
     moba.debug_copy(src, dst)
     assert torch.equal(src, dst)
+
+
+# ------------------------------------------------------- attention passes ---
+PASSES = [
+    # N, Hq, Hkv, B, topk, dtype, KV heads per pass
+    (3000, 8, 4, 256, 4, "bf16", 1),  # 64-query history engine, four passes
+    (3000, 8, 4, 256, 4, "bf16", 3),  # the last pass holds one KV head
+    (2000, 6, 3, 96, 5, "bf16", 2),   # 32-query engine (B not a multiple of 256)
+    (1500, 4, 2, 128, 3, "f32", 1),
+]
+
+
+@pytest.mark.parametrize("N,Hq,Hkv,B,topk,dtype,kvpp", PASSES)
+def test_attention_passes(N, Hq, Hkv, B, topk, dtype, kvpp):
+    """Attention in passes over groups of KV heads: the output equals the
+    one-pass output bit for bit (each (row, head) is computed by the same
+    tiles in the same order) and the oracle within the usual bars; every
+    pass records its two stage events."""
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=N + 10 * kvpp, dtype=dtype)
+    scale = 0.08
+    code = moba.MOBA_DTYPE_BF16 if dtype == "bf16" else moba.MOBA_DTYPE_F32
+    prob = moba.make_problem(N, Hq, Hkv, 128, B, topk, scale, code, kv_heads_per_pass=kvpp)
+    passes = -(-Hkv // kvpp)
+    assert moba.stage_events(prob) == 5 + 2 * passes
+    whole = moba.make_problem(N, Hq, Hkv, 128, B, topk, scale, code, kv_heads_per_pass=Hkv)
+    assert moba.workspace_size(prob) < moba.workspace_size(whole)
+    one = moba.prefill(tq, tk, tv, B, topk, scale, kv_heads_per_pass=Hkv)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(5 + 2 * passes)]
+    got = moba.prefill(tq, tk, tv, B, topk, scale, events=ev, kv_heads_per_pass=kvpp)
+    torch.cuda.synchronize()
+    assert all(ev[i].elapsed_time(ev[i + 1]) >= 0 for i in range(len(ev) - 1))
+    assert torch.equal(got, one)
+    sel = moba.select(tq, tk, B, topk).cpu().numpy()
+    rows, heads = all_rows(N, Hq)
+    (mx, mean), tied = compare_rows(q, k, v, B, topk, scale, rows, heads,
+                                    sel.reshape(-1, topk), to_np(got).reshape(-1, 128), dtype,
+                                    f"passes {kvpp}")
+    print(f"{passes} passes ({dtype}, B={B}): max|dO| {mx:.2e} mean {mean:.2e}")
+
+
+def test_attention_passes_varlen_chunk_noalloc():
+    """Packed sequences, a chunk and the allocation-free entry point in one
+    KV head per pass equal their one-pass results bit for bit."""
+    lens = [1000, 1, 0, 2500, 333, 4113]
+    cu = np.concatenate([[0], np.cumsum(lens)]).astype(np.int64)
+    N, Hq, Hkv, B, topk = int(cu[-1]), 8, 4, 256, 4
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=41)
+    a = moba.prefill_varlen(tq, tk, tv, cu, B, topk, 0.09, kv_heads_per_pass=Hkv)
+    b = moba.prefill_varlen(tq, tk, tv, cu, B, topk, 0.09, kv_heads_per_pass=1)
+    assert torch.equal(a, b)
+    C = 700
+    a = moba.prefill_chunk(tq[-C:], tk, tv, B, topk, 0.09, kv_heads_per_pass=Hkv)
+    b = moba.prefill_chunk(tq[-C:], tk, tv, B, topk, 0.09, kv_heads_per_pass=1)
+    assert torch.equal(a, b)
+    a = moba.prefill(tq, tk, tv, B, topk, 0.09, kv_heads_per_pass=Hkv)
+    b = moba.prefill_noalloc(tq, tk, tv, B, topk, 0.09, kv_heads_per_pass=2)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
 
 
 # ---------------------------------------------------------- packed (varlen) ---
