@@ -159,18 +159,41 @@ def _cpu_model():
     return None
 
 
-def cpu_baseline(w, q, k, v, rows_wanted):
-    import oracle  # the fp64 oracle: this leg only
+def cpu_sample(w, rows_wanted):
+    """The seeded (row, head) pairs of the CPU leg: every block, both edges."""
     rows, heads = synth.sample_rows(w, 4096)
-    sel = np.linspace(0, len(rows) - 1, rows_wanted).astype(np.int64)
-    rows, heads = rows[sel], heads[sel]
+    pick = np.linspace(0, len(rows) - 1, min(rows_wanted, len(rows))).astype(np.int64)
+    return rows[pick], heads[pick]
+
+
+def cpu_baseline(w, q, k, v, rows_wanted, gpu=None):
+    """The oracle timed on the host over a seeded sample of (row, head) pairs;
+    with ``gpu = (sel, o)``, the timed steps' selection and output at those
+    pairs (fetched after the timed region), the same evaluation also gives
+    the parity figures of the bench line."""
+    import oracle  # the fp64 oracle: this leg only
+    rows, heads = cpu_sample(w, rows_wanted)
     threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
     kbar = oracle.block_means(k, w.B)
     t1 = time.perf_counter()
-    oracle.rows(q, k, v, w.B, w.k, rows, heads, scale=w.scale, kbar=kbar, nthreads=threads)
+    ref_sel, ref_o, gap = oracle.rows(q, k, v, w.B, w.k, rows, heads, scale=w.scale, kbar=kbar,
+                                      nthreads=threads)
     t2 = time.perf_counter()
     tok_s = (len(rows) / w.Hq) / (t2 - t1)
+    parity = None
+    if gpu is not None:
+        got_sel, got_o = gpu
+        same = (got_sel == ref_sel).all(axis=1)
+        d = np.abs(got_o - ref_o)[same]
+        parity = {"pairs": int(len(rows)), "selection_equal_pairs": int(same.sum()),
+                  "selection_differs_pairs": int((~same).sum()),
+                  "max_abs_dO": float(d.max()) if d.size else None,
+                  "mean_abs_dO": float(d.mean()) if d.size else None,
+                  "bars": "bf16: max <= 1e-2, mean <= 1e-3 (the GPU tests' bars)",
+                  "note": "fp64 oracle on the seeded sample (every block, both block edges), "
+                          "against the last timed step's O; |dO| over the pairs whose selection "
+                          "equals the oracle's"}
     return {
         "value": tok_s, "unit": "tokens/s", "cores": threads, "kind": "oracle",
         "cpu_model": _cpu_model(),
@@ -178,7 +201,85 @@ def cpu_baseline(w, q, k, v, rows_wanted):
         "sample": (f"{len(rows)} seeded (row, head) pairs of the same layer spread over all blocks; "
                    f"value = pairs/{w.Hq} per second of the fp64 dense-masked row evaluation; the "
                    f"one-time fp64 block means took {t1 - t0:.2f} s and are not in the rate"),
+    }, parity
+
+
+def routing_summary(st, w):
+    """Summaries of moba_routing_stats over the whole layer: the histogram of
+    selection margins (last kept minus best left-out gate score, absolute,
+    per (row, head)), rows inside the tie band, how much the heads of one
+    group agree and how the selections spread over blocks."""
+    margin = st["margin"].float()
+    fin = margin[torch.isfinite(margin)]
+    edges = [0.0, 1e-6, 1e-5, 1e-4, 1e-3, 1e-2, 1e-1, 1.0, 10.0, float("inf")]
+    hist = [int(((fin >= a) & (fin < b)).sum()) for a, b in zip(edges[:-1], edges[1:])]
+    G = w.Hq // w.Hkv
+    rows = torch.arange(w.N, device=margin.device)
+    hist_sel = torch.clamp(rows // w.B, max=w.k - 1)  # history blocks per (row, head)
+    union = st["union_size"].float()
+    full = hist_sel.float().unsqueeze(1) * G  # union if the G heads chose disjoint sets
+    has = hist_sel > 0
+    overlap = (union[has] / full[has].clamp(min=1)).mean()
+    counts = st["counts"].double()
+    tot = counts.sum(dim=1, keepdim=True)
+    n = counts.shape[1]
+    # selections a block could receive: its later rows x heads of the group
+    nh = n - 1
+    per_block = counts[:, :nh]
+    top = torch.sort(per_block.flatten(), descending=True).values
+    return {
+        "margin_histogram": {"edges": edges[:-1] + ["inf"], "counts": hist,
+                             "nothing_left_out": int((~torch.isfinite(margin)).sum())},
+        "median_selection_margin": float(fin.median()) if fin.numel() else None,
+        "tie_band_pairs_1e-5_abs": int((fin < 1e-5).sum()),
+        "group_union_over_disjoint": float(overlap),
+        "group_union_note": f"distinct history blocks of a KV head's {G} query heads / "
+                            f"({G} x their history count): 1/{G} = all heads agree, 1 = disjoint",
+        "block_frequency": {
+            "history_selections": int(tot.sum()),
+            "max_over_mean": float(per_block.max() / per_block.mean()),
+            "top_1pct_share": float(top[: max(1, top.numel() // 100)].sum() / top.sum()),
+            "never_selected_blocks": int((per_block == 0).sum()),
+            "block0_share": float(per_block[:, 0].sum() / per_block.sum()),
+        },
     }
+
+
+def small_configs():
+    """Per-stage times of the smaller parity configurations (secondary rows:
+    launch-bound, reported rather than targeted)."""
+    rows = {}
+    for name in ("tiny2k", "mha8k", "mha32k_needles", "coarse32k"):
+        ws_ = synth.CONFIGS[name]
+        dt = "bf16" if ws_.dtype == "bf16" else "f32"
+        a, b, c = (to_dev(x) for x in synth.make_qkv(ws_, dt))
+        pr = moba.make_problem(ws_.N, ws_.Hq, ws_.Hkv, ws_.d, ws_.B, ws_.k, ws_.scale,
+                               moba.MOBA_DTYPE_BF16 if dt == "bf16" else moba.MOBA_DTYPE_F32)
+        wsp = moba.alloc_workspace(moba.workspace_size(pr), a.device)
+        o = torch.empty_like(a)
+        nev = moba.stage_events(pr)
+        passes = (nev - 5) // 2
+        for _ in range(3):
+            moba.prefill(a, b, c, ws_.B, ws_.k, ws_.scale, out=o, workspace=wsp)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(nev)] for _ in range(10)]
+        for ev in evs:
+            moba.prefill(a, b, c, ws_.B, ws_.k, ws_.scale, out=o, workspace=wsp, events=ev)
+        torch.cuda.synchronize()
+        span = {s: [(i, i + 1)] for i, s in enumerate(STAGES[:4])}
+        span["attn_hist"] = [(4 + 2 * i, 5 + 2 * i) for i in range(passes)]
+        span["attn_self_merge"] = [(5 + 2 * i, 6 + 2 * i) for i in range(passes)]
+        st = {s: float(np.median([sum(ev[x].elapsed_time(ev[y]) for x, y in span[s])
+                                  for ev in evs])) for s in STAGES}
+        tot = float(np.median([ev[0].elapsed_time(ev[-1]) for ev in evs]))
+        own, hist = pair_counts(ws_)
+        rows[name] = {"workload": f"N={ws_.N} Hq={ws_.Hq} Hkv={ws_.Hkv} d={ws_.d} B={ws_.B} "
+                                  f"topk={ws_.k} {dt}",
+                      "ms": tot, "tokens_per_s": ws_.N / (tot / 1e3),
+                      "attended_tflops": 4.0 * ws_.d * ws_.Hq * (own + hist) / (tot / 1e3) / 1e12,
+                      "stage_ms": st, "timing": "median of 10 event-timed calls"}
+        del a, b, c, o, wsp
+    return rows
 
 
 def backward_leg(name="mha32k_needles", reps=5):
@@ -284,7 +385,9 @@ def main():
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--config", default="llama8b_1m", choices=sorted(synth.CONFIGS))
-    ap.add_argument("--cpu-rows", type=int, default=1024)
+    ap.add_argument("--cpu-rows", type=int, default=4096)
+    ap.add_argument("--no-small", action="store_true",
+                    help="skip the per-stage rows of the smaller parity configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--no-varlen", action="store_true",
@@ -374,6 +477,18 @@ def main():
     print(f"[bench] {args.steps} steps: {ms_per_step:.2f} ms/step, stages {stage_ms}",
           file=sys.stderr, flush=True)
 
+    gpu_sample = None
+    if not args.no_cpu_baseline:
+        # the timed steps' output and selection at the CPU leg's pairs, read
+        # back now (later legs reuse the output buffer)
+        srows, sheads = cpu_sample(w, args.cpu_rows)
+        ir, ih = torch.from_numpy(srows).to(tq.device), torch.from_numpy(sheads.astype(np.int64)).to(tq.device)
+        got_o = out[ir, ih].double().cpu().numpy()
+        selt = moba.select(tq, tk, w.B, w.k)
+        got_sel = selt[ir, ih].cpu().numpy()
+        del selt
+        gpu_sample = (got_sel, got_o)
+
     own, hist = pair_counts(w)
     flop_total = 4.0 * w.d * w.Hq * (own + hist)
     flop_hist = 4.0 * w.d * w.Hq * hist
@@ -440,11 +555,9 @@ def main():
         e1.record()
         torch.cuda.synchronize()
         stats_ms = e0.elapsed_time(e1)
-        margin = st["margin"].float()
-        fin = margin[torch.isfinite(margin)]
         shared = {"ms": sms, "tokens_per_s": w.N / (sms / 1e3),
                   "routing_stats_ms": stats_ms,
-                  "median_selection_margin": float(fin.median()) if fin.numel() else None}
+                  "routing_stats": routing_summary(st, w)}
         del st
 
     backward = backward_large = None
@@ -452,11 +565,13 @@ def main():
         backward = backward_leg()
         backward_large = backward_leg("llama8b_128k", reps=3)
 
+    small = None if args.no_small else small_configs()
+
     peaks = None if args.no_peaks else measured_peaks()
 
-    cpu = None
+    cpu = parity = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(w, q, k, v, args.cpu_rows)
+        cpu, parity = cpu_baseline(w, q, k, v, args.cpu_rows, gpu_sample)
 
     rec = {
         "metric": METRIC,
@@ -504,6 +619,8 @@ def main():
         "chunked": chunk,
         "backward": backward,
         "backward_llama8b_128k": backward_large,
+        "small_configs": small,
+        "parity": parity,
         "cpu_baseline": cpu,
     }
     print(json.dumps(rec), flush=True)
