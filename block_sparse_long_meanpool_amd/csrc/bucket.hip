@@ -29,15 +29,28 @@ constexpr int kScanRowGroups = 16;
 // s < k-1 (the row's own block, always its largest, and -1 pads are not).
 __device__ inline bool hist_entry(int32_t b, int64_t c) { return b >= 0 && b < c; }
 
+// Chunk of rows and KV head of workgroup w (1-D grid of ceil(nchunk / 8) * 8
+// * Hkv). Workgroup w runs on XCD w % 8; in each run of 8 * Hkv workgroups
+// XCD x takes the Hkv heads of chunk 8 * run + x, so the workgroups that
+// read the same selection rows (each its head group's part of every row)
+// share one L2 and fetch each cache line of those rows from memory once.
+__device__ inline bool chunk_of(int64_t w, int Hkv, int64_t nchunk, int64_t& chunk, int& g) {
+  const int64_t run = w / (8 * Hkv), in = w % (8 * Hkv);
+  g = (int)(in / 8);
+  chunk = run * 8 + in % 8;
+  return chunk < nchunk;
+}
+
 __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restrict__ sel,
                                                          const int32_t* __restrict__ row_blk,
                                                          int32_t* __restrict__ chunk_base,
                                                          int64_t N, int Hq, int G, int k,
                                                          int64_t nh, int rows_per_chunk,
-                                                         int64_t nchunk) {
+                                                         int64_t nchunk, int Hkv) {
   extern __shared__ int32_t hist[];
-  const int g = blockIdx.y;
-  const int64_t chunk = blockIdx.x;
+  int g;
+  int64_t chunk;
+  if (!chunk_of(blockIdx.x, Hkv, nchunk, chunk, g)) return;
   for (int64_t b = threadIdx.x; b < nh; b += kThreads) hist[b] = 0;
   __syncthreads();
   const int KH = k - 1;
@@ -145,12 +158,13 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     uint32_t* __restrict__ entries, int64_t N, int Hq, int Hkv, int G, int k, int64_t nh,
     int rows_per_chunk, int64_t nchunk, int words, int kvpp) {
   extern __shared__ uint32_t bm[];  // [nh][words] bitmaps, then [nh][words] prefix counts
-  const int g = blockIdx.y;
+  int g;
+  int64_t chunk;
+  if (!chunk_of(blockIdx.x, Hkv, nchunk, chunk, g)) return;
   // the attention pass of KV head g: query heads [h0, h0 + Hs)
   const int g0 = (g / kvpp) * kvpp;
   const int h0 = g0 * G;
   const int64_t Hs = (int64_t)(Hkv - g0 < kvpp ? Hkv - g0 : kvpp) * G;
-  const int64_t chunk = blockIdx.x;
   const int64_t nw = nh * words;
   uint32_t* pre = bm + nw;  // pre[b][w] = entries of bin b in words 0..w-1
   for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
@@ -231,9 +245,10 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
     if (e == hipSuccess) e = launch_fill_i32(b.scalars, 0, 4, s);
     return e;
   }
-  dim3 grid((unsigned)bp.nchunk, (unsigned)P.Hkv);
+  const unsigned grid = (unsigned)(ceil_div(bp.nchunk, 8) * 8 * P.Hkv);
   bucket_count<<<grid, kThreads, sizeof(int32_t) * P.nh, s>>>(
-      sel, T.row_blk, b.chunk_base, P.Nq, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk);
+      sel, T.row_blk, b.chunk_base, P.Nq, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk,
+      P.Hkv);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   bucket_scan_cols<<<(unsigned)ceil_div(bp.nbins, 16), kThreads, 0, s>>>(b.chunk_base, b.bin_total,

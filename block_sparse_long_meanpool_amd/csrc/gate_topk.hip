@@ -167,6 +167,32 @@ struct KeyList {
       k[t] = hi;
     }
   }
+  // Merge another descending list of KM keys (disjoint from this one): the
+  // top KM of both are m_t = max(k[t], o[KM-1-t]), a bitonic sequence, which
+  // one bitonic merge (with maximal pads first) sorts. Same result as KM
+  // push() calls.
+  __device__ inline void merge(const uint32_t (&o)[KM]) {
+    constexpr int P = KM <= 4 ? 8 : KM <= 12 ? 16 : KM <= 16 ? 32 : 64;  // room for >= 1 pad
+    constexpr int PADS = P - KM;
+    uint32_t m[P];
+#pragma unroll
+    for (int t = 0; t < KM; ++t) m[t] = k[t] > o[KM - 1 - t] ? k[t] : o[KM - 1 - t];
+#pragma unroll
+    for (int t = KM; t < P; ++t) m[t] = 0xFFFFFFFFu;  // above every real key
+#pragma unroll
+    for (int stride = P >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const uint32_t hi = m[i] > m[j] ? m[i] : m[j], lo = m[i] > m[j] ? m[j] : m[i];
+          m[i] = hi;
+          m[j] = lo;
+        }
+      }
+#pragma unroll
+    for (int t = 0; t < KM; ++t) k[t] = m[PADS + t];
+  }
   // Add 16 keys at once: sort them descending with a bitonic network; then
   // m_t = max(k[t], c[KM-1-t]) is exactly the top KM of both lists (two
   // sorted lists, one read backwards) and is decreasing-then-increasing, so
@@ -214,16 +240,32 @@ struct KeyList {
   }
 };
 
-// out[0..n) = the n block indices of idx[0..n) in ascending order (n <= KM).
+// out[0..n) = the n block indices of idx[0..n) in ascending order (n <= KM,
+// indices distinct): a bitonic sorting network over the next power of two,
+// entries past n padded with INT_MAX (they sort last and are not written).
 template <int KM>
 __device__ inline void write_sorted(const int (&idx)[KM], int n, int32_t* out) {
+  constexpr int P = KM <= 4 ? 4 : KM <= 8 ? 8 : KM <= 16 ? 16 : 32;
+  int a[P];
 #pragma unroll
-  for (int a = 0; a < KM; ++a) {
-    int rank = 0;
+  for (int t = 0; t < P; ++t) a[t] = (t < KM && t < n) ? idx[t < KM ? t : 0] : 0x7FFFFFFF;
 #pragma unroll
-    for (int b = 0; b < KM; ++b) rank += (b < n && idx[b] < idx[a]) ? 1 : 0;
-    if (a < n) out[rank] = idx[a];
-  }
+  for (int size = 2; size <= P; size <<= 1)
+#pragma unroll
+    for (int stride = size >> 1; stride > 0; stride >>= 1)
+#pragma unroll
+      for (int i = 0; i < P; ++i) {
+        const int j = i ^ stride;
+        if (j > i) {
+          const int lo = a[i] < a[j] ? a[i] : a[j], hi = a[i] < a[j] ? a[j] : a[i];
+          const bool up = (i & size) == 0;  // the last stage sorts all P ascending
+          a[i] = up ? lo : hi;
+          a[j] = up ? hi : lo;
+        }
+      }
+#pragma unroll
+  for (int t = 0; t < KM; ++t)
+    if (t < n) out[t] = a[t];
 }
 
 // Issue the copy of planes of blocks [cb, cb + 32) (clamped to nh) into one LDS buffer.
@@ -254,6 +296,11 @@ __device__ inline void wait_chunk() {
 __device__ inline void chunk_scores(const uint16_t* lds, const bf16x8 (&q)[8], int lane,
                                     f32x16& s) {
   const int h = lane >> 5, lr = lane & 31;
+  // the rows' swizzle keys, opaque to the compiler so that it forms the 24
+  // operand addresses here, per chunk, instead of keeping them all live
+  // across the chunk loop
+  int z0 = (3 * lr) & 15, z1 = (3 * lr + 1) & 15, z2 = (3 * lr + 2) & 15;
+  asm volatile("" : "+v"(z0), "+v"(z1), "+v"(z2));
   f32x16 a0, a0b, a1, a2;
 #pragma unroll
   for (int r = 0; r < 16; ++r) a0[r] = a0b[r] = a1[r] = a2[r] = 0.f;
@@ -261,9 +308,9 @@ __device__ inline void chunk_scores(const uint16_t* lds, const bf16x8 (&q)[8], i
   for (int kk = 0; kk < 8; ++kk) {
     const int c = 2 * kk + h;
     const int r0 = 3 * lr, r1 = 3 * lr + 1, r2 = 3 * lr + 2;
-    const bf16x8 x0 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r0 * kHeadDim + 8 * swz(r0, c)));
-    const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r1 * kHeadDim + 8 * swz(r1, c)));
-    const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r2 * kHeadDim + 8 * swz(r2, c)));
+    const bf16x8 x0 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r0 * kHeadDim + 8 * (c ^ z0)));
+    const bf16x8 x1 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r1 * kHeadDim + 8 * (c ^ z1)));
+    const bf16x8 x2 = as_bf16x8(*reinterpret_cast<const uint4*>(lds + r2 * kHeadDim + 8 * (c ^ z2)));
     if (kk < 4)
       a0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(x0, q[kk], a0, 0, 0, 0);
     else
@@ -577,7 +624,10 @@ __global__ __launch_bounds__(256) void gate_refine_few(const T* __restrict__ Q,
 }
 
 template <int KM, bool SHARED>
-__global__ __launch_bounds__(kThreads) void gate_topk_kernel(
+// Per-head routing asks for three waves per SIMD (three workgroups per
+// compute unit; 48 KB of LDS each).
+__global__ __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(SHARED ? 1 : 3, SHARED ? 2 : 3))) void gate_topk_kernel(
     const uint16_t* __restrict__ Q, const uint16_t* __restrict__ planes,
     const float* __restrict__ maxnorm, const int32_t* __restrict__ qstart,
     const int32_t* __restrict__ qlen, const int32_t* __restrict__ blo, int32_t* __restrict__ sel,
@@ -703,8 +753,7 @@ __global__ __launch_bounds__(kThreads) void gate_topk_kernel(
   uint32_t other[KM];  // the partner's list as it was, before any merging
 #pragma unroll
   for (int t = 0; t < KM; ++t) other[t] = __shfl_xor(L.k[t], 32);
-#pragma unroll
-  for (int t = 0; t < KM; ++t) L.push(other[t]);
+  L.merge(other);
 
   // certification: kept (top KH) vs best left out. Decoded scores are at most
   // 2^ib units in the last place below the fp32 ones; the fp32 ones are within
