@@ -359,3 +359,10 @@ def test_attention_passes_cap_the_workspace():
     full = lib.moba_workspace_size(ctypes.byref(_prob(kvpp=2)))
     half = lib.moba_workspace_size(ctypes.byref(_prob(kvpp=1)))
     assert full - half == per_kv
+
+
+def test_value_range_limit_is_documented():
+    """The bf16 path keeps normalised partial rows in fp16: the header states
+    the resulting bound on |V| (the GPU suite checks values just below it)."""
+    text = open(os.path.join(ROOT, "include", "moba.h")).read()
+    assert "|V| must stay below 65504" in text

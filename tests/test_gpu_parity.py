@@ -354,6 +354,30 @@ def test_softmax_overflow_rerun(B):
                  to_np(o).reshape(-1, 128), "bf16", "spike keys")
 
 
+@pytest.mark.parametrize("B", [128, 256])
+def test_values_near_the_fp16_partial_limit(B):
+    """bf16 values up to 0.9 x 65504: the fp16 partial rows (history and the
+    own-block staging, both convex combinations of V rows) stay finite and O
+    matches the oracle at the usual bars relative to the value scale. Both
+    history engines (B = 128: 32-query, B = 256: 64-query)."""
+    N, Hq, Hkv, topk = 2048, 4, 2, 3
+    q, k, v, _, _, _ = small(N, Hq, Hkv, B, topk, seed=77)
+    big = np.float32(0.9 * 65504.0)
+    vf = np.random.default_rng(77).uniform(-1.0, 1.0, size=v.shape).astype(np.float32) * big
+    v = synth.f32_to_bf16(vf)
+    assert float(np.abs(synth.bf16_to_f32(v)).max()) < 65504.0
+    tq, tk, tv = to_dev(q), to_dev(k), to_dev(v)
+    scale = 0.09
+    o = moba.prefill(tq, tk, tv, B, topk, scale)
+    assert bool(torch.isfinite(o.float()).all())
+    sel = moba.select(tq, tk, B, topk).cpu().numpy()
+    rows, heads = all_rows(N, Hq)
+    ref_sel, ref_o, gap = oracle.rows(q, k, v, B, topk, rows, heads, scale=scale)
+    assert np.array_equal(sel.reshape(-1, topk), ref_sel)
+    check_output(to_np(o).reshape(-1, 128) / float(big), ref_o / float(big), "bf16",
+                 "values near the fp16 limit")
+
+
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_dense_baseline_and_full_coverage(dtype):
     """k covering every block equals causal full attention, and so does the dense kernel."""
