@@ -370,12 +370,12 @@ def _chunk_problem(q, k, block_size, topk, scale, routing, kv_heads_per_pass=0):
 
 
 def prefill_train(q, k, v, block_size, topk, scale=None, routing=MOBA_ROUTING_PER_HEAD,
-                  workspace=None):
+                  workspace=None, kv_heads_per_pass=0):
     """Forward for training: (O [N, Hq, d], lse [N, Hq] fp32), lse being each
     row's log2-sum-exp of scale*log2(e)*q.k over its keys."""
     lib = load_library()
     _check_dev(q, k, v)
-    prob = _problem_from(q, k, block_size, topk, scale, routing)
+    prob = _problem_from(q, k, block_size, topk, scale, routing, kv_heads_per_pass)
     out = torch.empty_like(q)
     lse = torch.empty(q.shape[:2], dtype=torch.float32, device=q.device)
     need = lib.moba_workspace_size(ctypes.byref(prob))

@@ -156,8 +156,12 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ row_blk,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ bin_off,
     uint32_t* __restrict__ entries, int64_t N, int Hq, int Hkv, int G, int k, int64_t nh,
-    int rows_per_chunk, int64_t nchunk, int words, int kvpp) {
-  extern __shared__ uint32_t bm[];  // [nh][words] bitmaps, then [nh][words] prefix counts
+    int rows_per_chunk, int64_t nchunk, int words, int ws, int kvpp) {
+  // [nh][ws] bitmaps, then [nh][ws] prefix counts. The row stride ws is odd
+  // where that fits (it spreads the words of different bins over the banks:
+  // with stride 32 the 64 lanes of one slot's atomics, each at a random bin
+  // but one of two words, land on at most four banks).
+  extern __shared__ uint32_t bm[];
   int g;
   int64_t chunk;
   if (!chunk_of(blockIdx.x, Hkv, nchunk, chunk, g)) return;
@@ -165,7 +169,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
   const int g0 = (g / kvpp) * kvpp;
   const int h0 = g0 * G;
   const int64_t Hs = (int64_t)(Hkv - g0 < kvpp ? Hkv - g0 : kvpp) * G;
-  const int64_t nw = nh * words;
+  const int64_t nw = nh * ws;
   uint32_t* pre = bm + nw;  // pre[b][w] = entries of bin b in words 0..w-1
   for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
   __syncthreads();
@@ -179,15 +183,15 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     const int32_t* row = sel + ((size_t)r * Hq + h) * k;
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
-      if (hist_entry(b, c)) atomicOr(&bm[(size_t)b * words + (pi >> 5)], 1u << (pi & 31));
+      if (hist_entry(b, c)) atomicOr(&bm[(size_t)b * ws + (pi >> 5)], 1u << (pi & 31));
     }
   }
   __syncthreads();
   for (int64_t b = threadIdx.x; b < nh; b += kThreads) {
     uint32_t run = 0;
     for (int w = 0; w < words; ++w) {
-      pre[b * words + w] = run;
-      run += __popc(bm[b * words + w]);
+      pre[b * ws + w] = run;
+      run += __popc(bm[b * ws + w]);
     }
   }
   __syncthreads();
@@ -203,7 +207,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     for (int s = 0; s < KH; ++s) {
       const int32_t b = row[s];
       if (!hist_entry(b, c)) continue;
-      const size_t wi = (size_t)b * words + (pi >> 5);
+      const size_t wi = (size_t)b * ws + (pi >> 5);
       const int rank = (int)pre[wi] + __popc(bm[wi] & ((1u << (pi & 31)) - 1u));
       entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(pslot + s);
     }
@@ -222,13 +226,16 @@ __global__ __launch_bounds__(kThreads) void bucket_tile_map(const int32_t* __res
 BucketPlan plan_bucket(const Prob& P) {
   BucketPlan bp{};
   const int64_t nh = P.nh > 0 ? P.nh : 1;
-  int64_t wmax = 8192 / nh;
+  int64_t wmax = 8192 / nh - 1;  // room for a padded stride (at least one word)
   if (wmax > 32) wmax = 32;
   if (wmax < 1) wmax = 1;
   int64_t rpc = (32 * wmax) / P.G;
   if (rpc < 1) rpc = 1;
   bp.rows_per_chunk = (int)rpc;
   bp.words = (int)ceil_div(rpc * P.G, 32);
+  // an odd bitmap stride (padded by one word when even) while the two
+  // arrays stay within 64 KB
+  bp.ws = nh * (bp.words | 1) <= 8192 ? (bp.words | 1) : bp.words;
   bp.nchunk = ceil_div(P.Nq, rpc);
   bp.nbins = (int64_t)P.Hkv * P.nh;
   bp.max_entries = P.hist_rows * P.Hq;
@@ -257,9 +264,9 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
   bucket_scan_bins<<<1, 1024, 0, s>>>(b.bin_total, b.bin_off, b.tile_off, b.scalars, bp.nbins,
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bucket_scatter<<<grid, kThreads, 2 * sizeof(uint32_t) * P.nh * bp.words, s>>>(
+  bucket_scatter<<<grid, kThreads, 2 * sizeof(uint32_t) * P.nh * bp.ws, s>>>(
       sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.Hkv, P.G, P.k, P.nh,
-      bp.rows_per_chunk, bp.nchunk, bp.words, P.kvpp);
+      bp.rows_per_chunk, bp.nchunk, bp.words, bp.ws, P.kvpp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (b.tile_map) {
     bucket_tile_map<<<(unsigned)bp.nbins, kThreads, 0, s>>>(b.tile_off, b.tile_map);

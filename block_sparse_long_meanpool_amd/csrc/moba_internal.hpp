@@ -81,6 +81,7 @@ struct BucketPlan {
   int rows_per_chunk;  // rows of one KV head group per counting chunk
   int64_t nchunk;      // chunks per KV head = ceil(N / rows_per_chunk)
   int words;           // 32-bit bitmap words per bin in a chunk
+  int ws;              // their row stride in LDS (odd where it fits)
   int64_t nbins;       // Hkv * nh
   int64_t max_entries; // Hq * sum_p min(k-1, c(p))
   int64_t max_tiles;   // bound on sum_b ceil(count_b / kTileQ)

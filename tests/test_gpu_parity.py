@@ -451,6 +451,23 @@ def test_attention_passes(N, Hq, Hkv, B, topk, dtype, kvpp):
     print(f"{passes} passes ({dtype}, B={B}): max|dO| {mx:.2e} mean {mean:.2e}")
 
 
+def test_attention_passes_training_forward_and_shared_routing():
+    """The training forward (O and the row log-sum-exps the backward reads)
+    and group-shared routing in one KV head per pass equal their one-pass
+    results bit for bit."""
+    N, Hq, Hkv, B, topk = 3000, 8, 4, 256, 4
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=43)
+    o1, l1 = moba.prefill_train(tq, tk, tv, B, topk, 0.09, kv_heads_per_pass=Hkv)
+    o2, l2 = moba.prefill_train(tq, tk, tv, B, topk, 0.09, kv_heads_per_pass=1)
+    assert torch.equal(o1, o2) and torch.equal(l1, l2)
+    a = moba.prefill(tq, tk, tv, B, topk, 0.09, routing=moba.MOBA_ROUTING_SHARED,
+                     kv_heads_per_pass=Hkv)
+    b = moba.prefill(tq, tk, tv, B, topk, 0.09, routing=moba.MOBA_ROUTING_SHARED,
+                     kv_heads_per_pass=1)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
 def test_attention_passes_varlen_chunk_noalloc():
     """Packed sequences, a chunk and the allocation-free entry point in one
     KV head per pass equal their one-pass results bit for bit."""
