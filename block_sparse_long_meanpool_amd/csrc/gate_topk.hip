@@ -172,7 +172,7 @@ struct KeyList {
   // one bitonic merge (with maximal pads first) sorts. Same result as KM
   // push() calls.
   __device__ inline void merge(const uint32_t (&o)[KM]) {
-    constexpr int P = KM <= 4 ? 8 : KM <= 12 ? 16 : KM <= 16 ? 32 : 64;  // room for >= 1 pad
+    constexpr int P = KM < 8 ? 8 : KM < 16 ? 16 : KM < 32 ? 32 : 64;  // room for >= 1 pad
     constexpr int PADS = P - KM;
     uint32_t m[P];
 #pragma unroll
@@ -214,7 +214,7 @@ struct KeyList {
             c[j] = desc ? lo : hi;
           }
         }
-    constexpr int P = KM <= 4 ? 8 : KM <= 12 ? 16 : KM <= 16 ? 32 : 64;  // room for >= 1 pad
+    constexpr int P = KM < 8 ? 8 : KM < 16 ? 16 : KM < 32 ? 32 : 64;  // room for >= 1 pad
     constexpr int PADS = P - KM;
     uint32_t m[P];
 #pragma unroll
@@ -352,6 +352,12 @@ __device__ inline void chunk_scores_shared(const uint16_t* lds, const bf16x8 (&q
 }
 
 constexpr int32_t kRefine = -2;  // sel marker: this row's history needs the exact tier
+// sel record of an uncertified row whose undecided blocks are all in the fast
+// tier's list: entry 0 = kBand - (n_in << 8 | n_end), entries 1.. hold the
+// list's first n_end block indices, two 16-bit halves per entry, in fast
+// order: n_in blocks certainly kept, then the band whose exact scores decide
+// the remaining k-1-n_in places (every other block is certainly left out).
+constexpr int32_t kBand = -(1 << 20);
 
 template <typename T>
 __device__ inline double widen(T x);
@@ -370,7 +376,8 @@ __device__ inline double widen<double>(double x) {
 
 // Exact tier: one wave per ppw consecutive (row, head) pairs (64; a few
 // rows use gate_refine_few instead); each marked row
-// (or, with all_rows, every row) is re-scored in fp64 — lane b handles blocks
+// (or, with all_rows, every row) is re-scored in fp64 (a row with a band
+// record only over its band, see kBand) — lane b handles blocks
 // b, b+64, ... reading the transposed block keys (coalesced) against q
 // staged in LDS — and selected by (value desc, index asc): each lane keeps a
 // sorted list of its blocks (they arrive in increasing order), then KH rounds
@@ -400,7 +407,8 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     if (lane < ppw && ph < nph) {
       const int64_t c = row_blk[ph / Hq], lo = blo[c];
       if (c - lo > KH && KH > 0) {
-        mine = all_rows || sel[ph * gq * k] == kRefine;
+        const int32_t rec = sel[ph * gq * k];
+        mine = all_rows || rec == kRefine || (rec <= kBand && rec > kBand - 65536);
       } else if (all_rows) {  // every earlier block of the sequence is taken
         const int nsel = (int)(c - lo < KH ? c - lo : KH);
         for (int hh = 0; hh < gq; ++hh) {
@@ -429,6 +437,60 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
     qs[2 * lane] = q0;
     qs[2 * lane + 1] = q1;
     __syncthreads();
+    const double* kt = kbarT + (int64_t)g * kHeadDim * nhp;
+    const int32_t rec = all_rows ? 0 : sel[ph * gq * k];
+    if (rec <= kBand && rec > kBand - 65536) {
+      // Band record: the first n_in listed blocks are kept, and the best
+      // KH - n_in of the listed blocks [n_in, n_end) by (exact score desc,
+      // index asc) fill the other places. Lane t holds listed block t; the
+      // band's lanes score their block in the same order of operations as
+      // the full path below, so either path gives the same values.
+      const int code = kBand - rec, n_in = code >> 8, n_end = code & 0xFF;
+      const int32_t* recp = sel + ph * gq * k;
+      int id = 0x7FFFFFFF;
+      if (lane < n_end)
+        id = (int)(((uint32_t)recp[1 + (lane >> 1)] >> (16 * (lane & 1))) & 0xFFFFu);
+      bool cand = lane >= n_in && lane < n_end, kept = lane < n_in;
+      double x = -INFINITY;
+      if (cand) {
+        double acc = 0.0;
+#pragma unroll 16
+        for (int d = 0; d < kHeadDim; ++d) acc = fma(qs[d], kt[(int64_t)d * nhp + id], acc);
+        x = acc;
+      }
+      for (int rnd = n_in; rnd < KH; ++rnd) {
+        double bv = cand ? x : -INFINITY;
+        int bi = cand ? id : 0x7FFFFFFF;
+#pragma unroll
+        for (int off = 32; off >= 1; off >>= 1) {
+          const double ov = __shfl_xor(bv, off);
+          const int oi = __shfl_xor(bi, off);
+          if (ov > bv || (ov == bv && oi < bi)) {
+            bv = ov;
+            bi = oi;
+          }
+        }
+        if (cand && id == bi) {
+          cand = false;
+          kept = true;
+        }
+      }
+      // each kept block's place in the ascending row: kept blocks below it
+      int pos = 0;
+      for (int t = 0; t < n_end; ++t) {
+        const int oid = __shfl(id, t);
+        const int ok = __shfl((int)kept, t);
+        pos += (ok && oid < id) ? 1 : 0;
+      }
+      for (int hh = 0; hh < gq; ++hh) {
+        int32_t* out = sel + (ph * gq + hh) * k;
+        if (kept) out[pos] = id;
+        if (lane == 0) out[KH] = (int32_t)c;
+        if (lane > KH && lane < k) out[lane] = -1;
+      }
+      __syncthreads();  // qs is rewritten for the next row
+      continue;
+    }
     double v[KM];
     int ix[KM];
 #pragma unroll
@@ -436,7 +498,6 @@ __global__ __launch_bounds__(64) void gate_refine(const T* __restrict__ Q,
       v[t] = -INFINITY;
       ix[t] = 0x7FFFFFFF;
     }
-    const double* kt = kbarT + (int64_t)g * kHeadDim * nhp;
     for (int64_t b = lo + lane; b < c; b += 64) {
       double acc = 0.0;
 #pragma unroll 16
@@ -771,6 +832,28 @@ __attribute__((amdgpu_waves_per_eu(SHARED ? 1 : 3, SHARED ? 2 : 3))) void gate_t
   const float trunc = ldexpf(big, ib - 22);  // >= 2^ib units in the last place of |score| <= big
   const float eps = (SHARED ? kEpsCoefShared : kEpsCoef) * sqrtf(qq) * 1.0001f * kmax;
   const bool certified = (theta - theta_n) > 2.f * eps + trunc + 1e-6f * big;
+  // Uncertified: the blocks the exact tier has to decide. With margins as
+  // above, list entry t < KH is certainly kept when its score exceeds the
+  // (KH+1)-th by more than the certification margin (it beats every block
+  // from rank KH+1 on), and entry t >= KH is certainly left out when the
+  // KH-th exceeds it by the margin of its own magnitude (every one of the top
+  // KH beats it); both sets are runs of the descending list. Blocks outside
+  // the list score at most the list's last entry, so they are left out when
+  // the left-out run starts inside the list (or the list holds every
+  // candidate).
+  const float m_in = 2.f * eps + trunc + 1e-6f * big;
+  const int n_real = (int)(nc < KM ? nc : KM);
+  int n_in = 0, n_end = n_real;
+#pragma unroll
+  for (int t = 0; t < KM; ++t) {
+    const float ph = key_score(L.k[t], ib);
+    if (t < KH && t == n_in && ph - theta_n > m_in) n_in = t + 1;
+    const float mag = fmaxf(big, fabsf(ph));
+    if (t >= KH && t < n_real && n_end == n_real &&
+        theta - ph > 2.f * eps + ldexpf(mag, ib - 22) + 1e-6f * mag)
+      n_end = t;
+  }
+  const bool band = (n_end < n_real || nc <= KM) && n_end <= 2 * KH;
   if (valid && h == 0) {
     if (certified) {
       for (int hh = 0; hh < gq; ++hh) {
@@ -779,6 +862,14 @@ __attribute__((amdgpu_waves_per_eu(SHARED ? 1 : 3, SHARED ? 2 : 3))) void gate_t
         o[KH] = (int32_t)c;
         for (int a = KH + 1; a < k; ++a) o[a] = -1;
       }
+    } else if (band) {
+      out[0] = kBand - ((n_in << 8) | n_end);  // gate_refine writes the pair's rows
+#pragma unroll
+      for (int t = 0; t < KM; t += 2)
+        if (t < n_end)
+          out[1 + t / 2] = (int32_t)((uint32_t)idx[t] |
+                                     ((t + 1 < n_end ? (uint32_t)idx[t + 1 < KM ? t + 1 : t] : 0u)
+                                      << 16));
     } else {
       out[0] = kRefine;  // gate_refine writes the pair's rows
     }
@@ -842,12 +933,13 @@ template <bool SHARED>
 hipError_t launch_fast(const Prob& P, const Blocks& T, const void* Q, const uint16_t* planes,
                        const float* maxnorm, const double* kbarT, int64_t nhp, int32_t* sel,
                        hipStream_t s) {
-  // list length: the k-1 kept blocks plus the best one left out
+  // list length: the k-1 kept blocks plus the best one left out, and two
+  // more where the sorting networks cost the same, so that the undecided
+  // blocks of an uncertified row usually fit in the list (a band record)
   const int need = P.KH + 1;
 #define MOBA_FAST(KM) launch_km<KM, SHARED>(P, T, Q, planes, maxnorm, kbarT, nhp, sel, s)
-  if (need <= 4) return MOBA_FAST(4);
-  if (need <= 8) return MOBA_FAST(8);
-  if (need <= 12) return MOBA_FAST(12);
+  if (need <= 6) return MOBA_FAST(6);
+  if (need <= 14) return MOBA_FAST(14);
   if (need <= 16) return MOBA_FAST(16);
   return MOBA_FAST(32);
 #undef MOBA_FAST
