@@ -29,6 +29,14 @@ constexpr int kScanRowGroups = 16;
 // s < k-1 (the row's own block, always its largest, and -1 pads are not).
 __device__ inline bool hist_entry(int32_t b, int64_t c) { return b >= 0 && b < c; }
 
+// The KH history slots of one selection row into registers, every load
+// issued before any value is used (one memory latency per row, not KH).
+__device__ inline void load_row(const int32_t* __restrict__ row, int KH,
+                                int32_t (&bs)[kMaxTopk]) {
+#pragma unroll
+  for (int s = 0; s < kMaxTopk; ++s) bs[s] = s < KH ? row[s] : -1;
+}
+
 // Chunk of rows and KV head of workgroup w (1-D grid of ceil(nchunk / 8) * 8
 // * Hkv). Workgroup w runs on XCD w % 8; in each run of 8 * Hkv workgroups
 // XCD x takes the Hkv heads of chunk 8 * run + x, so the workgroups that
@@ -60,11 +68,11 @@ __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restri
     if (r >= N) break;
     const int h = g * G + pi % G;
     const int64_t c = row_blk[r];
-    const int32_t* row = sel + ((size_t)r * Hq + h) * k;
-    for (int s = 0; s < KH; ++s) {
-      const int32_t b = row[s];
-      if (hist_entry(b, c)) atomicAdd(&hist[b], 1);
-    }
+    int32_t bs[kMaxTopk];
+    load_row(sel + ((size_t)r * Hq + h) * k, KH, bs);
+#pragma unroll
+    for (int s = 0; s < kMaxTopk; ++s)
+      if (s < KH && hist_entry(bs[s], c)) atomicAdd(&hist[bs[s]], 1);
   }
   __syncthreads();
   int32_t* out = chunk_base + ((size_t)g * nchunk + chunk) * nh;
@@ -170,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
   const int h0 = g0 * G;
   const int64_t Hs = (int64_t)(Hkv - g0 < kvpp ? Hkv - g0 : kvpp) * G;
   const int64_t nw = nh * ws;
-  uint32_t* pre = bm + nw;  // pre[b][w] = entries of bin b in words 0..w-1
+  uint32_t* pre = bm + nw;  // pre[b][w] = where the entries of bin b in word w start
   for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
   __syncthreads();
   const int KH = k - 1;
@@ -180,36 +188,39 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     if (r >= N) break;
     const int h = g * G + pi % G;
     const int64_t c = row_blk[r];
-    const int32_t* row = sel + ((size_t)r * Hq + h) * k;
-    for (int s = 0; s < KH; ++s) {
-      const int32_t b = row[s];
-      if (hist_entry(b, c)) atomicOr(&bm[(size_t)b * ws + (pi >> 5)], 1u << (pi & 31));
-    }
+    int32_t bs[kMaxTopk];
+    load_row(sel + ((size_t)r * Hq + h) * k, KH, bs);
+#pragma unroll
+    for (int s = 0; s < kMaxTopk; ++s)
+      if (s < KH && hist_entry(bs[s], c))
+        atomicOr(&bm[(size_t)bs[s] * ws + (pi >> 5)], 1u << (pi & 31));
   }
   __syncthreads();
+  const int32_t* cb = chunk_base + ((size_t)g * nchunk + chunk) * nh;
+  const int32_t* bo = bin_off + (size_t)g * nh;
   for (int64_t b = threadIdx.x; b < nh; b += kThreads) {
-    uint32_t run = 0;
+    uint32_t run = (uint32_t)(bo[b] + cb[b]);  // the chunk's first entry of bin b
     for (int w = 0; w < words; ++w) {
       pre[b * ws + w] = run;
       run += __popc(bm[b * ws + w]);
     }
   }
   __syncthreads();
-  const int32_t* cb = chunk_base + ((size_t)g * nchunk + chunk) * nh;
-  const int32_t* bo = bin_off + (size_t)g * nh;
   for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
     const int64_t c = row_blk[r];
-    const int32_t* row = sel + ((int64_t)r * Hq + h) * k;
+    int32_t bs[kMaxTopk];
+    load_row(sel + ((int64_t)r * Hq + h) * k, KH, bs);
     const int64_t pslot = ((int64_t)r * Hs + (h - h0)) * KH;
-    for (int s = 0; s < KH; ++s) {
-      const int32_t b = row[s];
-      if (!hist_entry(b, c)) continue;
+#pragma unroll
+    for (int s = 0; s < kMaxTopk; ++s) {
+      const int32_t b = bs[s];
+      if (s >= KH || !hist_entry(b, c)) continue;
       const size_t wi = (size_t)b * ws + (pi >> 5);
-      const int rank = (int)pre[wi] + __popc(bm[wi] & ((1u << (pi & 31)) - 1u));
-      entries[(size_t)bo[b] + cb[b] + rank] = (uint32_t)(pslot + s);
+      const uint32_t at = pre[wi] + __popc(bm[wi] & ((1u << (pi & 31)) - 1u));
+      entries[at] = (uint32_t)(pslot + s);
     }
   }
 }

@@ -608,6 +608,26 @@ def test_shared_fast_tier_equals_exact_tier():
                     ctx=(q, k, B, rows, heads, oracle.ROUTING_SHARED))
 
 
+@pytest.mark.parametrize("topk,integer", [(3, False), (8, False), (12, False), (12, True),
+                                           (16, False), (17, False)])
+def test_fast_tier_equals_exact_tier(topk, integer):
+    """Per-head routing: the fast tier with its exact tier for uncertified rows
+    (re-scoring either the whole row or only the undecided band of the fast
+    list) must select exactly what the exact tier selects when it ranks every
+    row. List lengths 6, 14, 16 and 32; integer data gives many exact ties."""
+    N, Hq, Hkv, B = 16384, 8, 2, 64
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=31 + topk, integer=integer)
+    fast = moba.select(tq, tk, B, topk).cpu().numpy()
+    exact = moba.routing_stats(tq, tk, B, topk)["sel"].cpu().numpy()
+    assert np.array_equal(fast, exact)
+    rng = np.random.default_rng(topk)
+    rows = np.sort(rng.choice(N, 256, replace=False))
+    heads = rng.integers(0, Hq, size=rows.size)
+    ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False)
+    check_selection(fast[rows, heads], ref_sel, gap, "fast tier",
+                    ctx=(q, k, B, rows, heads, 0))
+
+
 @pytest.mark.parametrize("kind", ["zero_k", "integer"])
 def test_shared_routing_ties_are_exact(kind):
     """Exact ties in the group score (all-zero keys, or integer data) must go
