@@ -381,8 +381,8 @@ typedef __bf16 b8 __attribute__((ext_vector_type(8)));
 // (normalised rows po[s], log2-sum-exps lse[s]) by PaperTrace "2.1.3 MoBA"
 // eqs. (7)-(8). NH >= nhist is a compile-time bound so the loads of a group
 // of partials of all R pairs are in flight before their values are used;
-// indices past nhist are clamped, so every load stays inside the pair's own
-// partials.
+// slots past nhist are not loaded (they count as log2-sum-exp -inf, weight
+// 0), so every load reads one of the pair's own partials once.
 template <int NH, int R>
 __device__ inline void merge_rows(const h8 (&own)[R], const float (&own_lse)[R],
                                   const float* const (&lse_src)[R],
@@ -393,13 +393,13 @@ __device__ inline void merge_rows(const h8 (&own)[R], const float (&own_lse)[R],
 #pragma unroll
   for (int i = 0; i < R; ++i)
 #pragma unroll
-    for (int s = 0; s < NH; ++s) lse[i][s] = lse_src[i][s < nhist ? s : nhist - 1];
+    for (int s = 0; s < NH; ++s) lse[i][s] = s < nhist ? lse_src[i][s] : -INFINITY;
   float M[R], L[R], acc[R][8];
 #pragma unroll
   for (int i = 0; i < R; ++i) {
     M[i] = own_lse[i];
 #pragma unroll
-    for (int s = 0; s < NH; ++s) M[i] = fmaxf(M[i], lse[i][s]);  // clamped copies repeat a real value
+    for (int s = 0; s < NH; ++s) M[i] = fmaxf(M[i], lse[i][s]);  // slots past nhist hold -inf
     L[i] = __builtin_amdgcn_exp2f(own_lse[i] - M[i]);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[i][e] = L[i] * (float)own[i][e];
@@ -412,8 +412,9 @@ __device__ inline void merge_rows(const h8 (&own)[R], const float (&own_lse)[R],
     for (int i = 0; i < R; ++i)
 #pragma unroll
       for (int j = 0; j < GRP; ++j) {
-        const int sj = s0 + j < nhist ? s0 + j : nhist - 1;
-        v[i][j] = *reinterpret_cast<const h8*>(po_src[i] + (size_t)sj * kHeadDim + 8 * c16);
+        v[i][j] = s0 + j < nhist
+                      ? *reinterpret_cast<const h8*>(po_src[i] + (size_t)(s0 + j) * kHeadDim + 8 * c16)
+                      : h8{};
       }
 #pragma unroll
     for (int i = 0; i < R; ++i)
