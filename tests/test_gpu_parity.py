@@ -323,15 +323,16 @@ def test_integer_ties_are_exact():
     assert np.array_equal(sel, ref_sel)
 
 
-@pytest.mark.parametrize("B", [128, 256])
+@pytest.mark.parametrize("B", [128, 256, 512])
 def test_softmax_overflow_rerun(B):
     """Spike keys past each block's first 32 keys score ~200 (log2 units) above
     the rest, beyond the 2^64 headroom of the fixed reference maximum and
     beyond fp32's range: the attention kernels must re-run those blocks from
     the true maxima (history and own block alike), else weights overflow to
     infinity. B = 128 runs the 32-query history engine (in-kernel re-run),
-    B = 256 the 64-query one (tiles listed and recomputed by a second
-    kernel)."""
+    B = 256 and 512 the 64-query one (tiles listed and recomputed by a second
+    kernel); the own-block kernel re-runs its workgroups in place, at B = 512
+    also those whose unmasked keys span several tiles."""
     N, Hq, Hkv, topk = 2048, 2, 1, 3
     q, k, v, _, _, _ = small(N, Hq, Hkv, B, topk, seed=41)
     u = np.random.default_rng(41).standard_normal(128)
