@@ -23,6 +23,11 @@ namespace moba {
 namespace {
 
 constexpr int kThreads = 256;
+// Count and scatter: 8 waves per workgroup, so with two workgroups' bitmaps
+// in a compute unit's LDS 16 waves keep its selection-row loads in flight
+// (4 waves per workgroup: 3.46 ms for the stage at the 1M-token layer, 8:
+// 3.27 ms, 16: 3.73 ms).
+constexpr int kRowThreads = 512;
 constexpr int kScanRowGroups = 16;
 
 // Valid history entry of a selection row of block c: a block b < c at slot
@@ -49,7 +54,7 @@ __device__ inline bool chunk_of(int64_t w, int Hkv, int64_t nchunk, int64_t& chu
   return chunk < nchunk;
 }
 
-__global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restrict__ sel,
+__global__ __launch_bounds__(kRowThreads) void bucket_count(const int32_t* __restrict__ sel,
                                                          const int32_t* __restrict__ row_blk,
                                                          int32_t* __restrict__ chunk_base,
                                                          int64_t N, int Hq, int G, int k,
@@ -59,11 +64,11 @@ __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restri
   int g;
   int64_t chunk;
   if (!chunk_of(blockIdx.x, Hkv, nchunk, chunk, g)) return;
-  for (int64_t b = threadIdx.x; b < nh; b += kThreads) hist[b] = 0;
+  for (int64_t b = threadIdx.x; b < nh; b += kRowThreads) hist[b] = 0;
   __syncthreads();
   const int KH = k - 1;
   const int npairs = rows_per_chunk * G;
-  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+  for (int pi = threadIdx.x; pi < npairs; pi += kRowThreads) {
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
@@ -76,7 +81,7 @@ __global__ __launch_bounds__(kThreads) void bucket_count(const int32_t* __restri
   }
   __syncthreads();
   int32_t* out = chunk_base + ((size_t)g * nchunk + chunk) * nh;
-  for (int64_t b = threadIdx.x; b < nh; b += kThreads) out[b] = hist[b];
+  for (int64_t b = threadIdx.x; b < nh; b += kRowThreads) out[b] = hist[b];
 }
 
 // Column-wise exclusive scan of chunk_base over chunks; 16 columns per
@@ -160,7 +165,7 @@ __global__ __launch_bounds__(1024) void bucket_scan_bins(const int32_t* __restri
   }
 }
 
-__global__ __launch_bounds__(kThreads) void bucket_scatter(
+__global__ __launch_bounds__(kRowThreads) void bucket_scatter(
     const int32_t* __restrict__ sel, const int32_t* __restrict__ row_blk,
     const int32_t* __restrict__ chunk_base, const int32_t* __restrict__ bin_off,
     uint32_t* __restrict__ entries, int64_t N, int Hq, int Hkv, int G, int k, int64_t nh,
@@ -179,11 +184,11 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
   const int64_t Hs = (int64_t)(Hkv - g0 < kvpp ? Hkv - g0 : kvpp) * G;
   const int64_t nw = nh * ws;
   uint32_t* pre = bm + nw;  // pre[b][w] = where the entries of bin b in word w start
-  for (int64_t i = threadIdx.x; i < nw; i += kThreads) bm[i] = 0u;
+  for (int64_t i = threadIdx.x; i < nw; i += kRowThreads) bm[i] = 0u;
   __syncthreads();
   const int KH = k - 1;
   const int npairs = rows_per_chunk * G;
-  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+  for (int pi = threadIdx.x; pi < npairs; pi += kRowThreads) {
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
@@ -198,7 +203,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
   __syncthreads();
   const int32_t* cb = chunk_base + ((size_t)g * nchunk + chunk) * nh;
   const int32_t* bo = bin_off + (size_t)g * nh;
-  for (int64_t b = threadIdx.x; b < nh; b += kThreads) {
+  for (int64_t b = threadIdx.x; b < nh; b += kRowThreads) {
     uint32_t run = (uint32_t)(bo[b] + cb[b]);  // the chunk's first entry of bin b
     for (int w = 0; w < words; ++w) {
       pre[b * ws + w] = run;
@@ -206,7 +211,7 @@ __global__ __launch_bounds__(kThreads) void bucket_scatter(
     }
   }
   __syncthreads();
-  for (int pi = threadIdx.x; pi < npairs; pi += kThreads) {
+  for (int pi = threadIdx.x; pi < npairs; pi += kRowThreads) {
     const int64_t r = chunk * rows_per_chunk + pi / G;
     if (r >= N) break;
     const int h = g * G + pi % G;
@@ -264,7 +269,7 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
     return e;
   }
   const unsigned grid = (unsigned)(ceil_div(bp.nchunk, 8) * 8 * P.Hkv);
-  bucket_count<<<grid, kThreads, sizeof(int32_t) * P.nh, s>>>(
+  bucket_count<<<grid, kRowThreads, sizeof(int32_t) * P.nh, s>>>(
       sel, T.row_blk, b.chunk_base, P.Nq, P.Hq, P.G, P.k, P.nh, bp.rows_per_chunk, bp.nchunk,
       P.Hkv);
   hipError_t e = hipGetLastError();
@@ -275,7 +280,7 @@ hipError_t launch_bucket(const Prob& P, const Blocks& T, const BucketPlan& bp, c
   bucket_scan_bins<<<1, 1024, 0, s>>>(b.bin_total, b.bin_off, b.tile_off, b.scalars, bp.nbins,
                                       kTileQ);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  bucket_scatter<<<grid, kThreads, 2 * sizeof(uint32_t) * P.nh * bp.ws, s>>>(
+  bucket_scatter<<<grid, kRowThreads, 2 * sizeof(uint32_t) * P.nh * bp.ws, s>>>(
       sel, T.row_blk, b.chunk_base, b.bin_off, b.entries, P.Nq, P.Hq, P.Hkv, P.G, P.k, P.nh,
       bp.rows_per_chunk, bp.nchunk, bp.words, bp.ws, P.kvpp);
   if ((e = hipGetLastError()) != hipSuccess) return e;
