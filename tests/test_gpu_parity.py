@@ -629,6 +629,23 @@ def test_fast_tier_equals_exact_tier(topk, integer):
                     ctx=(q, k, B, rows, heads, 0))
 
 
+def test_fast_tier_at_the_history_block_limit():
+    """8192 history blocks, the most the library takes: block indices need 13
+    of the fast tier's key bits (so its truncation margin is widest and many
+    rows go to the exact tier) and band records carry indices up to 8191."""
+    N, Hq, Hkv, B, topk = 8193 * 16, 2, 1, 16, 12
+    q, k, v, tq, tk, tv = small(N, Hq, Hkv, B, topk, seed=77)
+    fast = moba.select(tq, tk, B, topk).cpu().numpy()
+    exact = moba.routing_stats(tq, tk, B, topk)["sel"].cpu().numpy()
+    assert np.array_equal(fast, exact)
+    rng = np.random.default_rng(77)
+    rows = np.sort(np.concatenate([rng.choice(N - 64, 190, replace=False), np.arange(N - 64, N)]))
+    heads = rng.integers(0, Hq, size=rows.size)
+    ref_sel, _, gap = oracle.rows(q, k, None, B, topk, rows, heads, want_o=False)
+    check_selection(fast[rows, heads], ref_sel, gap, "fast tier, 8192 blocks",
+                    ctx=(q, k, B, rows, heads, 0))
+
+
 @pytest.mark.parametrize("kind", ["zero_k", "integer"])
 def test_shared_routing_ties_are_exact(kind):
     """Exact ties in the group score (all-zero keys, or integer data) must go
