@@ -152,6 +152,19 @@ __device__ inline int key_block(uint32_t k, int ib) {
   return (int)(low - (k & low));
 }
 
+// Batcher's odd-even merge sort of 16 keys (63 compare-exchanges, against 80
+// for the bitonic sort): larger key to the lower position, so the keys end
+// in descending order (checked on the host for all 2^16 0-1 inputs, which
+// by the 0-1 principle covers every input).
+constexpr int kOddEven16[63][2] = {
+    {0, 1}, {2, 3}, {4, 5}, {6, 7}, {8, 9}, {10, 11}, {12, 13}, {14, 15}, {0, 2}, {1, 3}, {4,
+    6}, {5, 7}, {8, 10}, {9, 11}, {12, 14}, {13, 15}, {1, 2}, {5, 6}, {9, 10}, {13, 14}, {0, 4},
+    {1, 5}, {2, 6}, {3, 7}, {8, 12}, {9, 13}, {10, 14}, {11, 15}, {2, 4}, {3, 5}, {10, 12}, {11,
+    13}, {1, 2}, {3, 4}, {5, 6}, {9, 10}, {11, 12}, {13, 14}, {0, 8}, {1, 9}, {2, 10}, {3, 11},
+    {4, 12}, {5, 13}, {6, 14}, {7, 15}, {4, 8}, {5, 9}, {6, 10}, {7, 11}, {2, 4}, {3, 5}, {6,
+    8}, {7, 9}, {10, 12}, {11, 13}, {1, 2}, {3, 4}, {5, 6}, {7, 8}, {9, 10}, {11, 12}, {13, 14},
+};
+
 template <int KM>
 struct KeyList {
   uint32_t k[KM];  // descending
@@ -193,7 +206,7 @@ struct KeyList {
 #pragma unroll
     for (int t = 0; t < KM; ++t) k[t] = m[PADS + t];
   }
-  // Add 16 keys at once: sort them descending with a bitonic network; then
+  // Add 16 keys at once: sort them descending (odd-even merge sort); then
   // m_t = max(k[t], c[KM-1-t]) is exactly the top KM of both lists (two
   // sorted lists, one read backwards) and is decreasing-then-increasing, so
   // with maximal keys appended it is bitonic and one bitonic merge of P =
@@ -201,19 +214,12 @@ struct KeyList {
   // dropped. Same result as 16 push() calls, in fewer operations.
   __device__ inline void push16(uint32_t (&c)[16]) {
 #pragma unroll
-    for (int size = 2; size <= 16; size <<= 1)
-#pragma unroll
-      for (int stride = size >> 1; stride > 0; stride >>= 1)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int j = i ^ stride;
-          if (j > i) {
-            const uint32_t hi = c[i] > c[j] ? c[i] : c[j], lo = c[i] > c[j] ? c[j] : c[i];
-            const bool desc = (i & size) == 0;  // the last stage sorts all 16 descending
-            c[i] = desc ? hi : lo;
-            c[j] = desc ? lo : hi;
-          }
-        }
+    for (int q = 0; q < 63; ++q) {
+      const int i = kOddEven16[q][0], j = kOddEven16[q][1];
+      const uint32_t hi = c[i] > c[j] ? c[i] : c[j], lo = c[i] > c[j] ? c[j] : c[i];
+      c[i] = hi;
+      c[j] = lo;
+    }
     constexpr int P = KM < 8 ? 8 : KM < 16 ? 16 : KM < 32 ? 32 : 64;  // room for >= 1 pad
     constexpr int PADS = P - KM;
     uint32_t m[P];
@@ -241,14 +247,28 @@ struct KeyList {
 };
 
 // out[0..n) = the n block indices of idx[0..n) in ascending order (n <= KM,
-// indices distinct): a bitonic sorting network over the next power of two,
-// entries past n padded with INT_MAX (they sort last and are not written).
+// indices distinct): a sorting network over the next power of two (16: the
+// odd-even one above; else bitonic), entries past n padded with INT_MAX
+// (they sort last and are not written).
 template <int KM>
 __device__ inline void write_sorted(const int (&idx)[KM], int n, int32_t* out) {
   constexpr int P = KM <= 4 ? 4 : KM <= 8 ? 8 : KM <= 16 ? 16 : 32;
   int a[P];
 #pragma unroll
   for (int t = 0; t < P; ++t) a[t] = (t < KM && t < n) ? idx[t < KM ? t : 0] : 0x7FFFFFFF;
+  if constexpr (P == 16) {  // the odd-even network, smaller index to the lower position
+#pragma unroll
+    for (int q = 0; q < 63; ++q) {
+      const int i = kOddEven16[q][0], j = kOddEven16[q][1];
+      const int lo = a[i] < a[j] ? a[i] : a[j], hi = a[i] < a[j] ? a[j] : a[i];
+      a[i] = lo;
+      a[j] = hi;
+    }
+#pragma unroll
+    for (int t = 0; t < KM; ++t)
+      if (t < n) out[t] = a[t];
+    return;
+  }
 #pragma unroll
   for (int size = 2; size <= P; size <<= 1)
 #pragma unroll
