@@ -138,7 +138,8 @@ __global__ __launch_bounds__(256) void kbar_maxnorm(const float* __restrict__ no
 // ---------------------------------------------------------------------------
 __device__ inline uint32_t score_key(float x, int block, int ib) {
   const uint32_t u = __float_as_uint(x);
-  const uint32_t k = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: every bit flipped; otherwise the sign bit set (one bitwise op)
+  const uint32_t k = u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
   const uint32_t low = (1u << ib) - 1u;
   return (k & ~low) | (low - (uint32_t)block);
 }
