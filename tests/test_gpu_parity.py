@@ -157,6 +157,9 @@ def test_prefill_llama8b_1m_sampled():
     ref_sel, _, gap = oracle.rows(q, k, None, w.B, w.k, r2, h2, want_o=False, kbar=kbar)
     check_selection(sel_np[r2, h2], ref_sel, gap, "llama8b_1m sel",
                     ctx=(q, k, w.B, r2, h2, oracle.ROUTING_PER_HEAD))
+    # every row: the fast tier (with band records) against the exact tier alone
+    exact = moba.routing_stats(tq, tk, w.B, w.k)["sel"]
+    assert torch.equal(sel, exact)
     print(f"llama8b_1m: max|dO| {mx:.2e} mean {mean:.2e} tie-excused rows {tied}")
 
 
